@@ -1,0 +1,242 @@
+"""Decode-step benchmark of retrieval-sparse paged decode attention on one GPU.
+
+A step is one layer's decode step for the whole batch: rkv_append_kv (write
+the token, and a just-completed block's representation) -> rkv_select
+(inner-product scores, per-(sequence, KV head) top-k, merged block table)
+-> rkv_decode_attn (split-K paged attention + log-sum-exp combine).
+Inputs are synthetic and already resident in HBM when timing starts.
+
+Consecutive steps cycle over `--layers` independent copies of the layer's
+KV cache (as a model's layers would), so a step never finds the previous
+step's pages in the 256 MB Infinity Cache.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from sparse_retrieval_kv_amd import binding as B  # noqa: E402
+from sparse_retrieval_kv_amd import synth  # noqa: E402
+from sparse_retrieval_kv_amd.decode import DecodeSession  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode attn steps/s and attended-KV HBM GB/s (% of peak) at 64K-128K ctx, 1 GPU"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def step_bytes(spec, context, t):
+    """Algorithmic bytes of one step: attended K+V (bf16) per (sequence, KV
+    head) plus the fp32 representations the scorer reads."""
+    kv = reps = 0
+    for L0 in context:
+        L = int(L0) + t
+        nb = -(-L // 128)
+        n_init = min(-(-spec.init_tokens // 128), nb)
+        ls = min(max(L - spec.local_tokens, 0) // 128, nb - 1)
+        n_off = max(ls - n_init, 0)
+        dense = L0 < spec.dense_boundary or spec.topk_ppm >= 1_000_000
+        k = n_off if dense else -(-(n_off * spec.topk_ppm) // 1_000_000)
+        n_merged = n_init + k + (nb - max(ls, n_init))
+        tokens = 128 * (n_merged - 1) + (L - 128 * (nb - 1))
+        kv += tokens * 128 * 2 * 2
+        if not dense and 0 < k < n_off:
+            reps += n_off * 128 * 4
+    return kv * spec.n_kv_heads, reps * spec.n_kv_heads
+
+
+def cpu_baseline(batch, budget_s=12.0, max_steps=8):
+    """Time the float64 oracle's decode step on the host over a bounded
+    sample of the same workload (first sequences of the batch)."""
+    import oracle as O
+    spec = batch.spec
+    G = spec.group
+    prm = O.Params(spec.n_q_heads, spec.n_kv_heads, spec.init_tokens,
+                   spec.local_tokens, spec.topk_ppm, spec.dense_boundary)
+    b = 0
+    L0 = int(batch.context[b])
+    nb = -(-(L0 + spec.steps - 1) // 128)
+    pages = torch.as_tensor(batch.table_np[b, :nb].astype(np.int64),
+                            device=batch.k_pages.device)
+    kp = batch.k_pages.index_select(0, pages).cpu().numpy().view(np.uint16)
+    vp = batch.v_pages.index_select(0, pages).cpu().numpy().view(np.uint16)
+    K, V = O.logical_kv(kp, vp, np.arange(nb), L0 + spec.steps - 1)
+    reps = np.stack([O.block_reps(K[h]) for h in range(spec.n_kv_heads)])
+    n = 0
+    t0 = time.perf_counter()
+    while n < max_steps and time.perf_counter() - t0 < budget_s:
+        t = n % spec.steps
+        q = O.bf16_to_f64(batch.q_bits(t)[b].cpu().numpy().view(np.uint16))
+        O.decode_step(q, K, V, L0 + t, L0, prm, reps=reps)
+        n += 1
+    dt = time.perf_counter() - t0
+    threads = torch.get_num_threads()
+    # one sequence of the batch per oracle step -> scale to batch steps
+    seq_steps_per_s = n / dt
+    return {
+        "value": seq_steps_per_s / spec.batch,
+        "unit": "steps/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{n} oracle decode steps of sequence 0 ({L0} tokens, "
+                   f"{spec.n_q_heads}/{spec.n_kv_heads} heads, float64 NumPy, "
+                   f"representations precomputed), {dt:.1f} s; value = "
+                   f"sequence-steps/s / batch {spec.batch}"),
+        "host": platform.processor() or platform.machine(),
+        "nproc": os.cpu_count(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4])
+    ap.add_argument("--layers", type=int, default=0,
+                    help="KV-cache copies cycled over (0: enough to exceed 1 GiB)")
+    ap.add_argument("--impl", default="auto", choices=["auto", "mfma", "valu"])
+    ap.add_argument("--split", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "this path has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B.lib()
+
+    spec = synth.CONFIGS[args.config]
+    log("config", args.config, spec.name)
+    base = synth.make_batch(spec, dev)
+    layer_bytes = 2 * base.k_pages.numel() * 2
+    n_layers = args.layers or max(1, min(16, math.ceil((1 << 30) / layer_bytes)))
+    impl = {"auto": B.ATTN_AUTO, "mfma": B.ATTN_MFMA, "valu": B.ATTN_VALU}[args.impl]
+    prm = B.params(spec.n_q_heads, spec.n_kv_heads, init_tokens=spec.init_tokens,
+                   local_tokens=spec.local_tokens, topk_ppm=spec.topk_ppm,
+                   dense_boundary=spec.dense_boundary, attn_impl=impl,
+                   split_blocks=args.split)
+    ctx = torch.as_tensor(base.context.astype(np.int32), device=dev)
+    sessions = []
+    for layer in range(n_layers):
+        kp = base.k_pages if layer == 0 else base.k_pages.clone()
+        vp = base.v_pages if layer == 0 else base.v_pages.clone()
+        s = DecodeSession(prm, kp, vp, base.block_table, ctx)
+        s.build_reps(ctx - 1)
+        sessions.append(s)
+    log(f"{n_layers} layer copies, {layer_bytes / 2**20:.0f} MiB each")
+
+    T = spec.steps
+    qs = [base.q_bits(t) for t in range(T)]
+    news = [base.new_kv_bits(t) for t in range(T)]
+    lens = [torch.as_tensor(base.lens_at(t), device=dev) for t in range(T)]
+    torch.cuda.synchronize()
+
+    def run(s_idx, ev=None):
+        layer = s_idx % n_layers
+        t = (s_idx // n_layers) % T
+        sess = sessions[layer]
+        kn, vn = news[t]
+        sess.append(kn, vn, lens[t])
+        sess.select(qs[t], lens[t])
+        if ev is not None:
+            ev[0].record()
+        sess.attend(qs[t], lens[t])
+        if ev is not None:
+            ev[1].record()
+        return t
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done; timing {args.steps} steps")
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    ts = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ts.append(run(args.warmup + i, evs[i]))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ms_per_step = wall * 1e3 / args.steps
+
+    kv_b = np.array([step_bytes(spec, base.context, t)[0] for t in ts], dtype=np.float64)
+    rep_b = np.array([step_bytes(spec, base.context, t)[1] for t in ts], dtype=np.float64)
+    step_gbs = (kv_b.sum() + rep_b.sum()) / wall / 1e9
+    attn_gbs = kv_b.sum() / (attn_ms.sum() * 1e-3) / 1e9
+    log(f"{ms_per_step * 1e3:.1f} us/step, attention {attn_ms.mean() * 1e3:.1f} us "
+        f"avg ({attn_gbs:.0f} GB/s), step-level {step_gbs:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(base)
+
+    res = {
+        "metric": METRIC,
+        "value": args.steps / wall,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 K/V/q, fp32 accumulate",
+        "data": "synthetic (seeded N(0,1) bf16 K/V/q, planted blocks per config)",
+        "config": {
+            "workload": spec.name,
+            "config_id": args.config,
+            "batch": spec.batch,
+            "context": [int(x) for x in base.context[:4]],
+            "heads_q_kv": [spec.n_q_heads, spec.n_kv_heads],
+            "init_local_topk_ppm": [spec.init_tokens, spec.local_tokens, spec.topk_ppm],
+            "layer_copies": n_layers,
+            "attn_impl": args.impl,
+            "split_blocks": args.split,
+        },
+        "attended_kv_gbs_step": step_gbs,
+        "attended_kv_pct_peak_step": 100.0 * step_gbs / HBM_PEAK_GBS,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "rkv_decode_attn (split-K partials + combine)",
+            "achieved": attn_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": attn_gbs / HBM_PEAK_GBS,
+            "traffic": None,
+            "bytes_per_launch": float(kv_b.mean()),
+            "avg_launch_us": float(attn_ms.mean() * 1e3),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

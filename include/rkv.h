@@ -1,0 +1,241 @@
+/*
+ * rkv.h -- C ABI of the retrieval-sparse paged decode attention library
+ * for AMD MI355X (gfx950).
+ *
+ * The method (openGauss DataVec docs, "KV Cache Query-Based Computation
+ * Inference Acceleration", section "Overall Solution"): each sequence's KV
+ * cache is split into initial tokens, a sliding window and offload tokens;
+ * every offload block of 128 tokens carries one key representation vector per
+ * KV head; at each decode step the current query is scored against those
+ * representations by inner product, the top ceil(ratio * n_offload) blocks are
+ * kept, and softmax(q K^T / sqrt(d)) V runs over the initial, window and kept
+ * blocks only.  The defaults come from the same page, section "Configuration
+ * Parameters".  Paged K/V read through a block table follows the rkmt.cn ATB
+ * KV-cache article, section 2.2 (PageAttention with a page table).
+ *
+ * Conventions shared by every call:
+ *  - Pointers are DEVICE pointers unless a parameter says "host".  The caller
+ *    owns every buffer; the library allocates nothing and keeps no state
+ *    between calls except the calling thread's last error text.
+ *  - bf16 values travel as their 16-bit patterns (uint16_t).
+ *  - All work is enqueued asynchronously on the given HIP stream; a call
+ *    returns once the work is enqueued.  Arguments are validated on the host
+ *    first: on any error status nothing is enqueued.
+ *  - Outputs must not alias inputs.
+ *  - Device-side values (lengths, page ids, counts) are clamped into range
+ *    by the kernels so that bad values never cause an out-of-bounds access:
+ *    a length above max_blocks * 128 is treated as max_blocks * 128, a
+ *    negative length as 0, and a page id outside [0, n_pages) makes its block
+ *    contribute nothing.
+ *
+ * Memory layouts (part of the ABI):
+ *  - k_pages: [n_pages][n_kv_heads][128 tokens][128 dims] bf16.  Each
+ *    (page, head) slice is one contiguous 32 KiB tile, token-major.
+ *  - v_pages: [n_pages][n_kv_heads][128 dims][128 tokens] bf16.  Each
+ *    (page, head) slice is one contiguous 32 KiB tile, dim-major (the value
+ *    tile is stored transposed so that the attention kernel reads the same
+ *    token range of one dimension as 16 contiguous bytes).
+ *  - block_table: [batch][max_blocks] int32, logical block -> page id.
+ *  - lens: [batch] int32, current length L_b of each sequence, counting the
+ *    token being decoded.
+ *  - q: [batch][n_q_heads][128] bf16.  Query head g belongs to KV head
+ *    g / (n_q_heads / n_kv_heads) (contiguous groups, as in grouped-query
+ *    attention; CSDN "KV cache" survey, section "Share--KV cache共享").
+ *  - reps: [batch][n_kv_heads][max_blocks][128] fp32, logical-indexed.
+ *  - out: [batch][n_q_heads][128] fp32.
+ */
+#ifndef RKV_H
+#define RKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RKV_ABI_VERSION 1
+#define RKV_BLOCK_SIZE 128
+#define RKV_HEAD_DIM 128
+#define RKV_PPM_ONE 1000000
+#define RKV_MAX_GROUP 16        /* query heads per KV head */
+#define RKV_MAX_BLOCKS 8192     /* blocks per sequence (1M tokens) */
+
+typedef enum rkv_status {
+  RKV_OK = 0,
+  RKV_ERR_INVALID_ARG = 1,  /* null pointer, negative size, bad value */
+  RKV_ERR_UNSUPPORTED = 2,  /* block/head size != 128, group > 16, ... */
+  RKV_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
+  RKV_ERR_HIP = 4           /* a HIP launch or copy failed; see rkv_last_error */
+} rkv_status;
+
+/* Attention kernel variants. */
+#define RKV_ATTN_AUTO 0
+#define RKV_ATTN_MFMA 1   /* query heads of a group packed against K tiles */
+#define RKV_ATTN_VALU 2   /* vector-ALU dot products, same memory schedule */
+
+/*
+ * Method parameters.  Names follow the page's environment variables
+ * (openGauss page, "Configuration Parameters").
+ */
+typedef struct rkv_params {
+  int32_t block_size;      /* tokens per block; must be 128 */
+  int32_t head_dim;        /* must be 128 */
+  int32_t n_q_heads;       /* > 0, multiple of n_kv_heads */
+  int32_t n_kv_heads;      /* > 0; n_q_heads / n_kv_heads <= 16 */
+  int32_t init_tokens;     /* VLLM_RETRIEVAL_INIT_TOKENS_NUM, default 1024, >= 0 */
+  int32_t local_tokens;    /* VLLM_RETRIEVAL_LOCAL_TOKENS_NUM, default 7192, >= 0 */
+  int32_t topk_ppm;        /* VLLM_RETRIEVAL_TOPK_PERCENT in parts per million,
+                              default 200000 (0.2); 0 .. 1000000 */
+  int32_t dense_boundary;  /* VLLM_RETRIEVAL_DENSE_BOUNDARY, default 32768;
+                              prompt_len < boundary attends to every block;
+                              0 disables the dense switch */
+  float scale;             /* softmax scale, default 1/sqrt(128) */
+  int32_t attn_impl;       /* RKV_ATTN_AUTO / _MFMA / _VALU */
+  int32_t split_blocks;    /* merged blocks per split-K work item; 0 = auto */
+} rkv_params;
+
+/* Defaults of the page (init 1024, local 7192, ratio 0.2, dense boundary
+ * 32K, block 128) for the given head counts. */
+rkv_params rkv_params_default(int32_t n_q_heads, int32_t n_kv_heads);
+
+int32_t rkv_abi_version(void);
+const char* rkv_status_string(rkv_status status);
+/* Text of the calling thread's last error ("" if none).  Valid until the
+ * thread's next failing call. */
+const char* rkv_last_error(void);
+
+/*
+ * rkv_build_reps -- block representation vectors (openGauss page, "Feature
+ * Description" and "Overall Solution": representation vectors are extracted
+ * block by block).  The representation of block j of sequence b at KV head h
+ * is the fp32 mean of the block's 128 keys:
+ *     reps[b][h][j][:] = (1/128) * sum_t K[block_table[b][j]][h][t][:]
+ * It is written for every COMPLETE block j in [block_begin[b], floor(L_b/128));
+ * the trailing partial block gets none.  Other entries of reps are untouched.
+ *   k_pages      bf16 pool, layout above; n_pages pages
+ *   block_table  [batch][max_blocks]
+ *   lens         [batch] lengths L_b
+ *   block_begin  [batch] first block to (re)build, or NULL for 0
+ *   reps         [batch][n_kv_heads][max_blocks][128] fp32 output
+ * Idempotent.  Errors: RKV_ERR_INVALID_ARG, RKV_ERR_UNSUPPORTED, RKV_ERR_HIP.
+ */
+rkv_status rkv_build_reps(const rkv_params* params, const uint16_t* k_pages,
+                          int64_t n_pages, const int32_t* block_table,
+                          int32_t max_blocks, const int32_t* lens,
+                          const int32_t* block_begin, int32_t batch,
+                          float* reps, hipStream_t stream);
+
+/*
+ * rkv_append_kv -- write the decoded token's K and V (one autoregressive
+ * step adds one token to the cache; rkmt.cn ATB article, section 1.1) into
+ * slot L_b - 1 of its page, and, when that token completes its block and
+ * reps is not NULL, write the block's representation as rkv_build_reps
+ * would.  Sequences with L_b <= 0 are skipped.
+ *   k_new, v_new [batch][n_kv_heads][128] bf16
+ *   k_pages, v_pages updated in place; reps optional (NULL: no rep)
+ * Errors: RKV_ERR_INVALID_ARG, RKV_ERR_UNSUPPORTED, RKV_ERR_HIP.
+ */
+rkv_status rkv_append_kv(const rkv_params* params, const uint16_t* k_new,
+                         const uint16_t* v_new, uint16_t* k_pages,
+                         uint16_t* v_pages, int64_t n_pages,
+                         const int32_t* block_table, int32_t max_blocks,
+                         const int32_t* lens, int32_t batch, float* reps,
+                         hipStream_t stream);
+
+/*
+ * Workspace bytes rkv_select needs for these sizes (may be 0).
+ */
+size_t rkv_select_workspace_size(const rkv_params* params, int32_t batch,
+                                 int32_t max_blocks);
+
+/*
+ * rkv_select -- inner-product retrieval and block-table merge (openGauss
+ * page, "Overall Solution": the IP between the current token's query and
+ * every representation, the top-K closest blocks, joined with the initial
+ * tokens and the sliding window).  For every (sequence b, KV head h):
+ *   nb          = ceil(L/128)
+ *   n_init      = min(ceil(init_tokens/128), nb)
+ *   local_start = min(floor(max(L - local_tokens, 0)/128), nb - 1)
+ *   offload     = blocks [n_init, local_start)  (n_off of them, maybe 0)
+ *   score s_j   = sum over the group's query heads g of q[b][g] . reps[b][h][j]
+ *   k           = n_off if prompt_len < dense_boundary or topk_ppm = 10^6,
+ *                 else ceil(n_off * topk_ppm / 10^6)
+ *   selected    = the k offload blocks with the largest s_j, ties to the
+ *                 smaller block index, written in ascending order
+ * Outputs:
+ *   sel_ids  [batch][n_kv_heads][k_cap] logical block ids (first n_sel valid)
+ *   n_sel    [batch][n_kv_heads]
+ *   merged   [batch][n_kv_heads][m_cap] PAGE ids of the attended blocks in
+ *            ascending logical order: init, selected, then local blocks
+ *            (optional: NULL skips the merge)
+ *   n_merged [batch][n_kv_heads] (required when merged is given)
+ * prompt_lens [batch] may be NULL (then the dense switch uses lens).
+ * Capacity rules, checked on the host: k_cap >= max_blocks when the dense
+ * switch can fire (dense_boundary > 0 or topk_ppm = 10^6), else
+ * k_cap >= ceil(max_blocks * topk_ppm / 10^6); m_cap >= max_blocks.
+ * Errors: RKV_ERR_INVALID_ARG, RKV_ERR_UNSUPPORTED, RKV_ERR_WORKSPACE,
+ * RKV_ERR_HIP.
+ */
+rkv_status rkv_select(const rkv_params* params, const uint16_t* q,
+                      const float* reps, const int32_t* block_table,
+                      const int32_t* lens, const int32_t* prompt_lens,
+                      int32_t batch, int32_t max_blocks, int32_t* sel_ids,
+                      int32_t* n_sel, int32_t k_cap, int32_t* merged,
+                      int32_t* n_merged, int32_t m_cap, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * rkv_merge_table -- the merge step of rkv_select on its own: builds merged /
+ * n_merged from given selections (sel_ids / n_sel, logical ids ascending,
+ * all inside the offload range) with the region rule above.
+ * Same capacity rule for m_cap.  Errors as rkv_select.
+ */
+rkv_status rkv_merge_table(const rkv_params* params, const int32_t* block_table,
+                           int32_t max_blocks, const int32_t* lens,
+                           const int32_t* sel_ids, const int32_t* n_sel,
+                           int32_t k_cap, int32_t batch, int32_t* merged,
+                           int32_t* n_merged, int32_t m_cap,
+                           hipStream_t stream);
+
+/*
+ * Workspace bytes rkv_decode_attn needs for these sizes.
+ */
+size_t rkv_attn_workspace_size(const rkv_params* params, int32_t batch,
+                               int32_t m_cap);
+
+/*
+ * rkv_decode_attn -- paged decode attention over a merged block table
+ * (rkmt.cn ATB article, section 1.1: softmax(Q K^T / sqrt(d_k)) V with one
+ * query token; section 2.2: K/V read through a page table).  For query head
+ * g of KV head h:
+ *     out[b][g] = sum_t softmax_t(scale * q[b][g] . K_t) V_t
+ * over every token t of the pages merged[b][h][0 .. n_merged-1].  Every entry
+ * holds 128 tokens except the LAST one, taken to be the sequence's trailing
+ * block, which holds L - 128 * (ceil(L/128) - 1) tokens.  A (b, h) with
+ * n_merged = 0 writes zeros.
+ * The work is split over the merged blocks (split-K, the Flash-Decoding
+ * idiom named in the CSDN survey's references) and the partial softmax
+ * results are merged by their log-sum-exp (the survey's cascade-inference
+ * paragraph: partial results merged the FlashDecoding way).
+ *   merged [batch][n_kv_heads][m_cap], n_merged [batch][n_kv_heads]
+ *   out [batch][n_q_heads][128] fp32
+ *   workspace >= rkv_attn_workspace_size(params, batch, m_cap) bytes
+ * Errors: RKV_ERR_INVALID_ARG, RKV_ERR_UNSUPPORTED, RKV_ERR_WORKSPACE,
+ * RKV_ERR_HIP.
+ */
+rkv_status rkv_decode_attn(const rkv_params* params, const uint16_t* q,
+                           const uint16_t* k_pages, const uint16_t* v_pages,
+                           int64_t n_pages, const int32_t* merged,
+                           const int32_t* n_merged, int32_t m_cap,
+                           const int32_t* lens, int32_t batch, float* out,
+                           void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RKV_H */

@@ -1,0 +1,205 @@
+"""Thin ctypes binding over librkv.so (the C ABI in include/rkv.h).
+
+Argument marshalling only: torch tensors become device pointers and sizes,
+the current HIP stream is passed through, and a non-OK status raises.  All
+arithmetic happens in the HIP kernels behind the C ABI.  There is no fallback:
+if the library is missing, loading fails loudly.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "librkv.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "rkv.h")
+
+RKV_OK, RKV_ERR_INVALID_ARG, RKV_ERR_UNSUPPORTED, RKV_ERR_WORKSPACE, RKV_ERR_HIP = range(5)
+ATTN_AUTO, ATTN_MFMA, ATTN_VALU = 0, 1, 2
+BLOCK = 128
+HEAD_DIM = 128
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("block_size", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("init_tokens", ctypes.c_int32), ("local_tokens", ctypes.c_int32),
+                ("topk_ppm", ctypes.c_int32), ("dense_boundary", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("attn_impl", ctypes.c_int32),
+                ("split_blocks", ctypes.c_int32)]
+
+    def __repr__(self):
+        return "Params(" + ", ".join(f"{n}={getattr(self, n)}"
+                                     for n, _ in self._fields_) + ")"
+
+
+class RkvError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"rkv status {status}: {msg}")
+        self.status = status
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_PP = ctypes.POINTER(Params)
+
+_SIGS = {
+    "rkv_params_default": (Params, [_I32, _I32]),
+    "rkv_abi_version": (_I32, []),
+    "rkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "rkv_last_error": (ctypes.c_char_p, []),
+    "rkv_build_reps": (ctypes.c_int, [_PP, _P, _I64, _P, _I32, _P, _P, _I32, _P, _P]),
+    "rkv_append_kv": (ctypes.c_int, [_PP, _P, _P, _P, _P, _I64, _P, _I32, _P, _I32,
+                                     _P, _P]),
+    "rkv_select_workspace_size": (_SZ, [_PP, _I32, _I32]),
+    "rkv_select": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _I32,
+                                  _P, _P, _I32, _P, _SZ, _P]),
+    "rkv_merge_table": (ctypes.c_int, [_PP, _P, _I32, _P, _P, _P, _I32, _I32, _P, _P,
+                                       _I32, _P]),
+    "rkv_attn_workspace_size": (_SZ, [_PP, _I32, _I32]),
+    "rkv_decode_attn": (ctypes.c_int, [_PP, _P, _P, _P, _I64, _P, _P, _I32, _P, _I32,
+                                       _P, _P, _SZ, _P]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load librkv.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it first "
+                "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of the functions include/rkv.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(rkv_\w+)\s*\(", text, re.M)))
+
+
+def _check(status: int):
+    if status != RKV_OK:
+        raise RkvError(status, lib().rkv_last_error().decode())
+
+
+def params(n_q_heads: int, n_kv_heads: int, **kw) -> Params:
+    p = lib().rkv_params_default(n_q_heads, n_kv_heads)
+    for k, v in kw.items():
+        if not hasattr(p, k):
+            raise AttributeError(k)
+        setattr(p, k, v)
+    return p
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def build_reps(p: Params, k_pages, block_table, lens, reps, block_begin=None):
+    _check(lib().rkv_build_reps(
+        ctypes.byref(p), _ptr(k_pages, torch.int16, "k_pages"), k_pages.shape[0],
+        _ptr(block_table, torch.int32, "block_table"), block_table.shape[1],
+        _ptr(lens, torch.int32, "lens"), _ptr(block_begin, torch.int32, "block_begin"),
+        lens.shape[0], _ptr(reps, torch.float32, "reps"), _stream(k_pages)))
+
+
+def append_kv(p: Params, k_new, v_new, k_pages, v_pages, block_table, lens,
+              reps=None):
+    _check(lib().rkv_append_kv(
+        ctypes.byref(p), _ptr(k_new, torch.int16, "k_new"),
+        _ptr(v_new, torch.int16, "v_new"), _ptr(k_pages, torch.int16, "k_pages"),
+        _ptr(v_pages, torch.int16, "v_pages"), k_pages.shape[0],
+        _ptr(block_table, torch.int32, "block_table"), block_table.shape[1],
+        _ptr(lens, torch.int32, "lens"), lens.shape[0],
+        _ptr(reps, torch.float32, "reps"), _stream(k_pages)))
+
+
+def select_workspace_size(p: Params, batch: int, max_blocks: int) -> int:
+    return lib().rkv_select_workspace_size(ctypes.byref(p), batch, max_blocks)
+
+
+def select(p: Params, q, reps, block_table, lens, sel_ids, n_sel,
+           merged=None, n_merged=None, prompt_lens=None, workspace=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().rkv_select(
+        ctypes.byref(p), _ptr(q, torch.int16, "q"), _ptr(reps, torch.float32, "reps"),
+        _ptr(block_table, torch.int32, "block_table"), _ptr(lens, torch.int32, "lens"),
+        _ptr(prompt_lens, torch.int32, "prompt_lens"), lens.shape[0],
+        block_table.shape[1], _ptr(sel_ids, torch.int32, "sel_ids"),
+        _ptr(n_sel, torch.int32, "n_sel"), sel_ids.shape[-1],
+        _ptr(merged, torch.int32, "merged"), _ptr(n_merged, torch.int32, "n_merged"),
+        merged.shape[-1] if merged is not None else 0,
+        _ptr(workspace, None, "workspace"), ws_bytes, _stream(q)))
+
+
+def merge_table(p: Params, block_table, lens, sel_ids, n_sel, merged, n_merged):
+    _check(lib().rkv_merge_table(
+        ctypes.byref(p), _ptr(block_table, torch.int32, "block_table"),
+        block_table.shape[1], _ptr(lens, torch.int32, "lens"),
+        _ptr(sel_ids, torch.int32, "sel_ids"), _ptr(n_sel, torch.int32, "n_sel"),
+        sel_ids.shape[-1], lens.shape[0], _ptr(merged, torch.int32, "merged"),
+        _ptr(n_merged, torch.int32, "n_merged"), merged.shape[-1], _stream(lens)))
+
+
+def attn_workspace_size(p: Params, batch: int, m_cap: int) -> int:
+    return lib().rkv_attn_workspace_size(ctypes.byref(p), batch, m_cap)
+
+
+def decode_attn(p: Params, q, k_pages, v_pages, merged, n_merged, lens, out,
+                workspace):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().rkv_decode_attn(
+        ctypes.byref(p), _ptr(q, torch.int16, "q"),
+        _ptr(k_pages, torch.int16, "k_pages"), _ptr(v_pages, torch.int16, "v_pages"),
+        k_pages.shape[0], _ptr(merged, torch.int32, "merged"),
+        _ptr(n_merged, torch.int32, "n_merged"), merged.shape[-1],
+        _ptr(lens, torch.int32, "lens"), lens.shape[0],
+        _ptr(out, torch.float32, "out"), _ptr(workspace, None, "workspace"),
+        ws_bytes, _stream(q)))
+
+
+def ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def topk_capacity(p: Params, max_blocks: int) -> int:
+    """Smallest k_cap rkv_select accepts (the header's capacity rule)."""
+    if p.dense_boundary > 0 or p.topk_ppm >= 1_000_000:
+        return max_blocks
+    return ceil_div(max_blocks * p.topk_ppm, 1_000_000)
+
+
+__all__ = ["Params", "RkvError", "lib", "params", "build_reps", "append_kv",
+           "select", "merge_table", "decode_attn", "attn_workspace_size",
+           "select_workspace_size", "topk_capacity", "header_functions",
+           "ATTN_AUTO", "ATTN_MFMA", "ATTN_VALU"]

@@ -1,0 +1,296 @@
+// Host side of the C ABI declared in include/rkv.h: argument validation,
+// workspace sizing, error reporting and kernel dispatch.  Nothing here
+// allocates device memory; every launch goes on the caller's stream.
+#include "rkv.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "rkv_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+rkv_status fail(rkv_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+rkv_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return RKV_OK;
+  return fail(RKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+#define RKV_REQUIRE(cond, status, ...) \
+  do {                                 \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+// Checks shared by every call; fills the kernels' view of the parameters.
+rkv_status check_params(const rkv_params* p, rkv::Method* m) {
+  RKV_REQUIRE(p != nullptr, RKV_ERR_INVALID_ARG, "params is NULL");
+  RKV_REQUIRE(p->block_size == RKV_BLOCK_SIZE, RKV_ERR_UNSUPPORTED,
+              "block_size %d unsupported (only 128)", p->block_size);
+  RKV_REQUIRE(p->head_dim == RKV_HEAD_DIM, RKV_ERR_UNSUPPORTED,
+              "head_dim %d unsupported (only 128)", p->head_dim);
+  RKV_REQUIRE(p->n_q_heads > 0 && p->n_kv_heads > 0, RKV_ERR_INVALID_ARG,
+              "head counts must be positive (q %d, kv %d)", p->n_q_heads,
+              p->n_kv_heads);
+  RKV_REQUIRE(p->n_q_heads % p->n_kv_heads == 0, RKV_ERR_INVALID_ARG,
+              "n_q_heads %d is not a multiple of n_kv_heads %d",
+              p->n_q_heads, p->n_kv_heads);
+  RKV_REQUIRE(p->n_q_heads / p->n_kv_heads <= RKV_MAX_GROUP,
+              RKV_ERR_UNSUPPORTED, "group size %d above %d",
+              p->n_q_heads / p->n_kv_heads, RKV_MAX_GROUP);
+  RKV_REQUIRE(p->init_tokens >= 0 && p->local_tokens >= 0, RKV_ERR_INVALID_ARG,
+              "init_tokens / local_tokens must be >= 0");
+  RKV_REQUIRE(p->topk_ppm >= 0 && p->topk_ppm <= RKV_PPM_ONE,
+              RKV_ERR_INVALID_ARG, "topk_ppm %d outside [0, 1000000]",
+              p->topk_ppm);
+  RKV_REQUIRE(p->dense_boundary >= 0, RKV_ERR_INVALID_ARG,
+              "dense_boundary must be >= 0");
+  RKV_REQUIRE(isfinite(p->scale), RKV_ERR_INVALID_ARG, "scale is not finite");
+  RKV_REQUIRE(p->attn_impl >= RKV_ATTN_AUTO && p->attn_impl <= RKV_ATTN_VALU,
+              RKV_ERR_INVALID_ARG, "attn_impl %d unknown", p->attn_impl);
+  RKV_REQUIRE(p->split_blocks >= 0, RKV_ERR_INVALID_ARG,
+              "split_blocks must be >= 0");
+  if (m) {
+    m->n_q_heads = p->n_q_heads;
+    m->n_kv_heads = p->n_kv_heads;
+    m->group = p->n_q_heads / p->n_kv_heads;
+    m->init_tokens = p->init_tokens;
+    m->local_tokens = p->local_tokens;
+    m->topk_ppm = p->topk_ppm;
+    m->dense_boundary = p->dense_boundary;
+  }
+  return RKV_OK;
+}
+
+rkv_status check_sizes(int32_t batch, int32_t max_blocks) {
+  RKV_REQUIRE(batch >= 0, RKV_ERR_INVALID_ARG, "batch %d < 0", batch);
+  RKV_REQUIRE(max_blocks >= 1 && max_blocks <= RKV_MAX_BLOCKS,
+              RKV_ERR_INVALID_ARG, "max_blocks %d outside [1, %d]",
+              max_blocks, RKV_MAX_BLOCKS);
+  return RKV_OK;
+}
+
+rkv_status check_pool(const void* pool, int64_t n_pages, const char* name) {
+  RKV_REQUIRE(pool != nullptr, RKV_ERR_INVALID_ARG, "%s is NULL", name);
+  RKV_REQUIRE(aligned16(pool), RKV_ERR_INVALID_ARG,
+              "%s is not 16-byte aligned", name);
+  RKV_REQUIRE(n_pages >= 1, RKV_ERR_INVALID_ARG, "n_pages %lld < 1",
+              (long long)n_pages);
+  return RKV_OK;
+}
+
+int64_t topk_cap(const rkv_params* p, int32_t max_blocks) {
+  const bool dense_possible =
+      p->dense_boundary > 0 || p->topk_ppm >= RKV_PPM_ONE;
+  if (dense_possible) return max_blocks;
+  return ((int64_t)max_blocks * p->topk_ppm + RKV_PPM_ONE - 1) / RKV_PPM_ONE;
+}
+
+#define RKV_TRY(expr)                  \
+  do {                                 \
+    rkv_status s_ = (expr);            \
+    if (s_ != RKV_OK) return s_;       \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+rkv_params rkv_params_default(int32_t n_q_heads, int32_t n_kv_heads) {
+  rkv_params p;
+  p.block_size = RKV_BLOCK_SIZE;
+  p.head_dim = RKV_HEAD_DIM;
+  p.n_q_heads = n_q_heads;
+  p.n_kv_heads = n_kv_heads;
+  p.init_tokens = 1024;
+  p.local_tokens = 7192;
+  p.topk_ppm = 200000;
+  p.dense_boundary = 32768;
+  p.scale = 1.0f / sqrtf((float)RKV_HEAD_DIM);
+  p.attn_impl = RKV_ATTN_AUTO;
+  p.split_blocks = 0;
+  return p;
+}
+
+int32_t rkv_abi_version(void) { return RKV_ABI_VERSION; }
+
+const char* rkv_status_string(rkv_status s) {
+  switch (s) {
+    case RKV_OK: return "ok";
+    case RKV_ERR_INVALID_ARG: return "invalid argument";
+    case RKV_ERR_UNSUPPORTED: return "unsupported";
+    case RKV_ERR_WORKSPACE: return "workspace too small";
+    case RKV_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* rkv_last_error(void) { return g_last_error.c_str(); }
+
+rkv_status rkv_build_reps(const rkv_params* params, const uint16_t* k_pages,
+                          int64_t n_pages, const int32_t* block_table,
+                          int32_t max_blocks, const int32_t* lens,
+                          const int32_t* block_begin, int32_t batch,
+                          float* reps, hipStream_t stream) {
+  rkv::Method m;
+  RKV_TRY(check_params(params, &m));
+  RKV_TRY(check_sizes(batch, max_blocks));
+  RKV_TRY(check_pool(k_pages, n_pages, "k_pages"));
+  RKV_REQUIRE(block_table && lens && reps, RKV_ERR_INVALID_ARG,
+              "block_table, lens and reps must not be NULL");
+  RKV_REQUIRE(aligned16(reps), RKV_ERR_INVALID_ARG, "reps is not 16-byte aligned");
+  return hip_status(rkv::launch_build_reps(k_pages, n_pages, block_table,
+                                           max_blocks, lens, block_begin, batch,
+                                           m.n_kv_heads, reps, stream),
+                    "rkv_build_reps launch");
+}
+
+rkv_status rkv_append_kv(const rkv_params* params, const uint16_t* k_new,
+                         const uint16_t* v_new, uint16_t* k_pages,
+                         uint16_t* v_pages, int64_t n_pages,
+                         const int32_t* block_table, int32_t max_blocks,
+                         const int32_t* lens, int32_t batch, float* reps,
+                         hipStream_t stream) {
+  rkv::Method m;
+  RKV_TRY(check_params(params, &m));
+  RKV_TRY(check_sizes(batch, max_blocks));
+  RKV_TRY(check_pool(k_pages, n_pages, "k_pages"));
+  RKV_TRY(check_pool(v_pages, n_pages, "v_pages"));
+  RKV_REQUIRE(k_new && v_new && block_table && lens, RKV_ERR_INVALID_ARG,
+              "k_new, v_new, block_table and lens must not be NULL");
+  RKV_REQUIRE(aligned16(k_new) && aligned16(v_new) && (!reps || aligned16(reps)),
+              RKV_ERR_INVALID_ARG, "k_new, v_new and reps must be 16-byte aligned");
+  return hip_status(rkv::launch_append_kv(k_new, v_new, k_pages, v_pages,
+                                          n_pages, block_table, max_blocks,
+                                          lens, batch, m.n_kv_heads, reps,
+                                          stream),
+                    "rkv_append_kv launch");
+}
+
+size_t rkv_select_workspace_size(const rkv_params* params, int32_t batch,
+                                 int32_t max_blocks) {
+  (void)params;
+  (void)batch;
+  (void)max_blocks;
+  return 0;
+}
+
+rkv_status rkv_select(const rkv_params* params, const uint16_t* q,
+                      const float* reps, const int32_t* block_table,
+                      const int32_t* lens, const int32_t* prompt_lens,
+                      int32_t batch, int32_t max_blocks, int32_t* sel_ids,
+                      int32_t* n_sel, int32_t k_cap, int32_t* merged,
+                      int32_t* n_merged, int32_t m_cap, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  rkv::Method m;
+  RKV_TRY(check_params(params, &m));
+  RKV_TRY(check_sizes(batch, max_blocks));
+  RKV_REQUIRE(q && reps && block_table && lens && sel_ids && n_sel,
+              RKV_ERR_INVALID_ARG,
+              "q, reps, block_table, lens, sel_ids and n_sel must not be NULL");
+  RKV_REQUIRE(aligned16(q) && aligned16(reps), RKV_ERR_INVALID_ARG,
+              "q and reps must be 16-byte aligned");
+  RKV_REQUIRE(k_cap >= topk_cap(params, max_blocks), RKV_ERR_INVALID_ARG,
+              "k_cap %d below the required %lld", k_cap,
+              (long long)topk_cap(params, max_blocks));
+  if (merged) {
+    RKV_REQUIRE(n_merged != nullptr, RKV_ERR_INVALID_ARG,
+                "n_merged must not be NULL when merged is given");
+    RKV_REQUIRE(m_cap >= max_blocks, RKV_ERR_INVALID_ARG,
+                "m_cap %d below max_blocks %d", m_cap, max_blocks);
+  }
+  const size_t need = rkv_select_workspace_size(params, batch, max_blocks);
+  RKV_REQUIRE(workspace_bytes >= need && (need == 0 || workspace),
+              RKV_ERR_WORKSPACE, "select workspace %zu bytes, need %zu",
+              workspace_bytes, need);
+  return hip_status(rkv::launch_select(m, q, reps, block_table, lens,
+                                       prompt_lens, batch, max_blocks, sel_ids,
+                                       n_sel, k_cap, merged, n_merged, m_cap,
+                                       stream),
+                    "rkv_select launch");
+}
+
+rkv_status rkv_merge_table(const rkv_params* params, const int32_t* block_table,
+                           int32_t max_blocks, const int32_t* lens,
+                           const int32_t* sel_ids, const int32_t* n_sel,
+                           int32_t k_cap, int32_t batch, int32_t* merged,
+                           int32_t* n_merged, int32_t m_cap,
+                           hipStream_t stream) {
+  rkv::Method m;
+  RKV_TRY(check_params(params, &m));
+  RKV_TRY(check_sizes(batch, max_blocks));
+  RKV_REQUIRE(block_table && lens && sel_ids && n_sel && merged && n_merged,
+              RKV_ERR_INVALID_ARG, "a required pointer is NULL");
+  RKV_REQUIRE(k_cap >= 0, RKV_ERR_INVALID_ARG, "k_cap %d < 0", k_cap);
+  RKV_REQUIRE(m_cap >= max_blocks, RKV_ERR_INVALID_ARG,
+              "m_cap %d below max_blocks %d", m_cap, max_blocks);
+  return hip_status(rkv::launch_merge(m, block_table, max_blocks, lens, sel_ids,
+                                      n_sel, k_cap, batch, merged, n_merged,
+                                      m_cap, stream),
+                    "rkv_merge_table launch");
+}
+
+size_t rkv_attn_workspace_size(const rkv_params* params, int32_t batch,
+                               int32_t m_cap) {
+  if (!params || params->n_q_heads <= 0 || params->n_kv_heads <= 0 ||
+      batch < 0 || m_cap < 1 || params->split_blocks < 0)
+    return 0;
+  const rkv::AttnPlan p = rkv::plan_attention(
+      batch, params->n_q_heads, params->n_kv_heads, m_cap, params->split_blocks);
+  return p.partial_bytes + p.ml_bytes;
+}
+
+rkv_status rkv_decode_attn(const rkv_params* params, const uint16_t* q,
+                           const uint16_t* k_pages, const uint16_t* v_pages,
+                           int64_t n_pages, const int32_t* merged,
+                           const int32_t* n_merged, int32_t m_cap,
+                           const int32_t* lens, int32_t batch, float* out,
+                           void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  rkv::Method m;
+  RKV_TRY(check_params(params, &m));
+  RKV_REQUIRE(batch >= 0, RKV_ERR_INVALID_ARG, "batch %d < 0", batch);
+  RKV_REQUIRE(m_cap >= 1 && m_cap <= RKV_MAX_BLOCKS, RKV_ERR_INVALID_ARG,
+              "m_cap %d outside [1, %d]", m_cap, RKV_MAX_BLOCKS);
+  RKV_TRY(check_pool(k_pages, n_pages, "k_pages"));
+  RKV_TRY(check_pool(v_pages, n_pages, "v_pages"));
+  RKV_REQUIRE(q && merged && n_merged && lens && out, RKV_ERR_INVALID_ARG,
+              "q, merged, n_merged, lens and out must not be NULL");
+  RKV_REQUIRE(aligned16(q) && aligned16(out), RKV_ERR_INVALID_ARG,
+              "q and out must be 16-byte aligned");
+  if (params->attn_impl == RKV_ATTN_VALU)
+    return fail(RKV_ERR_UNSUPPORTED, "the VALU attention variant is not built");
+  const rkv::AttnPlan plan = rkv::plan_attention(
+      batch, m.n_q_heads, m.n_kv_heads, m_cap, params->split_blocks);
+  const size_t need = plan.partial_bytes + plan.ml_bytes;
+  RKV_REQUIRE(workspace_bytes >= need && (need == 0 || workspace != nullptr),
+              RKV_ERR_WORKSPACE, "attention workspace %zu bytes, need %zu",
+              workspace_bytes, need);
+  RKV_REQUIRE(aligned16(workspace), RKV_ERR_INVALID_ARG,
+              "workspace is not 16-byte aligned");
+  return hip_status(
+      rkv::launch_decode_attn(m, params->attn_impl != RKV_ATTN_VALU, plan,
+                              params->scale, q, k_pages, v_pages, n_pages,
+                              merged, n_merged, m_cap, lens, batch, out,
+                              workspace, stream),
+      "rkv_decode_attn launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Device helpers shared by the HIP kernel files (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rkv {
+
+// bf16 bit pattern(s) -> fp32 (exact).
+__device__ __forceinline__ float bf16lo(uint32_t w) {
+  return __uint_as_float(w << 16);
+}
+__device__ __forceinline__ float bf16hi(uint32_t w) {
+  return __uint_as_float(w & 0xffff0000u);
+}
+
+// Current length of sequence b, clamped to [0, max_len].
+__device__ __forceinline__ int clamp_len(int L, int max_len) {
+  return L < 0 ? 0 : (L > max_len ? max_len : L);
+}
+
+// Block split of a sequence of L tokens (openGauss page, "Overall
+// Solution"): init blocks [0, n_init), offload [n_init, local_start) when
+// local_start > n_init, local blocks [max(local_start, n_init), nb).
+struct Regions {
+  int nb, n_init, local_start, n_off;
+};
+
+__device__ __forceinline__ Regions regions_of(int L, int init_tokens,
+                                              int local_tokens) {
+  Regions r;
+  if (L <= 0) {
+    r.nb = r.n_init = r.local_start = r.n_off = 0;
+    return r;
+  }
+  r.nb = (L + 127) >> 7;
+  const int ib = (int)(((int64_t)init_tokens + 127) >> 7);
+  r.n_init = ib < r.nb ? ib : r.nb;
+  int tail = L - local_tokens;
+  tail = tail > 0 ? tail : 0;
+  const int ls = tail >> 7;
+  r.local_start = ls < r.nb - 1 ? ls : r.nb - 1;
+  r.n_off = r.local_start > r.n_init ? r.local_start - r.n_init : 0;
+  return r;
+}
+
+// k = ceil(n * ppm / 10^6) in exact integer arithmetic.
+__device__ __forceinline__ int topk_of(int n_off, int ppm) {
+  return (int)(((int64_t)n_off * ppm + 999999) / 1000000);
+}
+
+// Wave-wide sum / max over all 64 lanes.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+}  // namespace rkv

@@ -1,0 +1,68 @@
+// Internal interface between the host API (rkv_api.cpp) and the kernel
+// files.  Each launcher enqueues its kernel(s) on `stream` and returns the
+// launch status; all argument checking happens in rkv_api.cpp before these
+// are called.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace rkv {
+
+constexpr int kBlock = 128;   // tokens per block / page
+constexpr int kDim = 128;     // head dimension
+constexpr int kPpmOne = 1000000;
+
+// Region and selection parameters as the kernels see them.
+struct Method {
+  int n_q_heads, n_kv_heads, group;
+  int init_tokens, local_tokens, topk_ppm, dense_boundary;
+};
+
+hipError_t launch_build_reps(const uint16_t* k_pages, int64_t n_pages,
+                             const int32_t* table, int max_blocks,
+                             const int32_t* lens, const int32_t* block_begin,
+                             int batch, int n_kv_heads, float* reps,
+                             hipStream_t stream);
+
+hipError_t launch_append_kv(const uint16_t* k_new, const uint16_t* v_new,
+                            uint16_t* k_pages, uint16_t* v_pages,
+                            int64_t n_pages, const int32_t* table,
+                            int max_blocks, const int32_t* lens, int batch,
+                            int n_kv_heads, float* reps, hipStream_t stream);
+
+hipError_t launch_select(const Method& m, const uint16_t* q, const float* reps,
+                         const int32_t* table, const int32_t* lens,
+                         const int32_t* prompt_lens, int batch, int max_blocks,
+                         int32_t* sel_ids, int32_t* n_sel, int k_cap,
+                         int32_t* merged, int32_t* n_merged, int m_cap,
+                         hipStream_t stream);
+
+hipError_t launch_merge(const Method& m, const int32_t* table, int max_blocks,
+                        const int32_t* lens, const int32_t* sel_ids,
+                        const int32_t* n_sel, int k_cap, int batch,
+                        int32_t* merged, int32_t* n_merged, int m_cap,
+                        hipStream_t stream);
+
+// Split-K decode attention: `chunk` merged blocks per work item,
+// `n_chunks` = ceil(m_cap / chunk) work items per (sequence, KV head).
+struct AttnPlan {
+  int chunk;
+  int n_chunks;
+  size_t partial_bytes;  // fp32 [batch][n_q_heads][n_chunks][kDim]
+  size_t ml_bytes;       // float2 [batch][n_q_heads][n_chunks]
+};
+AttnPlan plan_attention(int batch, int n_q_heads, int n_kv_heads, int m_cap,
+                        int split_blocks);
+
+hipError_t launch_decode_attn(const Method& m, bool use_mfma,
+                              const AttnPlan& plan, float scale,
+                              const uint16_t* q, const uint16_t* k_pages,
+                              const uint16_t* v_pages, int64_t n_pages,
+                              const int32_t* merged, const int32_t* n_merged,
+                              int m_cap, const int32_t* lens, int batch,
+                              float* out, void* workspace, hipStream_t stream);
+
+}  // namespace rkv

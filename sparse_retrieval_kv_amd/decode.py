@@ -1,0 +1,73 @@
+"""One layer's retrieval-sparse decode step over a batch of paged sequences.
+
+`DecodeSession` owns the device buffers the C ABI writes (representations,
+selections, merged tables, workspaces, output) and issues the per-step call
+sequence on the current stream:
+
+    rkv_append_kv   write the decoded token's K/V (and a just-completed
+                    block's representation)
+    rkv_select      inner-product scores, per-(sequence, KV head) top-k and
+                    the merged block table
+    rkv_decode_attn split-K paged attention and the log-sum-exp combine
+
+PyTorch only allocates memory and provides the stream here.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import binding as B
+
+
+class DecodeSession:
+    def __init__(self, prm: B.Params, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                 block_table: torch.Tensor, prompt_lens: torch.Tensor | None = None):
+        dev = k_pages.device
+        self.p = prm
+        self.k_pages, self.v_pages = k_pages, v_pages
+        self.block_table = block_table
+        self.batch, self.max_blocks = block_table.shape
+        self.prompt_lens = prompt_lens
+        hkv, hq = prm.n_kv_heads, prm.n_q_heads
+        self.k_cap = B.topk_capacity(prm, self.max_blocks)
+        self.m_cap = self.max_blocks
+        self.reps = torch.zeros((self.batch, hkv, self.max_blocks, B.HEAD_DIM),
+                                dtype=torch.float32, device=dev)
+        self.sel_ids = torch.zeros((self.batch, hkv, self.k_cap), dtype=torch.int32,
+                                   device=dev)
+        self.n_sel = torch.zeros((self.batch, hkv), dtype=torch.int32, device=dev)
+        self.merged = torch.zeros((self.batch, hkv, self.m_cap), dtype=torch.int32,
+                                  device=dev)
+        self.n_merged = torch.zeros((self.batch, hkv), dtype=torch.int32, device=dev)
+        self.out = torch.zeros((self.batch, hq, B.HEAD_DIM), dtype=torch.float32,
+                               device=dev)
+        ws = B.select_workspace_size(prm, self.batch, self.max_blocks)
+        self.ws_select = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev) \
+            if ws else None
+        wa = B.attn_workspace_size(prm, self.batch, self.m_cap)
+        self.ws_attn = torch.empty(max(wa, 16), dtype=torch.uint8, device=dev)
+
+    def build_reps(self, lens: torch.Tensor, block_begin: torch.Tensor | None = None):
+        B.build_reps(self.p, self.k_pages, self.block_table, lens, self.reps,
+                     block_begin)
+
+    def append(self, k_new, v_new, lens):
+        B.append_kv(self.p, k_new, v_new, self.k_pages, self.v_pages,
+                    self.block_table, lens, self.reps)
+
+    def select(self, q, lens):
+        B.select(self.p, q, self.reps, self.block_table, lens, self.sel_ids,
+                 self.n_sel, self.merged, self.n_merged, self.prompt_lens,
+                 self.ws_select)
+
+    def attend(self, q, lens):
+        B.decode_attn(self.p, q, self.k_pages, self.v_pages, self.merged,
+                      self.n_merged, lens, self.out, self.ws_attn)
+        return self.out
+
+    def step(self, q, k_new, v_new, lens):
+        """append -> select -> attend for one decode step; returns `out`."""
+        self.append(k_new, v_new, lens)
+        self.select(q, lens)
+        return self.attend(q, lens)

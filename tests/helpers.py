@@ -1,0 +1,68 @@
+"""Test harness helpers: the oracle's view of a synthetic batch and
+comparison utilities.  The oracle's inputs come from the generator (pool
+contents written before any library call, plus the generator's appended
+tokens), never from the library's outputs."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+from sparse_retrieval_kv_amd import synth
+
+
+def u16(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy().view(np.uint16)
+
+
+def oracle_params(spec, **kw) -> O.Params:
+    d = dict(init_tokens=spec.init_tokens, local_tokens=spec.local_tokens,
+             topk_ppm=spec.topk_ppm, dense_boundary=spec.dense_boundary)
+    d.update(kw)
+    return O.Params(spec.n_q_heads, spec.n_kv_heads, **d)
+
+
+def seq_pages_host(batch: synth.Batch, b: int, heads=None):
+    """Host copy of sequence b's pages (all heads or the given ones), taken
+    from the generator's pools.  Returns (k [nb,H,128,128], v, heads)."""
+    L_final = int(batch.context[b]) + batch.spec.steps - 1
+    nb = -(-L_final // 128)
+    pages = torch.as_tensor(batch.table_np[b, :nb].astype(np.int64),
+                            device=batch.k_pages.device)
+    hs = list(range(batch.spec.n_kv_heads)) if heads is None else list(heads)
+    hidx = torch.as_tensor(hs, device=batch.k_pages.device)
+    k = batch.k_pages.index_select(0, pages).index_select(1, hidx)
+    v = batch.v_pages.index_select(0, pages).index_select(1, hidx)
+    return u16(k), u16(v), hs
+
+
+def logical_at_step(batch: synth.Batch, b: int, t: int, pages=None):
+    """float64 logical K, V [H, L_t, d] of sequence b after step t's append,
+    plus L_t.  Prefill positions come from the pools, decoded positions from
+    the generator's appended tokens."""
+    if pages is None:
+        pages = seq_pages_host(batch, b)
+    kp, vp, hs = pages
+    L = int(batch.context[b]) + t
+    K, V = O.logical_kv(kp, vp, np.arange(kp.shape[0]), L)
+    first = int(batch.context[b]) - 1
+    for s in range(t + 1):
+        kn, vn = batch.new_kv_bits(s)
+        K[:, first + s] = O.bf16_to_f64(u16(kn[b])[hs])
+        V[:, first + s] = O.bf16_to_f64(u16(vn[b])[hs])
+    return K, V, L
+
+
+def q_f64(batch: synth.Batch, t: int) -> np.ndarray:
+    return O.bf16_to_f64(u16(batch.q_bits(t)))
+
+
+def close_report(got: np.ndarray, ref: np.ndarray, atol=2e-3, rtol=1e-2):
+    """BJ-style elementwise check plus relative L2 error."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(got - ref)
+    ok = bool(np.all(err <= atol + rtol * np.abs(ref)))
+    rel_l2 = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    return ok, float(err.max(initial=0.0)), rel_l2

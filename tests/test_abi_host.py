@@ -1,0 +1,142 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/rkv.h declares, returns the page's defaults, and
+rejects bad arguments before anything is enqueued."""
+
+import ctypes
+
+import pytest
+
+from sparse_retrieval_kv_amd import binding as B
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
+ODD = 0x10002
+
+
+@pytest.fixture(scope="module")
+def L():
+    return B.lib()
+
+
+def test_every_declared_function_is_exported(L):
+    names = B.header_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.rkv_abi_version() == 1
+
+
+def test_defaults_follow_the_page(L):
+    p = L.rkv_params_default(32, 8)
+    assert (p.block_size, p.head_dim, p.init_tokens, p.local_tokens,
+            p.topk_ppm, p.dense_boundary) == (128, 128, 1024, 7192, 200000, 32768)
+    assert p.scale == pytest.approx(128 ** -0.5)
+    assert (p.n_q_heads, p.n_kv_heads, p.attn_impl, p.split_blocks) == (32, 8, 0, 0)
+    assert L.rkv_status_string(0) == b"ok"
+    assert L.rkv_status_string(3) == b"workspace too small"
+
+
+def _attn(L, p, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, n_pages=10, merged=FAKE, n_merged=FAKE,
+             m_cap=16, lens=FAKE, batch=2, out=FAKE, ws=FAKE, ws_bytes=0)
+    a.update(kw)
+    return L.rkv_decode_attn(ctypes.byref(p), a["q"], a["k"], a["v"], a["n_pages"],
+                             a["merged"], a["n_merged"], a["m_cap"], a["lens"],
+                             a["batch"], a["out"], a["ws"], a["ws_bytes"], None)
+
+
+def test_param_validation(L):
+    base = L.rkv_params_default(32, 8)
+
+    def with_(**kw):
+        p = L.rkv_params_default(32, 8)
+        for k, v in kw.items():
+            setattr(p, k, v)
+        return p
+
+    cases = [
+        (with_(block_size=64), B.RKV_ERR_UNSUPPORTED),
+        (with_(head_dim=64), B.RKV_ERR_UNSUPPORTED),
+        (with_(n_q_heads=30), B.RKV_ERR_INVALID_ARG),
+        (with_(n_q_heads=0), B.RKV_ERR_INVALID_ARG),
+        (with_(n_q_heads=64, n_kv_heads=2), B.RKV_ERR_UNSUPPORTED),
+        (with_(topk_ppm=1_000_001), B.RKV_ERR_INVALID_ARG),
+        (with_(topk_ppm=-1), B.RKV_ERR_INVALID_ARG),
+        (with_(init_tokens=-1), B.RKV_ERR_INVALID_ARG),
+        (with_(dense_boundary=-5), B.RKV_ERR_INVALID_ARG),
+        (with_(scale=float("inf")), B.RKV_ERR_INVALID_ARG),
+        (with_(attn_impl=7), B.RKV_ERR_INVALID_ARG),
+        (with_(split_blocks=-1), B.RKV_ERR_INVALID_ARG),
+    ]
+    for p, want in cases:
+        assert _attn(L, p) == want, p
+        assert L.rkv_last_error() != b""
+    assert _attn(L, base, ws_bytes=0) == B.RKV_ERR_WORKSPACE
+    assert b"workspace" in L.rkv_last_error()
+    need = L.rkv_attn_workspace_size(ctypes.byref(base), 2, 16)
+    assert need > 0
+    assert _attn(L, base, ws_bytes=need - 1) == B.RKV_ERR_WORKSPACE
+    assert _attn(L, base, q=None, ws_bytes=need) == B.RKV_ERR_INVALID_ARG
+    assert _attn(L, base, out=ODD, ws_bytes=need) == B.RKV_ERR_INVALID_ARG
+    assert _attn(L, base, m_cap=0, ws_bytes=need) == B.RKV_ERR_INVALID_ARG
+    assert _attn(L, base, n_pages=0, ws_bytes=need) == B.RKV_ERR_INVALID_ARG
+    assert _attn(L, base, batch=-1, ws_bytes=need) == B.RKV_ERR_INVALID_ARG
+    assert L.rkv_decode_attn(None, FAKE, FAKE, FAKE, 10, FAKE, FAKE, 16, FAKE, 2,
+                             FAKE, FAKE, need, None) == B.RKV_ERR_INVALID_ARG
+
+
+def test_select_and_merge_capacity_rules(L):
+    p = L.rkv_params_default(32, 8)
+
+    def sel(k_cap, m_cap, merged=FAKE, n_merged=FAKE, max_blocks=100, q=FAKE):
+        return L.rkv_select(ctypes.byref(p), q, FAKE, FAKE, FAKE, None, 4,
+                            max_blocks, FAKE, FAKE, k_cap, merged, n_merged, m_cap,
+                            None, 0, None)
+
+    # dense switch possible (boundary 32768): k_cap must cover max_blocks
+    assert sel(99, 100) == B.RKV_ERR_INVALID_ARG
+    assert b"k_cap" in L.rkv_last_error()
+    assert sel(100, 99) == B.RKV_ERR_INVALID_ARG
+    assert sel(100, 100, n_merged=None) == B.RKV_ERR_INVALID_ARG
+    assert sel(100, 100, q=None) == B.RKV_ERR_INVALID_ARG
+    assert sel(100, 100, max_blocks=0) == B.RKV_ERR_INVALID_ARG
+    assert sel(100, 100, max_blocks=8193) == B.RKV_ERR_INVALID_ARG
+    # no dense switch: ceil(max_blocks * ppm / 1e6) suffices
+    p.dense_boundary = 0
+    assert sel(19, 100) == B.RKV_ERR_INVALID_ARG    # ceil(100 * 0.2) = 20
+    p.topk_ppm = 1_000_000
+    assert sel(99, 100) == B.RKV_ERR_INVALID_ARG
+    assert L.rkv_merge_table(ctypes.byref(p), FAKE, 100, FAKE, FAKE, FAKE, 20, 4,
+                             FAKE, FAKE, 99, None) == B.RKV_ERR_INVALID_ARG
+    assert L.rkv_merge_table(ctypes.byref(p), FAKE, 100, FAKE, None, FAKE, 20, 4,
+                             FAKE, FAKE, 100, None) == B.RKV_ERR_INVALID_ARG
+
+
+def test_reps_and_append_validation(L):
+    p = L.rkv_params_default(8, 2)
+    assert L.rkv_build_reps(ctypes.byref(p), None, 10, FAKE, 8, FAKE, None, 1,
+                            FAKE, None) == B.RKV_ERR_INVALID_ARG
+    assert L.rkv_build_reps(ctypes.byref(p), FAKE, 10, FAKE, 8, FAKE, None, 1,
+                            ODD, None) == B.RKV_ERR_INVALID_ARG
+    assert L.rkv_append_kv(ctypes.byref(p), FAKE, FAKE, FAKE, ODD, 10, FAKE, 8,
+                           FAKE, 1, None, None) == B.RKV_ERR_INVALID_ARG
+    p.block_size = 256
+    assert L.rkv_append_kv(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 10, FAKE, 8,
+                           FAKE, 1, None, None) == B.RKV_ERR_UNSUPPORTED
+
+
+def test_workspace_sizes_are_monotone(L):
+    p = L.rkv_params_default(32, 8)
+    a = L.rkv_attn_workspace_size(ctypes.byref(p), 1, 513)
+    b = L.rkv_attn_workspace_size(ctypes.byref(p), 16, 1025)
+    assert 0 < a < b
+    assert L.rkv_attn_workspace_size(None, 1, 10) == 0
+    assert L.rkv_select_workspace_size(ctypes.byref(p), 16, 1025) == 0
+
+
+def test_binding_refuses_host_tensors(L):
+    import torch
+    p = B.params(8, 2)
+    t = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        B.merge_table(p, t.view(1, 4), t[:1], t.view(1, 1, 4), t[:2].view(1, 2),
+                      t.view(1, 1, 4), t[:2].view(1, 2))

@@ -1,0 +1,441 @@
+"""GPU parity of the HIP path (through the C ABI) against the float64 oracle.
+
+Tolerances:
+  * representations: the recursive-summation bound of an fp32 sum of 128
+    terms, 127 * 2^-24 * sum|K| / 128, plus one fp32 rounding of the result;
+  * selections: the oracle's selected set exactly whenever its k-th/(k+1)-th
+    relative score gap exceeds 1e-3, otherwise any set whose oracle scores
+    dominate the rest within 1e-3 * |s_k|;
+  * merged tables and appended slots: bit-exact;
+  * attention outputs: |gpu - ref| <= 2e-3 + 1e-2 |ref| elementwise, and a
+    relative L2 error <= 1e-4 (fp32 accumulation, weights kept to ~16 bits).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sparse_retrieval_kv_amd import binding as B
+from sparse_retrieval_kv_amd import synth
+from sparse_retrieval_kv_amd.decode import DecodeSession
+from tests.helpers import (close_report, logical_at_step, oracle_params,
+                           q_f64, seq_pages_host, u16)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+REL_L2 = 1e-4
+GAP = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def i32(x):
+    return torch.as_tensor(np.asarray(x, dtype=np.int32), device=DEV)
+
+
+def make_session(batch, **pkw):
+    s = batch.spec
+    prm = B.params(s.n_q_heads, s.n_kv_heads, init_tokens=s.init_tokens,
+                   local_tokens=s.local_tokens, topk_ppm=s.topk_ppm,
+                   dense_boundary=s.dense_boundary, **pkw)
+    sess = DecodeSession(prm, batch.k_pages, batch.v_pages, batch.block_table,
+                         i32(batch.context))
+    return prm, sess
+
+
+def prefill(batch, sess):
+    sess.build_reps(i32(batch.context - 1))
+
+
+def step(batch, sess, t):
+    lens = i32(batch.lens_at(t))
+    kn, vn = batch.new_kv_bits(t)
+    return sess.step(batch.q_bits(t), kn, vn, lens)
+
+
+def check_selection(sel_gpu, hr, n_init, ctx):
+    ref = hr.selected
+    assert len(sel_gpu) == len(ref) == hr.k, ctx
+    if hr.gap_rel > GAP:
+        assert np.array_equal(sel_gpu, ref), (ctx, hr.gap_rel)
+        return
+    # near tie: the GPU set only has to be a valid top-k of the oracle scores
+    s = hr.scores
+    mask = np.zeros(len(s), bool)
+    mask[np.asarray(sel_gpu) - n_init] = True
+    assert np.all(np.diff(sel_gpu) > 0), ctx
+    if mask.all() or not mask.any():
+        return
+    tol = GAP * abs(np.sort(s)[::-1][hr.k - 1])
+    assert s[mask].min() >= s[~mask].max() - tol, ctx
+
+
+def gpu_selection(sess, b, h):
+    n = int(sess.n_sel[b, h])
+    return sess.sel_ids[b, h, :n].cpu().numpy()
+
+
+def gpu_merged_logical(sess, batch, b, h):
+    n = int(sess.n_merged[b, h])
+    pages = sess.merged[b, h, :n].cpu().numpy()
+    inv = {int(p): j for j, p in enumerate(batch.table_np[b]) if p >= 0}
+    return np.array([inv[int(p)] for p in pages], dtype=np.int64), pages
+
+
+def check_head_output(out_gpu, ref, ctx):
+    ok, mx, rl2 = close_report(out_gpu, ref)
+    assert ok, (ctx, mx, rl2)
+    assert rl2 <= REL_L2, (ctx, mx, rl2)
+
+
+def oracle_full_check(batch, sess, t, seqs=None, heads=None, step_res=None):
+    """Check selections, merged tables and outputs of step t for the given
+    sequences / KV heads against the oracle."""
+    spec = batch.spec
+    G = spec.group
+    out = sess.out.cpu().numpy()
+    qall = q_f64(batch, t)
+    for b in (range(spec.batch) if seqs is None else seqs):
+        hs = list(range(spec.n_kv_heads)) if heads is None else heads
+        pages = seq_pages_host(batch, b, hs)
+        K, V, L = logical_at_step(batch, b, t, pages)
+        prm1 = oracle_params(spec)
+        prm1 = O.Params(G, 1, prm1.init_tokens, prm1.local_tokens, prm1.topk_ppm,
+                        prm1.dense_boundary)
+        for i, h in enumerate(hs):
+            ctx = f"{spec.name} step {t} seq {b} head {h}"
+            q = qall[b, h * G:(h + 1) * G]
+            res = O.decode_step(q, K[i:i + 1], V[i:i + 1], L,
+                                int(batch.context[b]), prm1)
+            hr = res.heads[0]
+            sel = gpu_selection(sess, b, h)
+            check_selection(sel, hr, res.regions.n_init, ctx)
+            mlog, mpages = gpu_merged_logical(sess, batch, b, h)
+            if np.array_equal(sel, hr.selected):
+                assert np.array_equal(mlog, hr.merged), ctx
+                assert np.array_equal(mpages, batch.table_np[b, hr.merged]), ctx
+                ref = res.out
+            else:
+                ref = O.decode_step(q, K[i:i + 1], V[i:i + 1], L,
+                                    int(batch.context[b]), prm1,
+                                    merged_override=[mlog]).out
+            check_head_output(out[b, h * G:(h + 1) * G], ref, ctx)
+
+
+# ---------------------------------------------------------------------------
+
+
+def test_build_reps_parity_and_block_begin():
+    spec = synth.custom("reps", batch=3, n_q_heads=8, n_kv_heads=2,
+                        context=(1000, 2000, 129), shuffle=True, config_id=91)
+    batch = synth.make_batch(spec, DEV)
+    prm, sess = make_session(batch)
+    say("build_reps", spec.context)
+    prefill(batch, sess)
+    torch.cuda.synchronize()
+    reps = sess.reps.cpu().numpy()
+    for b in range(3):
+        K, _, _ = logical_at_step(batch, b, 0)
+        Lp = int(batch.context[b]) - 1
+        ref = np.stack([O.block_reps(K[h, :Lp]) for h in range(2)])
+        nc = ref.shape[1]
+        absK = np.abs(K[:, :nc * 128]).reshape(2, nc, 128, 128).sum(axis=2)
+        bound = 127 * 2.0 ** -24 * absK / 128 + 2.0 ** -24 * np.abs(ref) + 1e-30
+        assert (np.abs(reps[b, :, :nc] - ref) <= bound).all(), b
+        assert (reps[b, :, nc:] == 0).all()  # partial / unused blocks untouched
+    # rebuild from block 3 / 5 / 0 into zeroed reps: earlier rows stay zero
+    sess.reps.zero_()
+    sess.build_reps(i32(batch.context - 1), i32([3, 5, 0]))
+    torch.cuda.synchronize()
+    again = sess.reps.cpu().numpy()
+    assert (again[0, :, :3] == 0).all() and (again[1, :, :5] == 0).all()
+    assert np.array_equal(again[0, :, 3:7], reps[0, :, 3:7])
+    assert np.array_equal(again[1, :, 5:15], reps[1, :, 5:15])
+    assert np.array_equal(again[2, :, :1], reps[2, :, :1])
+
+
+def test_append_writes_slots_and_completed_block_rep():
+    spec = synth.custom("append", batch=2, n_q_heads=4, n_kv_heads=2,
+                        context=(767, 300), steps=3, config_id=92)
+    batch = synth.make_batch(spec, DEV)
+    prm, sess = make_session(batch)
+    say("append", spec.context)
+    for t in range(3):
+        kn, vn = batch.new_kv_bits(t)
+        sess.append(kn, vn, i32(batch.lens_at(t)))
+    torch.cuda.synchronize()
+    kp, vp = u16(batch.k_pages), u16(batch.v_pages)
+    for b in range(2):
+        for t in range(3):
+            pos = int(batch.context[b]) - 1 + t
+            page, slot = batch.table_np[b, pos // 128], pos % 128
+            kn, vn = batch.new_kv_bits(t)
+            assert np.array_equal(kp[page, :, slot, :], u16(kn[b]))
+            assert np.array_equal(vp[page, :, :, slot], u16(vn[b]))
+        nxt = int(batch.context[b]) - 1 + 3
+        page, slot = batch.table_np[b, nxt // 128], nxt % 128
+        assert (kp[page, :, slot, :] == synth.BF16_QNAN).all()
+    # sequence 0 completed block 5 at step 1 (position 767)
+    K, _, _ = logical_at_step(batch, 0, 2)
+    ref = K[:, 640:768].mean(axis=1)
+    got = sess.reps[0, :, 5].cpu().numpy()
+    assert np.allclose(got, ref, rtol=0, atol=1e-6)
+    assert (sess.reps[1].cpu().numpy() == 0).all()
+
+
+def test_tiny_config_end_to_end_planted():
+    batch = synth.make_batch(synth.CONFIGS[1], DEV)
+    prm, sess = make_session(batch)
+    say("config 1")
+    prefill(batch, sess)
+    step(batch, sess, 0)
+    torch.cuda.synchronize()
+    for h in range(2):
+        assert set(batch.planted[0]) <= set(gpu_selection(sess, 0, h).tolist())
+        assert int(sess.n_merged[0, h]) == 12
+    oracle_full_check(batch, sess, 0)
+
+
+@pytest.mark.parametrize("ppm,dense_boundary", [(200_000, 0), (70_000, 0),
+                                                (1_000_000, 0), (0, 0),
+                                                (200_000, 32768)])
+def test_mixed_lengths_selection_and_attention(ppm, dense_boundary):
+    spec = synth.custom("mixed", batch=4, n_q_heads=16, n_kv_heads=4,
+                        context=(20000, 33000, 9000, 40960), steps=2,
+                        init_tokens=1000, local_tokens=2000, topk_ppm=ppm,
+                        dense_boundary=dense_boundary, shuffle=True, config_id=93)
+    batch = synth.make_batch(spec, DEV)
+    prm, sess = make_session(batch)
+    say("mixed", ppm, dense_boundary)
+    prefill(batch, sess)
+    for t in range(2):
+        step(batch, sess, t)
+        torch.cuda.synchronize()
+        oracle_full_check(batch, sess, t)
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (32, 2), (12, 4)])
+def test_group_sizes(hq, hkv):
+    spec = synth.custom("groups", batch=2, n_q_heads=hq, n_kv_heads=hkv,
+                        context=(5000, 3333), init_tokens=256, local_tokens=700,
+                        dense_boundary=0, config_id=94)
+    batch = synth.make_batch(spec, DEV)
+    prm, sess = make_session(batch)
+    say("groups", hq, hkv)
+    prefill(batch, sess)
+    step(batch, sess, 0)
+    torch.cuda.synchronize()
+    oracle_full_check(batch, sess, 0)
+
+
+def test_short_and_degenerate_lengths():
+    spec = synth.custom("short", batch=6, n_q_heads=8, n_kv_heads=2,
+                        context=(1, 2, 127, 128, 129, 700), init_tokens=128,
+                        local_tokens=128, dense_boundary=0, config_id=95)
+    batch = synth.make_batch(spec, DEV)
+    prm, sess = make_session(batch)
+    say("short lengths")
+    prefill(batch, sess)
+    step(batch, sess, 0)
+    torch.cuda.synchronize()
+    oracle_full_check(batch, sess, 0)
+
+
+def test_zero_length_sequence_gives_zeros():
+    spec = synth.custom("empty", batch=2, n_q_heads=8, n_kv_heads=2,
+                        context=(1, 1000), config_id=96)
+    batch = synth.make_batch(spec, DEV)
+    prm, sess = make_session(batch)
+    say("zero length")
+    lens = i32([0, 1000])
+    sess.build_reps(i32([0, 999]))
+    kn, vn = batch.new_kv_bits(0)
+    sess.append(kn, vn, lens)
+    sess.select(batch.q_bits(0), lens)
+    sess.attend(batch.q_bits(0), lens)
+    torch.cuda.synchronize()
+    assert (sess.n_merged[0].cpu().numpy() == 0).all()
+    assert (sess.out[0].cpu().numpy() == 0).all()
+    assert np.isfinite(sess.out[1].cpu().numpy()).all()
+
+
+def test_ties_go_to_lower_block_index():
+    """Identical blocks give bit-identical scores on both sides; the tie rule
+    (smaller logical block first) decides the selection exactly."""
+    spec = synth.custom("ties", batch=1, n_q_heads=8, n_kv_heads=2,
+                        context=(6000,), init_tokens=128, local_tokens=256,
+                        dense_boundary=0, config_id=97)
+    batch = synth.make_batch(spec, DEV)
+    t = batch.table_np[0]
+    src = t[10]
+    for j in (3, 7, 12, 20, 33, 40):  # six copies of block 10 -> 7 equal reps
+        batch.k_pages[t[j]] = batch.k_pages[src]
+    prm, sess = make_session(batch, topk_ppm=100_000)
+    say("ties")
+    prefill(batch, sess)
+    step(batch, sess, 0)
+    torch.cuda.synchronize()
+    K, V, L = logical_at_step(batch, 0, 0)
+    res = O.decode_step(q_f64(batch, 0)[0], K, V, L, L,
+                        oracle_params(spec, topk_ppm=100_000))
+    for h in range(2):
+        assert np.array_equal(gpu_selection(sess, 0, h), res.heads[h].selected)
+
+
+def test_split_sizes_agree_and_runs_are_deterministic():
+    spec = synth.custom("splits", batch=2, n_q_heads=32, n_kv_heads=8,
+                        context=(30000, 17001), init_tokens=1024,
+                        local_tokens=3000, dense_boundary=0, shuffle=True,
+                        config_id=98)
+    batch = synth.make_batch(spec, DEV)
+    lens = i32(batch.lens_at(0))
+    kn, vn = batch.new_kv_bits(0)
+    outs = []
+    for split in (1, 2, 3, 5, 64):
+        prm, sess = make_session(batch, split_blocks=split)
+        say("split", split)
+        prefill(batch, sess)
+        if split == 1:
+            sess.append(kn, vn, lens)  # once: the pools are shared
+        sess.select(batch.q_bits(0), lens)
+        o1 = sess.attend(batch.q_bits(0), lens).clone()
+        o2 = sess.attend(batch.q_bits(0), lens).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2)
+        outs.append(o1.cpu().numpy())
+        if split in (1, 5):
+            oracle_full_check(batch, sess, 0)
+    for o in outs[1:]:
+        assert np.allclose(o, outs[0], rtol=1e-5, atol=1e-6)
+
+
+def _permuted_copy(batch, seed=5):
+    """Same logical contents at different physical pages."""
+    rng = np.random.default_rng(seed)
+    P = batch.n_pages
+    perm = rng.permutation(P)
+    kp = torch.empty_like(batch.k_pages)
+    vp = torch.empty_like(batch.v_pages)
+    idx = torch.as_tensor(perm, device=DEV)
+    kp[idx] = batch.k_pages
+    vp[idx] = batch.v_pages
+    table = np.where(batch.table_np >= 0, perm[np.maximum(batch.table_np, 0)], -1)
+    return kp, vp, torch.as_tensor(table.astype(np.int32), device=DEV)
+
+
+def test_page_permutation_and_shared_pages_bitwise():
+    spec = synth.custom("perm", batch=3, n_q_heads=16, n_kv_heads=4,
+                        context=(12000, 12000, 9000), init_tokens=512,
+                        local_tokens=1500, dense_boundary=0,
+                        shared_prefix_pages=20, config_id=99)
+    batch = synth.make_batch(spec, DEV)
+    say("permutation / shared pages")
+
+    def run(kp, vp, table):
+        prm = B.params(16, 4, init_tokens=512, local_tokens=1500, dense_boundary=0)
+        sess = DecodeSession(prm, kp, vp, table, i32(batch.context))
+        sess.build_reps(i32(batch.context - 1))
+        kn, vn = batch.new_kv_bits(0)
+        out = sess.step(batch.q_bits(0), kn, vn, i32(batch.lens_at(0)))
+        torch.cuda.synchronize()
+        return out.clone(), sess.sel_ids.clone(), sess.n_sel.clone()
+
+    base = run(batch.k_pages.clone(), batch.v_pages.clone(), batch.block_table)
+    perm = run(*_permuted_copy(batch))
+    assert torch.equal(base[0], perm[0]) and torch.equal(base[1], perm[1])
+    # private copies of the 20 shared prefix pages for sequences 1 and 2
+    t = batch.table_np.copy()
+    extra = []
+    kp, vp = batch.k_pages.clone(), batch.v_pages.clone()
+    nxt = batch.n_pages
+    for b in (1, 2):
+        for j in range(20):
+            extra.append(int(t[b, j]))
+            t[b, j] = nxt
+            nxt += 1
+    src = torch.as_tensor(extra, device=DEV)
+    kp = torch.cat([kp, batch.k_pages[src]])
+    vp = torch.cat([vp, batch.v_pages[src]])
+    private = run(kp, vp, torch.as_tensor(t, device=DEV))
+    assert torch.equal(base[0], private[0]) and torch.equal(base[1], private[1])
+
+
+def test_invalid_page_ids_are_skipped():
+    spec = synth.custom("badpage", batch=1, n_q_heads=8, n_kv_heads=2,
+                        context=(3000,), init_tokens=256, local_tokens=512,
+                        dense_boundary=0, config_id=100)
+    batch = synth.make_batch(spec, DEV)
+    prm, sess = make_session(batch)
+    say("invalid page ids")
+    prefill(batch, sess)
+    lens = i32(batch.context)
+    kn, vn = batch.new_kv_bits(0)
+    sess.append(kn, vn, lens)
+    sess.select(batch.q_bits(0), lens)
+    torch.cuda.synchronize()
+    mlog, _ = gpu_merged_logical(sess, batch, 0, 1)
+    sess.merged[0, 1, 3] = -5
+    sess.merged[0, 1, 4] = batch.n_pages + 7
+    sess.attend(batch.q_bits(0), lens)
+    torch.cuda.synchronize()
+    K, V, L = logical_at_step(batch, 0, 0)
+    keep = np.delete(mlog, [3, 4])
+    G = 4
+    q = q_f64(batch, 0)[0, G:2 * G]
+    tok = (keep[:, None] * 128 + np.arange(128)).reshape(-1)
+    tok = tok[tok < int(batch.context[0])]
+    ref = O.attend(q, K[1, tok], V[1, tok], 1 / np.sqrt(128))
+    assert L == int(batch.context[0])
+    check_head_output(sess.out[0, G:2 * G].cpu().numpy(), ref, "bad pages")
+
+
+def test_llama_layer_full_size_steps():
+    batch = synth.make_batch(synth.CONFIGS[2], DEV)
+    prm, sess = make_session(batch)
+    say("config 2 (64K, 64 steps)")
+    prefill(batch, sess)
+    for t in range(64):
+        step(batch, sess, t)
+        if t in (0, 24, 63):
+            torch.cuda.synchronize()
+            for h in range(8):
+                assert set(batch.planted[0]) <= set(gpu_selection(sess, 0, h).tolist())
+            oracle_full_check(batch, sess, t)
+
+
+def test_batched_ragged_full_size_sampled():
+    batch = synth.make_batch(synth.CONFIGS[3], DEV)
+    prm, sess = make_session(batch)
+    say("config 3 (16 x 32K-128K, shuffled)", batch.context.tolist())
+    prefill(batch, sess)
+    for t in range(32):
+        step(batch, sess, t)
+        if t in (0, 31):
+            torch.cuda.synchronize()
+            lo, hi = int(np.argmin(batch.context)), int(np.argmax(batch.context))
+            oracle_full_check(batch, sess, t, seqs=[lo, hi, 7], heads=[0, 5])
+
+
+def test_70b_shared_prefix_full_size_sampled():
+    batch = synth.make_batch(synth.CONFIGS[4], DEV)
+    prm, sess = make_session(batch)
+    say("config 4 (8 x 128K, 64/8, shared prefix)")
+    prefill(batch, sess)
+    for t in range(16):
+        step(batch, sess, t)
+        if t in (0, 15):
+            torch.cuda.synchronize()
+            oracle_full_check(batch, sess, t, seqs=[0, 6], heads=[1, 7])
