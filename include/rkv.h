@@ -166,7 +166,8 @@ size_t rkv_select_workspace_size(const rkv_params* params, int32_t batch,
  *   selected    = the k offload blocks with the largest s_j, ties to the
  *                 smaller block index, written in ascending order
  * Outputs:
- *   sel_ids  [batch][n_kv_heads][k_cap] logical block ids (first n_sel valid)
+ *   sel_ids  [batch][n_kv_heads][k_cap] logical block ids (first n_sel valid);
+ *            may be NULL only when k_cap is 0
  *   n_sel    [batch][n_kv_heads]
  *   merged   [batch][n_kv_heads][m_cap] PAGE ids of the attended blocks in
  *            ascending logical order: init, selected, then local blocks

@@ -240,6 +240,176 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
   if (lane < G) a.part_ml[(head0 + lane) * a.n_chunks + i] = make_float2(m_run, lt);
 }
 
+// Vector-ALU variant with the same memory schedule (same tiles, same
+// per-lane 16-byte pieces, same token order): the q.k products use
+// v_dot2_f32_bf16 on bf16 pairs and the p.v products fp32 FMAs, so the two
+// variants differ only in where the dot products run.
+//   QK: lane (col, grp) holds 32 dims (chunks 4kk+grp) of token row col of
+//       each tile; partial dots for the G heads are summed over the four lane
+//       groups, leaving S[token(t, col)][head] in every lane of column col.
+//   PV: lane (col, grp) owns dims 16n+col and tokens 32pp+8grp..+7; the
+//       weights of those tokens are fetched from the lanes that own their
+//       rows, and the per-lane partial sums are folded over the lane groups
+//       once per work item.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot8(uint4 k, uint4 q, float c) {
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, k.x),
+                                      __builtin_bit_cast(bf16x2, q.x), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, k.y),
+                                      __builtin_bit_cast(bf16x2, q.y), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, k.z),
+                                      __builtin_bit_cast(bf16x2, q.z), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, k.w),
+                                      __builtin_bit_cast(bf16x2, q.w), c, false);
+  return c;
+}
+
+template <int G>
+__global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
+  const int lane = threadIdx.x;
+  const int col = lane & 15, grp = lane >> 4;
+  const int n_bh = a.batch * a.n_kv;
+  const int i = blockIdx.x / n_bh;
+  const int bh = blockIdx.x - i * n_bh;
+  int n = a.n_merged[bh];
+  n = n < 0 ? 0 : (n > a.m_cap ? a.m_cap : n);
+  const int e0 = i * a.chunk;
+  if (e0 >= n) return;
+  const int e1 = e0 + a.chunk < n ? e0 + a.chunk : n;
+  const int b = bh / a.n_kv, h = bh - b * a.n_kv;
+  const int Hq = a.n_kv * G;
+  const int L = clamp_len(a.lens[b], a.max_len);
+  const int last_valid = L - (((L + 127) >> 7) - 1) * kBlock;
+
+  uint4 qv[G][4];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qv[hh][kk] = ld16(a.q + ((int64_t)b * Hq + h * G + hh) * kDim +
+                        (4 * kk + grp) * 8);
+
+  float acc[8][G];
+#pragma unroll
+  for (int n8 = 0; n8 < 8; ++n8)
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) acc[n8][hh] = 0.f;
+  float m_run[G], l_run[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    m_run[hh] = kNegInf;
+    l_run[hh] = 0.f;
+  }
+  const int32_t* mrow = a.merged + (int64_t)bh * a.m_cap;
+
+  for (int e = e0; e < e1; ++e) {
+    const int page = mrow[e];
+    if ((uint64_t)(int64_t)page >= (uint64_t)a.n_pages) continue;
+    const int valid = (e == n - 1) ? last_valid : kBlock;
+    const int64_t tile = ((int64_t)page * a.n_kv + h) * (kBlock * kDim);
+    const uint16_t* K = a.k_pages + tile;
+    const uint16_t* V = a.v_pages + tile;
+
+    uint4 kf[8][4];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int row = 32 * (t >> 1) + 8 * (col >> 2) + 4 * (t & 1) + (col & 3);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        kf[t][kk] = ld16(K + row * kDim + (4 * kk + grp) * 8);
+    }
+    uint4 vf[4][8];
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+      for (int n8 = 0; n8 < 8; ++n8)
+        vf[pp][n8] = ld16(V + (16 * n8 + col) * kBlock + 32 * pp + 8 * grp);
+
+    // S[t][hh] for token row col of tile t, summed over the lane groups
+    float s[8][G];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float c = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) c = dot8(kf[t][kk], qv[hh][kk], c);
+        c += __shfl_xor(c, 16);
+        c += __shfl_xor(c, 32);
+        const int tok = 32 * (t >> 1) + 8 * (col >> 2) + 4 * (t & 1) + (col & 3);
+        s[t][hh] = tok < valid ? c * a.scale_log2 : kNegInf;
+      }
+    float alpha[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) mx = fmaxf(mx, s[t][hh]);
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      const float m_new = fmaxf(m_run[hh], mx);
+      alpha[hh] = fast_exp2(m_run[hh] - m_new);
+      float ps = 0.f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        s[t][hh] = fast_exp2(s[t][hh] - m_new);
+        ps += s[t][hh];
+      }
+      l_run[hh] = l_run[hh] * alpha[hh] + ps;  // over this lane's token rows
+      m_run[hh] = m_new;
+#pragma unroll
+      for (int n8 = 0; n8 < 8; ++n8) acc[n8][hh] *= alpha[hh];
+    }
+
+    if (valid < kBlock) {
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+        for (int n8 = 0; n8 < 8; ++n8)
+          vf[pp][n8] = mask_tokens(vf[pp][n8], 32 * pp + 8 * grp, valid);
+    }
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        // weight of token 32pp+8grp+j: tile 2pp+(j>=4), row 4grp+(j&3)
+        float w[G];
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh)
+          w[hh] = __shfl(s[2 * pp + (j >> 2)][hh], 16 * grp + 4 * grp + (j & 3));
+#pragma unroll
+        for (int n8 = 0; n8 < 8; ++n8) {
+          const uint4 v = vf[pp][n8];
+          const uint32_t vw = (j >> 1) == 0 ? v.x : (j >> 1) == 1 ? v.y
+                            : (j >> 1) == 2 ? v.z : v.w;
+          const float x = (j & 1) ? bf16hi(vw) : bf16lo(vw);
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) acc[n8][hh] = fmaf(w[hh], x, acc[n8][hh]);
+        }
+      }
+    }
+  }
+
+  const int64_t head0 = (int64_t)b * Hq + h * G;
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    float lt = l_run[hh];
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) lt += __shfl_xor(lt, o);
+#pragma unroll
+    for (int n8 = 0; n8 < 8; ++n8) {
+      float x = acc[n8][hh];
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      if (grp == 0)
+        a.part_acc[((head0 + hh) * a.n_chunks + i) * kDim + 16 * n8 + col] = x;
+    }
+    if (lane == 0)
+      a.part_ml[(head0 + hh) * a.n_chunks + i] = make_float2(m_run[hh], lt);
+  }
+}
+
 // One 128-thread workgroup per (sequence, query head): merge the partials of
 // its active chunks in chunk order.
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a,
@@ -299,7 +469,6 @@ hipError_t launch_decode_attn(const Method& m, bool use_mfma,
                               const int32_t* merged, const int32_t* n_merged,
                               int m_cap, const int32_t* lens, int batch,
                               float* out, void* workspace, hipStream_t stream) {
-  (void)use_mfma;
   if (batch == 0) return hipSuccess;
   AttnArgs a;
   a.q = q;
@@ -322,8 +491,18 @@ hipError_t launch_decode_attn(const Method& m, bool use_mfma,
   a.scale_log2 = scale * 1.4426950408889634f;
   const int64_t items = (int64_t)plan.n_chunks * batch * m.n_kv_heads;
   if (items > 0) {
-    hipLaunchKernelGGL(attn_mfma_kernel, dim3((unsigned)items), dim3(64), 0,
-                       stream, a);
+    const dim3 grid((unsigned)items), block(64);
+    if (use_mfma) {
+      hipLaunchKernelGGL(attn_mfma_kernel, grid, block, 0, stream, a);
+    } else {
+      switch (m.group) {
+        case 1: hipLaunchKernelGGL(attn_valu_kernel<1>, grid, block, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL(attn_valu_kernel<2>, grid, block, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL(attn_valu_kernel<4>, grid, block, 0, stream, a); break;
+        case 8: hipLaunchKernelGGL(attn_valu_kernel<8>, grid, block, 0, stream, a); break;
+        default: return hipErrorInvalidValue;
+      }
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

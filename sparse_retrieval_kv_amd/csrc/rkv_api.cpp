@@ -202,7 +202,7 @@ rkv_status rkv_select(const rkv_params* params, const uint16_t* q,
   rkv::Method m;
   RKV_TRY(check_params(params, &m));
   RKV_TRY(check_sizes(batch, max_blocks));
-  RKV_REQUIRE(q && reps && block_table && lens && sel_ids && n_sel,
+  RKV_REQUIRE(q && reps && block_table && lens && n_sel && (sel_ids || k_cap == 0),
               RKV_ERR_INVALID_ARG,
               "q, reps, block_table, lens, sel_ids and n_sel must not be NULL");
   RKV_REQUIRE(aligned16(q) && aligned16(reps), RKV_ERR_INVALID_ARG,
@@ -275,8 +275,12 @@ rkv_status rkv_decode_attn(const rkv_params* params, const uint16_t* q,
               "q, merged, n_merged, lens and out must not be NULL");
   RKV_REQUIRE(aligned16(q) && aligned16(out), RKV_ERR_INVALID_ARG,
               "q and out must be 16-byte aligned");
-  if (params->attn_impl == RKV_ATTN_VALU)
-    return fail(RKV_ERR_UNSUPPORTED, "the VALU attention variant is not built");
+  const bool use_mfma = params->attn_impl != RKV_ATTN_VALU;
+  RKV_REQUIRE(use_mfma || m.group == 1 || m.group == 2 || m.group == 4 ||
+                  m.group == 8,
+              RKV_ERR_UNSUPPORTED,
+              "the VALU attention variant supports groups 1, 2, 4 and 8 (got %d)",
+              m.group);
   const rkv::AttnPlan plan = rkv::plan_attention(
       batch, m.n_q_heads, m.n_kv_heads, m_cap, params->split_blocks);
   const size_t need = plan.partial_bytes + plan.ml_bytes;
@@ -286,7 +290,7 @@ rkv_status rkv_decode_attn(const rkv_params* params, const uint16_t* q,
   RKV_REQUIRE(aligned16(workspace), RKV_ERR_INVALID_ARG,
               "workspace is not 16-byte aligned");
   return hip_status(
-      rkv::launch_decode_attn(m, params->attn_impl != RKV_ATTN_VALU, plan,
+      rkv::launch_decode_attn(m, use_mfma, plan,
                               params->scale, q, k_pages, v_pages, n_pages,
                               merged, n_merged, m_cap, lens, batch, out,
                               workspace, stream),

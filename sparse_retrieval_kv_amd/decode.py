@@ -30,7 +30,7 @@ class DecodeSession:
         self.batch, self.max_blocks = block_table.shape
         self.prompt_lens = prompt_lens
         hkv, hq = prm.n_kv_heads, prm.n_q_heads
-        self.k_cap = B.topk_capacity(prm, self.max_blocks)
+        self.k_cap = max(1, B.topk_capacity(prm, self.max_blocks))
         self.m_cap = self.max_blocks
         self.reps = torch.zeros((self.batch, hkv, self.max_blocks, B.HEAD_DIM),
                                 dtype=torch.float32, device=dev)

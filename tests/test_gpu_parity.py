@@ -48,9 +48,10 @@ def i32(x):
 
 def make_session(batch, **pkw):
     s = batch.spec
-    prm = B.params(s.n_q_heads, s.n_kv_heads, init_tokens=s.init_tokens,
-                   local_tokens=s.local_tokens, topk_ppm=s.topk_ppm,
-                   dense_boundary=s.dense_boundary, **pkw)
+    kw = dict(init_tokens=s.init_tokens, local_tokens=s.local_tokens,
+              topk_ppm=s.topk_ppm, dense_boundary=s.dense_boundary)
+    kw.update(pkw)
+    prm = B.params(s.n_q_heads, s.n_kv_heads, **kw)
     sess = DecodeSession(prm, batch.k_pages, batch.v_pages, batch.block_table,
                          i32(batch.context))
     return prm, sess
@@ -439,3 +440,25 @@ def test_70b_shared_prefix_full_size_sampled():
         if t in (0, 15):
             torch.cuda.synchronize()
             oracle_full_check(batch, sess, t, seqs=[0, 6], heads=[1, 7])
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (16, 4), (64, 8)])
+def test_valu_variant_matches_oracle_and_mfma(hq, hkv):
+    spec = synth.custom("valu", batch=2, n_q_heads=hq, n_kv_heads=hkv,
+                        context=(9000, 4321), init_tokens=512, local_tokens=1000,
+                        dense_boundary=0, config_id=101)
+    batch = synth.make_batch(spec, DEV)
+    say("valu", hq, hkv)
+    outs = {}
+    for impl in (B.ATTN_MFMA, B.ATTN_VALU):
+        prm, sess = make_session(batch, attn_impl=impl)
+        prefill(batch, sess)
+        if impl == B.ATTN_MFMA:
+            kn, vn = batch.new_kv_bits(0)
+            sess.append(kn, vn, i32(batch.lens_at(0)))
+        sess.select(batch.q_bits(0), i32(batch.lens_at(0)))
+        sess.attend(batch.q_bits(0), i32(batch.lens_at(0)))
+        torch.cuda.synchronize()
+        oracle_full_check(batch, sess, 0)
+        outs[impl] = sess.out.cpu().numpy()
+    assert np.allclose(outs[B.ATTN_MFMA], outs[B.ATTN_VALU], rtol=1e-4, atol=1e-5)
