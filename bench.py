@@ -1,9 +1,10 @@
 """Decode-step benchmark of retrieval-sparse paged decode attention on one GPU.
 
-A step is one layer's decode step for the whole batch: rkv_append_kv (write
-the token, and a just-completed block's representation) -> rkv_select
-(inner-product scores, per-(sequence, KV head) top-k, merged block table)
--> rkv_decode_attn (split-K paged attention + log-sum-exp combine).
+A step is one layer's decode step for the whole batch: rkv_append_select
+(write the token and a just-completed block's representation; inner-product
+scores, per-(sequence, KV head) top-k and the merged block table, in one
+launch) -> rkv_decode_attn (split-K paged attention + log-sum-exp combine).
+The host tier adds rkv_stage_blocks + rkv_merge_table on a side stream.
 Inputs are synthetic and already resident in HBM when timing starts.
 
 Consecutive steps cycle over `--layers` independent copies of the layer's
@@ -31,7 +32,7 @@ sys.path.insert(0, ROOT)
 
 from sparse_retrieval_kv_amd import binding as B  # noqa: E402
 from sparse_retrieval_kv_amd import synth  # noqa: E402
-from sparse_retrieval_kv_amd.decode import DecodeSession  # noqa: E402
+from sparse_retrieval_kv_amd.decode import DecodeSession, HostTierSession  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "decode attn steps/s and attended-KV HBM GB/s (% of peak) at 64K-128K ctx, 1 GPU"
@@ -43,8 +44,9 @@ def log(*a):
 
 def step_bytes(spec, context, t):
     """Algorithmic bytes of one step: attended K+V (bf16) per (sequence, KV
-    head) plus the fp32 representations the scorer reads."""
-    kv = reps = 0
+    head), the fp32 representations the scorer reads, and the K+V of the
+    kept offload blocks (what the host tier stages)."""
+    kv = reps = kept = 0
     for L0 in context:
         L = int(L0) + t
         nb = -(-L // 128)
@@ -58,15 +60,15 @@ def step_bytes(spec, context, t):
         kv += tokens * 128 * 2 * 2
         if not dense and 0 < k < n_off:
             reps += n_off * 128 * 4
-    return kv * spec.n_kv_heads, reps * spec.n_kv_heads
+        kept += k * 128 * 128 * 2 * 2
+    return kv * spec.n_kv_heads, reps * spec.n_kv_heads, kept * spec.n_kv_heads
 
 
-def cpu_baseline(batch, budget_s=12.0, max_steps=8):
+def cpu_baseline(batch, host=None, budget_s=12.0, max_steps=8):
     """Time the float64 oracle's decode step on the host over a bounded
-    sample of the same workload (first sequences of the batch)."""
+    sample of the same workload (first sequence of the batch)."""
     import oracle as O
     spec = batch.spec
-    G = spec.group
     prm = O.Params(spec.n_q_heads, spec.n_kv_heads, spec.init_tokens,
                    spec.local_tokens, spec.topk_ppm, spec.dense_boundary)
     b = 0
@@ -76,6 +78,12 @@ def cpu_baseline(batch, budget_s=12.0, max_steps=8):
                             device=batch.k_pages.device)
     kp = batch.k_pages.index_select(0, pages).cpu().numpy().view(np.uint16)
     vp = batch.v_pages.index_select(0, pages).cpu().numpy().view(np.uint16)
+    if host is not None:  # blocks kept in host memory: read the host pools
+        ht = host.host_table_np[b, :nb]
+        on = np.nonzero(ht >= 0)[0]
+        hp = torch.as_tensor(ht[on].astype(np.int64))
+        kp[on] = host.host_k.index_select(0, hp).numpy().view(np.uint16)
+        vp[on] = host.host_v.index_select(0, hp).numpy().view(np.uint16)
     K, V = O.logical_kv(kp, vp, np.arange(nb), L0 + spec.steps - 1)
     reps = np.stack([O.block_reps(K[h]) for h in range(spec.n_kv_heads)])
     n = 0
@@ -103,17 +111,39 @@ def cpu_baseline(batch, budget_s=12.0, max_steps=8):
     }
 
 
+def stream_read_probe(dev, gib=2, reps=5):
+    """Achievable streaming-read bandwidth: rkv_read_probe over a buffer
+    larger than the Infinity Cache, median of `reps` timed launches."""
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    B.read_probe(buf, sink)
+    ms = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        B.read_probe(buf, sink)
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    del buf
+    return (gib << 30) / (sorted(ms)[len(ms) // 2] * 1e-3) / 1e9
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4])
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--layers", type=int, default=0,
                     help="KV-cache copies cycled over (0: enough to exceed 1 GiB)")
     ap.add_argument("--impl", default="auto", choices=["auto", "mfma", "valu"])
     ap.add_argument("--split", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one plain 1 GiB device-to-device copy first "
+                         "(a known-size reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -127,23 +157,50 @@ def main():
     torch.cuda.set_device(dev)
     B.lib()
 
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("calibration copy: 1 GiB read + 1 GiB written")
+
+    probe_gbs = stream_read_probe(dev)
+    log(f"streaming-read probe: {probe_gbs:.0f} GB/s")
+
     spec = synth.CONFIGS[args.config]
     log("config", args.config, spec.name)
-    base = synth.make_batch(spec, dev)
+    host = None
+    if spec.host_offload:
+        max_blocks = -(-(max(spec.context) + spec.steps - 1) // 128)
+        base = synth.make_batch(spec, dev, extra_pages=spec.batch * max_blocks)
+    else:
+        base = synth.make_batch(spec, dev)
     layer_bytes = 2 * base.k_pages.numel() * 2
     n_layers = args.layers or max(1, min(16, math.ceil((1 << 30) / layer_bytes)))
     impl = {"auto": B.ATTN_AUTO, "mfma": B.ATTN_MFMA, "valu": B.ATTN_VALU}[args.impl]
     prm = B.params(spec.n_q_heads, spec.n_kv_heads, init_tokens=spec.init_tokens,
                    local_tokens=spec.local_tokens, topk_ppm=spec.topk_ppm,
                    dense_boundary=spec.dense_boundary, attn_impl=impl,
-                   split_blocks=args.split)
+                   split_waves=args.split)
     ctx = torch.as_tensor(base.context.astype(np.int32), device=dev)
     sessions = []
     for layer in range(n_layers):
         kp = base.k_pages if layer == 0 else base.k_pages.clone()
         vp = base.v_pages if layer == 0 else base.v_pages.clone()
-        s = DecodeSession(prm, kp, vp, base.block_table, ctx)
-        s.build_reps(ctx - 1)
+        if spec.host_offload:
+            # representations are built with every block in HBM, then the
+            # offload blocks move to pinned host memory
+            s = HostTierSession(prm, kp, vp, base.block_table, ctx)
+            s.build_reps(ctx - 1)
+            torch.cuda.synchronize()
+            host = synth.move_offload_to_host(base)
+            s.attach_host(host.host_k, host.host_v, host.host_table)
+            log(f"host tier: {host.host_k.numel() * 4 / 2**30:.2f} GiB of K/V "
+                "in pinned host memory")
+        else:
+            s = DecodeSession(prm, kp, vp, base.block_table, ctx)
+            s.build_reps(ctx - 1)
         sessions.append(s)
     log(f"{n_layers} layer copies, {layer_bytes / 2**20:.0f} MiB each")
 
@@ -153,18 +210,19 @@ def main():
     lens = [torch.as_tensor(base.lens_at(t), device=dev) for t in range(T)]
     torch.cuda.synchronize()
 
-    def run(s_idx, ev=None):
+    def run(s_idx):
         layer = s_idx % n_layers
         t = (s_idx // n_layers) % T
         sess = sessions[layer]
         kn, vn = news[t]
-        sess.append(kn, vn, lens[t])
-        sess.select(qs[t], lens[t])
-        if ev is not None:
-            ev[0].record()
+        sess.append_select(qs[t], kn, vn, lens[t])
+        if host is not None:  # stage the kept host blocks on the side stream
+            main = torch.cuda.current_stream(dev)
+            sess.side.wait_stream(main)
+            with torch.cuda.stream(sess.side):
+                sess.stage(lens[t])
+            main.wait_stream(sess.side)
         sess.attend(qs[t], lens[t])
-        if ev is not None:
-            ev[1].record()
         return t
 
     for i in range(args.warmup):
@@ -172,29 +230,60 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} done; timing {args.steps} steps")
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # timed region: K whole steps, nothing else on the stream
     ts = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        ts.append(run(args.warmup + i, evs[i]))
+        ts.append(run(args.warmup + i))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    attn_ms = np.array([a.elapsed_time(b) for a, b in evs])
     ms_per_step = wall * 1e3 / args.steps
+
+    # the attention call alone, replayed on every layer copy's current merged
+    # tables between one pair of HIP events on its stream (an event pair per
+    # launch would add its own overhead to every launch)
+    reps_attn = max(args.steps, 2 * n_layers)
+    t_last = ts[-1]
+    ev0, ev1 = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(reps_attn):
+        sessions[i % n_layers].attend(qs[t_last], lens[t_last])
+    ev1.record()
+    torch.cuda.synchronize()
+    attn_us = ev0.elapsed_time(ev1) * 1e3 / reps_attn
+    kv_attn = step_bytes(spec, base.context, t_last)[0]
+
+    staging = None
+    if host is not None:
+        sess = sessions[0]
+        n_st = 8
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(n_st):
+            sess.stage(lens[t_last])
+        ev1.record()
+        torch.cuda.synchronize()
+        st_us = ev0.elapsed_time(ev1) * 1e3 / n_st
+        kept = step_bytes(spec, base.context, t_last)[2]
+        staging = {"bytes_per_step": float(kept), "avg_us": st_us,
+                   "gbs": kept / (st_us * 1e-6) / 1e9,
+                   "path": "pinned host DRAM -> HBM staging pages (gather kernel "
+                           "reading host memory) + merge, side stream"}
+        log(f"staging {st_us:.0f} us/step, {staging['gbs']:.1f} GB/s")
 
     kv_b = np.array([step_bytes(spec, base.context, t)[0] for t in ts], dtype=np.float64)
     rep_b = np.array([step_bytes(spec, base.context, t)[1] for t in ts], dtype=np.float64)
     step_gbs = (kv_b.sum() + rep_b.sum()) / wall / 1e9
-    attn_gbs = kv_b.sum() / (attn_ms.sum() * 1e-3) / 1e9
-    log(f"{ms_per_step * 1e3:.1f} us/step, attention {attn_ms.mean() * 1e3:.1f} us "
-        f"avg ({attn_gbs:.0f} GB/s), step-level {step_gbs:.0f} GB/s")
+    attn_gbs = kv_attn / (attn_us * 1e-6) / 1e9
+    log(f"{ms_per_step * 1e3:.1f} us/step, attention {attn_us:.1f} us avg "
+        f"({attn_gbs:.0f} GB/s), step-level {step_gbs:.0f} GB/s")
 
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(base)
+        cpu = cpu_baseline(base, host)
 
     res = {
         "metric": METRIC,
@@ -218,20 +307,25 @@ def main():
             "init_local_topk_ppm": [spec.init_tokens, spec.local_tokens, spec.topk_ppm],
             "layer_copies": n_layers,
             "attn_impl": args.impl,
-            "split_blocks": args.split,
+            "split_waves": args.split,
         },
+        "stream_read_probe_gbs": probe_gbs,
+        "host_staging": staging,
         "attended_kv_gbs_step": step_gbs,
         "attended_kv_pct_peak_step": 100.0 * step_gbs / HBM_PEAK_GBS,
         "roofline": {
             "bound": "hbm",
-            "kernel": "rkv_decode_attn (split-K partials + combine)",
+            "kernel": "rkv_decode_attn (attn_mfma_kernel + attn_combine_kernel)",
             "achieved": attn_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": attn_gbs / HBM_PEAK_GBS,
+            "frac_of_read_probe": attn_gbs / probe_gbs,
             "traffic": None,
-            "bytes_per_launch": float(kv_b.mean()),
-            "avg_launch_us": float(attn_ms.mean() * 1e3),
+            "bytes_per_launch": float(kv_attn),
+            "avg_launch_us": float(attn_us),
+            "timing": (f"{reps_attn} back-to-back rkv_decode_attn calls over the "
+                       f"{n_layers} layer copies between one HIP event pair"),
         },
         "cpu_baseline": cpu,
     }

@@ -94,7 +94,8 @@ typedef struct rkv_params {
                               0 disables the dense switch */
   float scale;             /* softmax scale, default 1/sqrt(128) */
   int32_t attn_impl;       /* RKV_ATTN_AUTO / _MFMA / _VALU */
-  int32_t split_blocks;    /* merged blocks per split-K work item; 0 = auto */
+  int32_t split_waves;     /* waves the attention split is spread over;
+                              0 = auto (1024: one per SIMD on MI355X) */
 } rkv_params;
 
 /* Defaults of the page (init 1024, local 7192, ratio 0.2, dense boundary
@@ -189,17 +190,76 @@ rkv_status rkv_select(const rkv_params* params, const uint16_t* q,
                       size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * rkv_append_select -- rkv_append_kv followed by rkv_select in ONE launch
+ * (same arguments and results as the two calls in that order; reps is
+ * written for a block the appended token completes).  The selection never
+ * reads the appended token or that block's representation: the block
+ * holding slot L - 1 is the sequence's last, which is always local.  For a
+ * decode step this saves one launch and its memory round trips.
+ * Errors: as rkv_append_kv and rkv_select.
+ */
+rkv_status rkv_append_select(const rkv_params* params, const uint16_t* k_new,
+                             const uint16_t* v_new, uint16_t* k_pages,
+                             uint16_t* v_pages, int64_t n_pages,
+                             const uint16_t* q, float* reps,
+                             const int32_t* block_table, const int32_t* lens,
+                             const int32_t* prompt_lens, int32_t batch,
+                             int32_t max_blocks, int32_t* sel_ids,
+                             int32_t* n_sel, int32_t k_cap, int32_t* merged,
+                             int32_t* n_merged, int32_t m_cap, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/*
  * rkv_merge_table -- the merge step of rkv_select on its own: builds merged /
  * n_merged from given selections (sel_ids / n_sel, logical ids ascending,
- * all inside the offload range) with the region rule above.
+ * all inside the offload range) with the region rule above.  Init and local
+ * blocks come from block_table.  host_table ([batch][max_blocks] device
+ * int32, or NULL) marks blocks kept in host memory (entry >= 0): the r-th
+ * kept block of sequence b, when it is such a block, is taken to live at
+ * page stage_page0 + b * k_cap + r (the staging pages rkv_stage_blocks
+ * fills); every other block comes from block_table.  Ids outside the offload
+ * range are written as page -1, which rkv_decode_attn skips.
  * Same capacity rule for m_cap.  Errors as rkv_select.
  */
 rkv_status rkv_merge_table(const rkv_params* params, const int32_t* block_table,
                            int32_t max_blocks, const int32_t* lens,
                            const int32_t* sel_ids, const int32_t* n_sel,
-                           int32_t k_cap, int32_t batch, int32_t* merged,
-                           int32_t* n_merged, int32_t m_cap,
+                           int32_t k_cap, int32_t batch,
+                           const int32_t* host_table, int64_t stage_page0,
+                           int32_t* merged, int32_t* n_merged, int32_t m_cap,
                            hipStream_t stream);
+
+/*
+ * rkv_stage_blocks -- host tier (openGauss page, "Feature Description" and
+ * "Overall Solution": the offload part of the KV cache is kept in host DDR
+ * and the blocks selected at a decode round are loaded into HBM before
+ * attention; "Configuration Parameters": prompts beyond the offload boundary
+ * keep their offload region on the host).
+ * For every (b, h) and r < min(n_sel[b][h], k_cap): copies the K tile and the
+ * V tile of head h of logical block j = sel_ids[b][h][r] from host page
+ * host_table[b][j] of the host pools to page stage_page0 + b * k_cap + r of
+ * the device pools (head h's slice only).  One kernel reads the host pools
+ * directly over the bus; no host round trip is needed for the ids.
+ *   host_k, host_v  HOST pointers to pinned, device-mapped memory (e.g.
+ *                   hipHostMalloc), n_host_pages pages, same tile layouts as
+ *                   k_pages / v_pages; checked on the host
+ *   host_table      [batch][max_blocks] device int32: host page of each
+ *                   block, -1 when the block is not in host memory (such
+ *                   entries, and ids outside [0, max_blocks), copy nothing)
+ *   sel_ids, n_sel  as written by rkv_select
+ *   k_pages, v_pages device pools of n_pages pages; pages
+ *                   [stage_page0, stage_page0 + batch * k_cap) are the
+ *                   staging area and must lie inside the pool
+ * Errors: RKV_ERR_INVALID_ARG (including host pools that are not pinned and
+ * mapped), RKV_ERR_UNSUPPORTED, RKV_ERR_HIP.
+ */
+rkv_status rkv_stage_blocks(const rkv_params* params, const uint16_t* host_k,
+                            const uint16_t* host_v, int64_t n_host_pages,
+                            const int32_t* host_table, int32_t max_blocks,
+                            const int32_t* sel_ids, const int32_t* n_sel,
+                            int32_t k_cap, int32_t batch, uint16_t* k_pages,
+                            uint16_t* v_pages, int64_t n_pages,
+                            int64_t stage_page0, hipStream_t stream);
 
 /*
  * Workspace bytes rkv_decode_attn needs for these sizes.
@@ -218,9 +278,11 @@ size_t rkv_attn_workspace_size(const rkv_params* params, int32_t batch,
  * block, which holds L - 128 * (ceil(L/128) - 1) tokens.  A (b, h) with
  * n_merged = 0 writes zeros.
  * The work is split over the merged blocks (split-K, the Flash-Decoding
- * idiom named in the CSDN survey's references) and the partial softmax
- * results are merged by their log-sum-exp (the survey's cascade-inference
- * paragraph: partial results merged the FlashDecoding way).
+ * idiom named in the CSDN survey's references): the 64-token halves of all
+ * merged blocks of the batch are spread evenly over split_waves waves, and
+ * the partial softmax results are merged by their log-sum-exp (the
+ * survey's cascade-inference paragraph: partial results merged the
+ * FlashDecoding way).  batch * n_kv_heads * m_cap must stay below 2^30.
  *   merged [batch][n_kv_heads][m_cap], n_merged [batch][n_kv_heads]
  *   out [batch][n_q_heads][128] fp32
  *   workspace >= rkv_attn_workspace_size(params, batch, m_cap) bytes
@@ -234,6 +296,17 @@ rkv_status rkv_decode_attn(const rkv_params* params, const uint16_t* q,
                            const int32_t* lens, int32_t batch, float* out,
                            void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
+
+/*
+ * rkv_read_probe -- measurement helper, not part of the method: reads
+ * `bytes` (rounded down to 16) of device memory once with 16-byte loads from
+ * every compute unit and XORs the data into *sink (a device uint32), so that
+ * a caller can time the achievable streaming-read bandwidth next to the
+ * nominal HBM peak.  buffer must be 16-byte aligned.
+ * Errors: RKV_ERR_INVALID_ARG, RKV_ERR_HIP.
+ */
+rkv_status rkv_read_probe(const void* buffer, size_t bytes, uint32_t* sink,
+                          hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -15,7 +15,7 @@ import re
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "librkv.so")
+LIB_PATH = os.environ.get("RKV_LIB") or os.path.join(HERE, "librkv.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "rkv.h")
 
 RKV_OK, RKV_ERR_INVALID_ARG, RKV_ERR_UNSUPPORTED, RKV_ERR_WORKSPACE, RKV_ERR_HIP = range(5)
@@ -30,7 +30,7 @@ class Params(ctypes.Structure):
                 ("init_tokens", ctypes.c_int32), ("local_tokens", ctypes.c_int32),
                 ("topk_ppm", ctypes.c_int32), ("dense_boundary", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("attn_impl", ctypes.c_int32),
-                ("split_blocks", ctypes.c_int32)]
+                ("split_waves", ctypes.c_int32)]
 
     def __repr__(self):
         return "Params(" + ", ".join(f"{n}={getattr(self, n)}"
@@ -60,11 +60,17 @@ _SIGS = {
     "rkv_select_workspace_size": (_SZ, [_PP, _I32, _I32]),
     "rkv_select": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _I32,
                                   _P, _P, _I32, _P, _SZ, _P]),
-    "rkv_merge_table": (ctypes.c_int, [_PP, _P, _I32, _P, _P, _P, _I32, _I32, _P, _P,
-                                       _I32, _P]),
+    "rkv_append_select": (ctypes.c_int, [_PP, _P, _P, _P, _P, _I64, _P, _P, _P, _P,
+                                         _P, _I32, _I32, _P, _P, _I32, _P, _P, _I32,
+                                         _P, _SZ, _P]),
+    "rkv_merge_table": (ctypes.c_int, [_PP, _P, _I32, _P, _P, _P, _I32, _I32, _P,
+                                       _I64, _P, _P, _I32, _P]),
+    "rkv_stage_blocks": (ctypes.c_int, [_PP, _P, _P, _I64, _P, _I32, _P, _P, _I32,
+                                        _I32, _P, _P, _I64, _I64, _P]),
     "rkv_attn_workspace_size": (_SZ, [_PP, _I32, _I32]),
     "rkv_decode_attn": (ctypes.c_int, [_PP, _P, _P, _P, _I64, _P, _P, _I32, _P, _I32,
                                        _P, _P, _SZ, _P]),
+    "rkv_read_probe": (ctypes.c_int, [_P, _SZ, _P, _P]),
 }
 
 _lib = None
@@ -80,7 +86,9 @@ def lib() -> ctypes.CDLL:
                 "(python -c 'import __graft_entry__ as g; g.build()')")
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGS.items():
-            f = getattr(L, name)
+            f = getattr(L, name, None)
+            if f is None:  # an older library without this export
+                continue
             f.restype = res
             f.argtypes = args
         _lib = L
@@ -162,13 +170,53 @@ def select(p: Params, q, reps, block_table, lens, sel_ids, n_sel,
         _ptr(workspace, None, "workspace"), ws_bytes, _stream(q)))
 
 
-def merge_table(p: Params, block_table, lens, sel_ids, n_sel, merged, n_merged):
+def append_select(p: Params, k_new, v_new, k_pages, v_pages, q, reps, block_table,
+                  lens, sel_ids, n_sel, merged=None, n_merged=None,
+                  prompt_lens=None, workspace=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().rkv_append_select(
+        ctypes.byref(p), _ptr(k_new, torch.int16, "k_new"),
+        _ptr(v_new, torch.int16, "v_new"), _ptr(k_pages, torch.int16, "k_pages"),
+        _ptr(v_pages, torch.int16, "v_pages"), k_pages.shape[0],
+        _ptr(q, torch.int16, "q"), _ptr(reps, torch.float32, "reps"),
+        _ptr(block_table, torch.int32, "block_table"), _ptr(lens, torch.int32, "lens"),
+        _ptr(prompt_lens, torch.int32, "prompt_lens"), lens.shape[0],
+        block_table.shape[1], _ptr(sel_ids, torch.int32, "sel_ids"),
+        _ptr(n_sel, torch.int32, "n_sel"), sel_ids.shape[-1],
+        _ptr(merged, torch.int32, "merged"), _ptr(n_merged, torch.int32, "n_merged"),
+        merged.shape[-1] if merged is not None else 0,
+        _ptr(workspace, None, "workspace"), ws_bytes, _stream(q)))
+
+
+def merge_table(p: Params, block_table, lens, sel_ids, n_sel, merged, n_merged,
+                host_table=None, stage_page0: int = -1):
     _check(lib().rkv_merge_table(
         ctypes.byref(p), _ptr(block_table, torch.int32, "block_table"),
         block_table.shape[1], _ptr(lens, torch.int32, "lens"),
         _ptr(sel_ids, torch.int32, "sel_ids"), _ptr(n_sel, torch.int32, "n_sel"),
-        sel_ids.shape[-1], lens.shape[0], _ptr(merged, torch.int32, "merged"),
+        sel_ids.shape[-1], lens.shape[0],
+        _ptr(host_table, torch.int32, "host_table"), stage_page0,
+        _ptr(merged, torch.int32, "merged"),
         _ptr(n_merged, torch.int32, "n_merged"), merged.shape[-1], _stream(lens)))
+
+
+def _host_ptr(t, name):
+    if not isinstance(t, torch.Tensor) or t.is_cuda or not t.is_pinned():
+        raise ValueError(f"{name} must be a pinned host tensor")
+    if t.dtype != torch.int16 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int16 tensor")
+    return t.data_ptr()
+
+
+def stage_blocks(p: Params, host_k, host_v, host_table, sel_ids, n_sel,
+                 k_pages, v_pages, stage_page0: int):
+    _check(lib().rkv_stage_blocks(
+        ctypes.byref(p), _host_ptr(host_k, "host_k"), _host_ptr(host_v, "host_v"),
+        host_k.shape[0], _ptr(host_table, torch.int32, "host_table"),
+        host_table.shape[1], _ptr(sel_ids, torch.int32, "sel_ids"),
+        _ptr(n_sel, torch.int32, "n_sel"), sel_ids.shape[-1], n_sel.shape[0],
+        _ptr(k_pages, torch.int16, "k_pages"), _ptr(v_pages, torch.int16, "v_pages"),
+        k_pages.shape[0], stage_page0, _stream(k_pages)))
 
 
 def attn_workspace_size(p: Params, batch: int, m_cap: int) -> int:
@@ -188,6 +236,13 @@ def decode_attn(p: Params, q, k_pages, v_pages, merged, n_merged, lens, out,
         ws_bytes, _stream(q)))
 
 
+def read_probe(buf, sink):
+    """Stream-read `buf` once on the device (bandwidth measurement helper)."""
+    _check(lib().rkv_read_probe(_ptr(buf, None, "buffer"),
+                                buf.numel() * buf.element_size(),
+                                _ptr(sink, None, "sink"), _stream(buf)))
+
+
 def ceil_div(a: int, b: int) -> int:
     return -(-a // b)
 
@@ -201,5 +256,6 @@ def topk_capacity(p: Params, max_blocks: int) -> int:
 
 __all__ = ["Params", "RkvError", "lib", "params", "build_reps", "append_kv",
            "select", "merge_table", "decode_attn", "attn_workspace_size",
-           "select_workspace_size", "topk_capacity", "header_functions",
+           "select_workspace_size", "topk_capacity", "header_functions", "read_probe",
+           "stage_blocks", "append_select",
            "ATTN_AUTO", "ATTN_MFMA", "ATTN_VALU"]

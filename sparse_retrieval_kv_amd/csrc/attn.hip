@@ -3,16 +3,27 @@
 // softmax(q K^T / sqrt(d)) V for one query token per head (rkmt.cn ATB
 // KV-cache article, section 1.1), reading K/V pages through a block table
 // (same article, section 2.2), over the merged block list of each
-// (sequence, KV head).  The list is cut into chunks of `chunk` blocks; one
-// wave computes the online-softmax partial (m, l, acc) of one chunk for all
-// query heads of the group, and a second kernel merges the partials of a
-// head by their log-sum-exp (partial results merged the FlashDecoding way,
-// CSDN "KV cache" survey, section "Share--KV cache共享").
+// (sequence, KV head).  Partial softmax results are merged by their
+// log-sum-exp (partial results merged the FlashDecoding way, CSDN "KV cache"
+// survey, section "Share--KV cache共享").
 //
-// MFMA schedule for one 128-token block (query heads padded to 16):
+// Work partition.  Every merged block is cut into two 64-token halves
+// ("units"); the units of all (sequence, KV head) lists, taken in order,
+// form one range of T units that is split evenly over a fixed number W of
+// waves: wave w owns units [floor(wT/W), floor((w+1)T/W)).  A wave's range
+// meets one or a few lists; for each list it meets it writes one partial
+// (m, l, acc) to slot w + bh (unique: along the range both w and bh only
+// grow).  T is known only on the device, so every wave (and the combine)
+// derives the partition from n_merged itself: ragged batches stay balanced
+// and no host round trip is needed.  Within a list, a wave's loads are
+// software-pipelined: unit u+1's K tile is requested right after unit u's V
+// tile, so about 32 KiB per wave stay in flight while unit u's softmax and
+// PV products run (one wave per SIMD, 1024 waves on 256 compute units).
+//
+// MFMA math for one 64-token unit (query heads padded to 16):
 //   S^T[16 tokens x 16 heads] = K_tile[16 x 128] . Q^T[128 x 16]
 //     with v_mfma_f32_16x16x32_bf16, four K-steps of 32 dims per tile,
-//     eight tiles per block.  The accumulator layout (lane l holds rows
+//     four tiles per unit.  The accumulator layout (lane l holds rows
 //     4(l/16)+r, column l%16) puts four tokens of head l%16 in each lane.
 //   O[16 heads x 16 dims] += P[16 x 32 tokens] . V[32 tokens x 16 dims]
 //     with the same instruction: the two S^T tiles of a 32-token pair are
@@ -20,12 +31,12 @@
 //     lane group), so P never leaves the registers.  P is split into a bf16
 //     high part and a bf16 residual (two MFMAs) so the weights keep ~16
 //     significant bits; V is bf16 already.
-// Token order inside a block is chosen so that every load is 16 contiguous
+// Token order inside a unit is chosen so that every load is 16 contiguous
 // bytes per lane: in pair pp, lane group g owns tokens 32pp+8g .. 32pp+8g+7.
 //   K tile (pair pp, half e): row m holds token 32pp + 8(m/4) + 4e + m%4,
 //   V: lane (col, g) reads dim 16n+col, tokens 32pp+8g..+7 (one 16-byte
 //   piece of the dim-major V tile).
-// Every block's (page, head) K and V tiles are read exactly once.
+// Every (page, head) K and V tile is read exactly once.
 #include "rkv_device.h"
 #include "rkv_internal.h"
 
@@ -35,9 +46,11 @@ namespace rkv {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -INFINITY;
+constexpr int kUnit = 64;  // tokens per work unit (half a block)
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
@@ -88,90 +101,125 @@ struct AttnArgs {
   const int32_t* merged;
   const int32_t* n_merged;
   const int32_t* lens;
-  float* part_acc;   // [B*Hq][n_chunks][128]
-  float2* part_ml;   // [B*Hq][n_chunks]
-  int m_cap, max_len, batch, n_kv, group, chunk, n_chunks;
+  float* part_acc;   // [n_slots][group][128]
+  float2* part_ml;   // [n_slots][group]
+  int m_cap, max_len, batch, n_kv, group, n_waves;
   float scale_log2;  // scale * log2(e)
 };
 
-// Work item = (chunk i, sequence-head bh), chunk-major so that the first
-// chunks of every (b, h) come first.
-__global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
-  const int lane = threadIdx.x;
-  const int col = lane & 15, grp = lane >> 4;
-  const int n_bh = a.batch * a.n_kv;
-  const int i = blockIdx.x / n_bh;
-  const int bh = blockIdx.x - i * n_bh;
+// ---------------------------------------------------------------------------
+// The unit partition, shared by the split kernel and the combine.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int units_of(const AttnArgs& a, int bh) {
   int n = a.n_merged[bh];
   n = n < 0 ? 0 : (n > a.m_cap ? a.m_cap : n);
-  const int e0 = i * a.chunk;
-  if (e0 >= n) return;
-  const int e1 = e0 + a.chunk < n ? e0 + a.chunk : n;
-  const int b = bh / a.n_kv, h = bh - b * a.n_kv;
-  const int G = a.group;
-  const int Hq = a.n_kv * G;
-  const int L = clamp_len(a.lens[b], a.max_len);
-  const int last_valid = L - (((L + 127) >> 7) - 1) * kBlock;
+  return 2 * n;
+}
+
+__device__ __forceinline__ int64_t unit_start(int w, int64_t T, int W) {
+  return (int64_t)w * T / W;
+}
+
+// The wave whose range holds unit u (0 <= u < T): the largest w with
+// unit_start(w) <= u.
+__device__ __forceinline__ int wave_of(int64_t u, int64_t T, int W) {
+  return (int)(((u + 1) * W - 1) / T);
+}
+
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// One unit's K and V tiles.
+// ---------------------------------------------------------------------------
+
+// K tile of unit hf (tokens 64hf..64hf+63) into the S^T A-operand layout:
+// tile t (16 tokens) and K-step kk, lane (col, grp) -> token row(t, col),
+// dims 8*(4kk+grp)..+7.
+__device__ __forceinline__ void load_k_unit(uint4 (&kf)[4][4], const uint16_t* K,
+                                            int hf, int col, int grp) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int row = kUnit * hf + 32 * (t >> 1) + 8 * (col >> 2) + 4 * (t & 1) + (col & 3);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      kf[t][kk] = ld16(K + row * kDim + (4 * kk + grp) * 8);
+  }
+}
+
+// V tile of unit hf into the PV B-operand layout: pair pp, dim tile n8,
+// lane (col, grp) -> dim 16*n8+col, tokens 64hf+32pp+8grp..+7.
+__device__ __forceinline__ void load_v_unit(uint4 (&vf)[2][8], const uint16_t* V,
+                                            int hf, int col, int grp) {
+#pragma unroll
+  for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+    for (int n8 = 0; n8 < 8; ++n8)
+      vf[pp][n8] = ld16(V + (16 * n8 + col) * kBlock + kUnit * hf + 32 * pp + 8 * grp);
+}
+
+// ---------------------------------------------------------------------------
+// Math policies: MFMA (query heads packed against K tiles) and VALU.
+// ---------------------------------------------------------------------------
+
+struct MfmaMath {
+  typedef f32x4 Scores[4];
+  bf16x8 bq[4];
+  f32x4 acc[8];
+  float m_run, l_run;
 
   // Q^T as the B operand: lane (col, grp) holds head col, dims of chunk
   // 4kk+grp (8 bf16) for kk = 0..3; padded heads are zero.
-  bf16x8 bq[4];
-  {
-    const uint16_t* qrow = a.q + ((int64_t)b * Hq + h * G + col) * kDim;
+  __device__ __forceinline__ void begin(const AttnArgs& a, int b, int h, int col,
+                                        int grp) {
+    const int G = a.group;
+    const uint16_t* qrow = a.q + ((int64_t)b * a.n_kv * G + h * G + col) * kDim;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       uint4 v = make_uint4(0, 0, 0, 0);
       if (col < G) v = ld16(qrow + (4 * kk + grp) * 8);
       bq[kk] = as_bf16x8(v);
     }
+#pragma unroll
+    for (int n8 = 0; n8 < 8; ++n8) acc[n8] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    m_run = kNegInf;
+    l_run = 0.f;
   }
 
-  f32x4 acc[8];
+  __device__ __forceinline__ void scores(const uint4 (&kf)[4][4], Scores& s) {
 #pragma unroll
-  for (int n8 = 0; n8 < 8; ++n8) acc[n8] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf, l_run = 0.f;
-  const int32_t* mrow = a.merged + (int64_t)bh * a.m_cap;
-
-  for (int e = e0; e < e1; ++e) {
-    const int page = mrow[e];
-    if ((uint64_t)(int64_t)page >= (uint64_t)a.n_pages) continue;
-    const int valid = (e == n - 1) ? last_valid : kBlock;
-    const int64_t tile = ((int64_t)page * a.n_kv + h) * (kBlock * kDim);
-    const uint16_t* K = a.k_pages + tile;
-    const uint16_t* V = a.v_pages + tile;
-
-    uint4 kf[8][4];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int row = 32 * (t >> 1) + 8 * (col >> 2) + 4 * (t & 1) + (col & 3);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        kf[t][kk] = ld16(K + row * kDim + (4 * kk + grp) * 8);
-    }
-    uint4 vf[4][8];
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp)
-#pragma unroll
-      for (int n8 = 0; n8 < 8; ++n8)
-        vf[pp][n8] = ld16(V + (16 * n8 + col) * kBlock + 32 * pp + 8 * grp);
-
-    f32x4 s[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < 4; ++t) {
       s[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
         s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[t][kk]),
                                                        bq[kk], s[t], 0, 0, 0);
     }
+  }
 
-    // log2-domain logits, mask past the sequence end, block max per head
+  __device__ __forceinline__ void accumulate(Scores& s, uint4 (&vf)[2][8],
+                                             int valid, float sl2, int col, int grp) {
+    (void)col;
+    // log2-domain logits, mask past the sequence end, unit max per head
     float mx = kNegInf;
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float x = s[t][r] * a.scale_log2;
+        float x = s[t][r] * sl2;
         const int tok = 32 * (t >> 1) + 8 * grp + 4 * (t & 1) + r;
         x = tok < valid ? x : kNegInf;
         s[t][r] = x;
@@ -183,7 +231,7 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
     const float alpha = fast_exp2(m_run - m_new);
     float psum = 0.f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float p = fast_exp2(s[t][r] - m_new);
@@ -199,17 +247,15 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
       for (int n8 = 0; n8 < 8; ++n8) acc[n8][r] *= ar;
     }
-
-    if (valid < kBlock) {
+    if (valid < kUnit) {
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp)
+      for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
         for (int n8 = 0; n8 < 8; ++n8)
           vf[pp][n8] = mask_tokens(vf[pp][n8], 32 * pp + 8 * grp, valid);
     }
-
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
+    for (int pp = 0; pp < 2; ++pp) {
       const float p8[8] = {s[2 * pp][0],     s[2 * pp][1],     s[2 * pp][2],
                            s[2 * pp][3],     s[2 * pp + 1][0], s[2 * pp + 1][1],
                            s[2 * pp + 1][2], s[2 * pp + 1][3]};
@@ -224,35 +270,36 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
     }
   }
 
-  // the four lane groups of a head hold disjoint token subsets of l
-  float lt = l_run + __shfl_xor(l_run, 16);
-  lt += __shfl_xor(lt, 32);
-  const int64_t head0 = (int64_t)b * Hq + h * G;
+  __device__ __forceinline__ void finish(const AttnArgs& a, int64_t slot, int lane,
+                                         int col, int grp) {
+    const int G = a.group;
+    // the four lane groups of a head hold disjoint token subsets of l
+    float lt = l_run + __shfl_xor(l_run, 16);
+    lt += __shfl_xor(lt, 32);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int hh = 4 * grp + r;
-    if (hh < G) {
-      float* dst = a.part_acc + ((head0 + hh) * a.n_chunks + i) * kDim + col;
+    for (int r = 0; r < 4; ++r) {
+      const int hh = 4 * grp + r;
+      if (hh < G) {
+        float* dst = a.part_acc + (slot * G + hh) * kDim + col;
 #pragma unroll
-      for (int n8 = 0; n8 < 8; ++n8) dst[16 * n8] = acc[n8][r];
+        for (int n8 = 0; n8 < 8; ++n8) dst[16 * n8] = acc[n8][r];
+      }
     }
+    if (lane < G) a.part_ml[slot * G + lane] = make_float2(m_run, lt);
   }
-  if (lane < G) a.part_ml[(head0 + lane) * a.n_chunks + i] = make_float2(m_run, lt);
-}
+};
 
-// Vector-ALU variant with the same memory schedule (same tiles, same
-// per-lane 16-byte pieces, same token order): the q.k products use
-// v_dot2_f32_bf16 on bf16 pairs and the p.v products fp32 FMAs, so the two
-// variants differ only in where the dot products run.
+// Vector-ALU variant with the same memory schedule (same units, same
+// per-lane 16-byte pieces, same token order): q.k by v_dot2_f32_bf16 on bf16
+// pairs, p.v by fp32 FMAs, so the two variants differ only in where the dot
+// products run.
 //   QK: lane (col, grp) holds 32 dims (chunks 4kk+grp) of token row col of
 //       each tile; partial dots for the G heads are summed over the four lane
 //       groups, leaving S[token(t, col)][head] in every lane of column col.
 //   PV: lane (col, grp) owns dims 16n+col and tokens 32pp+8grp..+7; the
 //       weights of those tokens are fetched from the lanes that own their
 //       rows, and the per-lane partial sums are folded over the lane groups
-//       once per work item.
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
+//       once per list piece.
 __device__ __forceinline__ float dot8(uint4 k, uint4 q, float c) {
   c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, k.x),
                                       __builtin_bit_cast(bf16x2, q.x), c, false);
@@ -266,70 +313,35 @@ __device__ __forceinline__ float dot8(uint4 k, uint4 q, float c) {
 }
 
 template <int G>
-__global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
-  const int lane = threadIdx.x;
-  const int col = lane & 15, grp = lane >> 4;
-  const int n_bh = a.batch * a.n_kv;
-  const int i = blockIdx.x / n_bh;
-  const int bh = blockIdx.x - i * n_bh;
-  int n = a.n_merged[bh];
-  n = n < 0 ? 0 : (n > a.m_cap ? a.m_cap : n);
-  const int e0 = i * a.chunk;
-  if (e0 >= n) return;
-  const int e1 = e0 + a.chunk < n ? e0 + a.chunk : n;
-  const int b = bh / a.n_kv, h = bh - b * a.n_kv;
-  const int Hq = a.n_kv * G;
-  const int L = clamp_len(a.lens[b], a.max_len);
-  const int last_valid = L - (((L + 127) >> 7) - 1) * kBlock;
-
+struct ValuMath {
+  typedef float Scores[4][G];
   uint4 qv[G][4];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      qv[hh][kk] = ld16(a.q + ((int64_t)b * Hq + h * G + hh) * kDim +
-                        (4 * kk + grp) * 8);
-
   float acc[8][G];
-#pragma unroll
-  for (int n8 = 0; n8 < 8; ++n8)
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) acc[n8][hh] = 0.f;
   float m_run[G], l_run[G];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    m_run[hh] = kNegInf;
-    l_run[hh] = 0.f;
-  }
-  const int32_t* mrow = a.merged + (int64_t)bh * a.m_cap;
 
-  for (int e = e0; e < e1; ++e) {
-    const int page = mrow[e];
-    if ((uint64_t)(int64_t)page >= (uint64_t)a.n_pages) continue;
-    const int valid = (e == n - 1) ? last_valid : kBlock;
-    const int64_t tile = ((int64_t)page * a.n_kv + h) * (kBlock * kDim);
-    const uint16_t* K = a.k_pages + tile;
-    const uint16_t* V = a.v_pages + tile;
-
-    uint4 kf[8][4];
+  __device__ __forceinline__ void begin(const AttnArgs& a, int b, int h, int col,
+                                        int grp) {
+    (void)col;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int row = 32 * (t >> 1) + 8 * (col >> 2) + 4 * (t & 1) + (col & 3);
+    for (int hh = 0; hh < G; ++hh)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        kf[t][kk] = ld16(K + row * kDim + (4 * kk + grp) * 8);
+        qv[hh][kk] = ld16(a.q + ((int64_t)b * a.n_kv * G + h * G + hh) * kDim +
+                          (4 * kk + grp) * 8);
+#pragma unroll
+    for (int n8 = 0; n8 < 8; ++n8)
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) acc[n8][hh] = 0.f;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      m_run[hh] = kNegInf;
+      l_run[hh] = 0.f;
     }
-    uint4 vf[4][8];
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp)
-#pragma unroll
-      for (int n8 = 0; n8 < 8; ++n8)
-        vf[pp][n8] = ld16(V + (16 * n8 + col) * kBlock + 32 * pp + 8 * grp);
+  }
 
-    // S[t][hh] for token row col of tile t, summed over the lane groups
-    float s[8][G];
+  __device__ __forceinline__ void scores(const uint4 (&kf)[4][4], Scores& s) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
         float c = 0.f;
@@ -337,40 +349,48 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
         for (int kk = 0; kk < 4; ++kk) c = dot8(kf[t][kk], qv[hh][kk], c);
         c += __shfl_xor(c, 16);
         c += __shfl_xor(c, 32);
-        const int tok = 32 * (t >> 1) + 8 * (col >> 2) + 4 * (t & 1) + (col & 3);
-        s[t][hh] = tok < valid ? c * a.scale_log2 : kNegInf;
+        s[t][hh] = c;
       }
-    float alpha[G];
+  }
+
+  __device__ __forceinline__ void accumulate(Scores& s, uint4 (&vf)[2][8],
+                                             int valid, float sl2, int col, int grp) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int tok = 32 * (t >> 1) + 8 * (col >> 2) + 4 * (t & 1) + (col & 3);
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh)
+        s[t][hh] = tok < valid ? s[t][hh] * sl2 : kNegInf;
+    }
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       float mx = kNegInf;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) mx = fmaxf(mx, s[t][hh]);
+      for (int t = 0; t < 4; ++t) mx = fmaxf(mx, s[t][hh]);
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
       const float m_new = fmaxf(m_run[hh], mx);
-      alpha[hh] = fast_exp2(m_run[hh] - m_new);
+      const float alpha = fast_exp2(m_run[hh] - m_new);
       float ps = 0.f;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
+      for (int t = 0; t < 4; ++t) {
         s[t][hh] = fast_exp2(s[t][hh] - m_new);
         ps += s[t][hh];
       }
-      l_run[hh] = l_run[hh] * alpha[hh] + ps;  // over this lane's token rows
+      l_run[hh] = l_run[hh] * alpha + ps;  // over this lane's token rows
       m_run[hh] = m_new;
 #pragma unroll
-      for (int n8 = 0; n8 < 8; ++n8) acc[n8][hh] *= alpha[hh];
+      for (int n8 = 0; n8 < 8; ++n8) acc[n8][hh] *= alpha;
     }
-
-    if (valid < kBlock) {
+    if (valid < kUnit) {
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp)
+      for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
         for (int n8 = 0; n8 < 8; ++n8)
           vf[pp][n8] = mask_tokens(vf[pp][n8], 32 * pp + 8 * grp, valid);
     }
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
+    for (int pp = 0; pp < 2; ++pp) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         // weight of token 32pp+8grp+j: tile 2pp+(j>=4), row 4grp+(j&3)
@@ -391,74 +411,282 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
     }
   }
 
-  const int64_t head0 = (int64_t)b * Hq + h * G;
+  __device__ __forceinline__ void finish(const AttnArgs& a, int64_t slot, int lane,
+                                         int col, int grp) {
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    float lt = l_run[hh];
+    for (int hh = 0; hh < G; ++hh) {
+      float lt = l_run[hh];
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) lt += __shfl_xor(lt, o);
+      for (int o = 1; o < 16; o <<= 1) lt += __shfl_xor(lt, o);
 #pragma unroll
-    for (int n8 = 0; n8 < 8; ++n8) {
-      float x = acc[n8][hh];
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
-      if (grp == 0)
-        a.part_acc[((head0 + hh) * a.n_chunks + i) * kDim + 16 * n8 + col] = x;
+      for (int n8 = 0; n8 < 8; ++n8) {
+        float x = acc[n8][hh];
+        x += __shfl_xor(x, 16);
+        x += __shfl_xor(x, 32);
+        if (grp == 0) a.part_acc[(slot * G + hh) * kDim + 16 * n8 + col] = x;
+      }
+      if (lane == 0) a.part_ml[slot * G + hh] = make_float2(m_run[hh], lt);
     }
-    if (lane == 0)
-      a.part_ml[(head0 + hh) * a.n_chunks + i] = make_float2(m_run[hh], lt);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Split kernel: one wave per range of units.
+// ---------------------------------------------------------------------------
+
+// Units [u0, u1) of list bh, written to partial slot `slot`.
+template <class Math>
+__device__ __forceinline__ void run_piece(const AttnArgs& a, Math& math, int bh,
+                                          int u0, int u1, int64_t slot, int lane,
+                                          int col, int grp) {
+  const int b = bh / a.n_kv, h = bh - b * a.n_kv;
+  const int32_t* mrow = a.merged + (int64_t)bh * a.m_cap;
+  const int n = units_of(a, bh) >> 1;
+  const int L = clamp_len(a.lens[b], a.max_len);
+  const int last_valid = L - (((L + 127) >> 7) - 1) * kBlock;
+  const int64_t head_off = (int64_t)h * (kBlock * kDim);
+  const int64_t page_stride = (int64_t)a.n_kv * (kBlock * kDim);
+  // an out-of-range page id is read from page 0 (always present) and its
+  // unit is skipped
+  auto page_ok = [&](int p) { return (uint64_t)(int64_t)p < (uint64_t)a.n_pages; };
+  auto tile_of = [&](int p) {
+    return (page_ok(p) ? (int64_t)p * page_stride : 0) + head_off;
+  };
+  auto valid_of = [&](int u) {
+    const int e = u >> 1;
+    const int v = (e == n - 1 ? last_valid : kBlock) - kUnit * (u & 1);
+    return v < 0 ? 0 : (v > kUnit ? kUnit : v);
+  };
+
+  math.begin(a, b, h, col, grp);
+  int page = mrow[u0 >> 1];
+  int64_t tile = tile_of(page);
+  uint4 kf[4][4];
+  load_k_unit(kf, a.k_pages + tile, u0 & 1, col, grp);
+  // page id of the entry after the current one, requested one unit early
+  int page_next = ((u0 >> 1) + 1 < n) ? mrow[(u0 >> 1) + 1] : 0;
+
+  for (int u = u0; u < u1; ++u) {
+    typename Math::Scores s;
+    math.scores(kf, s);
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 vf[2][8];
+    load_v_unit(vf, a.v_pages + tile, u & 1, col, grp);
+    const bool cur_ok = page_ok(page);
+    const int valid = valid_of(u);
+    if (u + 1 < u1) {  // prefetch the next unit's K tile
+      if (u & 1) {     // the next unit starts the next entry
+        page = page_next;
+        tile = tile_of(page);
+        const int e2 = (u >> 1) + 2;
+        page_next = e2 < n ? mrow[e2] : 0;
+      }
+      load_k_unit(kf, a.k_pages + tile, (u + 1) & 1, col, grp);
+    }
+    if (!cur_ok || valid == 0) continue;
+    math.accumulate(s, vf, valid, a.scale_log2, col, grp);
+  }
+  math.finish(a, slot, lane, col, grp);
+}
+
+template <class Math>
+__device__ __forceinline__ void split_body(const AttnArgs& a) {
+  const int lane = threadIdx.x;
+  const int col = lane & 15, grp = lane >> 4;
+  const int w = blockIdx.x;
+  const int NB = a.batch * a.n_kv;
+  int64_t T = 0;
+  for (int base = 0; base < NB; base += 64) {
+    const int bh = base + lane;
+    T += wave_sum_i(bh < NB ? units_of(a, bh) : 0);
+  }
+  if (T == 0) return;
+  const int W = a.n_waves;
+  const int64_t lo = unit_start(w, T, W), hi = unit_start(w + 1, T, W);
+  if (lo >= hi) return;
+  Math math;
+  int64_t run = 0;  // units of the lists before this group of 64
+  for (int base = 0; base < NB && run < hi; base += 64) {
+    const int bh = base + lane;
+    const int u = bh < NB ? units_of(a, bh) : 0;
+    const int incl = wave_incl_scan(u, lane);
+    const int64_t s0 = run + incl - u, s1 = run + incl;
+    uint64_t hit = __ballot(u > 0 && s0 < hi && s1 > lo);
+    while (hit) {
+      const int src = __builtin_ctzll(hit);
+      hit &= hit - 1;
+      const int pbh = base + src;
+      const int64_t ps = run + __shfl(incl - u, src);
+      const int pu = __shfl(u, src);
+      const int64_t a0 = lo > ps ? lo : ps;
+      const int64_t a1 = hi < ps + pu ? hi : ps + pu;
+      run_piece(a, math, pbh, (int)(a0 - ps), (int)(a1 - ps), (int64_t)w + pbh,
+                lane, col, grp);
+    }
+    run += __shfl(incl, 63);
   }
 }
 
-// One 128-thread workgroup per (sequence, query head): merge the partials of
-// its active chunks in chunk order.
-__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a,
-                                                           float* __restrict__ out) {
+__global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
+  split_body<MfmaMath>(a);
+}
+
+template <int G>
+__global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
+  split_body<ValuMath<G>>(a);
+}
+
+// ---------------------------------------------------------------------------
+// Combine: one 512-thread workgroup per (sequence, query head) merges the
+// partials of the waves that met its list.  The piece weights 2^(m - M) go
+// to LDS, then 16 groups of 32 threads each sum a strided subset of pieces
+// over float4 slices of the 128 dims (up to eight partial rows in flight per
+// thread), and the groups are added in a fixed order.
+// ---------------------------------------------------------------------------
+constexpr int kCombThreads = 512;
+constexpr int kCombGroups = kCombThreads / 32;
+
+template <class Op>
+__device__ __forceinline__ float block_reduce(float v, float* sh, Op op) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = op(v, __shfl_xor(v, o));
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  float r = sh[0];
+#pragma unroll
+  for (int w = 1; w < kCombThreads / 64; ++w) r = op(r, sh[w]);
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ int block_sum_i(int v, int* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_sum_i(v);
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  int r = 0;
+#pragma unroll
+  for (int w = 0; w < kCombThreads / 64; ++w) r += sh[w];
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ void fma4(float4& acc, float w, const float4& v) {
+  acc.x += w * v.x;
+  acc.y += w * v.y;
+  acc.z += w * v.z;
+  acc.w += w * v.w;
+}
+
+__global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(
+    AttnArgs a, float* __restrict__ out) {
+  extern __shared__ float wsh[];  // [n_waves] piece weights
+  __shared__ float4 red[kCombGroups][32];
+  __shared__ float sh[kCombThreads / 64];
+  __shared__ int ish[kCombThreads / 64];
+  const int tid = threadIdx.x;
   const int bq = blockIdx.x;
   const int G = a.group;
   const int Hq = a.n_kv * G;
   const int b = bq / Hq, qh = bq - b * Hq;
-  int n = a.n_merged[b * a.n_kv + qh / G];
-  n = n < 0 ? 0 : (n > a.m_cap ? a.m_cap : n);
-  const int nc = (n + a.chunk - 1) / a.chunk;
-  const float2* ml = a.part_ml + (int64_t)bq * a.n_chunks;
-  const float* pa = a.part_acc + (int64_t)bq * a.n_chunks * kDim + threadIdx.x;
-  float M = kNegInf;
-  for (int c = 0; c < nc; ++c) {
-    const float2 v = ml[c];
-    if (v.y > 0.f) M = fmaxf(M, v.x);
+  const int bh = b * a.n_kv + qh / G, hh = qh - (qh / G) * G;
+  const int NB = a.batch * a.n_kv;
+  const int W = a.n_waves;
+  auto add = [](float x, float y) { return x + y; };
+  auto mx = [](float x, float y) { return fmaxf(x, y); };
+
+  // T and the offset of this list
+  int tot = 0, before = 0;
+  for (int i = tid; i < NB; i += kCombThreads) {
+    const int u = units_of(a, i);
+    tot += u;
+    before += i < bh ? u : 0;
   }
-  float num = 0.f, den = 0.f;
-  for (int c = 0; c < nc; ++c) {
-    const float2 v = ml[c];
-    if (v.y > 0.f) {
-      const float w = fast_exp2(v.x - M);
-      den += w * v.y;
-      num += w * pa[(int64_t)c * kDim];
+  const int64_t T = block_sum_i(tot, ish);
+  const int64_t off = block_sum_i(before, ish);
+  const int units = units_of(a, bh);
+  float* dst = out + (int64_t)bq * kDim;
+  if (units == 0) {
+    if (tid < kDim) dst[tid] = 0.f;
+    return;
+  }
+  const int w0 = wave_of(off, T, W), w1 = wave_of(off + units - 1, T, W);
+  const int np = w1 - w0 + 1;
+  // pieces: waves w0..w1 with a non-empty range, slot w + bh
+  float mloc = kNegInf;
+  for (int i = tid; i < np; i += kCombThreads) {
+    const int w = w0 + i;
+    if (unit_start(w, T, W) < unit_start(w + 1, T, W)) {
+      const float2 v = a.part_ml[((int64_t)w + bh) * G + hh];
+      if (v.y > 0.f) mloc = fmaxf(mloc, v.x);
     }
   }
-  out[(int64_t)bq * kDim + threadIdx.x] = den > 0.f ? num / den : 0.f;
+  const float M = block_reduce(mloc, sh, mx);
+  float dl = 0.f;
+  for (int i = tid; i < np; i += kCombThreads) {
+    const int w = w0 + i;
+    float wt = 0.f;
+    if (unit_start(w, T, W) < unit_start(w + 1, T, W)) {
+      const float2 v = a.part_ml[((int64_t)w + bh) * G + hh];
+      if (v.y > 0.f) {
+        wt = fast_exp2(v.x - M);
+        dl += wt * v.y;
+      }
+    }
+    wsh[i] = wt;
+  }
+  const float den = block_reduce(dl, sh, add);  // also publishes wsh
+  const int d4 = tid & 31, cg = tid >> 5;
+  auto row = [&](int i) {
+    return reinterpret_cast<const float4*>(
+               a.part_acc + (((int64_t)w0 + i + bh) * G + hh) * kDim)[d4];
+  };
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  int i = cg;
+  for (; i + 7 * kCombGroups < np; i += 8 * kCombGroups) {
+    float4 v[8];
+    float wt[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      wt[u] = wsh[i + u * kCombGroups];
+      v[u] = wt[u] != 0.f ? row(i + u * kCombGroups) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) fma4(acc, wt[u], v[u]);
+  }
+  for (; i < np; i += kCombGroups) {
+    const float wt = wsh[i];
+    if (wt != 0.f) fma4(acc, wt, row(i));
+  }
+  red[cg][d4] = acc;
+  __syncthreads();
+  if (tid < 32) {
+    float4 t = red[0][tid];
+#pragma unroll
+    for (int g = 1; g < kCombGroups; ++g) {
+      t.x += red[g][tid].x;
+      t.y += red[g][tid].y;
+      t.z += red[g][tid].z;
+      t.w += red[g][tid].w;
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    reinterpret_cast<float4*>(dst)[tid] =
+        make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+  }
 }
 
 }  // namespace
 
-AttnPlan plan_attention(int batch, int n_q_heads, int n_kv_heads, int m_cap,
-                        int split_blocks) {
+AttnPlan plan_attention(int batch, int n_q_heads, int n_kv_heads, int waves) {
   AttnPlan p;
-  int chunk = split_blocks;
-  if (chunk <= 0) {
-    // about 16K potential work items: one block per item for single
-    // sequences, more for large batches (each item streams chunk x 64 KiB)
-    const int64_t cells = (int64_t)batch * n_kv_heads * m_cap;
-    chunk = (int)(cells / 16384);
-    chunk = chunk < 1 ? 1 : (chunk > 64 ? 64 : chunk);
-  }
-  if (chunk > m_cap) chunk = m_cap > 0 ? m_cap : 1;
-  p.chunk = chunk;
-  p.n_chunks = (m_cap + chunk - 1) / chunk;
-  const size_t heads = (size_t)batch * n_q_heads * (size_t)p.n_chunks;
-  p.partial_bytes = heads * kDim * sizeof(float);
-  p.ml_bytes = heads * 2 * sizeof(float);
+  // one wave per SIMD on 256 compute units: the whole split runs in one
+  // round, each wave streaming its own run of units
+  p.n_waves = waves > 0 ? waves : 1024;
+  const int group = n_kv_heads > 0 ? n_q_heads / n_kv_heads : 0;
+  const size_t slots = (size_t)p.n_waves + (size_t)batch * n_kv_heads;
+  p.partial_bytes = slots * group * kDim * sizeof(float);
+  p.ml_bytes = slots * group * 2 * sizeof(float);
   return p;
 }
 
@@ -486,28 +714,25 @@ hipError_t launch_decode_attn(const Method& m, bool use_mfma,
   a.batch = batch;
   a.n_kv = m.n_kv_heads;
   a.group = m.group;
-  a.chunk = plan.chunk;
-  a.n_chunks = plan.n_chunks;
+  a.n_waves = plan.n_waves;
   a.scale_log2 = scale * 1.4426950408889634f;
-  const int64_t items = (int64_t)plan.n_chunks * batch * m.n_kv_heads;
-  if (items > 0) {
-    const dim3 grid((unsigned)items), block(64);
-    if (use_mfma) {
-      hipLaunchKernelGGL(attn_mfma_kernel, grid, block, 0, stream, a);
-    } else {
-      switch (m.group) {
-        case 1: hipLaunchKernelGGL(attn_valu_kernel<1>, grid, block, 0, stream, a); break;
-        case 2: hipLaunchKernelGGL(attn_valu_kernel<2>, grid, block, 0, stream, a); break;
-        case 4: hipLaunchKernelGGL(attn_valu_kernel<4>, grid, block, 0, stream, a); break;
-        case 8: hipLaunchKernelGGL(attn_valu_kernel<8>, grid, block, 0, stream, a); break;
-        default: return hipErrorInvalidValue;
-      }
+  const dim3 grid((unsigned)plan.n_waves), block(64);
+  if (use_mfma) {
+    hipLaunchKernelGGL(attn_mfma_kernel, grid, block, 0, stream, a);
+  } else {
+    switch (m.group) {
+      case 1: hipLaunchKernelGGL(attn_valu_kernel<1>, grid, block, 0, stream, a); break;
+      case 2: hipLaunchKernelGGL(attn_valu_kernel<2>, grid, block, 0, stream, a); break;
+      case 4: hipLaunchKernelGGL(attn_valu_kernel<4>, grid, block, 0, stream, a); break;
+      case 8: hipLaunchKernelGGL(attn_valu_kernel<8>, grid, block, 0, stream, a); break;
+      default: return hipErrorInvalidValue;
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(batch * m.n_q_heads), dim3(128),
-                     0, stream, a, out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(batch * m.n_q_heads),
+                     dim3(kCombThreads), (size_t)plan.n_waves * sizeof(float),
+                     stream, a, out);
   return hipGetLastError();
 }
 

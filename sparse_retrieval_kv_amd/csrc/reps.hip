@@ -113,6 +113,35 @@ __global__ __launch_bounds__(64) void append_kv_kernel(
   finish_rep(s, lane, reps + ((int64_t)bh * max_blocks + j) * kDim);
 }
 
+
+// Streaming-read probe (a measurement helper, not part of the method): each
+// workgroup reads one contiguous segment, 4 KiB per load instruction across
+// its 256 threads, sixteen loads in flight per thread, and folds the data
+// into one XOR per wave so the loads cannot be elided.
+__global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ src,
+                                                         int64_t n16, int64_t per_wg,
+                                                         uint32_t* __restrict__ sink) {
+  const int64_t begin = (int64_t)blockIdx.x * per_wg;
+  int64_t end = begin + per_wg;
+  end = end < n16 ? end : n16;
+  uint32_t x = 0;
+  int64_t i = begin + threadIdx.x;
+  for (; i + 15 * 256 < end; i += 16 * 256) {
+    uint4 v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = src[i + u * 256];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < end; i += 256) {
+    const uint4 v = src[i];
+    x ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x ^= __shfl_xor(x, o);
+  if ((threadIdx.x & 63) == 0) atomicXor(sink, x);
+}
+
 }  // namespace
 
 hipError_t launch_build_reps(const uint16_t* k_pages, int64_t n_pages,
@@ -138,6 +167,20 @@ hipError_t launch_append_kv(const uint16_t* k_new, const uint16_t* v_new,
   hipLaunchKernelGGL(append_kv_kernel, dim3(batch * n_kv_heads), dim3(64), 0,
                      stream, k_new, v_new, k_pages, v_pages, n_pages, table,
                      max_blocks, lens, n_kv_heads, reps);
+  return hipGetLastError();
+}
+
+hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
+                             int n_cu, hipStream_t stream) {
+  const int64_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  // 64 KiB-aligned segments, several per compute unit
+  int64_t wgs = (int64_t)n_cu * 16;
+  int64_t per_wg = (n16 + wgs - 1) / wgs;
+  per_wg = (per_wg + 4095) / 4096 * 4096;
+  wgs = (n16 + per_wg - 1) / per_wg;
+  hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)wgs), dim3(256), 0, stream,
+                     static_cast<const uint4*>(buf), n16, per_wg, sink);
   return hipGetLastError();
 }
 

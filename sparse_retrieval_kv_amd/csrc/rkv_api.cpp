@@ -65,8 +65,9 @@ rkv_status check_params(const rkv_params* p, rkv::Method* m) {
   RKV_REQUIRE(isfinite(p->scale), RKV_ERR_INVALID_ARG, "scale is not finite");
   RKV_REQUIRE(p->attn_impl >= RKV_ATTN_AUTO && p->attn_impl <= RKV_ATTN_VALU,
               RKV_ERR_INVALID_ARG, "attn_impl %d unknown", p->attn_impl);
-  RKV_REQUIRE(p->split_blocks >= 0, RKV_ERR_INVALID_ARG,
-              "split_blocks must be >= 0");
+  RKV_REQUIRE(p->split_waves >= 0 && p->split_waves <= (1 << 20),
+              RKV_ERR_INVALID_ARG, "split_waves %d outside [0, 2^20]",
+              p->split_waves);
   if (m) {
     m->n_q_heads = p->n_q_heads;
     m->n_kv_heads = p->n_kv_heads;
@@ -125,7 +126,7 @@ rkv_params rkv_params_default(int32_t n_q_heads, int32_t n_kv_heads) {
   p.dense_boundary = 32768;
   p.scale = 1.0f / sqrtf((float)RKV_HEAD_DIM);
   p.attn_impl = RKV_ATTN_AUTO;
-  p.split_blocks = 0;
+  p.split_waves = 0;
   return p;
 }
 
@@ -192,13 +193,16 @@ size_t rkv_select_workspace_size(const rkv_params* params, int32_t batch,
   return 0;
 }
 
-rkv_status rkv_select(const rkv_params* params, const uint16_t* q,
-                      const float* reps, const int32_t* block_table,
-                      const int32_t* lens, const int32_t* prompt_lens,
-                      int32_t batch, int32_t max_blocks, int32_t* sel_ids,
-                      int32_t* n_sel, int32_t k_cap, int32_t* merged,
-                      int32_t* n_merged, int32_t m_cap, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+rkv_status select_common(const rkv_params* params, const uint16_t* q,
+                         const float* reps, const int32_t* block_table,
+                         const int32_t* lens, const int32_t* prompt_lens,
+                         int32_t batch, int32_t max_blocks, int32_t* sel_ids,
+                         int32_t* n_sel, int32_t k_cap, int32_t* merged,
+                         int32_t* n_merged, int32_t m_cap, void* workspace,
+                         size_t workspace_bytes, const rkv::AppendOp* append,
+                         hipStream_t stream, const char* what) {
   rkv::Method m;
   RKV_TRY(check_params(params, &m));
   RKV_TRY(check_sizes(batch, max_blocks));
@@ -223,15 +227,53 @@ rkv_status rkv_select(const rkv_params* params, const uint16_t* q,
   return hip_status(rkv::launch_select(m, q, reps, block_table, lens,
                                        prompt_lens, batch, max_blocks, sel_ids,
                                        n_sel, k_cap, merged, n_merged, m_cap,
-                                       stream),
-                    "rkv_select launch");
+                                       append, stream),
+                    what);
+}
+
+}  // namespace
+
+rkv_status rkv_select(const rkv_params* params, const uint16_t* q,
+                      const float* reps, const int32_t* block_table,
+                      const int32_t* lens, const int32_t* prompt_lens,
+                      int32_t batch, int32_t max_blocks, int32_t* sel_ids,
+                      int32_t* n_sel, int32_t k_cap, int32_t* merged,
+                      int32_t* n_merged, int32_t m_cap, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  return select_common(params, q, reps, block_table, lens, prompt_lens, batch,
+                       max_blocks, sel_ids, n_sel, k_cap, merged, n_merged,
+                       m_cap, workspace, workspace_bytes, nullptr, stream,
+                       "rkv_select launch");
+}
+
+rkv_status rkv_append_select(const rkv_params* params, const uint16_t* k_new,
+                             const uint16_t* v_new, uint16_t* k_pages,
+                             uint16_t* v_pages, int64_t n_pages,
+                             const uint16_t* q, float* reps,
+                             const int32_t* block_table, const int32_t* lens,
+                             const int32_t* prompt_lens, int32_t batch,
+                             int32_t max_blocks, int32_t* sel_ids,
+                             int32_t* n_sel, int32_t k_cap, int32_t* merged,
+                             int32_t* n_merged, int32_t m_cap, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  RKV_TRY(check_pool(k_pages, n_pages, "k_pages"));
+  RKV_TRY(check_pool(v_pages, n_pages, "v_pages"));
+  RKV_REQUIRE(k_new && v_new, RKV_ERR_INVALID_ARG, "k_new and v_new must not be NULL");
+  RKV_REQUIRE(aligned16(k_new) && aligned16(v_new), RKV_ERR_INVALID_ARG,
+              "k_new and v_new must be 16-byte aligned");
+  const rkv::AppendOp op{k_new, v_new, k_pages, v_pages, n_pages, reps};
+  return select_common(params, q, reps, block_table, lens, prompt_lens, batch,
+                       max_blocks, sel_ids, n_sel, k_cap, merged, n_merged,
+                       m_cap, workspace, workspace_bytes, &op, stream,
+                       "rkv_append_select launch");
 }
 
 rkv_status rkv_merge_table(const rkv_params* params, const int32_t* block_table,
                            int32_t max_blocks, const int32_t* lens,
                            const int32_t* sel_ids, const int32_t* n_sel,
-                           int32_t k_cap, int32_t batch, int32_t* merged,
-                           int32_t* n_merged, int32_t m_cap,
+                           int32_t k_cap, int32_t batch,
+                           const int32_t* host_table, int64_t stage_page0,
+                           int32_t* merged, int32_t* n_merged, int32_t m_cap,
                            hipStream_t stream) {
   rkv::Method m;
   RKV_TRY(check_params(params, &m));
@@ -241,19 +283,71 @@ rkv_status rkv_merge_table(const rkv_params* params, const int32_t* block_table,
   RKV_REQUIRE(k_cap >= 0, RKV_ERR_INVALID_ARG, "k_cap %d < 0", k_cap);
   RKV_REQUIRE(m_cap >= max_blocks, RKV_ERR_INVALID_ARG,
               "m_cap %d below max_blocks %d", m_cap, max_blocks);
+  RKV_REQUIRE(!host_table || (stage_page0 >= 0 &&
+                               stage_page0 + (int64_t)batch * k_cap <= (int64_t)INT32_MAX),
+              RKV_ERR_INVALID_ARG,
+              "with a host table, stage_page0 must be >= 0 and staging page "
+              "ids must fit int32");
   return hip_status(rkv::launch_merge(m, block_table, max_blocks, lens, sel_ids,
-                                      n_sel, k_cap, batch, merged, n_merged,
-                                      m_cap, stream),
+                                      n_sel, k_cap, batch, host_table, stage_page0,
+                                      merged, n_merged, m_cap, stream),
                     "rkv_merge_table launch");
+}
+
+rkv_status rkv_stage_blocks(const rkv_params* params, const uint16_t* host_k,
+                            const uint16_t* host_v, int64_t n_host_pages,
+                            const int32_t* host_table, int32_t max_blocks,
+                            const int32_t* sel_ids, const int32_t* n_sel,
+                            int32_t k_cap, int32_t batch, uint16_t* k_pages,
+                            uint16_t* v_pages, int64_t n_pages,
+                            int64_t stage_page0, hipStream_t stream) {
+  rkv::Method m;
+  RKV_TRY(check_params(params, &m));
+  RKV_TRY(check_sizes(batch, max_blocks));
+  RKV_TRY(check_pool(k_pages, n_pages, "k_pages"));
+  RKV_TRY(check_pool(v_pages, n_pages, "v_pages"));
+  RKV_TRY(check_pool(host_k, n_host_pages, "host_k"));
+  RKV_TRY(check_pool(host_v, n_host_pages, "host_v"));
+  RKV_REQUIRE(host_table && sel_ids && n_sel, RKV_ERR_INVALID_ARG,
+              "host_table, sel_ids and n_sel must not be NULL");
+  RKV_REQUIRE(k_cap >= 1, RKV_ERR_INVALID_ARG, "k_cap %d < 1", k_cap);
+  RKV_REQUIRE(stage_page0 >= 0 &&
+                  stage_page0 + (int64_t)batch * k_cap <= n_pages &&
+                  stage_page0 + (int64_t)batch * k_cap <= (int64_t)INT32_MAX,
+              RKV_ERR_INVALID_ARG,
+              "staging pages [%lld, +%lld) do not fit in the %lld-page pool",
+              (long long)stage_page0, (long long)batch * k_cap,
+              (long long)n_pages);
+  // the kernel reads the host pools directly: they must be pinned host
+  // memory mapped into the device address space
+  const uint16_t* dev_view[2] = {nullptr, nullptr};
+  const uint16_t* pools[2] = {host_k, host_v};
+  for (int i = 0; i < 2; ++i) {
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, pools[i]) != hipSuccess ||
+        attr.type != hipMemoryTypeHost || attr.devicePointer == nullptr ||
+        attr.hostPointer != static_cast<const void*>(pools[i])) {
+      (void)hipGetLastError();
+      return fail(RKV_ERR_INVALID_ARG,
+                  "%s is not pinned host memory mapped for the device",
+                  i == 0 ? "host_k" : "host_v");
+    }
+    dev_view[i] = static_cast<const uint16_t*>(attr.devicePointer);
+  }
+  return hip_status(rkv::launch_stage(dev_view[0], dev_view[1], n_host_pages,
+                                      host_table, max_blocks, sel_ids, n_sel,
+                                      k_cap, batch, m.n_kv_heads, k_pages,
+                                      v_pages, n_pages, stage_page0, stream),
+                    "rkv_stage_blocks launch");
 }
 
 size_t rkv_attn_workspace_size(const rkv_params* params, int32_t batch,
                                int32_t m_cap) {
   if (!params || params->n_q_heads <= 0 || params->n_kv_heads <= 0 ||
-      batch < 0 || m_cap < 1 || params->split_blocks < 0)
+      batch < 0 || m_cap < 1 || params->split_waves < 0)
     return 0;
   const rkv::AttnPlan p = rkv::plan_attention(
-      batch, params->n_q_heads, params->n_kv_heads, m_cap, params->split_blocks);
+      batch, params->n_q_heads, params->n_kv_heads, params->split_waves);
   return p.partial_bytes + p.ml_bytes;
 }
 
@@ -281,8 +375,10 @@ rkv_status rkv_decode_attn(const rkv_params* params, const uint16_t* q,
               RKV_ERR_UNSUPPORTED,
               "the VALU attention variant supports groups 1, 2, 4 and 8 (got %d)",
               m.group);
+  RKV_REQUIRE((int64_t)batch * m.n_kv_heads * m_cap < ((int64_t)1 << 30),
+              RKV_ERR_UNSUPPORTED, "batch * n_kv_heads * m_cap too large");
   const rkv::AttnPlan plan = rkv::plan_attention(
-      batch, m.n_q_heads, m.n_kv_heads, m_cap, params->split_blocks);
+      batch, m.n_q_heads, m.n_kv_heads, params->split_waves);
   const size_t need = plan.partial_bytes + plan.ml_bytes;
   RKV_REQUIRE(workspace_bytes >= need && (need == 0 || workspace != nullptr),
               RKV_ERR_WORKSPACE, "attention workspace %zu bytes, need %zu",
@@ -295,6 +391,18 @@ rkv_status rkv_decode_attn(const rkv_params* params, const uint16_t* q,
                               merged, n_merged, m_cap, lens, batch, out,
                               workspace, stream),
       "rkv_decode_attn launch");
+}
+
+rkv_status rkv_read_probe(const void* buffer, size_t bytes, uint32_t* sink,
+                          hipStream_t stream) {
+  RKV_REQUIRE(buffer && sink, RKV_ERR_INVALID_ARG, "buffer and sink must not be NULL");
+  RKV_REQUIRE(aligned16(buffer), RKV_ERR_INVALID_ARG, "buffer is not 16-byte aligned");
+  int dev = 0, n_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_status(e, "rkv_read_probe device query");
+  return hip_status(rkv::launch_read_probe(buffer, (int64_t)bytes, sink, n_cu, stream),
+                    "rkv_read_probe launch");
 }
 
 }  // extern "C"

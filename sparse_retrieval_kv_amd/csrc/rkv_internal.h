@@ -33,29 +33,47 @@ hipError_t launch_append_kv(const uint16_t* k_new, const uint16_t* v_new,
                             int max_blocks, const int32_t* lens, int batch,
                             int n_kv_heads, float* reps, hipStream_t stream);
 
+// Optional decode-token append carried out by the selection launch.
+struct AppendOp {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* k_pages;
+  uint16_t* v_pages;
+  int64_t n_pages;
+  float* reps;  // may be null
+};
+
 hipError_t launch_select(const Method& m, const uint16_t* q, const float* reps,
                          const int32_t* table, const int32_t* lens,
                          const int32_t* prompt_lens, int batch, int max_blocks,
                          int32_t* sel_ids, int32_t* n_sel, int k_cap,
                          int32_t* merged, int32_t* n_merged, int m_cap,
-                         hipStream_t stream);
+                         const AppendOp* append, hipStream_t stream);
 
 hipError_t launch_merge(const Method& m, const int32_t* table, int max_blocks,
                         const int32_t* lens, const int32_t* sel_ids,
                         const int32_t* n_sel, int k_cap, int batch,
+                        const int32_t* host_table, int64_t stage_page0,
                         int32_t* merged, int32_t* n_merged, int m_cap,
                         hipStream_t stream);
 
-// Split-K decode attention: `chunk` merged blocks per work item,
-// `n_chunks` = ceil(m_cap / chunk) work items per (sequence, KV head).
+hipError_t launch_stage(const uint16_t* host_k, const uint16_t* host_v,
+                        int64_t n_host_pages, const int32_t* host_table,
+                        int max_blocks, const int32_t* sel_ids,
+                        const int32_t* n_sel, int k_cap, int batch, int n_kv,
+                        uint16_t* k_pages, uint16_t* v_pages, int64_t n_pages,
+                        int64_t stage_page0, hipStream_t stream);
+
+// Split-K decode attention over a fixed number of waves: the 64-token units
+// of all merged lists are spread evenly over `n_waves` waves; the workspace
+// holds one partial per (wave, list) piece, n_waves + batch * n_kv_heads
+// slots of `group` heads.
 struct AttnPlan {
-  int chunk;
-  int n_chunks;
-  size_t partial_bytes;  // fp32 [batch][n_q_heads][n_chunks][kDim]
-  size_t ml_bytes;       // float2 [batch][n_q_heads][n_chunks]
+  int n_waves;
+  size_t partial_bytes;  // fp32 [slots][group][kDim]
+  size_t ml_bytes;       // float2 [slots][group]
 };
-AttnPlan plan_attention(int batch, int n_q_heads, int n_kv_heads, int m_cap,
-                        int split_blocks);
+AttnPlan plan_attention(int batch, int n_q_heads, int n_kv_heads, int waves);
 
 hipError_t launch_decode_attn(const Method& m, bool use_mfma,
                               const AttnPlan& plan, float scale,
@@ -64,5 +82,8 @@ hipError_t launch_decode_attn(const Method& m, bool use_mfma,
                               const int32_t* merged, const int32_t* n_merged,
                               int m_cap, const int32_t* lens, int batch,
                               float* out, void* workspace, hipStream_t stream);
+
+hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
+                             int n_cu, hipStream_t stream);
 
 }  // namespace rkv

@@ -66,8 +66,67 @@ class DecodeSession:
                       self.n_merged, lens, self.out, self.ws_attn)
         return self.out
 
+    def append_select(self, q, k_new, v_new, lens):
+        """The append and the selection in one launch."""
+        B.append_select(self.p, k_new, v_new, self.k_pages, self.v_pages, q,
+                        self.reps, self.block_table, lens, self.sel_ids,
+                        self.n_sel, self.merged, self.n_merged, self.prompt_lens,
+                        self.ws_select)
+
     def step(self, q, k_new, v_new, lens):
-        """append -> select -> attend for one decode step; returns `out`."""
-        self.append(k_new, v_new, lens)
-        self.select(q, lens)
+        """append + select (one launch) -> attend for one decode step;
+        returns `out`."""
+        self.append_select(q, k_new, v_new, lens)
+        return self.attend(q, lens)
+
+
+class HostTierSession(DecodeSession):
+    """Decode step with the offload region in pinned host memory: the kept
+    offload blocks are staged into HBM staging pages (the last
+    batch * k_cap pages of the device pools) before attention, on a side
+    stream that the main stream waits for.
+
+    Representations are built while every block is still in HBM (after
+    prefill); `attach_host` then hands over the host pools that hold the
+    offload blocks from then on."""
+
+    def __init__(self, prm: B.Params, k_pages, v_pages, block_table,
+                 prompt_lens=None, side_stream=True):
+        super().__init__(prm, k_pages, v_pages, block_table, prompt_lens)
+        self.host_k = self.host_v = self.host_table = None
+        self.stage_page0 = k_pages.shape[0] - self.batch * self.k_cap
+        if self.stage_page0 < 0:
+            raise ValueError("the device pools have no room for staging pages")
+        self.side = torch.cuda.Stream(device=k_pages.device) if side_stream else None
+
+    def attach_host(self, host_k, host_v, host_table):
+        self.host_k, self.host_v, self.host_table = host_k, host_v, host_table
+
+    def select(self, q, lens):
+        # the selection only: the merged table is built after staging
+        B.select(self.p, q, self.reps, self.block_table, lens, self.sel_ids,
+                 self.n_sel, None, None, self.prompt_lens, self.ws_select)
+
+    def stage(self, lens):
+        B.stage_blocks(self.p, self.host_k, self.host_v, self.host_table,
+                       self.sel_ids, self.n_sel, self.k_pages, self.v_pages,
+                       self.stage_page0)
+        B.merge_table(self.p, self.block_table, lens, self.sel_ids, self.n_sel,
+                      self.merged, self.n_merged, self.host_table, self.stage_page0)
+
+    def append_select(self, q, k_new, v_new, lens):
+        B.append_select(self.p, k_new, v_new, self.k_pages, self.v_pages, q,
+                        self.reps, self.block_table, lens, self.sel_ids,
+                        self.n_sel, None, None, self.prompt_lens, self.ws_select)
+
+    def step(self, q, k_new, v_new, lens):
+        self.append_select(q, k_new, v_new, lens)
+        if self.side is None:
+            self.stage(lens)
+        else:
+            main = torch.cuda.current_stream(self.k_pages.device)
+            self.side.wait_stream(main)
+            with torch.cuda.stream(self.side):
+                self.stage(lens)
+            main.wait_stream(self.side)
         return self.attend(q, lens)

@@ -203,8 +203,11 @@ def _plant_blocks(spec: Spec, rng: np.random.Generator) -> dict:
     return out
 
 
-def make_batch(spec: Spec, device="cpu", poison_tail: bool = True) -> Batch:
-    """Build the pools, tables and per-step generators of a workload."""
+def make_batch(spec: Spec, device="cpu", poison_tail: bool = True,
+               extra_pages: int = 0) -> Batch:
+    """Build the pools, tables and per-step generators of a workload.
+    `extra_pages` NaN-filled pages are appended to the pools (e.g. staging
+    pages for the host tier); they belong to no block table."""
     device = torch.device(device)
     B, Hkv, G = spec.batch, spec.n_kv_heads, spec.group
     if spec.len_range is not None:
@@ -298,10 +301,56 @@ def make_batch(spec: Spec, device="cpu", poison_tail: bool = True) -> Batch:
         for b in range(B):
             host_pages[table[b, lo:hi]] = True
 
+    if extra_pages:
+        pad = torch.full((extra_pages, Hkv, BLOCK, HEAD_DIM), BF16_QNAN,
+                         dtype=torch.int16, device=device)
+        k_pages = torch.cat([k_pages, pad])
+        v_pages = torch.cat([v_pages, pad])
+        del pad
+
     return Batch(spec, device, k_pages, v_pages,
                  torch.from_numpy(table).to(device), table, context,
                  max_blocks, n_pages, planted, pool.refcount.copy(), u,
                  head_offset, q0, host_pages)
+
+
+@dataclass
+class HostPools:
+    host_k: torch.Tensor       # pinned int16 [P_host, Hkv, 128, 128]
+    host_v: torch.Tensor       # pinned int16 [P_host, Hkv, 128, 128] (dim-major)
+    host_table: torch.Tensor   # int32 [B, max_blocks] on the device, -1 = in HBM
+    host_table_np: np.ndarray
+
+
+def move_offload_to_host(batch: Batch) -> HostPools:
+    """Place the offload blocks (the spec's block range at step 0) of every
+    sequence in pinned host memory: copy their pages to host pools, record
+    the host page of each block, and fill the device copies with NaN so that
+    only the host copies carry the data."""
+    spec = batch.spec
+    lo, hi = spec.plant_range
+    B, Hkv = spec.batch, spec.n_kv_heads
+    pages = np.concatenate([batch.table_np[b, lo:hi] for b in range(B)])
+    host_table = np.full_like(batch.table_np, -1)
+    for b in range(B):
+        host_table[b, lo:hi] = b * (hi - lo) + np.arange(hi - lo)
+    n_host = len(pages)
+    host_k = torch.empty((n_host, Hkv, BLOCK, HEAD_DIM), dtype=torch.int16,
+                         pin_memory=True)
+    host_v = torch.empty_like(host_k, pin_memory=True)
+    idx = torch.as_tensor(pages.astype(np.int64), device=batch.k_pages.device)
+    step = 1024
+    for s0 in range(0, n_host, step):
+        sl = idx[s0:s0 + step]
+        host_k[s0:s0 + step].copy_(batch.k_pages.index_select(0, sl))
+        host_v[s0:s0 + step].copy_(batch.v_pages.index_select(0, sl))
+        batch.k_pages[sl] = BF16_QNAN
+        batch.v_pages[sl] = BF16_QNAN
+    if batch.k_pages.is_cuda:
+        torch.cuda.synchronize(batch.k_pages.device)
+    return HostPools(host_k, host_v,
+                     torch.from_numpy(host_table).to(batch.k_pages.device),
+                     host_table)
 
 
 def custom(name="custom", batch=1, n_q_heads=8, n_kv_heads=2, context=(4096,),

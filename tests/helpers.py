@@ -23,18 +23,26 @@ def oracle_params(spec, **kw) -> O.Params:
     return O.Params(spec.n_q_heads, spec.n_kv_heads, **d)
 
 
-def seq_pages_host(batch: synth.Batch, b: int, heads=None):
+def seq_pages_host(batch: synth.Batch, b: int, heads=None, host=None):
     """Host copy of sequence b's pages (all heads or the given ones), taken
-    from the generator's pools.  Returns (k [nb,H,128,128], v, heads)."""
+    from the generator's pools (device pools, and for blocks placed in host
+    memory the host pools `host`).  Returns (k [nb,H,128,128], v, heads)."""
     L_final = int(batch.context[b]) + batch.spec.steps - 1
     nb = -(-L_final // 128)
     pages = torch.as_tensor(batch.table_np[b, :nb].astype(np.int64),
                             device=batch.k_pages.device)
     hs = list(range(batch.spec.n_kv_heads)) if heads is None else list(heads)
     hidx = torch.as_tensor(hs, device=batch.k_pages.device)
-    k = batch.k_pages.index_select(0, pages).index_select(1, hidx)
-    v = batch.v_pages.index_select(0, pages).index_select(1, hidx)
-    return u16(k), u16(v), hs
+    k = u16(batch.k_pages.index_select(0, pages).index_select(1, hidx))
+    v = u16(batch.v_pages.index_select(0, pages).index_select(1, hidx))
+    if host is not None:
+        ht = host.host_table_np[b, :nb]
+        on_host = np.nonzero(ht >= 0)[0]
+        hp = torch.as_tensor(ht[on_host].astype(np.int64))
+        hh = torch.as_tensor(hs)
+        k[on_host] = u16(host.host_k.index_select(0, hp).index_select(1, hh))
+        v[on_host] = u16(host.host_v.index_select(0, hp).index_select(1, hh))
+    return k, v, hs
 
 
 def logical_at_step(batch: synth.Batch, b: int, t: int, pages=None):

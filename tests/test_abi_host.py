@@ -30,7 +30,7 @@ def test_defaults_follow_the_page(L):
     assert (p.block_size, p.head_dim, p.init_tokens, p.local_tokens,
             p.topk_ppm, p.dense_boundary) == (128, 128, 1024, 7192, 200000, 32768)
     assert p.scale == pytest.approx(128 ** -0.5)
-    assert (p.n_q_heads, p.n_kv_heads, p.attn_impl, p.split_blocks) == (32, 8, 0, 0)
+    assert (p.n_q_heads, p.n_kv_heads, p.attn_impl, p.split_waves) == (32, 8, 0, 0)
     assert L.rkv_status_string(0) == b"ok"
     assert L.rkv_status_string(3) == b"workspace too small"
 
@@ -65,7 +65,8 @@ def test_param_validation(L):
         (with_(dense_boundary=-5), B.RKV_ERR_INVALID_ARG),
         (with_(scale=float("inf")), B.RKV_ERR_INVALID_ARG),
         (with_(attn_impl=7), B.RKV_ERR_INVALID_ARG),
-        (with_(split_blocks=-1), B.RKV_ERR_INVALID_ARG),
+        (with_(split_waves=-1), B.RKV_ERR_INVALID_ARG),
+        (with_(split_waves=(1 << 20) + 1), B.RKV_ERR_INVALID_ARG),
     ]
     for p, want in cases:
         assert _attn(L, p) == want, p
@@ -106,9 +107,29 @@ def test_select_and_merge_capacity_rules(L):
     p.topk_ppm = 1_000_000
     assert sel(99, 100) == B.RKV_ERR_INVALID_ARG
     assert L.rkv_merge_table(ctypes.byref(p), FAKE, 100, FAKE, FAKE, FAKE, 20, 4,
-                             FAKE, FAKE, 99, None) == B.RKV_ERR_INVALID_ARG
+                             None, -1, FAKE, FAKE, 99, None) == B.RKV_ERR_INVALID_ARG
     assert L.rkv_merge_table(ctypes.byref(p), FAKE, 100, FAKE, None, FAKE, 20, 4,
-                             FAKE, FAKE, 100, None) == B.RKV_ERR_INVALID_ARG
+                             None, -1, FAKE, FAKE, 100, None) == B.RKV_ERR_INVALID_ARG
+    assert L.rkv_merge_table(ctypes.byref(p), FAKE, 100, FAKE, FAKE, FAKE, 20, 4,
+                             FAKE, 2**31 - 10, FAKE, FAKE, 100, None) == B.RKV_ERR_INVALID_ARG
+    assert L.rkv_merge_table(ctypes.byref(p), FAKE, 100, FAKE, FAKE, FAKE, 20, 4,
+                             FAKE, -1, FAKE, FAKE, 100, None) == B.RKV_ERR_INVALID_ARG
+
+
+def test_stage_validation(L):
+    p = L.rkv_params_default(32, 8)
+
+    def stage(stage_page0=0, n_pages=1000, k_cap=100, batch=4, host_k=FAKE):
+        return L.rkv_stage_blocks(ctypes.byref(p), host_k, FAKE, 50, FAKE, 200,
+                                  FAKE, FAKE, k_cap, batch, FAKE, FAKE, n_pages,
+                                  stage_page0, None)
+
+    assert stage(stage_page0=601) == B.RKV_ERR_INVALID_ARG   # 601 + 400 > 1000
+    assert b"staging" in L.rkv_last_error()
+    assert stage(stage_page0=-1) == B.RKV_ERR_INVALID_ARG
+    assert stage(k_cap=0) == B.RKV_ERR_INVALID_ARG
+    assert stage(host_k=None) == B.RKV_ERR_INVALID_ARG
+    assert stage(host_k=ODD) == B.RKV_ERR_INVALID_ARG
 
 
 def test_reps_and_append_validation(L):

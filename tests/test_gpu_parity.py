@@ -20,7 +20,7 @@ import torch
 import oracle as O
 from sparse_retrieval_kv_amd import binding as B
 from sparse_retrieval_kv_amd import synth
-from sparse_retrieval_kv_amd.decode import DecodeSession
+from sparse_retrieval_kv_amd.decode import DecodeSession, HostTierSession
 from tests.helpers import (close_report, logical_at_step, oracle_params,
                            q_f64, seq_pages_host, u16)
 
@@ -89,10 +89,16 @@ def gpu_selection(sess, b, h):
     return sess.sel_ids[b, h, :n].cpu().numpy()
 
 
-def gpu_merged_logical(sess, batch, b, h):
+def gpu_merged_logical(sess, batch, b, h, staged=False):
+    """The GPU's merged list of (b, h) as logical blocks (and page ids).
+    Staging page stage_page0 + b*k_cap + r stands for the r-th kept block."""
     n = int(sess.n_merged[b, h])
     pages = sess.merged[b, h, :n].cpu().numpy()
     inv = {int(p): j for j, p in enumerate(batch.table_np[b]) if p >= 0}
+    if staged:
+        sel = gpu_selection(sess, b, h)
+        for r, j in enumerate(sel):
+            inv[int(sess.stage_page0 + b * sess.k_cap + r)] = int(j)
     return np.array([inv[int(p)] for p in pages], dtype=np.int64), pages
 
 
@@ -102,7 +108,7 @@ def check_head_output(out_gpu, ref, ctx):
     assert rl2 <= REL_L2, (ctx, mx, rl2)
 
 
-def oracle_full_check(batch, sess, t, seqs=None, heads=None, step_res=None):
+def oracle_full_check(batch, sess, t, seqs=None, heads=None, host=None):
     """Check selections, merged tables and outputs of step t for the given
     sequences / KV heads against the oracle."""
     spec = batch.spec
@@ -111,7 +117,7 @@ def oracle_full_check(batch, sess, t, seqs=None, heads=None, step_res=None):
     qall = q_f64(batch, t)
     for b in (range(spec.batch) if seqs is None else seqs):
         hs = list(range(spec.n_kv_heads)) if heads is None else heads
-        pages = seq_pages_host(batch, b, hs)
+        pages = seq_pages_host(batch, b, hs, host)
         K, V, L = logical_at_step(batch, b, t, pages)
         prm1 = oracle_params(spec)
         prm1 = O.Params(G, 1, prm1.init_tokens, prm1.local_tokens, prm1.topk_ppm,
@@ -124,10 +130,11 @@ def oracle_full_check(batch, sess, t, seqs=None, heads=None, step_res=None):
             hr = res.heads[0]
             sel = gpu_selection(sess, b, h)
             check_selection(sel, hr, res.regions.n_init, ctx)
-            mlog, mpages = gpu_merged_logical(sess, batch, b, h)
+            mlog, mpages = gpu_merged_logical(sess, batch, b, h, host is not None)
             if np.array_equal(sel, hr.selected):
                 assert np.array_equal(mlog, hr.merged), ctx
-                assert np.array_equal(mpages, batch.table_np[b, hr.merged]), ctx
+                if host is None:
+                    assert np.array_equal(mpages, batch.table_np[b, hr.merged]), ctx
                 ref = res.out
             else:
                 ref = O.decode_step(q, K[i:i + 1], V[i:i + 1], L,
@@ -305,11 +312,11 @@ def test_split_sizes_agree_and_runs_are_deterministic():
     lens = i32(batch.lens_at(0))
     kn, vn = batch.new_kv_bits(0)
     outs = []
-    for split in (1, 2, 3, 5, 64):
-        prm, sess = make_session(batch, split_blocks=split)
+    for split in (7, 64, 301, 2048, 5000):
+        prm, sess = make_session(batch, split_waves=split)
         say("split", split)
         prefill(batch, sess)
-        if split == 1:
+        if split == 7:
             sess.append(kn, vn, lens)  # once: the pools are shared
         sess.select(batch.q_bits(0), lens)
         o1 = sess.attend(batch.q_bits(0), lens).clone()
@@ -317,7 +324,7 @@ def test_split_sizes_agree_and_runs_are_deterministic():
         torch.cuda.synchronize()
         assert torch.equal(o1, o2)
         outs.append(o1.cpu().numpy())
-        if split in (1, 5):
+        if split in (7, 2048, 5000):
             oracle_full_check(batch, sess, 0)
     for o in outs[1:]:
         assert np.allclose(o, outs[0], rtol=1e-5, atol=1e-6)
@@ -462,3 +469,79 @@ def test_valu_variant_matches_oracle_and_mfma(hq, hkv):
         oracle_full_check(batch, sess, 0)
         outs[impl] = sess.out.cpu().numpy()
     assert np.allclose(outs[B.ATTN_MFMA], outs[B.ATTN_VALU], rtol=1e-4, atol=1e-5)
+
+
+def make_host_session(spec, **pkw):
+    """Host-tier session: prefill representations are built with every block
+    in HBM, then the offload blocks move to pinned host memory."""
+    max_blocks = -(-(max(spec.context) + spec.steps - 1) // 128)
+    batch = synth.make_batch(spec, DEV, extra_pages=spec.batch * max_blocks)
+    kw = dict(init_tokens=spec.init_tokens, local_tokens=spec.local_tokens,
+              topk_ppm=spec.topk_ppm, dense_boundary=spec.dense_boundary)
+    kw.update(pkw)
+    prm = B.params(spec.n_q_heads, spec.n_kv_heads, **kw)
+    sess = HostTierSession(prm, batch.k_pages, batch.v_pages, batch.block_table,
+                           i32(batch.context))
+    assert sess.stage_page0 >= batch.n_pages  # staging pages are the extra ones
+    prefill(batch, sess)
+    torch.cuda.synchronize()
+    host = synth.move_offload_to_host(batch)
+    sess.attach_host(host.host_k, host.host_v, host.host_table)
+    return batch, host, sess
+
+
+def test_host_tier_small():
+    # host blocks [8, 90) of the offload range [8, 100): blocks 90..99 stay in
+    # HBM and are read in place when kept
+    spec = synth.scaled(synth.CONFIGS[5], batch=2, context=(20000, 20000), steps=3,
+                        plant_range=(8, 90), plant_count=5, local_tokens=7192,
+                        dense_boundary=0, config_id=102)
+    say("host tier small")
+    batch, host, sess = make_host_session(spec)
+    for t in range(3):
+        step(batch, sess, t)
+        torch.cuda.synchronize()
+        for b in range(2):
+            for h in range(8):
+                assert set(batch.planted[b]) <= set(gpu_selection(sess, b, h).tolist())
+        oracle_full_check(batch, sess, t, host=host)
+
+
+def test_host_tier_full_size_sampled():
+    say("config 5 (4 x 256K, host tier)")
+    batch, host, sess = make_host_session(synth.CONFIGS[5])
+    for t in range(16):
+        step(batch, sess, t)
+        if t in (0, 15):
+            torch.cuda.synchronize()
+            oracle_full_check(batch, sess, t, seqs=[0, 3], heads=[2, 6], host=host)
+
+
+def test_append_select_equals_append_then_select():
+    """The fused launch gives bit-identical pools, representations,
+    selections and merged tables to rkv_append_kv followed by rkv_select."""
+    spec = synth.custom("fused", batch=3, n_q_heads=16, n_kv_heads=4,
+                        context=(767, 9000, 20480), steps=2, init_tokens=256,
+                        local_tokens=1000, dense_boundary=0, config_id=103)
+    say("append_select vs append + select")
+    results = []
+    for fused in (False, True):
+        batch = synth.make_batch(spec, DEV)
+        prm, sess = make_session(batch)
+        prefill(batch, sess)
+        for t in range(2):
+            lens = i32(batch.lens_at(t))
+            kn, vn = batch.new_kv_bits(t)
+            if fused:
+                sess.append_select(batch.q_bits(t), kn, vn, lens)
+            else:
+                sess.append(kn, vn, lens)
+                sess.select(batch.q_bits(t), lens)
+        torch.cuda.synchronize()
+        results.append((batch.k_pages.clone(), batch.v_pages.clone(), sess.reps.clone(),
+                        sess.sel_ids.clone(), sess.n_sel.clone(), sess.merged.clone(),
+                        sess.n_merged.clone()))
+    for x, y in zip(*results):
+        assert torch.equal(x, y)
+    # sequence 0 completed block 5 at step 1: its representation exists
+    assert results[1][2][0, :, 5].abs().sum() > 0
