@@ -94,8 +94,8 @@ typedef struct rkv_params {
                               0 disables the dense switch */
   float scale;             /* softmax scale, default 1/sqrt(128) */
   int32_t attn_impl;       /* RKV_ATTN_AUTO / _MFMA / _VALU */
-  int32_t split_waves;     /* waves the attention split is spread over;
-                              0 = auto (1024: one per SIMD on MI355X) */
+  int32_t split_waves;     /* waves the attention split is spread over,
+                              at most 65536; 0 = auto (1024: one per SIMD) */
 } rkv_params;
 
 /* Defaults of the page (init 1024, local 7192, ratio 0.2, dense boundary
@@ -282,10 +282,12 @@ size_t rkv_attn_workspace_size(const rkv_params* params, int32_t batch,
  * merged blocks of the batch are spread evenly over split_waves waves, and
  * the partial softmax results are merged by their log-sum-exp (the
  * survey's cascade-inference paragraph: partial results merged the
- * FlashDecoding way).  batch * n_kv_heads * m_cap must stay below 2^30.
+ * FlashDecoding way) by a second kernel.  batch * n_kv_heads * m_cap must
+ * stay below 2^30.
  *   merged [batch][n_kv_heads][m_cap], n_merged [batch][n_kv_heads]
  *   out [batch][n_q_heads][128] fp32
- *   workspace >= rkv_attn_workspace_size(params, batch, m_cap) bytes
+ *   workspace >= rkv_attn_workspace_size(params, batch, m_cap) bytes of
+ *   scratch (partials); calls that overlap on one workspace race.
  * Errors: RKV_ERR_INVALID_ARG, RKV_ERR_UNSUPPORTED, RKV_ERR_WORKSPACE,
  * RKV_ERR_HIP.
  */

@@ -65,8 +65,8 @@ rkv_status check_params(const rkv_params* p, rkv::Method* m) {
   RKV_REQUIRE(isfinite(p->scale), RKV_ERR_INVALID_ARG, "scale is not finite");
   RKV_REQUIRE(p->attn_impl >= RKV_ATTN_AUTO && p->attn_impl <= RKV_ATTN_VALU,
               RKV_ERR_INVALID_ARG, "attn_impl %d unknown", p->attn_impl);
-  RKV_REQUIRE(p->split_waves >= 0 && p->split_waves <= (1 << 20),
-              RKV_ERR_INVALID_ARG, "split_waves %d outside [0, 2^20]",
+  RKV_REQUIRE(p->split_waves >= 0 && p->split_waves <= (1 << 16),
+              RKV_ERR_INVALID_ARG, "split_waves %d outside [0, 65536]",
               p->split_waves);
   if (m) {
     m->n_q_heads = p->n_q_heads;
