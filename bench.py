@@ -17,6 +17,7 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -35,6 +36,21 @@ from sparse_retrieval_kv_amd import synth  # noqa: E402
 from sparse_retrieval_kv_amd.decode import DecodeSession, HostTierSession  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+
+# HBM bytes moved by one rkv_decode_attn call (both of its kernels), from
+# two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE; KiB
+# per dispatch, mean over the dispatches of the timed steps).  Each counter
+# is scaled by what it reads for a plain 1 GiB device-to-device copy:
+# FETCH_SIZE reads 524315.6 KiB (x2.0), WRITE_SIZE 1048576 KiB (x1.0).
+# A record holds only for the attention source it was taken on; after any
+# change to that file the figure is reported as null until measured again.
+COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
+ATTN_SOURCE = os.path.join(ROOT, "sparse_retrieval_kv_amd", "csrc", "attn.hip")
+MEASURED_TRAFFIC = {
+    # config: (sha256 prefix of attn.hip, FETCH_SIZE KiB, WRITE_SIZE KiB)
+    2: ("639b242ce046f464", 40051.6 + 1161.0, 2080.0 + 16.0),
+    4: ("639b242ce046f464", 511090.4 + 2390.0, 4160.0 + 256.0),
+}
 METRIC = "decode attn steps/s and attended-KV HBM GB/s (% of peak) at 64K-128K ctx, 1 GPU"
 
 
@@ -64,7 +80,30 @@ def step_bytes(spec, context, t):
     return kv * spec.n_kv_heads, reps * spec.n_kv_heads, kept * spec.n_kv_heads
 
 
-def cpu_baseline(batch, host=None, budget_s=12.0, max_steps=8):
+def attn_traffic(config):
+    """Counter-measured HBM bytes per attention call, or None when no
+    record exists for this config and this attention source."""
+    rec = MEASURED_TRAFFIC.get(config)
+    if rec is None:
+        return None
+    with open(ATTN_SOURCE, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if not sha.startswith(rec[0]):
+        return None
+    return 1024.0 * (rec[1] * COUNTER_SCALE["FETCH_SIZE"] +
+                     rec[2] * COUNTER_SCALE["WRITE_SIZE"])
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return None
+
+
+def cpu_baseline(batch, host=None, budget_s=12.0, max_steps=100000):
     """Time the float64 oracle's decode step on the host over a bounded
     sample of the same workload (first sequence of the batch)."""
     import oracle as O
@@ -94,7 +133,7 @@ def cpu_baseline(batch, host=None, budget_s=12.0, max_steps=8):
         O.decode_step(q, K, V, L0 + t, L0, prm, reps=reps)
         n += 1
     dt = time.perf_counter() - t0
-    threads = torch.get_num_threads()
+    threads = blas_threads() or torch.get_num_threads()
     # one sequence of the batch per oracle step -> scale to batch steps
     seq_steps_per_s = n / dt
     return {
@@ -321,7 +360,9 @@ def main():
             "unit": "GB/s",
             "frac": attn_gbs / HBM_PEAK_GBS,
             "frac_of_read_probe": attn_gbs / probe_gbs,
-            "traffic": None,
+            "traffic": attn_traffic(args.config),
+            "traffic_source": ("rocprofv3 FETCH_SIZE + WRITE_SIZE per call, "
+                               "scaled by a 1 GiB copy's readings"),
             "bytes_per_launch": float(kv_attn),
             "avg_launch_us": float(attn_us),
             "timing": (f"{reps_attn} back-to-back rkv_decode_attn calls over the "
