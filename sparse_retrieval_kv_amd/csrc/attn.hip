@@ -117,14 +117,21 @@ __device__ __forceinline__ int units_of(const AttnArgs& a, int bh) {
   return 2 * n;
 }
 
-__device__ __forceinline__ int64_t unit_start(int w, int64_t T, int W) {
-  return (int64_t)w * T / W;
+// Every wave takes c = ceil(T / W) consecutive units (the last active wave
+// fewer; waves past the end none), so no wave carries more units than the
+// slowest one must.
+__device__ __forceinline__ int64_t units_per_wave(int64_t T, int W) {
+  return (T + W - 1) / W;
 }
 
-// The wave whose range holds unit u (0 <= u < T): the largest w with
-// unit_start(w) <= u.
+__device__ __forceinline__ int64_t unit_start(int w, int64_t T, int W) {
+  const int64_t s = (int64_t)w * units_per_wave(T, W);
+  return s < T ? s : T;
+}
+
+// The wave whose range holds unit u (0 <= u < T).
 __device__ __forceinline__ int wave_of(int64_t u, int64_t T, int W) {
-  return (int)(((u + 1) * W - 1) / T);
+  return (int)(u / units_per_wave(T, W));
 }
 
 __device__ __forceinline__ int wave_sum_i(int x) {
@@ -538,27 +545,15 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------------------
 // Combine: one 512-thread workgroup per (sequence, query head) merges the
-// partials of the waves that met its list.  The piece weights 2^(m - M) go
-// to LDS, then 16 groups of 32 threads each sum a strided subset of pieces
-// over float4 slices of the 128 dims (up to eight partial rows in flight per
-// thread), and the groups are added in a fixed order.
+// partials of the waves that met its list.  16 groups of 32 threads each
+// take a strided subset of the pieces over float4 slices of the 128 dims:
+// the (m, l) pairs and rows of up to eight pieces are requested at once and
+// folded with a running maximum, then the groups are merged in a fixed
+// order by their log-sum-exp.
 // ---------------------------------------------------------------------------
 constexpr int kCombThreads = 512;
 constexpr int kCombGroups = kCombThreads / 32;
-
-template <class Op>
-__device__ __forceinline__ float block_reduce(float v, float* sh, Op op) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = op(v, __shfl_xor(v, o));
-  if (lane == 0) sh[wave] = v;
-  __syncthreads();
-  float r = sh[0];
-#pragma unroll
-  for (int w = 1; w < kCombThreads / 64; ++w) r = op(r, sh[w]);
-  __syncthreads();
-  return r;
-}
+constexpr int kCombDepth = 8;
 
 __device__ __forceinline__ int block_sum_i(int v, int* sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -572,18 +567,10 @@ __device__ __forceinline__ int block_sum_i(int v, int* sh) {
   return r;
 }
 
-__device__ __forceinline__ void fma4(float4& acc, float w, const float4& v) {
-  acc.x += w * v.x;
-  acc.y += w * v.y;
-  acc.z += w * v.z;
-  acc.w += w * v.w;
-}
-
 __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(
     AttnArgs a, float* __restrict__ out) {
-  extern __shared__ float wsh[];  // [n_waves] piece weights
   __shared__ float4 red[kCombGroups][32];
-  __shared__ float sh[kCombThreads / 64];
+  __shared__ float2 gml[kCombGroups];
   __shared__ int ish[kCombThreads / 64];
   const int tid = threadIdx.x;
   const int bq = blockIdx.x;
@@ -593,8 +580,6 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(
   const int bh = b * a.n_kv + qh / G, hh = qh - (qh / G) * G;
   const int NB = a.batch * a.n_kv;
   const int W = a.n_waves;
-  auto add = [](float x, float y) { return x + y; };
-  auto mx = [](float x, float y) { return fmaxf(x, y); };
 
   // T and the offset of this list
   int tot = 0, before = 0;
@@ -611,64 +596,59 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(
     if (tid < kDim) dst[tid] = 0.f;
     return;
   }
+  // pieces: waves w0..w1 (each has a non-empty range), slot w + bh
   const int w0 = wave_of(off, T, W), w1 = wave_of(off + units - 1, T, W);
   const int np = w1 - w0 + 1;
-  // pieces: waves w0..w1 with a non-empty range, slot w + bh
-  float mloc = kNegInf;
-  for (int i = tid; i < np; i += kCombThreads) {
-    const int w = w0 + i;
-    if (unit_start(w, T, W) < unit_start(w + 1, T, W)) {
-      const float2 v = a.part_ml[((int64_t)w + bh) * G + hh];
-      if (v.y > 0.f) mloc = fmaxf(mloc, v.x);
+  const int d4 = tid & 31, cg = tid >> 5;
+  const int64_t slot0 = (int64_t)w0 + bh;
+  float mrun = kNegInf, lrun = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int base = cg; base < np; base += kCombDepth * kCombGroups) {
+    float2 ml[kCombDepth];
+    float4 v[kCombDepth];
+#pragma unroll
+    for (int u = 0; u < kCombDepth; ++u) {
+      const int i = base + u * kCombGroups;
+      const int64_t slot = slot0 + (i < np ? i : 0);
+      ml[u] = i < np ? a.part_ml[slot * G + hh] : make_float2(kNegInf, 0.f);
+      v[u] = reinterpret_cast<const float4*>(a.part_acc + (slot * G + hh) * kDim)[d4];
     }
-  }
-  const float M = block_reduce(mloc, sh, mx);
-  float dl = 0.f;
-  for (int i = tid; i < np; i += kCombThreads) {
-    const int w = w0 + i;
-    float wt = 0.f;
-    if (unit_start(w, T, W) < unit_start(w + 1, T, W)) {
-      const float2 v = a.part_ml[((int64_t)w + bh) * G + hh];
-      if (v.y > 0.f) {
-        wt = fast_exp2(v.x - M);
-        dl += wt * v.y;
+#pragma unroll
+    for (int u = 0; u < kCombDepth; ++u) {
+      if (ml[u].y > 0.f) {
+        const float mn = fmaxf(mrun, ml[u].x);
+        const float sc = fast_exp2(mrun - mn), wt = fast_exp2(ml[u].x - mn);
+        acc.x = acc.x * sc + wt * v[u].x;
+        acc.y = acc.y * sc + wt * v[u].y;
+        acc.z = acc.z * sc + wt * v[u].z;
+        acc.w = acc.w * sc + wt * v[u].w;
+        lrun = lrun * sc + wt * ml[u].y;
+        mrun = mn;
       }
     }
-    wsh[i] = wt;
-  }
-  const float den = block_reduce(dl, sh, add);  // also publishes wsh
-  const int d4 = tid & 31, cg = tid >> 5;
-  auto row = [&](int i) {
-    return reinterpret_cast<const float4*>(
-               a.part_acc + (((int64_t)w0 + i + bh) * G + hh) * kDim)[d4];
-  };
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  int i = cg;
-  for (; i + 7 * kCombGroups < np; i += 8 * kCombGroups) {
-    float4 v[8];
-    float wt[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      wt[u] = wsh[i + u * kCombGroups];
-      v[u] = wt[u] != 0.f ? row(i + u * kCombGroups) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) fma4(acc, wt[u], v[u]);
-  }
-  for (; i < np; i += kCombGroups) {
-    const float wt = wsh[i];
-    if (wt != 0.f) fma4(acc, wt, row(i));
   }
   red[cg][d4] = acc;
+  if (d4 == 0) gml[cg] = make_float2(mrun, lrun);
   __syncthreads();
   if (tid < 32) {
-    float4 t = red[0][tid];
+    float M = kNegInf;
 #pragma unroll
-    for (int g = 1; g < kCombGroups; ++g) {
-      t.x += red[g][tid].x;
-      t.y += red[g][tid].y;
-      t.z += red[g][tid].z;
-      t.w += red[g][tid].w;
+    for (int g = 0; g < kCombGroups; ++g) M = fmaxf(M, gml[g].x);
+    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+    float den = 0.f;
+    if (M > kNegInf) {
+#pragma unroll
+      for (int g = 0; g < kCombGroups; ++g) {
+        const float2 gm = gml[g];
+        if (gm.y > 0.f) {
+          const float wt = fast_exp2(gm.x - M);
+          t.x += wt * red[g][tid].x;
+          t.y += wt * red[g][tid].y;
+          t.z += wt * red[g][tid].z;
+          t.w += wt * red[g][tid].w;
+          den += wt * gm.y;
+        }
+      }
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
     reinterpret_cast<float4*>(dst)[tid] =
@@ -731,8 +711,7 @@ hipError_t launch_decode_attn(const Method& m, bool use_mfma,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(batch * m.n_q_heads),
-                     dim3(kCombThreads), (size_t)plan.n_waves * sizeof(float),
-                     stream, a, out);
+                     dim3(kCombThreads), 0, stream, a, out);
   return hipGetLastError();
 }
 

@@ -187,10 +187,8 @@ rkv_status rkv_append_kv(const rkv_params* params, const uint16_t* k_new,
 
 size_t rkv_select_workspace_size(const rkv_params* params, int32_t batch,
                                  int32_t max_blocks) {
-  (void)params;
-  (void)batch;
-  (void)max_blocks;
-  return 0;
+  if (!params || batch <= 0 || max_blocks <= 0 || params->n_kv_heads <= 0) return 0;
+  return rkv::select_keys_bytes(batch, params->n_kv_heads, max_blocks);
 }
 
 namespace {
@@ -227,7 +225,7 @@ rkv_status select_common(const rkv_params* params, const uint16_t* q,
   return hip_status(rkv::launch_select(m, q, reps, block_table, lens,
                                        prompt_lens, batch, max_blocks, sel_ids,
                                        n_sel, k_cap, merged, n_merged, m_cap,
-                                       append, stream),
+                                       workspace, append, stream),
                     what);
 }
 

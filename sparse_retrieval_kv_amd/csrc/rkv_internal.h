@@ -43,12 +43,17 @@ struct AppendOp {
   float* reps;  // may be null
 };
 
+// Workspace of launch_select: one uint32 order key per (sequence, KV head,
+// block).
+size_t select_keys_bytes(int batch, int n_kv_heads, int max_blocks);
+
 hipError_t launch_select(const Method& m, const uint16_t* q, const float* reps,
                          const int32_t* table, const int32_t* lens,
                          const int32_t* prompt_lens, int batch, int max_blocks,
                          int32_t* sel_ids, int32_t* n_sel, int k_cap,
                          int32_t* merged, int32_t* n_merged, int m_cap,
-                         const AppendOp* append, hipStream_t stream);
+                         void* workspace, const AppendOp* append,
+                         hipStream_t stream);
 
 hipError_t launch_merge(const Method& m, const int32_t* table, int max_blocks,
                         const int32_t* lens, const int32_t* sel_ids,

@@ -7,17 +7,20 @@
 // sliding-window blocks.  Defaults and the dense switch: same page,
 // "Configuration Parameters".
 //
-// One workgroup of 1024 threads handles one (sequence, KV head):
-//  1. the group's query heads are summed once (sum_g q_g . r = (sum_g q_g) . r);
-//  2. eight lanes score one representation (512 B, one 128-byte line per
-//     lane-octet per load), 128 representations per pass; scores become
-//     order-preserving uint32 keys in LDS;
-//  3. one wave (no workgroup barriers) runs a 4-pass 8-bit radix select over
-//     the keys to find the k-th largest key T (LDS histogram, reversed wave
-//     scan);
-//  4. the same wave compacts in index order with ballots: every key > T and
-//     the lowest-index keys == T, ids ascending; the merged page list gets
-//     the init blocks, the kept blocks and the local blocks.
+// Two launches per selection:
+//  1. score_kernel: 256-thread workgroups, each scoring 64 representations
+//     (32 KiB) of one (sequence, KV head), so the scan of a long sequence is
+//     spread over many compute units (one compute unit alone streams only a
+//     few tens of GB/s).  The group's query heads are summed once
+//     (sum_g q_g . r = (sum_g q_g) . r); eight lanes score one
+//     representation; scores become order-preserving uint32 keys in the
+//     workspace.  Extra workgroups append the decoded token meanwhile.
+//  2. topk_kernel: one 1024-thread workgroup per (sequence, KV head) holds
+//     the keys and block-table entries in registers, finds the k-th largest
+//     key T by a 4-pass 8-bit radix select over an LDS histogram (wave-
+//     aggregated atomics), then keeps every key > T and the lowest-index
+//     keys == T with one workgroup scan, writing the kept ids ascending and
+//     the merged page list (init blocks, kept blocks, local blocks).
 #include "rkv.h"
 #include "rkv_device.h"
 #include "rkv_internal.h"
@@ -25,81 +28,12 @@
 namespace rkv {
 namespace {
 
-constexpr int kSelThreads = 1024;
 
 // fp32 -> uint32 whose unsigned order is the float order (-0 taken as +0).
 __device__ __forceinline__ uint32_t order_key(float f) {
   f = f + 0.0f;  // -0 + +0 = +0 under round-to-nearest
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Exact top-k of keys[0..n) (1 <= k < n) by one wave: a 4-pass 8-bit radix
-// select finds the k-th largest key T (LDS histogram, reversed wave scan),
-// then an ordered ballot compaction keeps every key > T and the
-// lowest-index keys == T, writing the kept ids ascending to srow and
-// replacing each key by its rank + 1 (0 when not kept).
-__device__ __forceinline__ void select_in_wave(uint32_t* keys, int n, int k,
-                                               int id0, int32_t* srow,
-                                               uint32_t* hist) {
-  const int lane = threadIdx.x & 63;
-  uint32_t prefix = 0, pmask = 0;
-  int remaining = k;  // keys still to take among those matching prefix
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hist[4 * lane + i] = 0;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    for (int j = lane; j < n; j += 64) {
-      const uint32_t key = keys[j];
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
-    const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
-    const uint32_t s = h0 + h1 + h2 + h3;
-    uint32_t incl = s;  // sum over lanes >= this lane
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t y = __shfl_down(incl, off);
-      if (lane + off < 64) incl += y;
-    }
-    const uint32_t a3 = incl - s;  // count in bins above 4*lane+3
-    const uint32_t a2 = a3 + h3, a1 = a2 + h2, a0 = a1 + h1;
-    const uint32_t rem = (uint32_t)remaining;
-    int digit = -1, above = 0;
-    if (a3 < rem && rem <= a3 + h3) { digit = 4 * lane + 3; above = (int)a3; }
-    if (a2 < rem && rem <= a2 + h2) { digit = 4 * lane + 2; above = (int)a2; }
-    if (a1 < rem && rem <= a1 + h1) { digit = 4 * lane + 1; above = (int)a1; }
-    if (a0 < rem && rem <= a0 + h0) { digit = 4 * lane;     above = (int)a0; }
-    // exactly one lane found the digit holding the remaining-th key
-    const uint64_t who = __ballot(digit >= 0);
-    const int src = __builtin_ctzll(who);
-    digit = __shfl(digit, src);
-    above = __shfl(above, src);
-    remaining -= above;
-    prefix |= (uint32_t)digit << shift;
-    pmask |= 255u << shift;
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  }
-  const uint32_t T = prefix;  // the k-th largest key; take `remaining` of == T
-  int out = 0;
-  for (int base = 0; base < n; base += 64) {
-    const int j = base + lane;
-    const uint32_t key = j < n ? keys[j] : 0u;
-    const bool eq = j < n && key == T;
-    const uint64_t eqm = __ballot(eq);
-    const int eq_rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(eqm >> 32),
-                            __builtin_amdgcn_mbcnt_lo((uint32_t)eqm, 0u));
-    const bool keep = (j < n && key > T) || (eq && eq_rank < remaining);
-    const uint64_t km = __ballot(keep);
-    const int pos = out + __builtin_amdgcn_mbcnt_hi((uint32_t)(km >> 32),
-                              __builtin_amdgcn_mbcnt_lo((uint32_t)km, 0u));
-    if (keep) srow[pos] = id0 + j;
-    if (j < n) keys[j] = keep ? (uint32_t)(pos + 1) : 0u;
-    out += __popcll(km);
-    remaining -= __popcll(eqm);
-  }
 }
 
 // Merged page list: init blocks, the given kept offload blocks (written by
@@ -178,6 +112,10 @@ struct SelArgs {
   const int32_t* lens;
   const int32_t* prompt_lens;
   int max_blocks;
+  int ib;        // first offload block: min(ceil(init / 128), max_blocks)
+  int n_chunks;  // score chunks per (sequence, KV head)
+  int n_bh;      // batch * n_kv_heads
+  uint32_t* keys;  // workspace [batch][n_kv_heads][max_blocks]
   int32_t* sel_ids;
   int32_t* n_sel;
   int k_cap;
@@ -186,25 +124,58 @@ struct SelArgs {
   int m_cap;
 };
 
-constexpr int kTabRegs = RKV_MAX_BLOCKS / kSelThreads;  // table entries per thread
-constexpr int kSlots = kSelThreads / 8;                  // reps per scoring round
+constexpr int kScoreThreads = 256;
+constexpr int kScoreChunk = 64;  // representations per score workgroup
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kTabRegs = RKV_MAX_BLOCKS / kTopkThreads;  // blocks per thread
 
-// Everything that does not depend on the sequence length -- the length, the
-// query, this thread's block-table entries and the first round of
-// representations -- is requested at once, so the selection costs about one
-// memory round trip before its LDS work.
+// Regions, k and whether scores are needed, from the raw lengths.
+struct Pick {
+  Regions R;
+  int k;
+  bool ranked;  // 0 < k < n_off: the top-k needs the scores
+};
+
+__device__ __forceinline__ Pick pick_of(const Method& m, int lraw, int plen,
+                                        int max_blocks) {
+  Pick p;
+  const int L = clamp_len(lraw, max_blocks * kBlock);
+  p.R = regions_of(L, m.init_tokens, m.local_tokens);
+  const bool dense = plen < m.dense_boundary || m.topk_ppm >= kPpmOne;
+  const int n = p.R.n_off;
+  int k = dense ? n : topk_of(n, m.topk_ppm);
+  p.k = k < n ? k : n;
+  p.ranked = p.k > 0 && p.k < n;
+  return p;
+}
+
+// Workgroup item = (bh, chunk c): representations of blocks
+// [ib + 64c, ib + 64c + 64) of the offload range.  Items past the score
+// grid append the decoded token of sequence-head item - n_bh * n_chunks
+// (one wave).
 template <bool APPEND>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(SelArgs a, AppendArgs ap) {
-  extern __shared__ uint32_t keys[];  // [max_blocks]: scores, then ranks
+__global__ __launch_bounds__(kScoreThreads) void score_kernel(SelArgs a,
+                                                              AppendArgs ap) {
   __shared__ float qs[kDim];
-  __shared__ uint32_t hist[256];
-
   const Method& m = a.m;
   const int tid = threadIdx.x;
-  const int bh = blockIdx.x;
-  const int b = bh / m.n_kv_heads, h = bh - b * m.n_kv_heads;
+  const int64_t item = blockIdx.x;
   const int max_blocks = a.max_blocks;
-  const int32_t* trow = a.table + (int64_t)b * max_blocks;
+  const int64_t n_items = (int64_t)a.n_chunks * a.n_bh;
+  if (item >= n_items) {
+    if (APPEND && tid < 64) {
+      const int bh = (int)(item - n_items);
+      const int b = bh / m.n_kv_heads, h = bh - b * m.n_kv_heads;
+      const int L = clamp_len(a.lens[b], max_blocks * kBlock);
+      append_in_wave(ap, bh, h, m.n_kv_heads, L, max_blocks,
+                     a.table + (int64_t)b * max_blocks);
+    }
+    return;
+  }
+  const int bh = (int)(item / a.n_chunks);
+  const int c = (int)(item - (int64_t)bh * a.n_chunks);
+  const int b = bh / m.n_kv_heads, h = bh - b * m.n_kv_heads;
 
   // --- requests independent of the length ---
   const int lraw = a.lens[b];
@@ -215,101 +186,221 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelArgs a, AppendAr
     for (int g = 0; g < m.group; ++g)
       qsum += __uint_as_float((uint32_t)qh[g * kDim + tid] << 16);
   }
+  const int o = tid & 7, slot = tid >> 3;  // lane octet o of slot 0..31
+  const int j0 = a.ib + c * kScoreChunk;
+  float4 v[2][4];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    int j = j0 + u * 32 + slot;
+    j = j < max_blocks ? j : max_blocks - 1;
+    const float4* p = reinterpret_cast<const float4*>(
+        a.reps + ((int64_t)bh * max_blocks + j) * kDim);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[u][i] = p[o + 8 * i];
+  }
+
+  // --- this chunk's share of the offload range ---
+  const Pick pk = pick_of(m, lraw, plen, max_blocks);
+  const int ls = pk.R.n_init + pk.R.n_off;  // offload end
+  if (!pk.ranked || j0 >= ls) return;  // uniform over the workgroup
+  if (tid < kDim) qs[tid] = qsum;
+  __syncthreads();
+  float4 qv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    qv[i] = *reinterpret_cast<const float4*>(&qs[4 * (o + 8 * i)]);
+  uint32_t* krow = a.keys + (int64_t)bh * max_blocks;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int j = j0 + u * 32 + slot;
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      part += v[u][i].x * qv[i].x + v[u][i].y * qv[i].y +
+              v[u][i].z * qv[i].z + v[u][i].w * qv[i].w;
+    part += __shfl_xor(part, 1);
+    part += __shfl_xor(part, 2);
+    part += __shfl_xor(part, 4);
+    if (o == 0 && j < ls) krow[j] = order_key(part);
+  }
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave in lane order: row
+// shifts by 1, 2, 4, 8 within each row of 16 lanes, then the last lane of
+// row 0 / row 2 is broadcast into rows 1 / 3 and the last lane of row 1
+// into rows 2 and 3 (DPP row_shr and row_bcast).
+__device__ __forceinline__ uint32_t wave_prefix_incl(uint32_t x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);
+  return x;
+}
+
+// Inclusive workgroup scan helper: returns the sum of `x` over the waves
+// before this one and the total; `sh` holds kTopkWaves words.
+__device__ __forceinline__ uint32_t waves_before(uint32_t x, uint32_t* sh,
+                                                 uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) sh[wave] = x;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    const uint32_t y = sh[w];
+    before += w < wave ? y : 0u;
+    all += y;
+  }
+  __syncthreads();  // sh may be reused right after
+  *total = all;
+  return before;
+}
+
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelArgs a) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t wsh[kTopkWaves];
+  __shared__ int sdig[3];
+  const Method& m = a.m;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int bh = blockIdx.x;
+  const int b = bh / m.n_kv_heads;
+  const int max_blocks = a.max_blocks;
+  const int32_t* trow = a.table + (int64_t)b * max_blocks;
+  const uint32_t* krow = a.keys + (int64_t)bh * max_blocks;
+
+  // --- requests independent of the length ---
+  const int lraw = a.lens[b];
+  const int plen = a.prompt_lens ? a.prompt_lens[b] : lraw;
   int tab[kTabRegs];
+  uint32_t key[kTabRegs];
 #pragma unroll
   for (int i = 0; i < kTabRegs; ++i) {
-    const int j = tid + kSelThreads * i;
-    tab[i] = j < max_blocks ? trow[j] : -1;
+    const int j = tid + kTopkThreads * i;
+    const bool in = j < max_blocks;
+    tab[i] = in ? trow[j] : -1;
+    key[i] = in ? krow[j] : 0u;
   }
-  // offload blocks start at ceil(init/128) whenever there are any
-  int ib = (int)(((int64_t)m.init_tokens + 127) >> 7);
-  ib = ib < max_blocks ? ib : max_blocks;
-  const int n_cap = max_blocks - ib;  // rows of reps that exist after ib
-  const float* rbase = a.reps + ((int64_t)bh * max_blocks + ib) * kDim;
-  const int o = tid & 7;
-  float4 v[4][4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int jj = u * kSlots + (tid >> 3);
-    const float4* p = reinterpret_cast<const float4*>(
-        rbase + (int64_t)(jj < n_cap ? jj : 0) * kDim);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      v[u][i] = n_cap > 0 ? p[o + 8 * i] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  if (tid < 256) hist[tid] = 0u;
 
-  // --- regions and k ---
-  const int L = clamp_len(lraw, max_blocks * kBlock);
-  const Regions R = regions_of(L, m.init_tokens, m.local_tokens);
-  const bool dense = plen < m.dense_boundary || m.topk_ppm >= kPpmOne;
-  const int n = R.n_off;  // when n > 0, R.n_init == ib
-  int k = dense ? n : topk_of(n, m.topk_ppm);
-  k = k < n ? k : n;
+  const Pick pk = pick_of(m, lraw, plen, max_blocks);
+  const Regions& R = pk.R;
+  const int k = pk.k;
+  const int ls = R.n_init + R.n_off;
   int32_t* srow = a.sel_ids + (int64_t)bh * a.k_cap;
   int32_t* mrow = a.merged ? a.merged + (int64_t)bh * a.m_cap : nullptr;
+  const int lstart = R.local_start > R.n_init ? R.local_start : R.n_init;
 
-  if (k > 0 && k < n) {
-    if (tid < kDim) qs[tid] = qsum;
-    __syncthreads();
-    float4 qv[4];
+  // rank + 1 of each kept offload block this thread holds (0: not kept)
+  int rank1[kTabRegs];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      qv[i] = *reinterpret_cast<const float4*>(&qs[4 * (o + 8 * i)]);
-    // scores -> order keys; lane octet o covers floats 4(o+8i)..+3 of a rep
-    for (int base = 0; base < n; base += 4 * kSlots) {
-      if (base > 0) {  // later rounds: only when n > 512
+  for (int i = 0; i < kTabRegs; ++i) rank1[i] = 0;
+
+  if (pk.ranked) {  // uniform over the workgroup
+    __syncthreads();  // hist zeroed
+    uint32_t prefix = 0, pmask = 0;
+    int remaining = k;  // keys still to take among those matching prefix
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int jj = base + u * kSlots + (tid >> 3);
-          const float4* p = reinterpret_cast<const float4*>(
-              rbase + (int64_t)(jj < n ? jj : 0) * kDim);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[u][i] = p[o + 8 * i];
+      for (int i = 0; i < kTabRegs; ++i) {
+        const int j = tid + kTopkThreads * i;
+        if (kTopkThreads * i >= ls) break;  // uniform
+        const bool has = j >= R.n_init && j < ls && (key[i] & pmask) == prefix;
+        const uint32_t d = (key[i] >> shift) & 255u;
+        // lanes sharing the first active lane's digit add with one atomic
+        const uint64_t act = __ballot(has);
+        if (act == 0) continue;
+        const int first = __builtin_ctzll(act);
+        const uint32_t d0 = __builtin_amdgcn_readlane(d, first);
+        const uint64_t same = __ballot(has && d == d0);
+        if (lane == first) atomicAdd(&hist[d0], (uint32_t)__popcll(same));
+        if (has && d != d0) atomicAdd(&hist[d], 1u);
+      }
+      __syncthreads();
+      if (tid < 64) {
+        const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
+        const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+        hist[4 * lane] = 0u;
+        hist[4 * lane + 1] = 0u;
+        hist[4 * lane + 2] = 0u;
+        hist[4 * lane + 3] = 0u;
+        const uint32_t s4 = h0 + h1 + h2 + h3;
+        const uint32_t incl = wave_prefix_incl(s4);
+        const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
+        const uint32_t a3 = total - incl;  // count in bins above 4*lane+3
+        const uint32_t a2 = a3 + h3, a1 = a2 + h2, a0 = a1 + h1;
+        const uint32_t rem = (uint32_t)remaining;
+        int digit = -1, above = 0, cnt = 0;
+        if (a3 < rem && rem <= a3 + h3) { digit = 4 * lane + 3; above = (int)a3; cnt = (int)h3; }
+        if (a2 < rem && rem <= a2 + h2) { digit = 4 * lane + 2; above = (int)a2; cnt = (int)h2; }
+        if (a1 < rem && rem <= a1 + h1) { digit = 4 * lane + 1; above = (int)a1; cnt = (int)h1; }
+        if (a0 < rem && rem <= a0 + h0) { digit = 4 * lane;     above = (int)a0; cnt = (int)h0; }
+        // exactly one lane holds the digit of the remaining-th key
+        if (digit >= 0) {
+          sdig[0] = digit;
+          sdig[1] = above;
+          sdig[2] = cnt;
         }
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int jj = base + u * kSlots + (tid >> 3);
-        float part = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          part += v[u][i].x * qv[i].x + v[u][i].y * qv[i].y +
-                  v[u][i].z * qv[i].z + v[u][i].w * qv[i].w;
-        part += __shfl_xor(part, 1);
-        part += __shfl_xor(part, 2);
-        part += __shfl_xor(part, 4);
-        if (o == 0 && jj < n) keys[jj] = order_key(part);
-      }
+      __syncthreads();
+      remaining -= sdig[1];
+      prefix |= (uint32_t)sdig[0] << shift;
+      pmask |= 255u << shift;
+      // every key left in the chosen bin is taken: the class is settled
+      if (remaining == sdig[2]) break;  // uniform
     }
-    __syncthreads();
-    // wave 0 selects; the last wave appends the decoded token meanwhile
-    if (tid < 64) select_in_wave(keys, n, k, R.n_init, srow, hist);
-    if (APPEND && tid >= kSelThreads - 64)
-      append_in_wave(ap, bh, h, m.n_kv_heads, L, max_blocks, trow);
-    __syncthreads();  // ranks in keys[] are visible to every thread
+    // keys whose masked value exceeds the prefix are kept, and the first
+    // `remaining` keys (in block order) whose masked value equals it
+    uint32_t gt_carry = 0, eq_carry = 0;
+#pragma unroll
+    for (int i = 0; i < kTabRegs; ++i) {
+      if (kTopkThreads * i >= ls) break;  // uniform
+      const int j = tid + kTopkThreads * i;
+      const bool cand = j >= R.n_init && j < ls;
+      const uint32_t mk = key[i] & pmask;
+      const bool gt = cand && mk > prefix, eq = cand && mk == prefix;
+      const uint64_t gm = __ballot(gt), em = __ballot(eq);
+      // gt counts in the low 16 bits, eq counts in the high 16 (n < 2^16)
+      const uint32_t wcnt = (uint32_t)__popcll(gm) | ((uint32_t)__popcll(em) << 16);
+      uint32_t tot;
+      const uint32_t wb = waves_before(wcnt, wsh, &tot);
+      const uint32_t gt_before = gt_carry + (wb & 0xffffu) + (uint32_t)lanes_below(gm);
+      const uint32_t eq_before = eq_carry + (wb >> 16) + (uint32_t)lanes_below(em);
+      const uint32_t rem = (uint32_t)remaining;
+      const uint32_t pos = gt_before + (eq_before < rem ? eq_before : rem);
+      if ((gt || (eq && eq_before < rem)) && pos < (uint32_t)k) {
+        srow[pos] = j;
+        rank1[i] = (int)pos + 1;
+      }
+      gt_carry += tot & 0xffffu;
+      eq_carry += tot >> 16;
+    }
   } else {
-    for (int r = tid; r < k; r += kSelThreads) srow[r] = R.n_init + r;
-    if (APPEND && tid >= kSelThreads - 64)
-      append_in_wave(ap, bh, h, m.n_kv_heads, L, max_blocks, trow);
+    for (int r = tid; r < k; r += kTopkThreads) srow[r] = R.n_init + r;
   }
 
   // merged page list from the block-table entries each thread holds
   if (mrow) {
-    const int lstart = R.local_start > R.n_init ? R.local_start : R.n_init;
 #pragma unroll
     for (int i = 0; i < kTabRegs; ++i) {
-      const int j = tid + kSelThreads * i;
+      const int j = tid + kTopkThreads * i;
       if (j >= R.nb) continue;
       int dst = -1;
       if (j < R.n_init) {
         dst = j;
       } else if (j >= lstart) {
         dst = R.n_init + k + (j - lstart);
-      } else if (k == n) {
+      } else if (k == R.n_off) {
         dst = j;
-      } else if (k > 0) {
-        const uint32_t rank = keys[j - R.n_init];
-        if (rank) dst = R.n_init + (int)rank - 1;
+      } else if (rank1[i]) {
+        dst = R.n_init + rank1[i] - 1;
       }
       if (dst >= 0) mrow[dst] = tab[i];
     }
@@ -356,27 +447,39 @@ __global__ __launch_bounds__(256) void merge_kernel(
 
 }  // namespace
 
+size_t select_keys_bytes(int batch, int n_kv_heads, int max_blocks) {
+  return (size_t)batch * n_kv_heads * max_blocks * sizeof(uint32_t);
+}
+
 hipError_t launch_select(const Method& m, const uint16_t* q, const float* reps,
                          const int32_t* table, const int32_t* lens,
                          const int32_t* prompt_lens, int batch, int max_blocks,
                          int32_t* sel_ids, int32_t* n_sel, int k_cap,
                          int32_t* merged, int32_t* n_merged, int m_cap,
-                         const AppendOp* append, hipStream_t stream) {
+                         void* workspace, const AppendOp* append,
+                         hipStream_t stream) {
   const int groups = batch * m.n_kv_heads;
   if (groups == 0) return hipSuccess;
-  const size_t lds = (size_t)max_blocks * sizeof(uint32_t);
-  SelArgs a{m, q, reps, table, lens, prompt_lens, max_blocks, sel_ids, n_sel,
-            k_cap, merged, n_merged, m_cap};
+  int ib = (int)(((int64_t)m.init_tokens + 127) >> 7);
+  ib = ib < max_blocks ? ib : max_blocks;
+  const int n_chunks = (max_blocks - ib + kScoreChunk - 1) / kScoreChunk;
+  SelArgs a{m, q, reps, table, lens, prompt_lens, max_blocks, ib, n_chunks,
+            groups, static_cast<uint32_t*>(workspace), sel_ids, n_sel, k_cap,
+            merged, n_merged, m_cap};
+  const int64_t score_wgs = (int64_t)groups * n_chunks;
   if (append) {
     AppendArgs ap{append->k_new, append->v_new, append->k_pages, append->v_pages,
                   append->n_pages, append->reps};
-    hipLaunchKernelGGL(select_kernel<true>, dim3(groups), dim3(kSelThreads), lds,
-                       stream, a, ap);
-  } else {
+    hipLaunchKernelGGL(score_kernel<true>, dim3((unsigned)(score_wgs + groups)),
+                       dim3(kScoreThreads), 0, stream, a, ap);
+  } else if (score_wgs > 0) {
     AppendArgs ap{};
-    hipLaunchKernelGGL(select_kernel<false>, dim3(groups), dim3(kSelThreads), lds,
-                       stream, a, ap);
+    hipLaunchKernelGGL(score_kernel<false>, dim3((unsigned)score_wgs),
+                       dim3(kScoreThreads), 0, stream, a, ap);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_kernel, dim3(groups), dim3(kTopkThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -151,7 +151,8 @@ def test_workspace_sizes_are_monotone(L):
     b = L.rkv_attn_workspace_size(ctypes.byref(p), 16, 1025)
     assert 0 < a < b
     assert L.rkv_attn_workspace_size(None, 1, 10) == 0
-    assert L.rkv_select_workspace_size(ctypes.byref(p), 16, 1025) == 0
+    assert L.rkv_select_workspace_size(ctypes.byref(p), 16, 1025) == 16 * p.n_kv_heads * 1025 * 4
+    assert L.rkv_select_workspace_size(None, 16, 1025) == 0
 
 
 def test_binding_refuses_host_tensors(L):
