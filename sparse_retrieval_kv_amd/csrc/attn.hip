@@ -101,9 +101,10 @@ struct AttnArgs {
   const int32_t* merged;
   const int32_t* n_merged;
   const int32_t* lens;
-  float* part_acc;   // [n_slots][group][128]
-  float2* part_ml;   // [n_slots][group]
-  int m_cap, max_len, batch, n_kv, group, n_waves;
+  float* part_acc;   // [batch * n_kv][piece_cap][group][128]
+  float2* part_ml;   // [batch * n_kv][piece_cap][group]
+  int* n_pieces;     // [batch * n_kv]: pieces of each non-empty list
+  int m_cap, max_len, batch, n_kv, group, n_waves, piece_cap;
   float scale_log2;  // scale * log2(e)
 };
 
@@ -527,8 +528,12 @@ __device__ __forceinline__ void split_body(const AttnArgs& a) {
       const int pu = __shfl(u, src);
       const int64_t a0 = lo > ps ? lo : ps;
       const int64_t a1 = hi < ps + pu ? hi : ps + pu;
-      run_piece(a, math, pbh, (int)(a0 - ps), (int)(a1 - ps), (int64_t)w + pbh,
-                lane, col, grp);
+      // piece w - w0 of list pbh; the list's first wave records the count
+      const int w0 = wave_of(ps, T, W);
+      if (w == w0 && lane == 0)
+        a.n_pieces[pbh] = wave_of(ps + pu - 1, T, W) - w0 + 1;
+      run_piece(a, math, pbh, (int)(a0 - ps), (int)(a1 - ps),
+                (int64_t)pbh * a.piece_cap + (w - w0), lane, col, grp);
     }
     run += __shfl(incl, 63);
   }
@@ -544,129 +549,100 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Combine: one 512-thread workgroup per (sequence, query head) merges the
-// partials of the waves that met its list.  16 groups of 32 threads each
-// take a strided subset of the pieces over float4 slices of the 128 dims:
-// the (m, l) pairs and rows of up to eight pieces are requested at once and
-// folded with a running maximum, then the groups are merged in a fixed
-// order by their log-sum-exp.
+// Combine: one wave per (sequence, query head, 32-dim slice), so that even a
+// batch of one sequence spreads the partial reads over many compute units.
+// A list's pieces sit in its own run of piece_cap slots.  Lane (pg, d4)
+// takes pieces pg, pg + 8, ... (up to 16 requested at once) over the float4
+// d4 of the slice and folds them with a running maximum; the eight piece
+// groups are then merged by log-sum-exp in a fixed butterfly order.
 // ---------------------------------------------------------------------------
-constexpr int kCombThreads = 512;
-constexpr int kCombGroups = kCombThreads / 32;
-constexpr int kCombDepth = 8;
+constexpr int kCombSlices = 4;   // 32-dim slices per query head
+constexpr int kCombGroups = 8;   // piece groups per wave
+constexpr int kCombDepth = 16;   // pieces in flight per lane
 
-__device__ __forceinline__ int block_sum_i(int v, int* sh) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  v = wave_sum_i(v);
-  if (lane == 0) sh[wave] = v;
-  __syncthreads();
-  int r = 0;
-#pragma unroll
-  for (int w = 0; w < kCombThreads / 64; ++w) r += sh[w];
-  __syncthreads();
-  return r;
+__device__ __forceinline__ void lse_fold(float& m, float& l, float4& acc, float m2,
+                                         float l2, const float4& acc2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == kNegInf) return;  // both sides empty
+  const float s1 = fast_exp2(m - mn), s2 = fast_exp2(m2 - mn);
+  acc.x = acc.x * s1 + acc2.x * s2;
+  acc.y = acc.y * s1 + acc2.y * s2;
+  acc.z = acc.z * s1 + acc2.z * s2;
+  acc.w = acc.w * s1 + acc2.w * s2;
+  l = l * s1 + l2 * s2;
+  m = mn;
 }
 
-__global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(
-    AttnArgs a, float* __restrict__ out) {
-  __shared__ float4 red[kCombGroups][32];
-  __shared__ float2 gml[kCombGroups];
-  __shared__ int ish[kCombThreads / 64];
-  const int tid = threadIdx.x;
-  const int bq = blockIdx.x;
+__global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a,
+                                                          float* __restrict__ out) {
+  const int lane = threadIdx.x;
+  const int pg = lane >> 3, d4 = lane & 7;
+  const int bq = blockIdx.x / kCombSlices, slice = blockIdx.x % kCombSlices;
   const int G = a.group;
   const int Hq = a.n_kv * G;
   const int b = bq / Hq, qh = bq - b * Hq;
   const int bh = b * a.n_kv + qh / G, hh = qh - (qh / G) * G;
-  const int NB = a.batch * a.n_kv;
-  const int W = a.n_waves;
+  const int P = a.piece_cap;
+  const int64_t slot0 = (int64_t)bh * P;
+  const int dim0 = 32 * slice + 4 * d4;
+  float4* dst = reinterpret_cast<float4*>(out + (int64_t)bq * kDim + dim0);
 
-  // T and the offset of this list
-  int tot = 0, before = 0;
-  for (int i = tid; i < NB; i += kCombThreads) {
-    const int u = units_of(a, i);
-    tot += u;
-    before += i < bh ? u : 0;
-  }
-  const int64_t T = block_sum_i(tot, ish);
-  const int64_t off = block_sum_i(before, ish);
   const int units = units_of(a, bh);
-  float* dst = out + (int64_t)bq * kDim;
-  if (units == 0) {
-    if (tid < kDim) dst[tid] = 0.f;
-    return;
-  }
-  // pieces: waves w0..w1 (each has a non-empty range), slot w + bh
-  const int w0 = wave_of(off, T, W), w1 = wave_of(off + units - 1, T, W);
-  const int np = w1 - w0 + 1;
-  const int d4 = tid & 31, cg = tid >> 5;
-  const int64_t slot0 = (int64_t)w0 + bh;
-  float mrun = kNegInf, lrun = 0.f;
+  int np = a.n_pieces[bh];
+  np = units == 0 ? 0 : (np < 1 ? 1 : (np > P ? P : np));
+  float m = kNegInf, l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int base = cg; base < np; base += kCombDepth * kCombGroups) {
+  for (int base = pg; base < np; base += kCombDepth * kCombGroups) {
     float2 ml[kCombDepth];
     float4 v[kCombDepth];
 #pragma unroll
     for (int u = 0; u < kCombDepth; ++u) {
       const int i = base + u * kCombGroups;
-      const int64_t slot = slot0 + (i < np ? i : 0);
-      ml[u] = i < np ? a.part_ml[slot * G + hh] : make_float2(kNegInf, 0.f);
-      v[u] = reinterpret_cast<const float4*>(a.part_acc + (slot * G + hh) * kDim)[d4];
-    }
-#pragma unroll
-    for (int u = 0; u < kCombDepth; ++u) {
-      if (ml[u].y > 0.f) {
-        const float mn = fmaxf(mrun, ml[u].x);
-        const float sc = fast_exp2(mrun - mn), wt = fast_exp2(ml[u].x - mn);
-        acc.x = acc.x * sc + wt * v[u].x;
-        acc.y = acc.y * sc + wt * v[u].y;
-        acc.z = acc.z * sc + wt * v[u].z;
-        acc.w = acc.w * sc + wt * v[u].w;
-        lrun = lrun * sc + wt * ml[u].y;
-        mrun = mn;
+      if (i < np) {
+        const int64_t slot = slot0 + i;
+        ml[u] = a.part_ml[slot * G + hh];
+        v[u] = *reinterpret_cast<const float4*>(a.part_acc + (slot * G + hh) * kDim + dim0);
+      } else {
+        ml[u] = make_float2(kNegInf, 0.f);
       }
     }
+#pragma unroll
+    for (int u = 0; u < kCombDepth; ++u)
+      if (ml[u].y > 0.f) lse_fold(m, l, acc, ml[u].x, ml[u].y, v[u]);
   }
-  red[cg][d4] = acc;
-  if (d4 == 0) gml[cg] = make_float2(mrun, lrun);
-  __syncthreads();
-  if (tid < 32) {
-    float M = kNegInf;
 #pragma unroll
-    for (int g = 0; g < kCombGroups; ++g) M = fmaxf(M, gml[g].x);
-    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
-    float den = 0.f;
-    if (M > kNegInf) {
-#pragma unroll
-      for (int g = 0; g < kCombGroups; ++g) {
-        const float2 gm = gml[g];
-        if (gm.y > 0.f) {
-          const float wt = fast_exp2(gm.x - M);
-          t.x += wt * red[g][tid].x;
-          t.y += wt * red[g][tid].y;
-          t.z += wt * red[g][tid].z;
-          t.w += wt * red[g][tid].w;
-          den += wt * gm.y;
-        }
-      }
-    }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    reinterpret_cast<float4*>(dst)[tid] =
-        make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+  for (int off = 8; off < 64; off <<= 1) {
+    const float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
+    float4 a2;
+    a2.x = __shfl_xor(acc.x, off);
+    a2.y = __shfl_xor(acc.y, off);
+    a2.z = __shfl_xor(acc.z, off);
+    a2.w = __shfl_xor(acc.w, off);
+    lse_fold(m, l, acc, m2, l2, a2);
+  }
+  if (pg == 0) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    *dst = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
 }
 
 }  // namespace
 
-AttnPlan plan_attention(int batch, int n_q_heads, int n_kv_heads, int waves) {
+AttnPlan plan_attention(int batch, int n_q_heads, int n_kv_heads, int waves,
+                        int m_cap) {
   AttnPlan p;
   // one wave per SIMD on 256 compute units: the whole split runs in one
   // round, each wave streaming its own run of units
   p.n_waves = waves > 0 ? waves : 1024;
+  // a list of at most 2 * m_cap units meets at most min(W, 2 m_cap) + 1 waves
+  const int units_cap = 2 * (m_cap > 0 ? m_cap : 1);
+  p.piece_cap = (p.n_waves < units_cap ? p.n_waves : units_cap) + 1;
   const int group = n_kv_heads > 0 ? n_q_heads / n_kv_heads : 0;
-  const size_t slots = (size_t)p.n_waves + (size_t)batch * n_kv_heads;
+  const size_t slots = (size_t)batch * n_kv_heads * p.piece_cap;
   p.partial_bytes = slots * group * kDim * sizeof(float);
   p.ml_bytes = slots * group * 2 * sizeof(float);
+  p.count_bytes = ((size_t)batch * n_kv_heads * sizeof(int) + 255) / 256 * 256;
+  p.total_bytes = p.partial_bytes + p.ml_bytes + p.count_bytes;
   return p;
 }
 
@@ -689,6 +665,9 @@ hipError_t launch_decode_attn(const Method& m, bool use_mfma,
   a.part_acc = static_cast<float*>(workspace);
   a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) +
                                         plan.partial_bytes);
+  a.n_pieces = reinterpret_cast<int*>(static_cast<char*>(workspace) +
+                                      plan.partial_bytes + plan.ml_bytes);
+  a.piece_cap = plan.piece_cap;
   a.m_cap = m_cap;
   a.max_len = m_cap * kBlock;
   a.batch = batch;
@@ -710,8 +689,9 @@ hipError_t launch_decode_attn(const Method& m, bool use_mfma,
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(batch * m.n_q_heads),
-                     dim3(kCombThreads), 0, stream, a, out);
+  hipLaunchKernelGGL(attn_combine_kernel,
+                     dim3((unsigned)(batch * m.n_q_heads * kCombSlices)), dim3(64), 0,
+                     stream, a, out);
   return hipGetLastError();
 }
 

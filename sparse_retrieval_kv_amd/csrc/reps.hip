@@ -114,32 +114,34 @@ __global__ __launch_bounds__(64) void append_kv_kernel(
 }
 
 
-// Streaming-read probe (a measurement helper, not part of the method): each
-// workgroup reads one contiguous segment, 4 KiB per load instruction across
-// its 256 threads, sixteen loads in flight per thread, and folds the data
-// into one XOR per wave so the loads cannot be elided.
-__global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ src,
-                                                         int64_t n16, int64_t per_wg,
-                                                         uint32_t* __restrict__ sink) {
-  const int64_t begin = (int64_t)blockIdx.x * per_wg;
-  int64_t end = begin + per_wg;
-  end = end < n16 ? end : n16;
+// Streaming-read probe (a measurement helper, not part of the method): one
+// wave per 16 KiB chunk, chunks dealt round robin over the grid, sixteen
+// 16-byte loads in flight per lane (the access shape of the attention
+// kernel's tiles); the data is folded into one XOR per wave so the loads
+// cannot be elided.
+__global__ __launch_bounds__(64) void read_probe_kernel(const uint4* __restrict__ src,
+                                                        int64_t n16,
+                                                        uint32_t* __restrict__ sink) {
+  const int lane = threadIdx.x;
+  const int64_t n_chunks = n16 / 1024;
   uint32_t x = 0;
-  int64_t i = begin + threadIdx.x;
-  for (; i + 15 * 256 < end; i += 16 * 256) {
+  for (int64_t c = blockIdx.x; c < n_chunks; c += gridDim.x) {
+    const uint4* p = src + c * 1024;
     uint4 v[16];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) v[u] = src[i + u * 256];
+    for (int u = 0; u < 16; ++u) v[u] = p[u * 64 + lane];
 #pragma unroll
     for (int u = 0; u < 16; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  for (; i < end; i += 256) {
-    const uint4 v = src[i];
-    x ^= v.x ^ v.y ^ v.z ^ v.w;
+  if (blockIdx.x == 0) {
+    for (int64_t i = n_chunks * 1024 + lane; i < n16; i += 64) {
+      const uint4 v = src[i];
+      x ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x ^= __shfl_xor(x, o);
-  if ((threadIdx.x & 63) == 0) atomicXor(sink, x);
+  if (lane == 0) atomicXor(sink, x);
 }
 
 }  // namespace
@@ -174,13 +176,10 @@ hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
                              int n_cu, hipStream_t stream) {
   const int64_t n16 = bytes / 16;
   if (n16 == 0) return hipSuccess;
-  // 64 KiB-aligned segments, several per compute unit
-  int64_t wgs = (int64_t)n_cu * 16;
-  int64_t per_wg = (n16 + wgs - 1) / wgs;
-  per_wg = (per_wg + 4095) / 4096 * 4096;
-  wgs = (n16 + per_wg - 1) / per_wg;
-  hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)wgs), dim3(256), 0, stream,
-                     static_cast<const uint4*>(buf), n16, per_wg, sink);
+  // four waves per compute unit (one per SIMD), as the attention split
+  const int64_t waves = (int64_t)(n_cu > 0 ? n_cu : 256) * 4;
+  hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)waves), dim3(64), 0, stream,
+                     static_cast<const uint4*>(buf), n16, sink);
   return hipGetLastError();
 }
 

@@ -345,8 +345,8 @@ size_t rkv_attn_workspace_size(const rkv_params* params, int32_t batch,
       batch < 0 || m_cap < 1 || params->split_waves < 0)
     return 0;
   const rkv::AttnPlan p = rkv::plan_attention(
-      batch, params->n_q_heads, params->n_kv_heads, params->split_waves);
-  return p.partial_bytes + p.ml_bytes;
+      batch, params->n_q_heads, params->n_kv_heads, params->split_waves, m_cap);
+  return p.total_bytes;
 }
 
 rkv_status rkv_decode_attn(const rkv_params* params, const uint16_t* q,
@@ -376,8 +376,8 @@ rkv_status rkv_decode_attn(const rkv_params* params, const uint16_t* q,
   RKV_REQUIRE((int64_t)batch * m.n_kv_heads * m_cap < ((int64_t)1 << 30),
               RKV_ERR_UNSUPPORTED, "batch * n_kv_heads * m_cap too large");
   const rkv::AttnPlan plan = rkv::plan_attention(
-      batch, m.n_q_heads, m.n_kv_heads, params->split_waves);
-  const size_t need = plan.partial_bytes + plan.ml_bytes;
+      batch, m.n_q_heads, m.n_kv_heads, params->split_waves, m_cap);
+  const size_t need = plan.total_bytes;
   RKV_REQUIRE(workspace_bytes >= need && (need == 0 || workspace != nullptr),
               RKV_ERR_WORKSPACE, "attention workspace %zu bytes, need %zu",
               workspace_bytes, need);

@@ -75,10 +75,14 @@ hipError_t launch_stage(const uint16_t* host_k, const uint16_t* host_v,
 // slots of `group` heads.
 struct AttnPlan {
   int n_waves;
-  size_t partial_bytes;  // fp32 [slots][group][kDim]
-  size_t ml_bytes;       // float2 [slots][group]
+  int piece_cap;         // partial slots per (sequence, KV head) list
+  size_t partial_bytes;  // fp32 [lists][piece_cap][group][kDim]
+  size_t ml_bytes;       // float2 [lists][piece_cap][group]
+  size_t count_bytes;    // int [lists] piece counts (padded)
+  size_t total_bytes;
 };
-AttnPlan plan_attention(int batch, int n_q_heads, int n_kv_heads, int waves);
+AttnPlan plan_attention(int batch, int n_q_heads, int n_kv_heads, int waves,
+                        int m_cap);
 
 hipError_t launch_decode_attn(const Method& m, bool use_mfma,
                               const AttnPlan& plan, float scale,

@@ -8,10 +8,10 @@
 // "Configuration Parameters".
 //
 // Two launches per selection:
-//  1. score_kernel: 256-thread workgroups, each scoring 64 representations
-//     (32 KiB) of one (sequence, KV head), so the scan of a long sequence is
-//     spread over many compute units (one compute unit alone streams only a
-//     few tens of GB/s).  The group's query heads are summed once
+//  1. score_kernel: one wave per 32 representations (16 KiB) of one
+//     (sequence, KV head), so the scan of even one sequence is spread over
+//     most compute units (one compute unit alone streams only a few tens of
+//     GB/s).  The group's query heads are summed once
 //     (sum_g q_g . r = (sum_g q_g) . r); eight lanes score one
 //     representation; scores become order-preserving uint32 keys in the
 //     workspace.  Extra workgroups append the decoded token meanwhile.
@@ -124,8 +124,9 @@ struct SelArgs {
   int m_cap;
 };
 
-constexpr int kScoreThreads = 256;
-constexpr int kScoreChunk = 64;  // representations per score workgroup
+constexpr int kScoreThreads = 64;
+constexpr int kScoreChunk = 32;  // representations per score wave
+constexpr int kScoreRounds = kScoreChunk / 8;  // 8 representations per round
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kTabRegs = RKV_MAX_BLOCKS / kTopkThreads;  // blocks per thread
@@ -150,8 +151,8 @@ __device__ __forceinline__ Pick pick_of(const Method& m, int lraw, int plen,
   return p;
 }
 
-// Workgroup item = (bh, chunk c): representations of blocks
-// [ib + 64c, ib + 64c + 64) of the offload range.  Items past the score
+// Wave item = (bh, chunk c): representations of blocks
+// [ib + 32c, ib + 32c + 32) of the offload range.  Items past the score
 // grid append the decoded token of sequence-head item - n_bh * n_chunks
 // (one wave).
 template <bool APPEND>
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(SelArgs a,
   const int max_blocks = a.max_blocks;
   const int64_t n_items = (int64_t)a.n_chunks * a.n_bh;
   if (item >= n_items) {
-    if (APPEND && tid < 64) {
+    if (APPEND) {
       const int bh = (int)(item - n_items);
       const int b = bh / m.n_kv_heads, h = bh - b * m.n_kv_heads;
       const int L = clamp_len(a.lens[b], max_blocks * kBlock);
@@ -180,18 +181,20 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(SelArgs a,
   // --- requests independent of the length ---
   const int lraw = a.lens[b];
   const int plen = a.prompt_lens ? a.prompt_lens[b] : lraw;
-  float qsum = 0.f;
-  if (tid < kDim) {
+  float qsum0 = 0.f, qsum1 = 0.f;  // dims tid and tid + 64
+  {
     const uint16_t* qh = a.q + ((int64_t)b * m.n_q_heads + h * m.group) * kDim;
-    for (int g = 0; g < m.group; ++g)
-      qsum += __uint_as_float((uint32_t)qh[g * kDim + tid] << 16);
+    for (int g = 0; g < m.group; ++g) {
+      qsum0 += __uint_as_float((uint32_t)qh[g * kDim + tid] << 16);
+      qsum1 += __uint_as_float((uint32_t)qh[g * kDim + tid + 64] << 16);
+    }
   }
-  const int o = tid & 7, slot = tid >> 3;  // lane octet o of slot 0..31
+  const int o = tid & 7, slot = tid >> 3;  // lane octet o of slot 0..7
   const int j0 = a.ib + c * kScoreChunk;
-  float4 v[2][4];
+  float4 v[kScoreRounds][4];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    int j = j0 + u * 32 + slot;
+  for (int u = 0; u < kScoreRounds; ++u) {
+    int j = j0 + u * 8 + slot;
     j = j < max_blocks ? j : max_blocks - 1;
     const float4* p = reinterpret_cast<const float4*>(
         a.reps + ((int64_t)bh * max_blocks + j) * kDim);
@@ -202,8 +205,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(SelArgs a,
   // --- this chunk's share of the offload range ---
   const Pick pk = pick_of(m, lraw, plen, max_blocks);
   const int ls = pk.R.n_init + pk.R.n_off;  // offload end
-  if (!pk.ranked || j0 >= ls) return;  // uniform over the workgroup
-  if (tid < kDim) qs[tid] = qsum;
+  if (!pk.ranked || j0 >= ls) return;  // uniform over the wave
+  qs[tid] = qsum0;
+  qs[tid + 64] = qsum1;
   __syncthreads();
   float4 qv[4];
 #pragma unroll
@@ -211,8 +215,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(SelArgs a,
     qv[i] = *reinterpret_cast<const float4*>(&qs[4 * (o + 8 * i)]);
   uint32_t* krow = a.keys + (int64_t)bh * max_blocks;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int j = j0 + u * 32 + slot;
+  for (int u = 0; u < kScoreRounds; ++u) {
+    const int j = j0 + u * 8 + slot;
     float part = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
