@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define RKV_ABI_VERSION 1
+#define RKV_ABI_VERSION 2
 #define RKV_BLOCK_SIZE 128
 #define RKV_HEAD_DIM 128
 #define RKV_PPM_ONE 1000000
@@ -260,6 +260,56 @@ rkv_status rkv_stage_blocks(const rkv_params* params, const uint16_t* host_k,
                             int32_t k_cap, int32_t batch, uint16_t* k_pages,
                             uint16_t* v_pages, int64_t n_pages,
                             int64_t stage_page0, hipStream_t stream);
+
+/*
+ * Workspace bytes rkv_stage_resident needs for these sizes.
+ */
+size_t rkv_stage_workspace_size(const rkv_params* params, int32_t batch,
+                                int32_t k_cap);
+
+/*
+ * rkv_stage_resident -- host tier with residency across decode steps
+ * (openGauss page, "Feature Description" and "Overall Solution": the
+ * offload part of the KV cache stays in host DDR and the blocks retrieved at
+ * each decode round are loaded into HBM before attention).  Consecutive
+ * rounds keep many of the same blocks, so a block already held in HBM is
+ * not loaded again: the result is that of rkv_stage_blocks followed by
+ * rkv_merge_table with the same host table, with fewer bytes over the bus.
+ * Staging slot r of (sequence b, KV head h) is the head-h slice of device
+ * page stage_page0 + b * k_cap + r.  For every (b, h):
+ *   slot_ids [batch][n_kv_heads][k_cap] device int32, IN/OUT: the logical
+ *            block each slot holds (-1: none).  Fill it with -1 before the
+ *            first call for a sequence (and whenever the host pools, the host
+ *            table or the staging pages are changed by anyone else); leave
+ *            it untouched between calls.
+ *   A kept host-resident block already held by a slot keeps that slot; the
+ *   kept host-resident blocks not held take, in ascending block order, the
+ *   slots whose blocks are no longer kept, in ascending slot order, and are
+ *   copied there (K and V tiles of head h, 32 KiB each).  A slot not reused
+ *   keeps its block, which then costs no copy if kept again later.
+ *   merged / n_merged: as rkv_merge_table (init blocks, kept blocks, local
+ *   blocks; kept host-resident blocks at their slot's page, other kept
+ *   blocks at their block-table page).
+ *   n_staged [batch][n_kv_heads] (optional, may be NULL): blocks copied.
+ * host_table, host_k, host_v, n_host_pages, sel_ids, n_sel: as
+ * rkv_stage_blocks; lens as rkv_select.  k_cap <= 8192, m_cap >= max_blocks.
+ * Two launches on `stream` (slot planner, then the copies); calls that
+ * overlap on one slot_ids / workspace race.
+ * Errors: RKV_ERR_INVALID_ARG, RKV_ERR_UNSUPPORTED, RKV_ERR_WORKSPACE,
+ * RKV_ERR_HIP.
+ */
+rkv_status rkv_stage_resident(const rkv_params* params, const uint16_t* host_k,
+                              const uint16_t* host_v, int64_t n_host_pages,
+                              const int32_t* host_table,
+                              const int32_t* block_table, int32_t max_blocks,
+                              const int32_t* lens, const int32_t* sel_ids,
+                              const int32_t* n_sel, int32_t k_cap, int32_t batch,
+                              int32_t* slot_ids, uint16_t* k_pages,
+                              uint16_t* v_pages, int64_t n_pages,
+                              int64_t stage_page0, int32_t* merged,
+                              int32_t* n_merged, int32_t m_cap, int32_t* n_staged,
+                              void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
 
 /*
  * Workspace bytes rkv_decode_attn needs for these sizes.

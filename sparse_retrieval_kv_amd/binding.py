@@ -67,6 +67,10 @@ _SIGS = {
                                        _I64, _P, _P, _I32, _P]),
     "rkv_stage_blocks": (ctypes.c_int, [_PP, _P, _P, _I64, _P, _I32, _P, _P, _I32,
                                         _I32, _P, _P, _I64, _I64, _P]),
+    "rkv_stage_workspace_size": (_SZ, [_PP, _I32, _I32]),
+    "rkv_stage_resident": (ctypes.c_int, [_PP, _P, _P, _I64, _P, _P, _I32, _P, _P,
+                                          _P, _I32, _I32, _P, _P, _P, _I64, _I64, _P,
+                                          _P, _I32, _P, _P, _SZ, _P]),
     "rkv_attn_workspace_size": (_SZ, [_PP, _I32, _I32]),
     "rkv_decode_attn": (ctypes.c_int, [_PP, _P, _P, _P, _I64, _P, _P, _I32, _P, _I32,
                                        _P, _P, _SZ, _P]),
@@ -217,6 +221,28 @@ def stage_blocks(p: Params, host_k, host_v, host_table, sel_ids, n_sel,
         _ptr(n_sel, torch.int32, "n_sel"), sel_ids.shape[-1], n_sel.shape[0],
         _ptr(k_pages, torch.int16, "k_pages"), _ptr(v_pages, torch.int16, "v_pages"),
         k_pages.shape[0], stage_page0, _stream(k_pages)))
+
+
+def stage_workspace_size(p: Params, batch: int, k_cap: int) -> int:
+    return lib().rkv_stage_workspace_size(ctypes.byref(p), batch, k_cap)
+
+
+def stage_resident(p: Params, host_k, host_v, host_table, block_table, lens,
+                   sel_ids, n_sel, slot_ids, k_pages, v_pages, stage_page0: int,
+                   merged, n_merged, workspace, n_staged=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().rkv_stage_resident(
+        ctypes.byref(p), _host_ptr(host_k, "host_k"), _host_ptr(host_v, "host_v"),
+        host_k.shape[0], _ptr(host_table, torch.int32, "host_table"),
+        _ptr(block_table, torch.int32, "block_table"), block_table.shape[1],
+        _ptr(lens, torch.int32, "lens"), _ptr(sel_ids, torch.int32, "sel_ids"),
+        _ptr(n_sel, torch.int32, "n_sel"), sel_ids.shape[-1], n_sel.shape[0],
+        _ptr(slot_ids, torch.int32, "slot_ids"),
+        _ptr(k_pages, torch.int16, "k_pages"), _ptr(v_pages, torch.int16, "v_pages"),
+        k_pages.shape[0], stage_page0, _ptr(merged, torch.int32, "merged"),
+        _ptr(n_merged, torch.int32, "n_merged"), merged.shape[-1],
+        None if n_staged is None else _ptr(n_staged, torch.int32, "n_staged"),
+        _ptr(workspace, None, "workspace"), ws_bytes, _stream(k_pages)))
 
 
 def attn_workspace_size(p: Params, batch: int, m_cap: int) -> int:

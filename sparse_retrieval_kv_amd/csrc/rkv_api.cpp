@@ -292,6 +292,30 @@ rkv_status rkv_merge_table(const rkv_params* params, const int32_t* block_table,
                     "rkv_merge_table launch");
 }
 
+namespace {
+
+// The staging kernels read the host pools directly: they must be pinned host
+// memory mapped into the device address space.
+rkv_status host_views(const uint16_t* host_k, const uint16_t* host_v,
+                      const uint16_t* dev_view[2]) {
+  const uint16_t* pools[2] = {host_k, host_v};
+  for (int i = 0; i < 2; ++i) {
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, pools[i]) != hipSuccess ||
+        attr.type != hipMemoryTypeHost || attr.devicePointer == nullptr ||
+        attr.hostPointer != static_cast<const void*>(pools[i])) {
+      (void)hipGetLastError();
+      return fail(RKV_ERR_INVALID_ARG,
+                  "%s is not pinned host memory mapped for the device",
+                  i == 0 ? "host_k" : "host_v");
+    }
+    dev_view[i] = static_cast<const uint16_t*>(attr.devicePointer);
+  }
+  return RKV_OK;
+}
+
+}  // namespace
+
 rkv_status rkv_stage_blocks(const rkv_params* params, const uint16_t* host_k,
                             const uint16_t* host_v, int64_t n_host_pages,
                             const int32_t* host_table, int32_t max_blocks,
@@ -316,27 +340,68 @@ rkv_status rkv_stage_blocks(const rkv_params* params, const uint16_t* host_k,
               "staging pages [%lld, +%lld) do not fit in the %lld-page pool",
               (long long)stage_page0, (long long)batch * k_cap,
               (long long)n_pages);
-  // the kernel reads the host pools directly: they must be pinned host
-  // memory mapped into the device address space
   const uint16_t* dev_view[2] = {nullptr, nullptr};
-  const uint16_t* pools[2] = {host_k, host_v};
-  for (int i = 0; i < 2; ++i) {
-    hipPointerAttribute_t attr;
-    if (hipPointerGetAttributes(&attr, pools[i]) != hipSuccess ||
-        attr.type != hipMemoryTypeHost || attr.devicePointer == nullptr ||
-        attr.hostPointer != static_cast<const void*>(pools[i])) {
-      (void)hipGetLastError();
-      return fail(RKV_ERR_INVALID_ARG,
-                  "%s is not pinned host memory mapped for the device",
-                  i == 0 ? "host_k" : "host_v");
-    }
-    dev_view[i] = static_cast<const uint16_t*>(attr.devicePointer);
-  }
+  RKV_TRY(host_views(host_k, host_v, dev_view));
   return hip_status(rkv::launch_stage(dev_view[0], dev_view[1], n_host_pages,
                                       host_table, max_blocks, sel_ids, n_sel,
                                       k_cap, batch, m.n_kv_heads, k_pages,
                                       v_pages, n_pages, stage_page0, stream),
                     "rkv_stage_blocks launch");
+}
+
+size_t rkv_stage_workspace_size(const rkv_params* params, int32_t batch,
+                                int32_t k_cap) {
+  if (!params || params->n_kv_heads <= 0 || batch <= 0 || k_cap <= 0) return 0;
+  return rkv::resident_workspace_bytes(batch, params->n_kv_heads, k_cap);
+}
+
+rkv_status rkv_stage_resident(const rkv_params* params, const uint16_t* host_k,
+                              const uint16_t* host_v, int64_t n_host_pages,
+                              const int32_t* host_table,
+                              const int32_t* block_table, int32_t max_blocks,
+                              const int32_t* lens, const int32_t* sel_ids,
+                              const int32_t* n_sel, int32_t k_cap, int32_t batch,
+                              int32_t* slot_ids, uint16_t* k_pages,
+                              uint16_t* v_pages, int64_t n_pages,
+                              int64_t stage_page0, int32_t* merged,
+                              int32_t* n_merged, int32_t m_cap, int32_t* n_staged,
+                              void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  rkv::Method m;
+  RKV_TRY(check_params(params, &m));
+  RKV_TRY(check_sizes(batch, max_blocks));
+  RKV_TRY(check_pool(k_pages, n_pages, "k_pages"));
+  RKV_TRY(check_pool(v_pages, n_pages, "v_pages"));
+  RKV_TRY(check_pool(host_k, n_host_pages, "host_k"));
+  RKV_TRY(check_pool(host_v, n_host_pages, "host_v"));
+  RKV_REQUIRE(host_table && block_table && lens && sel_ids && n_sel && slot_ids &&
+                  merged && n_merged,
+              RKV_ERR_INVALID_ARG, "a required pointer is NULL");
+  RKV_REQUIRE(k_cap >= 1 && k_cap <= RKV_MAX_BLOCKS, RKV_ERR_INVALID_ARG,
+              "k_cap %d outside [1, %d]", k_cap, RKV_MAX_BLOCKS);
+  RKV_REQUIRE(m_cap >= max_blocks, RKV_ERR_INVALID_ARG,
+              "m_cap %d below max_blocks %d", m_cap, max_blocks);
+  RKV_REQUIRE(stage_page0 >= 0 &&
+                  stage_page0 + (int64_t)batch * k_cap <= n_pages &&
+                  stage_page0 + (int64_t)batch * k_cap <= (int64_t)INT32_MAX,
+              RKV_ERR_INVALID_ARG,
+              "staging pages [%lld, +%lld) do not fit in the %lld-page pool",
+              (long long)stage_page0, (long long)batch * k_cap,
+              (long long)n_pages);
+  const size_t need = rkv_stage_workspace_size(params, batch, k_cap);
+  RKV_REQUIRE(workspace_bytes >= need && (need == 0 || workspace),
+              RKV_ERR_WORKSPACE, "staging workspace %zu bytes, need %zu",
+              workspace_bytes, need);
+  RKV_REQUIRE(aligned16(workspace), RKV_ERR_INVALID_ARG,
+              "workspace is not 16-byte aligned");
+  const uint16_t* dev_view[2] = {nullptr, nullptr};
+  RKV_TRY(host_views(host_k, host_v, dev_view));
+  return hip_status(rkv::launch_stage_resident(
+                        m, dev_view[0], dev_view[1], n_host_pages, host_table,
+                        block_table, lens, max_blocks, sel_ids, n_sel, k_cap,
+                        batch, slot_ids, k_pages, v_pages, n_pages, stage_page0,
+                        merged, n_merged, m_cap, n_staged, workspace, stream),
+                    "rkv_stage_resident launch");
 }
 
 size_t rkv_attn_workspace_size(const rkv_params* params, int32_t batch,

@@ -69,6 +69,21 @@ hipError_t launch_stage(const uint16_t* host_k, const uint16_t* host_v,
                         uint16_t* k_pages, uint16_t* v_pages, int64_t n_pages,
                         int64_t stage_page0, hipStream_t stream);
 
+// Host tier with residency across steps (slot planner + copy of the blocks
+// new to the kept set).  Workspace: copy list + per-list counts.
+size_t resident_workspace_bytes(int batch, int n_kv, int k_cap);
+hipError_t launch_stage_resident(const Method& m, const uint16_t* host_k,
+                                 const uint16_t* host_v, int64_t n_host_pages,
+                                 const int32_t* host_table, const int32_t* table,
+                                 const int32_t* lens, int max_blocks,
+                                 const int32_t* sel_ids, const int32_t* n_sel,
+                                 int k_cap, int batch, int32_t* slot_ids,
+                                 uint16_t* k_pages, uint16_t* v_pages,
+                                 int64_t n_pages, int64_t stage_page0,
+                                 int32_t* merged, int32_t* n_merged, int m_cap,
+                                 int32_t* n_staged, void* workspace,
+                                 hipStream_t stream);
+
 // Split-K decode attention over a fixed number of waves: the 64-token units
 // of all merged lists are spread evenly over `n_waves` waves; the workspace
 // holds one partial per (wave, list) piece, n_waves + batch * n_kv_heads

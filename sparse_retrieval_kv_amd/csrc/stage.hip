@@ -14,6 +14,7 @@
 // host memory directly (16-byte loads, all issued before the first store,
 // 16 per thread), so a whole step's staging is one launch with no host
 // round trip for the selected ids.
+#include "rkv.h"
 #include "rkv_device.h"
 #include "rkv_internal.h"
 
@@ -22,6 +23,37 @@ namespace {
 
 constexpr int kStageThreads = 256;
 constexpr int kTile16 = kBlock * kDim * 2 / 16;  // 16-byte pieces per tile
+
+// K and V tiles (32 KiB each) from src to dst (16-byte piece offsets), every
+// load issued before the first store.
+__device__ __forceinline__ void copy_tiles(const uint4* __restrict__ host_k,
+                                           const uint4* __restrict__ host_v,
+                                           int64_t src, uint4* __restrict__ k_pages,
+                                           uint4* __restrict__ v_pages, int64_t dst) {
+  constexpr int kPer = kTile16 / kStageThreads;  // 8 pieces per thread per tile
+  uint4 kv[kPer], vv[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    kv[u] = host_k[src + u * kStageThreads + threadIdx.x];
+    vv[u] = host_v[src + u * kStageThreads + threadIdx.x];
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    k_pages[dst + u * kStageThreads + threadIdx.x] = kv[u];
+    v_pages[dst + u * kStageThreads + threadIdx.x] = vv[u];
+  }
+}
+
+// Merged-list entries of the init and local blocks (from the block table).
+__device__ __forceinline__ int write_fixed_entries_stage(const Regions& R, int k,
+                                                         const int32_t* trow,
+                                                         int32_t* mrow) {
+  const int lstart = R.local_start > R.n_init ? R.local_start : R.n_init;
+  for (int i = threadIdx.x; i < R.n_init; i += blockDim.x) mrow[i] = trow[i];
+  for (int i = lstart + threadIdx.x; i < R.nb; i += blockDim.x)
+    mrow[R.n_init + k + (i - lstart)] = trow[i];
+  return R.n_init + k + (R.nb - lstart);
+}
 
 __global__ __launch_bounds__(kStageThreads) void stage_kernel(
     const uint4* __restrict__ host_k, const uint4* __restrict__ host_v,
@@ -43,20 +75,193 @@ __global__ __launch_bounds__(kStageThreads) void stage_kernel(
   if ((uint64_t)(int64_t)hp >= (uint64_t)n_host_pages) return;
   const int64_t dst_page = stage_page0 + (int64_t)b * k_cap + r;
   if (dst_page < 0 || dst_page >= n_pages) return;
-  const int64_t src = ((int64_t)hp * n_kv + h) * kTile16;
-  const int64_t dst = (dst_page * n_kv + h) * kTile16;
-  constexpr int kPer = kTile16 / kStageThreads;  // 8 pieces per thread per tile
-  uint4 kv[kPer], vv[kPer];
+  copy_tiles(host_k, host_v, ((int64_t)hp * n_kv + h) * kTile16, k_pages, v_pages,
+             (dst_page * n_kv + h) * kTile16);
+}
+
+
+// ---------------------------------------------------------------------------
+// Residency across steps.  Staging slot r of (sequence b, KV head h) is the
+// head-h slice of page stage_page0 + b * k_cap + r; slot_ids[b][h][r] names
+// the logical block whose K/V the slot holds (-1: none).  A kept block that
+// already sits in a slot is not copied again; the blocks new to the kept set
+// take, in ascending order, the slots whose blocks were dropped, in
+// ascending slot order.  Results are those of staging every kept block: the
+// merged table points each kept host-resident block at its slot.
+// ---------------------------------------------------------------------------
+constexpr int kPlanThreads = 256;
+constexpr int kPlanWaves = kPlanThreads / 64;
+
+struct ResArgs {
+  int n_kv, init_tokens, local_tokens;
+  const int32_t* host_table;
+  const int32_t* table;
+  const int32_t* lens;
+  int max_blocks;
+  const int32_t* sel_ids;
+  const int32_t* n_sel;
+  int k_cap;
+  int32_t* slot_ids;
+  int2* copies;       // [bh][k_cap]: (block, slot) to copy
+  int32_t* n_copies;  // [bh]
+  int32_t* n_staged;  // optional copy of n_copies
+  int64_t stage_page0;
+  int32_t* merged;
+  int32_t* n_merged;
+  int m_cap;
+};
+
+// Position of this thread's flag among the set flags of the workgroup (in
+// thread order) and the total; `sh` holds kPlanWaves words.
+__device__ __forceinline__ int plan_scan(bool flag, int* sh, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t m = __ballot(flag);
+  const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+  if (lane == 0) sh[wave] = __popcll(m);
+  __syncthreads();
+  int before = 0, all = 0;
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    kv[u] = host_k[src + u * kStageThreads + threadIdx.x];
-    vv[u] = host_v[src + u * kStageThreads + threadIdx.x];
+  for (int w = 0; w < kPlanWaves; ++w) {
+    const int c = sh[w];
+    before += w < wave ? c : 0;
+    all += c;
   }
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    k_pages[dst + u * kStageThreads + threadIdx.x] = kv[u];
-    v_pages[dst + u * kStageThreads + threadIdx.x] = vv[u];
+  __syncthreads();
+  *total = all;
+  return before + below;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void stage_plan_kernel(ResArgs a) {
+  __shared__ uint32_t selbits[RKV_MAX_BLOCKS / 32];
+  __shared__ uint32_t heldbits[RKV_MAX_BLOCKS / 32];
+  __shared__ uint16_t rank_of[RKV_MAX_BLOCKS];
+  __shared__ uint16_t free_slots[RKV_MAX_BLOCKS];
+  __shared__ uint16_t new_ranks[RKV_MAX_BLOCKS];
+  __shared__ int sh[kPlanWaves];
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x;
+  const int b = bh / a.n_kv;
+  const int max_blocks = a.max_blocks;
+  const int k_cap = a.k_cap;
+  const int L = clamp_len(a.lens[b], max_blocks * kBlock);
+  const Regions R = regions_of(L, a.init_tokens, a.local_tokens);
+  int k = a.n_sel[bh];
+  k = k < 0 ? 0 : k;
+  k = k < R.n_off ? k : R.n_off;
+  k = k < k_cap ? k : k_cap;
+  const int32_t* trow = a.table + (int64_t)b * max_blocks;
+  const int32_t* hrow = a.host_table + (int64_t)b * max_blocks;
+  const int32_t* srow = a.sel_ids + (int64_t)bh * k_cap;
+  int32_t* slots = a.slot_ids + (int64_t)bh * k_cap;
+  int32_t* mrow = a.merged + (int64_t)bh * a.m_cap;
+  const int64_t page0 = a.stage_page0 + (int64_t)b * k_cap;
+  auto in_off = [&](int j) { return j >= R.n_init && j < R.n_init + R.n_off; };
+  auto bit = [](const uint32_t* bits, int j) { return (bits[j >> 5] >> (j & 31)) & 1u; };
+
+  for (int i = tid; i < RKV_MAX_BLOCKS / 32; i += kPlanThreads) {
+    selbits[i] = 0u;
+    heldbits[i] = 0u;
   }
+  __syncthreads();
+  // the kept set and each kept block's rank
+  for (int q = tid; q < k; q += kPlanThreads) {
+    const int j = srow[q];
+    if (in_off(j)) {
+      atomicOr(&selbits[j >> 5], 1u << (j & 31));
+      rank_of[j] = (uint16_t)q;
+    }
+  }
+  __syncthreads();
+  // slots whose block stays kept keep it (one slot per block); the others
+  // are free, in ascending slot order
+  int n_free = 0;
+  for (int base = 0; base < k_cap; base += kPlanThreads) {
+    const int r = base + tid;
+    bool is_free = false;
+    if (r < k_cap) {
+      const int j = slots[r];
+      bool keep = j >= 0 && j < max_blocks && in_off(j) && bit(selbits, j) &&
+                  hrow[j] >= 0;
+      if (keep) keep = (atomicOr(&heldbits[j >> 5], 1u << (j & 31)) &
+                        (1u << (j & 31))) == 0u;
+      if (keep) {
+        mrow[R.n_init + rank_of[j]] = (int32_t)(page0 + r);
+      } else {
+        is_free = true;
+      }
+    }
+    int tot;
+    const int pos = plan_scan(is_free, sh, &tot);
+    if (is_free) free_slots[n_free + pos] = (uint16_t)r;
+    n_free += tot;
+  }
+  // kept blocks: in HBM already (table page), held in a slot (done above),
+  // or new (ascending rank)
+  int n_new = 0;
+  for (int base = 0; base < k; base += kPlanThreads) {
+    const int q = base + tid;
+    bool is_new = false;
+    if (q < k) {
+      const int j = srow[q];
+      if (!in_off(j)) {
+        mrow[R.n_init + q] = -1;
+      } else if (hrow[j] < 0) {
+        mrow[R.n_init + q] = trow[j];
+      } else {
+        is_new = !bit(heldbits, j);
+      }
+    }
+    int tot;
+    const int pos = plan_scan(is_new, sh, &tot);
+    if (is_new) new_ranks[n_new + pos] = (uint16_t)q;
+    n_new += tot;
+  }
+  // (LDS lists are visible: plan_scan ends with a barrier)
+  const int n_cp = n_new < n_free ? n_new : n_free;
+  int2* crow = a.copies + (int64_t)bh * k_cap;
+  for (int i = tid; i < n_cp; i += kPlanThreads) {
+    const int q = new_ranks[i], r = free_slots[i];
+    const int j = srow[q];
+    slots[r] = j;
+    crow[i] = make_int2(j, r);
+    mrow[R.n_init + q] = (int32_t)(page0 + r);
+  }
+  // (cannot happen with k <= k_cap; kept blocks without a slot are skipped)
+  for (int i = n_cp + tid; i < n_new; i += kPlanThreads)
+    mrow[R.n_init + new_ranks[i]] = -1;
+  // a free slot that is not reused keeps its block's data and its id, so
+  // the block costs no copy if it is kept again later
+  const int cnt = write_fixed_entries_stage(R, k, trow, mrow);
+  if (tid == 0) {
+    a.n_merged[bh] = cnt;
+    a.n_copies[bh] = n_cp;
+    if (a.n_staged) a.n_staged[bh] = n_cp;
+  }
+}
+
+// Copy item (bh, i < n_copies[bh]): the K and V tiles of head h of block j
+// from the host pools to slot r.
+__global__ __launch_bounds__(kStageThreads) void stage_copy_kernel(
+    const uint4* __restrict__ host_k, const uint4* __restrict__ host_v,
+    int64_t n_host_pages, const int32_t* __restrict__ host_table,
+    int max_blocks, const int2* __restrict__ copies,
+    const int32_t* __restrict__ n_copies, int k_cap, int n_kv,
+    uint4* __restrict__ k_pages, uint4* __restrict__ v_pages, int64_t n_pages,
+    int64_t stage_page0) {
+  const int64_t item = blockIdx.x;  // (bh, i), i fastest
+  const int i = (int)(item % k_cap);
+  const int bh = (int)(item / k_cap);
+  const int b = bh / n_kv, h = bh - b * n_kv;
+  if (i >= n_copies[bh]) return;
+  const int2 c = copies[(int64_t)bh * k_cap + i];
+  if (c.x < 0 || c.x >= max_blocks || c.y < 0 || c.y >= k_cap) return;
+  const int hp = host_table[(int64_t)b * max_blocks + c.x];
+  if ((uint64_t)(int64_t)hp >= (uint64_t)n_host_pages) return;
+  const int64_t dst_page = stage_page0 + (int64_t)b * k_cap + c.y;
+  if (dst_page < 0 || dst_page >= n_pages) return;
+  copy_tiles(host_k, host_v, ((int64_t)hp * n_kv + h) * kTile16, k_pages, v_pages,
+             (dst_page * n_kv + h) * kTile16);
 }
 
 }  // namespace
@@ -75,6 +280,57 @@ hipError_t launch_stage(const uint16_t* host_k, const uint16_t* host_v,
                      host_table, max_blocks, sel_ids, n_sel, k_cap, n_kv,
                      reinterpret_cast<uint4*>(k_pages),
                      reinterpret_cast<uint4*>(v_pages), n_pages, stage_page0);
+  return hipGetLastError();
+}
+
+size_t resident_workspace_bytes(int batch, int n_kv, int k_cap) {
+  const size_t lists = (size_t)batch * n_kv;
+  return lists * k_cap * sizeof(int2) + (lists * sizeof(int32_t) + 255) / 256 * 256;
+}
+
+hipError_t launch_stage_resident(const Method& m, const uint16_t* host_k,
+                                 const uint16_t* host_v, int64_t n_host_pages,
+                                 const int32_t* host_table, const int32_t* table,
+                                 const int32_t* lens, int max_blocks,
+                                 const int32_t* sel_ids, const int32_t* n_sel,
+                                 int k_cap, int batch, int32_t* slot_ids,
+                                 uint16_t* k_pages, uint16_t* v_pages,
+                                 int64_t n_pages, int64_t stage_page0,
+                                 int32_t* merged, int32_t* n_merged, int m_cap,
+                                 int32_t* n_staged, void* workspace,
+                                 hipStream_t stream) {
+  const int lists = batch * m.n_kv_heads;
+  if (lists == 0) return hipSuccess;
+  ResArgs a;
+  a.n_kv = m.n_kv_heads;
+  a.init_tokens = m.init_tokens;
+  a.local_tokens = m.local_tokens;
+  a.host_table = host_table;
+  a.table = table;
+  a.lens = lens;
+  a.max_blocks = max_blocks;
+  a.sel_ids = sel_ids;
+  a.n_sel = n_sel;
+  a.k_cap = k_cap;
+  a.slot_ids = slot_ids;
+  a.copies = static_cast<int2*>(workspace);
+  a.n_copies = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                          (size_t)lists * k_cap * sizeof(int2));
+  a.n_staged = n_staged;
+  a.stage_page0 = stage_page0;
+  a.merged = merged;
+  a.n_merged = n_merged;
+  a.m_cap = m_cap;
+  hipLaunchKernelGGL(stage_plan_kernel, dim3(lists), dim3(kPlanThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t items = (int64_t)lists * k_cap;
+  hipLaunchKernelGGL(stage_copy_kernel, dim3((unsigned)items), dim3(kStageThreads), 0,
+                     stream, reinterpret_cast<const uint4*>(host_k),
+                     reinterpret_cast<const uint4*>(host_v), n_host_pages, host_table,
+                     max_blocks, a.copies, a.n_copies, k_cap, m.n_kv_heads,
+                     reinterpret_cast<uint4*>(k_pages), reinterpret_cast<uint4*>(v_pages),
+                     n_pages, stage_page0);
   return hipGetLastError();
 }
 

@@ -84,23 +84,40 @@ class HostTierSession(DecodeSession):
     """Decode step with the offload region in pinned host memory: the kept
     offload blocks are staged into HBM staging pages (the last
     batch * k_cap pages of the device pools) before attention, on a side
-    stream that the main stream waits for.
+    stream that the main stream waits for.  With `resident` (the default) a
+    kept block already held by a staging slot from an earlier step is not
+    copied again (rkv_stage_resident); otherwise every kept block is copied
+    each step (rkv_stage_blocks + rkv_merge_table).
 
     Representations are built while every block is still in HBM (after
     prefill); `attach_host` then hands over the host pools that hold the
     offload blocks from then on."""
 
     def __init__(self, prm: B.Params, k_pages, v_pages, block_table,
-                 prompt_lens=None, side_stream=True):
+                 prompt_lens=None, side_stream=True, resident=True):
         super().__init__(prm, k_pages, v_pages, block_table, prompt_lens)
         self.host_k = self.host_v = self.host_table = None
         self.stage_page0 = k_pages.shape[0] - self.batch * self.k_cap
         if self.stage_page0 < 0:
             raise ValueError("the device pools have no room for staging pages")
         self.side = torch.cuda.Stream(device=k_pages.device) if side_stream else None
+        # residency across steps: the block each staging slot holds
+        self.resident = resident
+        dev = k_pages.device
+        n_kv = prm.n_kv_heads
+        self.slot_ids = torch.full((self.batch, n_kv, self.k_cap), -1,
+                                   dtype=torch.int32, device=dev)
+        self.n_staged = torch.zeros((self.batch, n_kv), dtype=torch.int32, device=dev)
+        ws = B.stage_workspace_size(prm, self.batch, self.k_cap)
+        self.ws_stage = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
 
     def attach_host(self, host_k, host_v, host_table):
         self.host_k, self.host_v, self.host_table = host_k, host_v, host_table
+        self.reset_residency()
+
+    def reset_residency(self):
+        """Forget what the staging slots hold (new sequences or host pools)."""
+        self.slot_ids.fill_(-1)
 
     def select(self, q, lens):
         # the selection only: the merged table is built after staging
@@ -108,6 +125,13 @@ class HostTierSession(DecodeSession):
                  self.n_sel, None, None, self.prompt_lens, self.ws_select)
 
     def stage(self, lens):
+        if self.resident:
+            B.stage_resident(self.p, self.host_k, self.host_v, self.host_table,
+                             self.block_table, lens, self.sel_ids, self.n_sel,
+                             self.slot_ids, self.k_pages, self.v_pages,
+                             self.stage_page0, self.merged, self.n_merged,
+                             self.ws_stage, self.n_staged)
+            return
         B.stage_blocks(self.p, self.host_k, self.host_v, self.host_table,
                        self.sel_ids, self.n_sel, self.k_pages, self.v_pages,
                        self.stage_page0)

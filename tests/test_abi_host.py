@@ -22,7 +22,7 @@ def test_every_declared_function_is_exported(L):
     assert len(names) >= 11
     for n in names:
         assert hasattr(L, n), n
-    assert L.rkv_abi_version() == 1
+    assert L.rkv_abi_version() == 2
 
 
 def test_defaults_follow_the_page(L):
@@ -130,6 +130,33 @@ def test_stage_validation(L):
     assert stage(k_cap=0) == B.RKV_ERR_INVALID_ARG
     assert stage(host_k=None) == B.RKV_ERR_INVALID_ARG
     assert stage(host_k=ODD) == B.RKV_ERR_INVALID_ARG
+
+
+def test_stage_resident_validation(L):
+    p = L.rkv_params_default(32, 8)
+    need = L.rkv_stage_workspace_size(ctypes.byref(p), 4, 100)
+    assert need >= 4 * 8 * 100 * 8 + 4 * 8 * 4
+
+    def res(stage_page0=0, n_pages=1000, k_cap=100, batch=4, host_k=FAKE,
+            slot_ids=FAKE, m_cap=200, ws_bytes=None, merged=FAKE):
+        ws = need if ws_bytes is None else ws_bytes
+        return L.rkv_stage_resident(ctypes.byref(p), host_k, FAKE, 50, FAKE, FAKE,
+                                    200, FAKE, FAKE, FAKE, k_cap, batch, slot_ids,
+                                    FAKE, FAKE, n_pages, stage_page0, merged, FAKE,
+                                    m_cap, None, FAKE, ws, None)
+
+    assert res(stage_page0=601) == B.RKV_ERR_INVALID_ARG   # 601 + 400 > 1000
+    assert b"staging" in L.rkv_last_error()
+    assert res(k_cap=0) == B.RKV_ERR_INVALID_ARG
+    assert res(k_cap=8193, n_pages=10**6) == B.RKV_ERR_INVALID_ARG
+    assert res(slot_ids=None) == B.RKV_ERR_INVALID_ARG
+    assert res(merged=None) == B.RKV_ERR_INVALID_ARG
+    assert res(m_cap=199) == B.RKV_ERR_INVALID_ARG
+    assert res(host_k=ODD) == B.RKV_ERR_INVALID_ARG
+    assert res(ws_bytes=need - 1) == B.RKV_ERR_WORKSPACE
+    # fake host pools are not pinned, mapped host memory
+    assert res() == B.RKV_ERR_INVALID_ARG
+    assert b"pinned" in L.rkv_last_error()
 
 
 def test_reps_and_append_validation(L):

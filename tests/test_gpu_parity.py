@@ -91,14 +91,19 @@ def gpu_selection(sess, b, h):
 
 def gpu_merged_logical(sess, batch, b, h, staged=False):
     """The GPU's merged list of (b, h) as logical blocks (and page ids).
-    Staging page stage_page0 + b*k_cap + r stands for the r-th kept block."""
+    Staging page stage_page0 + b*k_cap + r stands for the block slot r holds:
+    the r-th kept block without residency, slot_ids[b][h][r] with it."""
     n = int(sess.n_merged[b, h])
     pages = sess.merged[b, h, :n].cpu().numpy()
     inv = {int(p): j for j, p in enumerate(batch.table_np[b]) if p >= 0}
     if staged:
-        sel = gpu_selection(sess, b, h)
-        for r, j in enumerate(sel):
-            inv[int(sess.stage_page0 + b * sess.k_cap + r)] = int(j)
+        if getattr(sess, "resident", False):
+            held = sess.slot_ids[b, h].cpu().numpy()
+        else:
+            held = gpu_selection(sess, b, h)
+        for r, j in enumerate(held):
+            if j >= 0:
+                inv[int(sess.stage_page0 + b * sess.k_cap + r)] = int(j)
     return np.array([inv[int(p)] for p in pages], dtype=np.int64), pages
 
 
@@ -471,7 +476,7 @@ def test_valu_variant_matches_oracle_and_mfma(hq, hkv):
     assert np.allclose(outs[B.ATTN_MFMA], outs[B.ATTN_VALU], rtol=1e-4, atol=1e-5)
 
 
-def make_host_session(spec, **pkw):
+def make_host_session(spec, resident=True, **pkw):
     """Host-tier session: prefill representations are built with every block
     in HBM, then the offload blocks move to pinned host memory."""
     max_blocks = -(-(max(spec.context) + spec.steps - 1) // 128)
@@ -481,7 +486,7 @@ def make_host_session(spec, **pkw):
     kw.update(pkw)
     prm = B.params(spec.n_q_heads, spec.n_kv_heads, **kw)
     sess = HostTierSession(prm, batch.k_pages, batch.v_pages, batch.block_table,
-                           i32(batch.context))
+                           i32(batch.context), resident=resident)
     assert sess.stage_page0 >= batch.n_pages  # staging pages are the extra ones
     prefill(batch, sess)
     torch.cuda.synchronize()
@@ -490,14 +495,15 @@ def make_host_session(spec, **pkw):
     return batch, host, sess
 
 
-def test_host_tier_small():
+@pytest.mark.parametrize("resident", [True, False])
+def test_host_tier_small(resident):
     # host blocks [8, 90) of the offload range [8, 100): blocks 90..99 stay in
     # HBM and are read in place when kept
     spec = synth.scaled(synth.CONFIGS[5], batch=2, context=(20000, 20000), steps=3,
                         plant_range=(8, 90), plant_count=5, local_tokens=7192,
                         dense_boundary=0, config_id=102)
-    say("host tier small")
-    batch, host, sess = make_host_session(spec)
+    say(f"host tier small (resident={resident})")
+    batch, host, sess = make_host_session(spec, resident=resident)
     for t in range(3):
         step(batch, sess, t)
         torch.cuda.synchronize()
@@ -505,6 +511,67 @@ def test_host_tier_small():
             for h in range(8):
                 assert set(batch.planted[b]) <= set(gpu_selection(sess, b, h).tolist())
         oracle_full_check(batch, sess, t, host=host)
+
+
+def mirror_residency(slots, kept, on_host):
+    """The slot policy of rkv_stage_resident, restated: slots holding a kept
+    host block keep it; the other kept host blocks, ascending, take the
+    remaining slots, ascending.  Returns the blocks copied."""
+    held = {}
+    for r, j in enumerate(slots):
+        if j >= 0 and j in kept and on_host[j] and j not in held:
+            held[j] = r
+    free = [r for r in range(len(slots)) if r not in held.values()]
+    new = [j for j in kept if on_host[j] and j not in held]
+    for j, r in zip(new, free):
+        slots[r] = j
+    return new[:len(free)]
+
+
+def test_host_tier_residency_matches_full_staging():
+    """Residency changes which bytes move, not the results: every step's
+    output and selection equal those of staging every kept block, and the
+    slot state, copy counts and merged page ids follow the stated policy."""
+    spec = synth.scaled(synth.CONFIGS[5], batch=2, context=(20000, 23000), steps=6,
+                        plant_range=(8, 90), plant_count=5, local_tokens=7192,
+                        dense_boundary=0, config_id=104)
+    say("host tier residency vs full staging")
+    batch_r, host_r, sess_r = make_host_session(spec, resident=True)
+    batch_f, _, sess_f = make_host_session(spec, resident=False)
+    k_cap = sess_r.k_cap
+    slots = {(b, h): [-1] * k_cap for b in range(2) for h in range(8)}
+    kept_total = copied_total = 0
+    for t in range(6):
+        step(batch_r, sess_r, t)
+        step(batch_f, sess_f, t)
+        torch.cuda.synchronize()
+        assert torch.equal(sess_r.out, sess_f.out), t
+        assert torch.equal(sess_r.n_sel, sess_f.n_sel), t
+        sel = sess_r.sel_ids.cpu().numpy()
+        n_sel = sess_r.n_sel.cpu().numpy()
+        slot_gpu = sess_r.slot_ids.cpu().numpy()
+        staged = sess_r.n_staged.cpu().numpy()
+        merged = sess_r.merged.cpu().numpy()
+        lens = batch_r.lens_at(t)
+        for b in range(2):
+            on_host = host_r.host_table_np[b] >= 0
+            n_init = min(8, -(-int(lens[b]) // 128))
+            for h in range(8):
+                kept = [int(j) for j in sel[b, h, :n_sel[b, h]]]
+                assert np.array_equal(kept, sess_f.sel_ids.cpu().numpy()[b, h, :n_sel[b, h]])
+                new = mirror_residency(slots[(b, h)], set(kept), on_host)
+                assert slot_gpu[b, h].tolist() == slots[(b, h)], (t, b, h)
+                assert staged[b, h] == len(new), (t, b, h)
+                for q, j in enumerate(kept):
+                    if on_host[j]:
+                        r = slots[(b, h)].index(j)
+                        assert merged[b, h, n_init + q] == sess_r.stage_page0 + b * k_cap + r
+                    else:
+                        assert merged[b, h, n_init + q] == batch_r.table_np[b, j]
+                if t > 0:
+                    kept_total += sum(1 for j in kept if on_host[j])
+                    copied_total += len(new)
+    assert copied_total < kept_total
 
 
 def test_host_tier_full_size_sampled():
