@@ -150,6 +150,42 @@ def cpu_baseline(batch, host=None, budget_s=12.0, max_steps=100000):
     }
 
 
+def measure_prefill(sess, host, lens, spec):
+    """Prefill hand-over to the host tier on one layer: the representation
+    build alone, the offload copies alone, then both overlapped on two
+    streams (HostTierSession.offload_prefill); each timed between HIP events
+    on the main stream.  Leaves the pools filled and the reps built."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        ev[0].record()
+        fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) * 1e-3
+
+    t_reps = timed(lambda: sess.build_reps(lens))
+    t_off = timed(lambda: B.offload_blocks(sess.p, sess.k_pages, sess.v_pages,
+                                           sess.block_table, lens, host.host_table,
+                                           host.host_k, host.host_v))
+    t_both = timed(lambda: sess.offload_prefill(host.host_k, host.host_v,
+                                                host.host_table, lens))
+    lens_np = lens.cpu().numpy()
+    complete = int(sum(int(L) // 128 for L in lens_np))
+    reps_bytes = complete * spec.n_kv_heads * 128 * 128 * 2
+    off_bytes = int((host.host_table_np >= 0).sum()) * spec.n_kv_heads * 128 * 128 * 2 * 2
+    out = {"reps_bytes": reps_bytes, "reps_ms": t_reps * 1e3,
+           "reps_gbs": reps_bytes / t_reps / 1e9,
+           "offload_bytes": off_bytes, "offload_ms": t_off * 1e3,
+           "offload_gbs": off_bytes / t_off / 1e9,
+           "overlapped_ms": t_both * 1e3}
+    log(f"prefill: reps {out['reps_gbs']:.0f} GB/s ({out['reps_ms']:.2f} ms), "
+        f"offload {out['offload_gbs']:.1f} GB/s ({out['offload_ms']:.1f} ms), "
+        f"both overlapped {out['overlapped_ms']:.1f} ms")
+    return out
+
+
 def stream_read_probe(dev, gib=2, reps=5):
     """Achievable streaming-read bandwidth: rkv_read_probe over a buffer
     larger than the Infinity Cache, median of `reps` timed launches."""
@@ -210,6 +246,7 @@ def main():
     spec = synth.CONFIGS[args.config]
     log("config", args.config, spec.name)
     host = None
+    prefill = None
     if spec.host_offload:
         max_blocks = -(-(max(spec.context) + spec.steps - 1) // 128)
         base = synth.make_batch(spec, dev, extra_pages=spec.batch * max_blocks)
@@ -228,13 +265,13 @@ def main():
         kp = base.k_pages if layer == 0 else base.k_pages.clone()
         vp = base.v_pages if layer == 0 else base.v_pages.clone()
         if spec.host_offload:
-            # representations are built with every block in HBM, then the
-            # offload blocks move to pinned host memory
+            # prefill hand-over: the offload blocks go to pinned host memory
+            # while the representations are built; then the device copies
+            # are poisoned so only the host copies carry the data
             s = HostTierSession(prm, kp, vp, base.block_table, ctx)
-            s.build_reps(ctx - 1)
-            torch.cuda.synchronize()
-            host = synth.move_offload_to_host(base)
-            s.attach_host(host.host_k, host.host_v, host.host_table)
+            host = synth.plan_host_pools(base)
+            prefill = measure_prefill(s, host, ctx - 1, spec)
+            synth.poison_device_copies(base, host)
             log(f"host tier: {host.host_k.numel() * 4 / 2**30:.2f} GiB of K/V "
                 "in pinned host memory")
         else:
@@ -376,6 +413,7 @@ def main():
         },
         "stream_read_probe_gbs": probe_gbs,
         "host_staging": staging,
+        "host_prefill": prefill,
         "attended_kv_gbs_step": step_gbs,
         "attended_kv_pct_peak_step": 100.0 * step_gbs / HBM_PEAK_GBS,
         "roofline": {

@@ -262,6 +262,34 @@ rkv_status rkv_stage_blocks(const rkv_params* params, const uint16_t* host_k,
                             int64_t stage_page0, hipStream_t stream);
 
 /*
+ * rkv_offload_blocks -- prefill-time move of the offload region into the
+ * host tier (openGauss page, "Feature Description" and "Configuration
+ * Parameters": beyond the offload boundary the offload part of the KV cache
+ * is kept in host DDR; "Overall Solution": representations are extracted
+ * block by block at prefill, so rkv_build_reps over the same pages can run
+ * on another stream meanwhile -- both only read the device pages).
+ * For every sequence b and every block j of its offload range
+ * [n_init, local_start) (region rule of rkv_select, from lens[b]) with
+ * host_table[b][j] >= 0: copies all KV heads of device page
+ * block_table[b][j] (K and V) to host page host_table[b][j] of the pinned
+ * pools.  Other host pages are not touched.
+ *   host_k, host_v  HOST pointers to pinned, device-mapped memory (e.g.
+ *                   hipHostMalloc), n_host_pages pages, same layouts as the
+ *                   device pools; written by the device over the bus
+ * The copies are complete when the stream's work is (synchronize before the
+ * host reads the pools or the device pages are reused).
+ * Errors: RKV_ERR_INVALID_ARG (including host pools that are not pinned and
+ * mapped), RKV_ERR_UNSUPPORTED, RKV_ERR_HIP.
+ */
+rkv_status rkv_offload_blocks(const rkv_params* params, const uint16_t* k_pages,
+                              const uint16_t* v_pages, int64_t n_pages,
+                              const int32_t* block_table, int32_t max_blocks,
+                              const int32_t* lens, int32_t batch,
+                              const int32_t* host_table, uint16_t* host_k,
+                              uint16_t* host_v, int64_t n_host_pages,
+                              hipStream_t stream);
+
+/*
  * Workspace bytes rkv_stage_resident needs for these sizes.
  */
 size_t rkv_stage_workspace_size(const rkv_params* params, int32_t batch,

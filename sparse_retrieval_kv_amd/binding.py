@@ -67,6 +67,8 @@ _SIGS = {
                                        _I64, _P, _P, _I32, _P]),
     "rkv_stage_blocks": (ctypes.c_int, [_PP, _P, _P, _I64, _P, _I32, _P, _P, _I32,
                                         _I32, _P, _P, _I64, _I64, _P]),
+    "rkv_offload_blocks": (ctypes.c_int, [_PP, _P, _P, _I64, _P, _I32, _P, _I32, _P,
+                                          _P, _P, _I64, _P]),
     "rkv_stage_workspace_size": (_SZ, [_PP, _I32, _I32]),
     "rkv_stage_resident": (ctypes.c_int, [_PP, _P, _P, _I64, _P, _P, _I32, _P, _P,
                                           _P, _I32, _I32, _P, _P, _P, _I64, _I64, _P,
@@ -221,6 +223,17 @@ def stage_blocks(p: Params, host_k, host_v, host_table, sel_ids, n_sel,
         _ptr(n_sel, torch.int32, "n_sel"), sel_ids.shape[-1], n_sel.shape[0],
         _ptr(k_pages, torch.int16, "k_pages"), _ptr(v_pages, torch.int16, "v_pages"),
         k_pages.shape[0], stage_page0, _stream(k_pages)))
+
+
+def offload_blocks(p: Params, k_pages, v_pages, block_table, lens, host_table,
+                   host_k, host_v):
+    _check(lib().rkv_offload_blocks(
+        ctypes.byref(p), _ptr(k_pages, torch.int16, "k_pages"),
+        _ptr(v_pages, torch.int16, "v_pages"), k_pages.shape[0],
+        _ptr(block_table, torch.int32, "block_table"), block_table.shape[1],
+        _ptr(lens, torch.int32, "lens"), lens.shape[0],
+        _ptr(host_table, torch.int32, "host_table"), _host_ptr(host_k, "host_k"),
+        _host_ptr(host_v, "host_v"), host_k.shape[0], _stream(k_pages)))
 
 
 def stage_workspace_size(p: Params, batch: int, k_cap: int) -> int:

@@ -349,6 +349,32 @@ rkv_status rkv_stage_blocks(const rkv_params* params, const uint16_t* host_k,
                     "rkv_stage_blocks launch");
 }
 
+rkv_status rkv_offload_blocks(const rkv_params* params, const uint16_t* k_pages,
+                              const uint16_t* v_pages, int64_t n_pages,
+                              const int32_t* block_table, int32_t max_blocks,
+                              const int32_t* lens, int32_t batch,
+                              const int32_t* host_table, uint16_t* host_k,
+                              uint16_t* host_v, int64_t n_host_pages,
+                              hipStream_t stream) {
+  rkv::Method m;
+  RKV_TRY(check_params(params, &m));
+  RKV_TRY(check_sizes(batch, max_blocks));
+  RKV_TRY(check_pool(k_pages, n_pages, "k_pages"));
+  RKV_TRY(check_pool(v_pages, n_pages, "v_pages"));
+  RKV_TRY(check_pool(host_k, n_host_pages, "host_k"));
+  RKV_TRY(check_pool(host_v, n_host_pages, "host_v"));
+  RKV_REQUIRE(block_table && lens && host_table, RKV_ERR_INVALID_ARG,
+              "block_table, lens and host_table must not be NULL");
+  const uint16_t* dev_view[2] = {nullptr, nullptr};
+  RKV_TRY(host_views(host_k, host_v, dev_view));
+  return hip_status(rkv::launch_offload(m, k_pages, v_pages, n_pages, block_table,
+                                        max_blocks, lens, batch, host_table,
+                                        const_cast<uint16_t*>(dev_view[0]),
+                                        const_cast<uint16_t*>(dev_view[1]),
+                                        n_host_pages, stream),
+                    "rkv_offload_blocks launch");
+}
+
 size_t rkv_stage_workspace_size(const rkv_params* params, int32_t batch,
                                 int32_t k_cap) {
   if (!params || params->n_kv_heads <= 0 || batch <= 0 || k_cap <= 0) return 0;

@@ -69,6 +69,14 @@ hipError_t launch_stage(const uint16_t* host_k, const uint16_t* host_v,
                         uint16_t* k_pages, uint16_t* v_pages, int64_t n_pages,
                         int64_t stage_page0, hipStream_t stream);
 
+// Prefill-time offload of the offload-region pages into pinned host pools.
+hipError_t launch_offload(const Method& m, const uint16_t* k_pages,
+                          const uint16_t* v_pages, int64_t n_pages,
+                          const int32_t* table, int max_blocks, const int32_t* lens,
+                          int batch, const int32_t* host_table, uint16_t* host_k,
+                          uint16_t* host_v, int64_t n_host_pages,
+                          hipStream_t stream);
+
 // Host tier with residency across steps (slot planner + copy of the blocks
 // new to the kept set).  Workspace: copy list + per-list counts.
 size_t resident_workspace_bytes(int batch, int n_kv, int k_cap);

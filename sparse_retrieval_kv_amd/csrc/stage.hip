@@ -26,21 +26,21 @@ constexpr int kTile16 = kBlock * kDim * 2 / 16;  // 16-byte pieces per tile
 
 // K and V tiles (32 KiB each) from src to dst (16-byte piece offsets), every
 // load issued before the first store.
-__device__ __forceinline__ void copy_tiles(const uint4* __restrict__ host_k,
-                                           const uint4* __restrict__ host_v,
-                                           int64_t src, uint4* __restrict__ k_pages,
-                                           uint4* __restrict__ v_pages, int64_t dst) {
+__device__ __forceinline__ void copy_tiles(const uint4* __restrict__ src_k,
+                                           const uint4* __restrict__ src_v,
+                                           int64_t src, uint4* __restrict__ dst_k,
+                                           uint4* __restrict__ dst_v, int64_t dst) {
   constexpr int kPer = kTile16 / kStageThreads;  // 8 pieces per thread per tile
   uint4 kv[kPer], vv[kPer];
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
-    kv[u] = host_k[src + u * kStageThreads + threadIdx.x];
-    vv[u] = host_v[src + u * kStageThreads + threadIdx.x];
+    kv[u] = src_k[src + u * kStageThreads + threadIdx.x];
+    vv[u] = src_v[src + u * kStageThreads + threadIdx.x];
   }
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
-    k_pages[dst + u * kStageThreads + threadIdx.x] = kv[u];
-    v_pages[dst + u * kStageThreads + threadIdx.x] = vv[u];
+    dst_k[dst + u * kStageThreads + threadIdx.x] = kv[u];
+    dst_v[dst + u * kStageThreads + threadIdx.x] = vv[u];
   }
 }
 
@@ -264,6 +264,32 @@ __global__ __launch_bounds__(kStageThreads) void stage_copy_kernel(
              (dst_page * n_kv + h) * kTile16);
 }
 
+// Prefill-time offload: item (b, j, h) copies head h of the device page of
+// offload block j of sequence b (blocks [n_init, local_start) for its
+// length) to host page host_table[b][j] of the pinned pools, K and V tiles,
+// every load issued before the first store.
+__global__ __launch_bounds__(kStageThreads) void offload_kernel(
+    const uint4* __restrict__ k_pages, const uint4* __restrict__ v_pages,
+    int64_t n_pages, const int32_t* __restrict__ table, int max_blocks,
+    const int32_t* __restrict__ lens, int n_kv, int init_tokens, int local_tokens,
+    const int32_t* __restrict__ host_table, uint4* __restrict__ host_k,
+    uint4* __restrict__ host_v, int64_t n_host_pages) {
+  const int64_t item = blockIdx.x;  // (b, j, h), h fastest
+  const int h = (int)(item % n_kv);
+  const int64_t rest = item / n_kv;
+  const int j = (int)(rest % max_blocks);
+  const int b = (int)(rest / max_blocks);
+  const int L = clamp_len(lens[b], max_blocks * kBlock);
+  const Regions R = regions_of(L, init_tokens, local_tokens);
+  if (j < R.n_init || j >= R.n_init + R.n_off) return;
+  const int hp = host_table[(int64_t)b * max_blocks + j];
+  if ((uint64_t)(int64_t)hp >= (uint64_t)n_host_pages) return;
+  const int page = table[(int64_t)b * max_blocks + j];
+  if ((uint64_t)(int64_t)page >= (uint64_t)n_pages) return;
+  copy_tiles(k_pages, v_pages, ((int64_t)page * n_kv + h) * kTile16, host_k, host_v,
+             ((int64_t)hp * n_kv + h) * kTile16);
+}
+
 }  // namespace
 
 hipError_t launch_stage(const uint16_t* host_k, const uint16_t* host_v,
@@ -331,6 +357,23 @@ hipError_t launch_stage_resident(const Method& m, const uint16_t* host_k,
                      max_blocks, a.copies, a.n_copies, k_cap, m.n_kv_heads,
                      reinterpret_cast<uint4*>(k_pages), reinterpret_cast<uint4*>(v_pages),
                      n_pages, stage_page0);
+  return hipGetLastError();
+}
+
+hipError_t launch_offload(const Method& m, const uint16_t* k_pages,
+                          const uint16_t* v_pages, int64_t n_pages,
+                          const int32_t* table, int max_blocks, const int32_t* lens,
+                          int batch, const int32_t* host_table, uint16_t* host_k,
+                          uint16_t* host_v, int64_t n_host_pages,
+                          hipStream_t stream) {
+  const int64_t items = (int64_t)batch * max_blocks * m.n_kv_heads;
+  if (items == 0) return hipSuccess;
+  hipLaunchKernelGGL(offload_kernel, dim3((unsigned)items), dim3(kStageThreads), 0,
+                     stream, reinterpret_cast<const uint4*>(k_pages),
+                     reinterpret_cast<const uint4*>(v_pages), n_pages, table,
+                     max_blocks, lens, m.n_kv_heads, m.init_tokens, m.local_tokens,
+                     host_table, reinterpret_cast<uint4*>(host_k),
+                     reinterpret_cast<uint4*>(host_v), n_host_pages);
   return hipGetLastError();
 }
 

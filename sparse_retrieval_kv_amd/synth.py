@@ -322,35 +322,55 @@ class HostPools:
     host_table_np: np.ndarray
 
 
-def move_offload_to_host(batch: Batch) -> HostPools:
-    """Place the offload blocks (the spec's block range at step 0) of every
-    sequence in pinned host memory: copy their pages to host pools, record
-    the host page of each block, and fill the device copies with NaN so that
-    only the host copies carry the data."""
+def plan_host_pools(batch: Batch) -> HostPools:
+    """Pinned host pools (uninitialised) and the host page of every offload
+    block of the spec's block range at step 0: sequence b's blocks
+    [lo, hi) take host pages b * (hi - lo) + 0, 1, ...; -1 elsewhere."""
     spec = batch.spec
     lo, hi = spec.plant_range
     B, Hkv = spec.batch, spec.n_kv_heads
-    pages = np.concatenate([batch.table_np[b, lo:hi] for b in range(B)])
     host_table = np.full_like(batch.table_np, -1)
     for b in range(B):
         host_table[b, lo:hi] = b * (hi - lo) + np.arange(hi - lo)
-    n_host = len(pages)
+    n_host = B * (hi - lo)
     host_k = torch.empty((n_host, Hkv, BLOCK, HEAD_DIM), dtype=torch.int16,
                          pin_memory=True)
     host_v = torch.empty_like(host_k, pin_memory=True)
+    return HostPools(host_k, host_v,
+                     torch.from_numpy(host_table).to(batch.k_pages.device),
+                     host_table)
+
+
+def poison_device_copies(batch: Batch, host: HostPools) -> None:
+    """Fill the device pages of host-resident blocks with NaN, so that only
+    the host copies carry their data."""
+    pages = batch.table_np[host.host_table_np >= 0]
     idx = torch.as_tensor(pages.astype(np.int64), device=batch.k_pages.device)
-    step = 1024
-    for s0 in range(0, n_host, step):
-        sl = idx[s0:s0 + step]
-        host_k[s0:s0 + step].copy_(batch.k_pages.index_select(0, sl))
-        host_v[s0:s0 + step].copy_(batch.v_pages.index_select(0, sl))
+    for s0 in range(0, len(pages), 1024):
+        sl = idx[s0:s0 + 1024]
         batch.k_pages[sl] = BF16_QNAN
         batch.v_pages[sl] = BF16_QNAN
     if batch.k_pages.is_cuda:
         torch.cuda.synchronize(batch.k_pages.device)
-    return HostPools(host_k, host_v,
-                     torch.from_numpy(host_table).to(batch.k_pages.device),
-                     host_table)
+
+
+def move_offload_to_host(batch: Batch) -> HostPools:
+    """Place the offload blocks (the spec's block range at step 0) of every
+    sequence in pinned host memory: copy their pages to host pools (torch
+    copies), record the host page of each block, and fill the device copies
+    with NaN so that only the host copies carry the data."""
+    host = plan_host_pools(batch)
+    B = batch.spec.batch
+    pages = np.concatenate([batch.table_np[b][host.host_table_np[b] >= 0]
+                            for b in range(B)])
+    idx = torch.as_tensor(pages.astype(np.int64), device=batch.k_pages.device)
+    n_host = len(pages)
+    for s0 in range(0, n_host, 1024):
+        sl = idx[s0:s0 + 1024]
+        host.host_k[s0:s0 + 1024].copy_(batch.k_pages.index_select(0, sl))
+        host.host_v[s0:s0 + 1024].copy_(batch.v_pages.index_select(0, sl))
+    poison_device_copies(batch, host)
+    return host
 
 
 def custom(name="custom", batch=1, n_q_heads=8, n_kv_heads=2, context=(4096,),

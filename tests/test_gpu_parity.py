@@ -574,6 +574,55 @@ def test_host_tier_residency_matches_full_staging():
     assert copied_total < kept_total
 
 
+def test_offload_prefill_native():
+    """rkv_offload_blocks copies exactly the offload blocks that have a host
+    page (bit-exact), leaves every other host page alone, and the decode
+    path then runs from the natively filled pools (oracle check)."""
+    spec = synth.scaled(synth.CONFIGS[5], batch=2, context=(20000, 23000), steps=2,
+                        plant_range=(8, 90), plant_count=5, local_tokens=7192,
+                        dense_boundary=0, config_id=105)
+    say("native prefill offload")
+    max_blocks = -(-(max(spec.context) + spec.steps - 1) // 128)
+    batch = synth.make_batch(spec, DEV, extra_pages=spec.batch * max_blocks)
+    host = synth.plan_host_pools(batch)
+    n_host = host.host_k.shape[0]
+    # one extra host page, assigned to an init block: outside the offload
+    # range, so it must stay untouched
+    hk = torch.full((n_host + 1,) + tuple(host.host_k.shape[1:]), 0x1234,
+                    dtype=torch.int16, pin_memory=True)
+    hv = torch.full_like(hk, 0x4321, pin_memory=True)
+    table = host.host_table_np.copy()
+    table[0, 0] = n_host
+    host_table = torch.from_numpy(table).to(DEV)
+    prm = B.params(spec.n_q_heads, spec.n_kv_heads, init_tokens=spec.init_tokens,
+                   local_tokens=spec.local_tokens, topk_ppm=spec.topk_ppm,
+                   dense_boundary=spec.dense_boundary)
+    sess = HostTierSession(prm, batch.k_pages, batch.v_pages, batch.block_table,
+                           i32(batch.context))
+    ref = DecodeSession(prm, batch.k_pages, batch.v_pages, batch.block_table,
+                        i32(batch.context))
+    prefill_lens = i32(batch.context - 1)
+    ref.build_reps(prefill_lens)
+    sess.offload_prefill(hk, hv, host_table, prefill_lens)
+    torch.cuda.synchronize()
+    assert torch.equal(sess.reps, ref.reps)
+    kp, vp = batch.k_pages.cpu(), batch.v_pages.cpu()
+    for b in range(2):
+        for j in range(8, 90):
+            hp, page = int(table[b, j]), int(batch.table_np[b, j])
+            assert torch.equal(hk[hp], kp[page]) and torch.equal(hv[hp], vp[page]), (b, j)
+    assert bool((hk[n_host] == 0x1234).all()) and bool((hv[n_host] == 0x4321).all())
+    # decode from the natively filled pools (the extra page is not used:
+    # block 0 is an init block, read from HBM)
+    pools = synth.HostPools(hk[:n_host], hv[:n_host], host.host_table, host.host_table_np)
+    synth.poison_device_copies(batch, pools)
+    sess.attach_host(pools.host_k, pools.host_v, pools.host_table)
+    for t in range(2):
+        step(batch, sess, t)
+        torch.cuda.synchronize()
+        oracle_full_check(batch, sess, t, host=pools)
+
+
 def test_host_tier_full_size_sampled():
     say("config 5 (4 x 256K, host tier)")
     batch, host, sess = make_host_session(synth.CONFIGS[5])
