@@ -28,7 +28,11 @@ Readings where the pages are silent (each one is also listed in the design doc):
   head, and only complete blocks get one;
 * "closest" by inner product means the largest inner product;
 * the query heads of one KV group are summed into one score per (sequence,
-  KV head), and the top-k runs per (sequence, KV head);
+  KV head), and the top-k runs per (sequence, KV head); the page keeps one
+  (representation, block index) record per block and leaves open whether
+  retrieval runs per KV head or once per sequence, so the other reading is
+  offered too (``per_sequence``): the scores of all KV heads are summed, one
+  top-k runs per sequence, and every KV head attends the same blocks;
 * query head h' belongs to KV head h' // G (contiguous groups);
 * init is ceil(init_tokens / 128) blocks; local is every block that meets the
   last ``local_tokens`` positions, and the last (possibly partial) block is
@@ -67,6 +71,7 @@ class Params:
     dense_boundary: int = 32768  # VLLM_RETRIEVAL_DENSE_BOUNDARY = 32K
     block: int = BLOCK
     scale: float = field(default=1.0 / np.sqrt(HEAD_DIM))
+    per_sequence: bool = False   # one selection per sequence (all KV heads)
 
     @property
     def group(self) -> int:
@@ -238,16 +243,24 @@ def decode_step(q: np.ndarray, K: np.ndarray, V: np.ndarray, L: int,
     dense = is_dense(prompt_len, prm.dense_boundary, prm.topk_ppm)
     out = np.zeros((prm.n_q_heads, q.shape[1]))
     heads = []
+    lo, hi = reg.n_init, reg.n_init + reg.n_off
+    k = reg.n_off if dense else topk_count(reg.n_off, prm.topk_ppm)
+    # scores of the offload blocks per KV head (group queries summed)
+    scores = []
     for h in range(prm.n_kv_heads):
         qg = q[h * G:(h + 1) * G]
-        lo, hi = reg.n_init, reg.n_init + reg.n_off
         if reg.n_off > 0:
             r = reps[h, lo:hi] if reps is not None else \
                 block_reps(K[h, :L], prm.block)[lo:hi]
-            s = ip_scores(qg, r)
+            scores.append(ip_scores(qg, r))
         else:
-            s = np.zeros(0)
-        k = reg.n_off if dense else topk_count(reg.n_off, prm.topk_ppm)
+            scores.append(np.zeros(0))
+    if prm.per_sequence:  # one score per block: the sum over the KV heads
+        total = np.sum(scores, axis=0)
+        scores = [total] * prm.n_kv_heads
+    for h in range(prm.n_kv_heads):
+        qg = q[h * G:(h + 1) * G]
+        s = scores[h]
         sel = top_k(s, k) + lo
         merged = merged_blocks(reg, sel)
         if merged_override is not None:

@@ -339,11 +339,13 @@ def test_attended_set_covers_init_and_window_tokens():
         assert L - 1 in toks
 
 
-def _oracle_batch_step(batch, t):
+def _oracle_batch_step(batch, t, **overrides):
     """Oracle result of step t for every sequence of a synth batch."""
     spec = batch.spec
-    prm = O.Params(spec.n_q_heads, spec.n_kv_heads, spec.init_tokens,
-                   spec.local_tokens, spec.topk_ppm, spec.dense_boundary)
+    kw = dict(init_tokens=spec.init_tokens, local_tokens=spec.local_tokens,
+              topk_ppm=spec.topk_ppm, dense_boundary=spec.dense_boundary)
+    kw.update(overrides)
+    prm = O.Params(spec.n_q_heads, spec.n_kv_heads, **kw)
     kp = batch.k_pages.cpu().numpy().view(np.uint16)
     vp = batch.v_pages.cpu().numpy().view(np.uint16)
     q = O.bf16_to_f64(batch.q_bits(t).cpu().numpy().view(np.uint16))
@@ -430,3 +432,72 @@ def test_attend_rows_independent_at_extreme_scales():
     out = O.attend(q, K, V, 1.0)
     np.testing.assert_allclose(out[0], V.mean(axis=0), rtol=1e-12)
     assert np.isfinite(out).all()
+
+
+# ----------------------------------------------------------------------------
+# Per-sequence selection (scores summed over all KV heads, one top-k per
+# sequence): the other reading of one record per block.
+# ----------------------------------------------------------------------------
+
+def test_per_sequence_selection_brute_force():
+    """The per-sequence set maximises the all-heads score of plain loops over
+    every k-subset (ties to the smaller block), and every KV head attends it."""
+    rng = np.random.default_rng(31)
+    hkv, hq, L = 3, 6, 12 * 128
+    G = hq // hkv
+    prm = O.Params(hq, hkv, init_tokens=128, local_tokens=128, topk_ppm=400_000,
+                   dense_boundary=0, per_sequence=True)
+    for trial in range(6):
+        q = rng.standard_normal((hq, 128))
+        K = rng.standard_normal((hkv, L, 128))
+        V = rng.standard_normal((hkv, L, 128))
+        res = O.decode_step(q, K, V, L, L, prm)
+        lo, n = res.regions.n_init, res.regions.n_off
+        assert (lo, n) == (1, 10)
+        k = res.heads[0].k
+        assert k == 4
+        # all-heads score of each offload block from plain loops
+        tot = []
+        for j in range(lo, lo + n):
+            terms = []
+            for h in range(hkv):
+                rep = [math.fsum(K[h, j * 128 + t, d] for t in range(128)) / 128
+                       for d in range(128)]
+                for g in range(G):
+                    terms.extend(q[h * G + g, d] * rep[d] for d in range(128))
+            tot.append(math.fsum(terms))
+        best = max(itertools.combinations(range(n), k),
+                   key=lambda sub: (math.fsum(tot[i] for i in sub),
+                                    [-i for i in sub]))
+        want = [lo + i for i in best]
+        for h in res.heads:
+            assert h.selected.tolist() == want
+            assert np.array_equal(h.merged, res.heads[0].merged)
+
+
+def test_per_sequence_equals_per_head_with_one_kv_head():
+    rng = np.random.default_rng(32)
+    L = 30 * 128 + 5
+    q = rng.standard_normal((4, 128))
+    K = rng.standard_normal((1, L, 128))
+    V = rng.standard_normal((1, L, 128))
+    a = O.decode_step(q, K, V, L, L, O.Params(4, 1, init_tokens=256,
+                                              local_tokens=512, dense_boundary=0))
+    b = O.decode_step(q, K, V, L, L, O.Params(4, 1, init_tokens=256, local_tokens=512,
+                                              dense_boundary=0, per_sequence=True))
+    assert np.array_equal(a.out, b.out)
+    assert np.array_equal(a.heads[0].selected, b.heads[0].selected)
+
+
+def test_per_sequence_planted_blocks_and_dense_switch():
+    """Blocks planted toward one KV group dominate the all-heads sum, so the
+    per-sequence set holds them for every head; with ratio 1.0 both readings
+    attend every block and agree."""
+    batch = synth.make_batch(synth.CONFIGS[1], "cpu")
+    (res,) = _oracle_batch_step(batch, 0, per_sequence=True)
+    for h in res.heads:
+        assert set(batch.planted[0]) <= set(h.selected.tolist())
+    (dense_a,) = _oracle_batch_step(batch, 0, topk_ppm=1_000_000)
+    (dense_b,) = _oracle_batch_step(batch, 0, topk_ppm=1_000_000, per_sequence=True)
+    assert not np.isnan(dense_a.out).any()
+    assert np.array_equal(dense_a.out, dense_b.out)
