@@ -215,6 +215,8 @@ def main():
                     help="KV-cache copies cycled over (0: enough to exceed 1 GiB)")
     ap.add_argument("--impl", default="auto", choices=["auto", "mfma", "valu"])
     ap.add_argument("--split", type=int, default=0)
+    ap.add_argument("--select", default="per-head", choices=["per-head", "per-sequence"],
+                    help="selection per (sequence, KV head) or once per sequence")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device-to-device copy first "
@@ -258,7 +260,9 @@ def main():
     prm = B.params(spec.n_q_heads, spec.n_kv_heads, init_tokens=spec.init_tokens,
                    local_tokens=spec.local_tokens, topk_ppm=spec.topk_ppm,
                    dense_boundary=spec.dense_boundary, attn_impl=impl,
-                   split_waves=args.split)
+                   split_waves=args.split,
+                   select_mode=(B.SELECT_PER_SEQUENCE if args.select == "per-sequence"
+                                else B.SELECT_PER_HEAD))
     ctx = torch.as_tensor(base.context.astype(np.int32), device=dev)
     sessions = []
     for layer in range(n_layers):
@@ -410,6 +414,7 @@ def main():
             "layer_copies": n_layers,
             "attn_impl": args.impl,
             "split_waves": args.split,
+            "select": args.select,
         },
         "stream_read_probe_gbs": probe_gbs,
         "host_staging": staging,

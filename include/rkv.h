@@ -72,6 +72,9 @@ typedef enum rkv_status {
 } rkv_status;
 
 /* Attention kernel variants. */
+#define RKV_SELECT_PER_HEAD 0
+#define RKV_SELECT_PER_SEQUENCE 1
+
 #define RKV_ATTN_AUTO 0
 #define RKV_ATTN_MFMA 1   /* query heads of a group packed against K tiles */
 #define RKV_ATTN_VALU 2   /* vector-ALU dot products, same memory schedule */
@@ -96,6 +99,8 @@ typedef struct rkv_params {
   int32_t attn_impl;       /* RKV_ATTN_AUTO / _MFMA / _VALU */
   int32_t split_waves;     /* waves the attention split is spread over,
                               at most 65536; 0 = auto (1024: one per SIMD) */
+  int32_t select_mode;     /* RKV_SELECT_PER_HEAD (default) or
+                              RKV_SELECT_PER_SEQUENCE, see rkv_select */
 } rkv_params;
 
 /* Defaults of the page (init 1024, local 7192, ratio 0.2, dense boundary
@@ -166,6 +171,10 @@ size_t rkv_select_workspace_size(const rkv_params* params, int32_t batch,
  *                 else ceil(n_off * topk_ppm / 10^6)
  *   selected    = the k offload blocks with the largest s_j, ties to the
  *                 smaller block index, written in ascending order
+ * With select_mode = RKV_SELECT_PER_SEQUENCE (the other reading of the
+ * page's one record per block), s_j is summed over all KV heads of the
+ * sequence (fp32, heads in order), one top-k runs per sequence and every
+ * KV head gets the same selected blocks and the same merged list.
  * Outputs:
  *   sel_ids  [batch][n_kv_heads][k_cap] logical block ids (first n_sel valid);
  *            may be NULL only when k_cap is 0

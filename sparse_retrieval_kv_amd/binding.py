@@ -30,7 +30,7 @@ class Params(ctypes.Structure):
                 ("init_tokens", ctypes.c_int32), ("local_tokens", ctypes.c_int32),
                 ("topk_ppm", ctypes.c_int32), ("dense_boundary", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("attn_impl", ctypes.c_int32),
-                ("split_waves", ctypes.c_int32)]
+                ("split_waves", ctypes.c_int32), ("select_mode", ctypes.c_int32)]
 
     def __repr__(self):
         return "Params(" + ", ".join(f"{n}={getattr(self, n)}"
@@ -42,6 +42,9 @@ class RkvError(RuntimeError):
         super().__init__(f"rkv status {status}: {msg}")
         self.status = status
 
+
+SELECT_PER_HEAD = 0
+SELECT_PER_SEQUENCE = 1
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32

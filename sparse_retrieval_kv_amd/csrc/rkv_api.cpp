@@ -68,7 +68,11 @@ rkv_status check_params(const rkv_params* p, rkv::Method* m) {
   RKV_REQUIRE(p->split_waves >= 0 && p->split_waves <= (1 << 16),
               RKV_ERR_INVALID_ARG, "split_waves %d outside [0, 65536]",
               p->split_waves);
+  RKV_REQUIRE(p->select_mode == RKV_SELECT_PER_HEAD ||
+                  p->select_mode == RKV_SELECT_PER_SEQUENCE,
+              RKV_ERR_INVALID_ARG, "select_mode %d unknown", p->select_mode);
   if (m) {
+    m->per_sequence = p->select_mode == RKV_SELECT_PER_SEQUENCE;
     m->n_q_heads = p->n_q_heads;
     m->n_kv_heads = p->n_kv_heads;
     m->group = p->n_q_heads / p->n_kv_heads;
@@ -127,6 +131,7 @@ rkv_params rkv_params_default(int32_t n_q_heads, int32_t n_kv_heads) {
   p.scale = 1.0f / sqrtf((float)RKV_HEAD_DIM);
   p.attn_impl = RKV_ATTN_AUTO;
   p.split_waves = 0;
+  p.select_mode = RKV_SELECT_PER_HEAD;
   return p;
 }
 

@@ -19,6 +19,7 @@ constexpr int kPpmOne = 1000000;
 struct Method {
   int n_q_heads, n_kv_heads, group;
   int init_tokens, local_tokens, topk_ppm, dense_boundary;
+  bool per_sequence;  // one selection per sequence (scores summed over heads)
 };
 
 hipError_t launch_build_reps(const uint16_t* k_pages, int64_t n_pages,

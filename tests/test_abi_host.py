@@ -67,6 +67,8 @@ def test_param_validation(L):
         (with_(attn_impl=7), B.RKV_ERR_INVALID_ARG),
         (with_(split_waves=-1), B.RKV_ERR_INVALID_ARG),
         (with_(split_waves=(1 << 16) + 1), B.RKV_ERR_INVALID_ARG),
+        (with_(select_mode=2), B.RKV_ERR_INVALID_ARG),
+        (with_(select_mode=-1), B.RKV_ERR_INVALID_ARG),
     ]
     for p, want in cases:
         assert _attn(L, p) == want, p

@@ -633,6 +633,66 @@ def test_host_tier_full_size_sampled():
             oracle_full_check(batch, sess, t, seqs=[0, 3], heads=[2, 6], host=host)
 
 
+def per_sequence_check(batch, sess, t, seqs=None):
+    """Per-sequence selection mode: one oracle step over all KV heads of each
+    sequence (scores summed over the heads), every head's GPU selection equal
+    to the others' and checked against it, and outputs per head."""
+    spec = batch.spec
+    G = spec.group
+    out = sess.out.cpu().numpy()
+    qall = q_f64(batch, t)
+    prm = oracle_params(spec, per_sequence=True)
+    for b in (range(spec.batch) if seqs is None else seqs):
+        hs = list(range(spec.n_kv_heads))
+        K, V, L = logical_at_step(batch, b, t, seq_pages_host(batch, b, hs))
+        res = O.decode_step(qall[b], K, V, L, int(batch.context[b]), prm)
+        sel0 = gpu_selection(sess, b, 0)
+        for h in hs:
+            ctx = f"{spec.name} per-sequence step {t} seq {b} head {h}"
+            sel = gpu_selection(sess, b, h)
+            assert np.array_equal(sel, sel0), ctx
+            hr = res.heads[h]
+            check_selection(sel, hr, res.regions.n_init, ctx)
+            mlog, _ = gpu_merged_logical(sess, batch, b, h)
+            q = qall[b, h * G:(h + 1) * G]
+            if np.array_equal(sel, hr.selected):
+                assert np.array_equal(mlog, hr.merged), ctx
+                ref = res.out[h * G:(h + 1) * G]
+            else:
+                prm1 = O.Params(G, 1, prm.init_tokens, prm.local_tokens, prm.topk_ppm,
+                                prm.dense_boundary)
+                ref = O.decode_step(q, K[h:h + 1], V[h:h + 1], L, int(batch.context[b]),
+                                    prm1, merged_override=[mlog]).out
+            check_head_output(out[b, h * G:(h + 1) * G], ref, ctx)
+
+
+def test_per_sequence_selection_mixed():
+    spec = synth.custom("perseq", batch=3, n_q_heads=16, n_kv_heads=4,
+                        context=(767, 9000, 20480), steps=2, init_tokens=256,
+                        local_tokens=1000, dense_boundary=0, config_id=106)
+    say("per-sequence selection, mixed lengths")
+    batch = synth.make_batch(spec, DEV)
+    prm, sess = make_session(batch, select_mode=B.SELECT_PER_SEQUENCE)
+    prefill(batch, sess)
+    for t in range(2):
+        step(batch, sess, t)
+        torch.cuda.synchronize()
+        per_sequence_check(batch, sess, t)
+
+
+def test_per_sequence_selection_llama_layer():
+    say("per-sequence selection, config 2 (1 x 64K), steps 0 and 5")
+    spec = synth.scaled(synth.CONFIGS[2], steps=6)
+    batch = synth.make_batch(spec, DEV)
+    prm, sess = make_session(batch, select_mode=B.SELECT_PER_SEQUENCE)
+    prefill(batch, sess)
+    for t in range(6):
+        step(batch, sess, t)
+        if t in (0, 5):
+            torch.cuda.synchronize()
+            per_sequence_check(batch, sess, t)
+
+
 def test_append_select_equals_append_then_select():
     """The fused launch gives bit-identical pools, representations,
     selections and merged tables to rkv_append_kv followed by rkv_select."""
