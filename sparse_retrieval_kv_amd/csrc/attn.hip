@@ -118,21 +118,28 @@ __device__ __forceinline__ int units_of(const AttnArgs& a, int bh) {
   return 2 * n;
 }
 
-// Every wave takes c = ceil(T / W) consecutive units (the last active wave
-// fewer; waves past the end none), so no wave carries more units than the
-// slowest one must.
-__device__ __forceinline__ int64_t units_per_wave(int64_t T, int W) {
-  return (T + W - 1) / W;
+// The T units are split evenly over W waves in a virtual order in which the
+// four waves that share a compute unit are neighbours: workgroups w, w + W/4,
+// w + W/2 and w + 3W/4 are placed on the same compute unit when the grid
+// fills an idle GPU (workgroups are dealt round robin over the 8 XCDs and,
+// within an XCD, over its 32 compute units).  Each compute unit then streams
+// 4T/W units (+-1) -- a compute unit's bandwidth, not a wave's, is what is
+// shared -- and every wave 2 or 3.  The placement only steers speed: any
+// placement gives the same results.
+__device__ __forceinline__ int virtual_wave(int w, int W) {
+  if (W % 4 != 0) return w;
+  const int q = W >> 2;
+  return (w % q) * 4 + w / q;
 }
 
-__device__ __forceinline__ int64_t unit_start(int w, int64_t T, int W) {
-  const int64_t s = (int64_t)w * units_per_wave(T, W);
-  return s < T ? s : T;
+__device__ __forceinline__ int64_t unit_start(int v, int64_t T, int W) {
+  return (int64_t)v * T / W;
 }
 
-// The wave whose range holds unit u (0 <= u < T).
+// The virtual wave whose range holds unit u (0 <= u < T): the largest v
+// with unit_start(v) <= u.
 __device__ __forceinline__ int wave_of(int64_t u, int64_t T, int W) {
-  return (int)(u / units_per_wave(T, W));
+  return (int)(((u + 1) * W - 1) / T);
 }
 
 __device__ __forceinline__ int wave_sum_i(int x) {
@@ -501,7 +508,8 @@ template <class Math>
 __device__ __forceinline__ void split_body(const AttnArgs& a) {
   const int lane = threadIdx.x;
   const int col = lane & 15, grp = lane >> 4;
-  const int w = blockIdx.x;
+  const int W = a.n_waves;
+  const int w = virtual_wave(blockIdx.x, W);
   const int NB = a.batch * a.n_kv;
   int64_t T = 0;
   for (int base = 0; base < NB; base += 64) {
@@ -509,7 +517,6 @@ __device__ __forceinline__ void split_body(const AttnArgs& a) {
     T += wave_sum_i(bh < NB ? units_of(a, bh) : 0);
   }
   if (T == 0) return;
-  const int W = a.n_waves;
   const int64_t lo = unit_start(w, T, W), hi = unit_start(w + 1, T, W);
   if (lo >= hi) return;
   Math math;
@@ -528,12 +535,17 @@ __device__ __forceinline__ void split_body(const AttnArgs& a) {
       const int pu = __shfl(u, src);
       const int64_t a0 = lo > ps ? lo : ps;
       const int64_t a1 = hi < ps + pu ? hi : ps + pu;
-      // piece w - w0 of list pbh; the list's first wave records the count
+      // pieces of a list are numbered along it: with T >= W every wave
+      // has units, so piece = w - w0; otherwise every non-empty wave has
+      // one unit, so piece = that unit's index in the list.  The wave that
+      // holds the list's first unit records the count.
       const int w0 = wave_of(ps, T, W);
-      if (w == w0 && lane == 0)
-        a.n_pieces[pbh] = wave_of(ps + pu - 1, T, W) - w0 + 1;
+      const bool dense_waves = T >= W;
+      const int piece = dense_waves ? w - w0 : (int)(a0 - ps);
+      if (a0 == ps && lane == 0)
+        a.n_pieces[pbh] = dense_waves ? wave_of(ps + pu - 1, T, W) - w0 + 1 : pu;
       run_piece(a, math, pbh, (int)(a0 - ps), (int)(a1 - ps),
-                (int64_t)pbh * a.piece_cap + (w - w0), lane, col, grp);
+                (int64_t)pbh * a.piece_cap + piece, lane, col, grp);
     }
     run += __shfl(incl, 63);
   }

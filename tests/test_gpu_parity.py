@@ -267,6 +267,24 @@ def test_short_and_degenerate_lengths():
     oracle_full_check(batch, sess, 0)
 
 
+def test_maximum_table_size():
+    """8192 blocks (the library's table limit; 1,048,566 tokens) for one
+    sequence: every register slot of the top-k, 254 score chunks, and a
+    combine that folds several batches of pieces for one list."""
+    L0 = 8192 * 128 - 10
+    spec = synth.custom("max", batch=1, n_q_heads=4, n_kv_heads=1, context=(L0,),
+                        dense_boundary=0, config_id=98)
+    batch = synth.make_batch(spec, DEV)
+    assert batch.table_np.shape[1] == 8192
+    prm, sess = make_session(batch)
+    say("maximum table size (8192 blocks)")
+    prefill(batch, sess)
+    step(batch, sess, 0)
+    torch.cuda.synchronize()
+    assert int(sess.n_sel[0, 0]) == -(-(8135 - 8) * 200_000 // 1_000_000)
+    oracle_full_check(batch, sess, 0)
+
+
 def test_zero_length_sequence_gives_zeros():
     spec = synth.custom("empty", batch=2, n_q_heads=8, n_kv_heads=2,
                         context=(1, 1000), config_id=96)
