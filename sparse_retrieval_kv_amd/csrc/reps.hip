@@ -67,12 +67,14 @@ __global__ __launch_bounds__(256) void build_reps_kernel(
   if ((uint64_t)(int64_t)page >= (uint64_t)n_pages) return;
   const uint16_t* K = k_pages + ((int64_t)page * n_kv + h) * (kBlock * kDim);
   const int c = lane & 15, g = lane >> 4;
+  // all 32 loads of the tile in flight at once, then summed in row order
+  uint4 w[32];
+#pragma unroll
+  for (int it = 0; it < 32; ++it)
+    w[it] = *reinterpret_cast<const uint4*>(K + (it * 4 + g) * kDim + c * 8);
   Sum8 s = {};
-#pragma unroll 8
-  for (int it = 0; it < 32; ++it) {
-    const int t = it * 4 + g;
-    add_chunk(s, *reinterpret_cast<const uint4*>(K + t * kDim + c * 8));
-  }
+#pragma unroll
+  for (int it = 0; it < 32; ++it) add_chunk(s, w[it]);
   finish_rep(s, lane,
              reps + (((int64_t)b * n_kv + h) * max_blocks + j) * kDim);
 }

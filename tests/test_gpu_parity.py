@@ -711,6 +711,49 @@ def test_per_sequence_selection_llama_layer():
             per_sequence_check(batch, sess, t)
 
 
+def test_decode_step_replays_from_a_hip_graph():
+    """A whole decode step (append + select + attention, four kernels, no
+    memsets, no host syncs) captured in a HIP graph: every replay, with eager
+    work and synchronisations in between, equals the eager step bit for
+    bit."""
+    spec = synth.custom("graph", batch=2, n_q_heads=16, n_kv_heads=4,
+                        context=(9000, 20480), steps=1, init_tokens=256,
+                        local_tokens=1000, dense_boundary=0, config_id=107)
+    say("HIP graph replay of a decode step")
+    batch = synth.make_batch(spec, DEV)
+    prm, sess = make_session(batch)
+    prefill(batch, sess)
+    lens = i32(batch.lens_at(0))
+    kn, vn = batch.new_kv_bits(0)
+    q = batch.q_bits(0)
+    sess.step(q, kn, vn, lens)
+    torch.cuda.synchronize()
+    eager = (sess.out.clone(), sess.merged.clone(), sess.n_merged.clone(),
+             sess.sel_ids.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sess.step(q, kn, vn, lens)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sess.step(q, kn, vn, lens)
+    for r in range(3):
+        sess.out.zero_()
+        sess.merged.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        # merged lists count only their first n_merged entries
+        live = (torch.arange(sess.merged.shape[-1], device=DEV)
+                < sess.n_merged[..., None])
+        assert torch.equal(sess.n_merged, eager[2]), r
+        assert torch.equal(sess.merged[live], eager[1][live]), r
+        assert torch.equal(sess.out, eager[0]), r
+        assert torch.equal(sess.sel_ids, eager[3]), r
+
+
 def test_append_select_equals_append_then_select():
     """The fused launch gives bit-identical pools, representations,
     selections and merged tables to rkv_append_kv followed by rkv_select."""
