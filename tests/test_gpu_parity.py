@@ -651,7 +651,7 @@ def test_host_tier_full_size_sampled():
             oracle_full_check(batch, sess, t, seqs=[0, 3], heads=[2, 6], host=host)
 
 
-def per_sequence_check(batch, sess, t, seqs=None):
+def per_sequence_check(batch, sess, t, seqs=None, host=None):
     """Per-sequence selection mode: one oracle step over all KV heads of each
     sequence (scores summed over the heads), every head's GPU selection equal
     to the others' and checked against it, and outputs per head."""
@@ -662,7 +662,7 @@ def per_sequence_check(batch, sess, t, seqs=None):
     prm = oracle_params(spec, per_sequence=True)
     for b in (range(spec.batch) if seqs is None else seqs):
         hs = list(range(spec.n_kv_heads))
-        K, V, L = logical_at_step(batch, b, t, seq_pages_host(batch, b, hs))
+        K, V, L = logical_at_step(batch, b, t, seq_pages_host(batch, b, hs, host))
         res = O.decode_step(qall[b], K, V, L, int(batch.context[b]), prm)
         sel0 = gpu_selection(sess, b, 0)
         for h in hs:
@@ -671,7 +671,7 @@ def per_sequence_check(batch, sess, t, seqs=None):
             assert np.array_equal(sel, sel0), ctx
             hr = res.heads[h]
             check_selection(sel, hr, res.regions.n_init, ctx)
-            mlog, _ = gpu_merged_logical(sess, batch, b, h)
+            mlog, _ = gpu_merged_logical(sess, batch, b, h, host is not None)
             q = qall[b, h * G:(h + 1) * G]
             if np.array_equal(sel, hr.selected):
                 assert np.array_equal(mlog, hr.merged), ctx
@@ -752,6 +752,19 @@ def test_decode_step_replays_from_a_hip_graph():
         assert torch.equal(sess.merged[live], eager[1][live]), r
         assert torch.equal(sess.out, eager[0]), r
         assert torch.equal(sess.sel_ids, eager[3]), r
+
+
+def test_per_sequence_selection_with_resident_host_tier():
+    spec = synth.scaled(synth.CONFIGS[5], batch=2, context=(20000, 23000), steps=3,
+                        plant_range=(8, 90), plant_count=5, local_tokens=7192,
+                        dense_boundary=0, config_id=108)
+    say("per-sequence selection + resident host tier")
+    batch, host, sess = make_host_session(spec, resident=True,
+                                          select_mode=B.SELECT_PER_SEQUENCE)
+    for t in range(3):
+        step(batch, sess, t)
+        torch.cuda.synchronize()
+        per_sequence_check(batch, sess, t, host=host)
 
 
 def test_append_select_equals_append_then_select():
