@@ -105,6 +105,7 @@ struct AttnArgs {
   float2* part_ml;   // [batch * n_kv][piece_cap][group]
   int* n_pieces;     // [batch * n_kv]: pieces of each non-empty list
   int m_cap, max_len, batch, n_kv, group, n_waves, piece_cap;
+  int comb_spec;     // pieces per combine lane requested before the count
   float scale_log2;  // scale * log2(e)
 };
 
@@ -571,6 +572,7 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
 constexpr int kCombSlices = 4;   // 32-dim slices per query head
 constexpr int kCombGroups = 8;   // piece groups per wave
 constexpr int kCombDepth = 16;   // pieces in flight per lane
+constexpr int kCombSpecMax = 20; // pieces per lane requested with the count
 
 __device__ __forceinline__ void lse_fold(float& m, float& l, float4& acc, float m2,
                                          float l2, const float4& acc2) {
@@ -599,12 +601,31 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a,
   const int dim0 = 32 * slice + 4 * d4;
   float4* dst = reinterpret_cast<float4*>(out + (int64_t)bq * kDim + dim0);
 
+  // the first `spec` pieces per lane are requested together with the
+  // piece count (spec is sized by the host for lists of average length)
+  const int spec = a.comb_spec;
+  float2 ml0[kCombSpecMax];
+  float4 v0[kCombSpecMax];
+#pragma unroll
+  for (int u = 0; u < kCombSpecMax; ++u) {
+    if (u < spec) {
+      const int i = pg + u * kCombGroups;
+      const int64_t slot = slot0 + (i < P ? i : P - 1);
+      ml0[u] = a.part_ml[slot * G + hh];
+      v0[u] = *reinterpret_cast<const float4*>(a.part_acc + (slot * G + hh) * kDim + dim0);
+    }
+  }
   const int units = units_of(a, bh);
   int np = a.n_pieces[bh];
   np = units == 0 ? 0 : (np < 1 ? 1 : (np > P ? P : np));
   float m = kNegInf, l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int base = pg; base < np; base += kCombDepth * kCombGroups) {
+#pragma unroll
+  for (int u = 0; u < kCombSpecMax; ++u) {
+    const int i = pg + u * kCombGroups;
+    if (u < spec && i < np && ml0[u].y > 0.f) lse_fold(m, l, acc, ml0[u].x, ml0[u].y, v0[u]);
+  }
+  for (int base = pg + spec * kCombGroups; base < np; base += kCombDepth * kCombGroups) {
     float2 ml[kCombDepth];
     float4 v[kCombDepth];
 #pragma unroll
@@ -654,6 +675,12 @@ AttnPlan plan_attention(int batch, int n_q_heads, int n_kv_heads, int waves,
   p.partial_bytes = slots * group * kDim * sizeof(float);
   p.ml_bytes = slots * group * 2 * sizeof(float);
   p.count_bytes = ((size_t)batch * n_kv_heads * sizeof(int) + 255) / 256 * 256;
+  // lists of average length meet about W / lists + 1 waves; the combine's
+  // eight lanes per slice request that many pieces before knowing the count
+  const int64_t lists = (int64_t)batch * n_kv_heads;
+  const int64_t avg = lists > 0 ? p.n_waves / lists + 2 : 1;
+  int spec = (int)((avg + 7) / 8);
+  p.comb_spec = spec < 1 ? 1 : (spec > 20 ? 20 : spec);
   p.total_bytes = p.partial_bytes + p.ml_bytes + p.count_bytes;
   return p;
 }
@@ -680,6 +707,7 @@ hipError_t launch_decode_attn(const Method& m, bool use_mfma,
   a.n_pieces = reinterpret_cast<int*>(static_cast<char*>(workspace) +
                                       plan.partial_bytes + plan.ml_bytes);
   a.piece_cap = plan.piece_cap;
+  a.comb_spec = plan.comb_spec;
   a.m_cap = m_cap;
   a.max_len = m_cap * kBlock;
   a.batch = batch;

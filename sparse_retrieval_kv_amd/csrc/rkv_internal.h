@@ -100,6 +100,7 @@ hipError_t launch_stage_resident(const Method& m, const uint16_t* host_k,
 struct AttnPlan {
   int n_waves;
   int piece_cap;         // partial slots per (sequence, KV head) list
+  int comb_spec;         // combine pieces per lane requested speculatively
   size_t partial_bytes;  // fp32 [lists][piece_cap][group][kDim]
   size_t ml_bytes;       // float2 [lists][piece_cap][group]
   size_t count_bytes;    // int [lists] piece counts (padded)
