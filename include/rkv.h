@@ -98,7 +98,8 @@ typedef struct rkv_params {
   float scale;             /* softmax scale, default 1/sqrt(128) */
   int32_t attn_impl;       /* RKV_ATTN_AUTO / _MFMA / _VALU */
   int32_t split_waves;     /* waves the attention split is spread over,
-                              at most 65536; 0 = auto (1024: one per SIMD) */
+                              at most 65536; 0 = auto (two per compute
+                              unit: 512 on MI355X) */
   int32_t select_mode;     /* RKV_SELECT_PER_HEAD (default) or
                               RKV_SELECT_PER_SEQUENCE, see rkv_select */
 } rkv_params;

@@ -106,6 +106,7 @@ struct AttnArgs {
   int* n_pieces;     // [batch * n_kv]: pieces of each non-empty list
   int m_cap, max_len, batch, n_kv, group, n_waves, piece_cap;
   int comb_spec;     // pieces per combine lane requested before the count
+  int n_cu;          // compute units of the device
   float scale_log2;  // scale * log2(e)
 };
 
@@ -120,17 +121,16 @@ __device__ __forceinline__ int units_of(const AttnArgs& a, int bh) {
 }
 
 // The T units are split evenly over W waves in a virtual order in which the
-// four waves that share a compute unit are neighbours: workgroups w, w + W/4,
-// w + W/2 and w + 3W/4 are placed on the same compute unit when the grid
-// fills an idle GPU (workgroups are dealt round robin over the 8 XCDs and,
-// within an XCD, over its 32 compute units).  Each compute unit then streams
-// 4T/W units (+-1) -- a compute unit's bandwidth, not a wave's, is what is
-// shared -- and every wave 2 or 3.  The placement only steers speed: any
-// placement gives the same results.
-__device__ __forceinline__ int virtual_wave(int w, int W) {
-  if (W % 4 != 0) return w;
-  const int q = W >> 2;
-  return (w % q) * 4 + w / q;
+// waves that share a compute unit are neighbours: when the grid fills an
+// idle GPU, workgroup w runs on compute unit w mod n_cu (workgroups are
+// dealt round robin over the 8 XCDs and, within an XCD, over its compute
+// units), so waves w, w + n_cu, w + 2 n_cu, ... share one.  Each compute
+// unit then streams its share of the units (+-1) -- a compute unit's
+// bandwidth, not a wave's, is what is shared.  The placement only steers
+// speed: any placement gives the same results.
+__device__ __forceinline__ int virtual_wave(int w, int W, int n_cu) {
+  if (n_cu <= 0 || W % n_cu != 0) return w;
+  return (w % n_cu) * (W / n_cu) + w / n_cu;
 }
 
 __device__ __forceinline__ int64_t unit_start(int v, int64_t T, int W) {
@@ -510,7 +510,7 @@ __device__ __forceinline__ void split_body(const AttnArgs& a) {
   const int lane = threadIdx.x;
   const int col = lane & 15, grp = lane >> 4;
   const int W = a.n_waves;
-  const int w = virtual_wave(blockIdx.x, W);
+  const int w = virtual_wave(blockIdx.x, W, a.n_cu);
   const int NB = a.batch * a.n_kv;
   int64_t T = 0;
   for (int base = 0; base < NB; base += 64) {
@@ -662,11 +662,12 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a,
 }  // namespace
 
 AttnPlan plan_attention(int batch, int n_q_heads, int n_kv_heads, int waves,
-                        int m_cap) {
+                        int m_cap, int n_cu) {
   AttnPlan p;
-  // one wave per SIMD on 256 compute units: the whole split runs in one
-  // round, each wave streaming its own run of units
-  p.n_waves = waves > 0 ? waves : 1024;
+  // two waves per compute unit (one per SIMD pair): the whole split runs in
+  // one round, each wave streaming its own run of units
+  p.n_cu = n_cu > 0 ? n_cu : 256;
+  p.n_waves = waves > 0 ? waves : 2 * p.n_cu;
   // a list of at most 2 * m_cap units meets at most min(W, 2 m_cap) + 1 waves
   const int units_cap = 2 * (m_cap > 0 ? m_cap : 1);
   p.piece_cap = (p.n_waves < units_cap ? p.n_waves : units_cap) + 1;
@@ -708,6 +709,7 @@ hipError_t launch_decode_attn(const Method& m, bool use_mfma,
                                       plan.partial_bytes + plan.ml_bytes);
   a.piece_cap = plan.piece_cap;
   a.comb_spec = plan.comb_spec;
+  a.n_cu = plan.n_cu;
   a.m_cap = m_cap;
   a.max_len = m_cap * kBlock;
   a.batch = batch;

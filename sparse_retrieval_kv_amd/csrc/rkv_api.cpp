@@ -7,6 +7,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <string>
 
 #include "rkv_internal.h"
@@ -441,7 +442,8 @@ size_t rkv_attn_workspace_size(const rkv_params* params, int32_t batch,
       batch < 0 || m_cap < 1 || params->split_waves < 0)
     return 0;
   const rkv::AttnPlan p = rkv::plan_attention(
-      batch, params->n_q_heads, params->n_kv_heads, params->split_waves, m_cap);
+      batch, params->n_q_heads, params->n_kv_heads, params->split_waves, m_cap,
+      rkv::device_cu_count());
   return p.total_bytes;
 }
 
@@ -472,7 +474,8 @@ rkv_status rkv_decode_attn(const rkv_params* params, const uint16_t* q,
   RKV_REQUIRE((int64_t)batch * m.n_kv_heads * m_cap < ((int64_t)1 << 30),
               RKV_ERR_UNSUPPORTED, "batch * n_kv_heads * m_cap too large");
   const rkv::AttnPlan plan = rkv::plan_attention(
-      batch, m.n_q_heads, m.n_kv_heads, params->split_waves, m_cap);
+      batch, m.n_q_heads, m.n_kv_heads, params->split_waves, m_cap,
+      rkv::device_cu_count());
   const size_t need = plan.total_bytes;
   RKV_REQUIRE(workspace_bytes >= need && (need == 0 || workspace != nullptr),
               RKV_ERR_WORKSPACE, "attention workspace %zu bytes, need %zu",
@@ -500,3 +503,26 @@ rkv_status rkv_read_probe(const void* buffer, size_t bytes, uint32_t* sink,
 }
 
 }  // extern "C"
+
+namespace rkv {
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];  // 0: not queried yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;  // no device visible (host-only use): MI355X's count
+  }
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+          hipSuccess ||
+      n <= 0) {
+    (void)hipGetLastError();
+    n = 256;
+  }
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+}  // namespace rkv

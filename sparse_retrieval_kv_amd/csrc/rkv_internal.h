@@ -101,13 +101,17 @@ struct AttnPlan {
   int n_waves;
   int piece_cap;         // partial slots per (sequence, KV head) list
   int comb_spec;         // combine pieces per lane requested speculatively
+  int n_cu;              // compute units of the device
   size_t partial_bytes;  // fp32 [lists][piece_cap][group][kDim]
   size_t ml_bytes;       // float2 [lists][piece_cap][group]
   size_t count_bytes;    // int [lists] piece counts (padded)
   size_t total_bytes;
 };
 AttnPlan plan_attention(int batch, int n_q_heads, int n_kv_heads, int waves,
-                        int m_cap);
+                        int m_cap, int n_cu);
+
+// Compute units of the current device (queried once per device).
+int device_cu_count();
 
 hipError_t launch_decode_attn(const Method& m, bool use_mfma,
                               const AttnPlan& plan, float scale,
