@@ -16,7 +16,8 @@
  * Conventions shared by every call:
  *  - Pointers are DEVICE pointers unless a parameter says "host".  The caller
  *    owns every buffer; the library allocates nothing and keeps no state
- *    between calls except the calling thread's last error text.
+ *    between calls except the calling thread's last error text and, per
+ *    device, its compute-unit count (queried once).
  *  - bf16 values travel as their 16-bit patterns (uint16_t).
  *  - All work is enqueued asynchronously on the given HIP stream; a call
  *    returns once the work is enqueued.  Arguments are validated on the host
@@ -71,10 +72,11 @@ typedef enum rkv_status {
   RKV_ERR_HIP = 4           /* a HIP launch or copy failed; see rkv_last_error */
 } rkv_status;
 
-/* Attention kernel variants. */
+/* Selection modes (rkv_params.select_mode, see rkv_select). */
 #define RKV_SELECT_PER_HEAD 0
 #define RKV_SELECT_PER_SEQUENCE 1
 
+/* Attention kernel variants. */
 #define RKV_ATTN_AUTO 0
 #define RKV_ATTN_MFMA 1   /* query heads of a group packed against K tiles */
 #define RKV_ATTN_VALU 2   /* vector-ALU dot products, same memory schedule */
@@ -185,6 +187,11 @@ size_t rkv_select_workspace_size(const rkv_params* params, int32_t batch,
  *            (optional: NULL skips the merge)
  *   n_merged [batch][n_kv_heads] (required when merged is given)
  * prompt_lens [batch] may be NULL (then the dense switch uses lens).
+ * workspace >= rkv_select_workspace_size(params, batch, max_blocks) bytes
+ * (the scores, one fp32 per (b, h, block)); calls that overlap on one
+ * workspace race.  Two launches: a scoring pass spread over many compute
+ * units, then one top-k + merge workgroup per (b, h) (per b in the
+ * per-sequence mode).
  * Capacity rules, checked on the host: k_cap >= max_blocks when the dense
  * switch can fire (dense_boundary > 0 or topk_ppm = 10^6), else
  * k_cap >= ceil(max_blocks * topk_ppm / 10^6); m_cap >= max_blocks.
@@ -200,12 +207,13 @@ rkv_status rkv_select(const rkv_params* params, const uint16_t* q,
                       size_t workspace_bytes, hipStream_t stream);
 
 /*
- * rkv_append_select -- rkv_append_kv followed by rkv_select in ONE launch
- * (same arguments and results as the two calls in that order; reps is
- * written for a block the appended token completes).  The selection never
- * reads the appended token or that block's representation: the block
- * holding slot L - 1 is the sequence's last, which is always local.  For a
- * decode step this saves one launch and its memory round trips.
+ * rkv_append_select -- rkv_append_kv followed by rkv_select, with the
+ * append folded into the selection's scoring launch (same arguments and
+ * results as the two calls in that order; reps is written for a block the
+ * appended token completes).  The selection never reads the appended token
+ * or that block's representation: the block holding slot L - 1 is the
+ * sequence's last, which is always local.  For a decode step this saves one
+ * launch and its memory round trips.
  * Errors: as rkv_append_kv and rkv_select.
  */
 rkv_status rkv_append_select(const rkv_params* params, const uint16_t* k_new,
