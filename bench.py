@@ -48,8 +48,8 @@ COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 ATTN_SOURCE = os.path.join(ROOT, "sparse_retrieval_kv_amd", "csrc", "attn.hip")
 MEASURED_TRAFFIC = {
     # config: (sha256 prefix of attn.hip, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    2: ("12d21ee76f2d8f7f", 40064.1 + 720.0, 1040.0 + 16.0),
-    4: ("12d21ee76f2d8f7f", 506573.2 + 2391.0, 2080.6 + 256.0),
+    2: ("4acfc0f39d0f2ebf", 40064.1 + 720.0, 1040.0 + 16.0),
+    4: ("4acfc0f39d0f2ebf", 506573.2 + 2391.0, 2080.6 + 256.0),
 }
 METRIC = "decode attn steps/s and attended-KV HBM GB/s (% of peak) at 64K-128K ctx, 1 GPU"
 

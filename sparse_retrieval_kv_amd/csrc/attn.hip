@@ -10,15 +10,17 @@
 // Work partition.  Every merged block is cut into two 64-token halves
 // ("units"); the units of all (sequence, KV head) lists, taken in order,
 // form one range of T units that is split evenly over a fixed number W of
-// waves: wave w owns units [floor(wT/W), floor((w+1)T/W)).  A wave's range
-// meets one or a few lists; for each list it meets it writes one partial
-// (m, l, acc) to slot w + bh (unique: along the range both w and bh only
-// grow).  T is known only on the device, so every wave (and the combine)
-// derives the partition from n_merged itself: ragged batches stay balanced
-// and no host round trip is needed.  Within a list, a wave's loads are
-// software-pipelined: unit u+1's K tile is requested right after unit u's V
-// tile, so about 32 KiB per wave stay in flight while unit u's softmax and
-// PV products run (one wave per SIMD, 1024 waves on 256 compute units).
+// waves (default two per compute unit), taken in a virtual order that puts
+// the waves sharing a compute unit next to each other, so every compute
+// unit streams the same share.  A wave's range meets one or a few lists;
+// for each list it writes one partial (m, l, acc) into that list's own run
+// of slots, numbered along the list, and the wave holding a list's first
+// unit records how many pieces the list has.  T is known only on the
+// device, so every wave derives the partition from n_merged itself: ragged
+// batches stay balanced and no host round trip is needed.  Within a list, a
+// wave's loads are software-pipelined: unit u+1's K tile is requested right
+// after unit u's V tile, so about 32 KiB per wave stay in flight while unit
+// u's softmax and PV products run.
 //
 // MFMA math for one 64-token unit (query heads padded to 16):
 //   S^T[16 tokens x 16 heads] = K_tile[16 x 128] . Q^T[128 x 16]
