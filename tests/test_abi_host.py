@@ -3,10 +3,13 @@ every function include/rkv.h declares, returns the page's defaults, and
 rejects bad arguments before anything is enqueued."""
 
 import ctypes
+import os
 
 import pytest
 
 from sparse_retrieval_kv_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
 ODD = 0x10002
@@ -191,3 +194,27 @@ def test_binding_refuses_host_tensors(L):
     with pytest.raises(ValueError):
         B.merge_table(p, t.view(1, 4), t[:1], t.view(1, 1, 4), t[:2].view(1, 2),
                       t.view(1, 1, 4), t[:2].view(1, 2))
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """With no built library the product path raises instead of falling
+    back to anything else."""
+    import subprocess
+    import sys
+    code = ("import os, sys; sys.path.insert(0, os.getcwd()); "
+            "from sparse_retrieval_kv_amd import binding as B\n"
+            "try:\n    B.lib()\nexcept ImportError as e:\n    print('refused:', e)\n"
+            "else:\n    print('loaded')\n")
+    env = dict(os.environ, RKV_LIB=str(tmp_path / "missing" / "librkv.so"))
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env,
+                         capture_output=True, text=True, timeout=120)
+    assert "refused:" in out.stdout, out.stdout + out.stderr
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    out = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=ROOT,
+                         capture_output=True, text=True, timeout=300)
+    assert out.returncode == 2
+    assert "one GPU" in out.stderr
