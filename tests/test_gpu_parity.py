@@ -767,6 +767,46 @@ def test_per_sequence_selection_with_resident_host_tier():
         per_sequence_check(batch, sess, t, host=host)
 
 
+def random_case(seed):
+    """One seeded random configuration of the method and launch."""
+    rng = np.random.default_rng(7000 + seed)
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    hkv = int(rng.choice([1, 2, 4]))
+    bsz = int(rng.integers(1, 5))
+    ctx = tuple(int(x) for x in rng.integers(1, 24000, size=bsz))
+    spec = synth.custom(f"random{seed}", batch=bsz, n_q_heads=G * hkv, n_kv_heads=hkv,
+                        context=ctx, steps=2,
+                        init_tokens=int(rng.choice([0, 128, 256, 1000, 1024])),
+                        local_tokens=int(rng.choice([0, 1, 128, 1000, 7192])),
+                        topk_ppm=int(rng.choice([1, 50_000, 200_000, 999_999, 1_000_000])),
+                        dense_boundary=int(rng.choice([0, 0, 5000, 32768])),
+                        shuffle=bool(rng.integers(0, 2)), config_id=300 + seed)
+    impls = [B.ATTN_MFMA] + ([B.ATTN_VALU] if G in (1, 2, 4, 8) else [])
+    launch = dict(split_waves=int(rng.choice([0, 7, 64, 512, 1000])),
+                  attn_impl=int(rng.choice(impls)),
+                  select_mode=int(rng.choice([B.SELECT_PER_HEAD, B.SELECT_PER_SEQUENCE])))
+    return spec, launch
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_configurations(seed):
+    spec, launch = random_case(seed)
+    say(f"random configuration {seed}: {spec.batch} x {spec.context}, "
+        f"{spec.n_q_heads}/{spec.n_kv_heads}, init {spec.init_tokens}, "
+        f"local {spec.local_tokens}, ppm {spec.topk_ppm}, dense {spec.dense_boundary}, "
+        f"{launch}")
+    batch = synth.make_batch(spec, DEV)
+    prm, sess = make_session(batch, **launch)
+    prefill(batch, sess)
+    for t in range(2):
+        step(batch, sess, t)
+        torch.cuda.synchronize()
+        if launch["select_mode"] == B.SELECT_PER_SEQUENCE:
+            per_sequence_check(batch, sess, t)
+        else:
+            oracle_full_check(batch, sess, t)
+
+
 def test_append_select_equals_append_then_select():
     """The fused launch gives bit-identical pools, representations,
     selections and merged tables to rkv_append_kv followed by rkv_select."""
