@@ -278,6 +278,73 @@ def decode_attn(p: Params, q, k_pages, v_pages, merged, n_merged, lens, out,
         ws_bytes, _stream(q)))
 
 
+def _dyn(t, dtype, shape, name):
+    """Pointer of a per-step tensor whose dtype / shape / device were fixed
+    when the call was prepared (cheap checks only)."""
+    if t.dtype is not dtype or tuple(t.shape) != shape or not t.is_cuda \
+            or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous GPU {dtype} tensor of shape {shape}")
+    return t.data_ptr()
+
+
+class PreparedStep:
+    """The two per-step calls of a decode session with every buffer that
+    does not change between steps validated and converted once; a call then
+    re-reads only the per-step tensors (q, k_new, v_new, lens) and the
+    current stream.  Same arguments, same checks on the C side."""
+
+    def __init__(self, p: Params, k_pages, v_pages, reps, block_table, sel_ids,
+                 n_sel, merged, n_merged, prompt_lens, ws_select, out, ws_attn):
+        L = lib()
+        self._L = L
+        self._p = p
+        self._pp = ctypes.byref(p)
+        self._dev = k_pages.device
+        batch, max_blocks = block_table.shape
+        hq, hkv = p.n_q_heads, p.n_kv_heads
+        self._q_shape = (batch, hq, HEAD_DIM)
+        self._kv_shape = (batch, hkv, HEAD_DIM)
+        self._lens_shape = (batch,)
+        ws_sel = 0 if ws_select is None else ws_select.numel() * ws_select.element_size()
+        self._sel_args = (
+            _ptr(k_pages, torch.int16, "k_pages"), _ptr(v_pages, torch.int16, "v_pages"),
+            k_pages.shape[0], _ptr(reps, torch.float32, "reps"),
+            _ptr(block_table, torch.int32, "block_table"),
+            _ptr(prompt_lens, torch.int32, "prompt_lens"), batch, max_blocks,
+            _ptr(sel_ids, torch.int32, "sel_ids"), _ptr(n_sel, torch.int32, "n_sel"),
+            sel_ids.shape[-1], _ptr(merged, torch.int32, "merged"),
+            _ptr(n_merged, torch.int32, "n_merged"),
+            merged.shape[-1] if merged is not None else 0,
+            _ptr(ws_select, None, "workspace"), ws_sel)
+        self._attn_args = (
+            _ptr(k_pages, torch.int16, "k_pages"), _ptr(v_pages, torch.int16, "v_pages"),
+            k_pages.shape[0], _ptr(merged, torch.int32, "merged"),
+            _ptr(n_merged, torch.int32, "n_merged"), merged.shape[-1] if merged is not None else 0,
+            batch, _ptr(out, torch.float32, "out"), _ptr(ws_attn, None, "workspace"),
+            ws_attn.numel() * ws_attn.element_size())
+        # keep every buffer alive as long as the prepared call
+        self._keep = (k_pages, v_pages, reps, block_table, sel_ids, n_sel, merged,
+                      n_merged, prompt_lens, ws_select, out, ws_attn)
+
+    def append_select(self, q, k_new, v_new, lens):
+        (kp, vp, n_pages, reps, bt, plens, batch, max_blocks, sel, nsel, k_cap,
+         merged, nmerged, m_cap, ws, ws_bytes) = self._sel_args
+        _check(self._L.rkv_append_select(
+            self._pp, _dyn(k_new, torch.int16, self._kv_shape, "k_new"),
+            _dyn(v_new, torch.int16, self._kv_shape, "v_new"), kp, vp, n_pages,
+            _dyn(q, torch.int16, self._q_shape, "q"), reps, bt,
+            _dyn(lens, torch.int32, self._lens_shape, "lens"), plens, batch, max_blocks,
+            sel, nsel, k_cap, merged, nmerged, m_cap, ws, ws_bytes,
+            torch.cuda.current_stream(self._dev).cuda_stream))
+
+    def decode_attn(self, q, lens):
+        kp, vp, n_pages, merged, nmerged, m_cap, batch, out, ws, ws_bytes = self._attn_args
+        _check(self._L.rkv_decode_attn(
+            self._pp, _dyn(q, torch.int16, self._q_shape, "q"), kp, vp, n_pages,
+            merged, nmerged, m_cap, _dyn(lens, torch.int32, self._lens_shape, "lens"),
+            batch, out, ws, ws_bytes, torch.cuda.current_stream(self._dev).cuda_stream))
+
+
 def read_probe(buf, sink):
     """Stream-read `buf` once on the device (bandwidth measurement helper)."""
     _check(lib().rkv_read_probe(_ptr(buf, None, "buffer"),

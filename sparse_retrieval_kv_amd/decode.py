@@ -47,6 +47,15 @@ class DecodeSession:
             if ws else None
         wa = B.attn_workspace_size(prm, self.batch, self.m_cap)
         self.ws_attn = torch.empty(max(wa, 16), dtype=torch.uint8, device=dev)
+        self._fast = None  # per-step calls with the session buffers bound once
+
+    def _prepared(self) -> B.PreparedStep:
+        if self._fast is None:
+            self._fast = B.PreparedStep(self.p, self.k_pages, self.v_pages, self.reps,
+                                        self.block_table, self.sel_ids, self.n_sel,
+                                        self.merged, self.n_merged, self.prompt_lens,
+                                        self.ws_select, self.out, self.ws_attn)
+        return self._fast
 
     def build_reps(self, lens: torch.Tensor, block_begin: torch.Tensor | None = None):
         B.build_reps(self.p, self.k_pages, self.block_table, lens, self.reps,
@@ -62,16 +71,12 @@ class DecodeSession:
                  self.ws_select)
 
     def attend(self, q, lens):
-        B.decode_attn(self.p, q, self.k_pages, self.v_pages, self.merged,
-                      self.n_merged, lens, self.out, self.ws_attn)
+        self._prepared().decode_attn(q, lens)
         return self.out
 
     def append_select(self, q, k_new, v_new, lens):
-        """The append and the selection in one launch."""
-        B.append_select(self.p, k_new, v_new, self.k_pages, self.v_pages, q,
-                        self.reps, self.block_table, lens, self.sel_ids,
-                        self.n_sel, self.merged, self.n_merged, self.prompt_lens,
-                        self.ws_select)
+        """The append folded into the selection's launches."""
+        self._prepared().append_select(q, k_new, v_new, lens)
 
     def step(self, q, k_new, v_new, lens):
         """append + select (one launch) -> attend for one decode step;
