@@ -402,7 +402,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 K/V/q, fp32 accumulate",
+        "dtype": "bf16",
+        "dtype_detail": "bf16 K/V/q on MFMA, fp32 accumulation, softmax and output",
         "data": "synthetic (seeded N(0,1) bf16 K/V/q, planted blocks per config)",
         "config": {
             "workload": spec.name,

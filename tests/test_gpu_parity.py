@@ -11,6 +11,7 @@ Tolerances:
     relative L2 error <= 1e-4 (fp32 accumulation, weights kept to ~16 bits).
 """
 
+import os
 import sys
 
 import numpy as np
@@ -788,7 +789,10 @@ def random_case(seed):
     return spec, launch
 
 
-@pytest.mark.parametrize("seed", range(16))
+RANDOM_CASES = int(os.environ.get("RKV_RANDOM_CASES", "16"))
+
+
+@pytest.mark.parametrize("seed", range(RANDOM_CASES))
 def test_random_configurations(seed):
     spec, launch = random_case(seed)
     say(f"random configuration {seed}: {spec.batch} x {spec.context}, "
