@@ -14,10 +14,11 @@
 //     GB/s).  The group's query heads are summed once
 //     (sum_g q_g . r = (sum_g q_g) . r); eight lanes score one
 //     representation; the fp32 scores go to the workspace.  Extra workgroups append the decoded token meanwhile.
-//  2. topk_kernel: one 1024-thread workgroup per (sequence, KV head) -- or
-//     per sequence, with the scores of all KV heads summed, in the
-//     per-sequence selection mode -- holds the scores as order-preserving
-//     uint32 keys and the block-table entries in registers, finds the k-th largest
+//  2. topk_kernel: one 1024-thread workgroup per (sequence, KV head) -- in
+//     the per-sequence selection mode each of them sums the scores of all
+//     KV heads of its sequence, in head order, so all find the same set --
+//     holds the scores as order-preserving uint32 keys and the block-table
+//     entries in registers, finds the k-th largest
 //     key T by a 4-pass 8-bit radix select over an LDS histogram (wave-
 //     aggregated atomics), then keeps every key > T and the lowest-index
 //     keys == T with one workgroup scan, writing the kept ids ascending and
@@ -274,14 +275,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelArgs a) {
   __shared__ int sdig[3];
   const Method& m = a.m;
   const int tid = threadIdx.x, lane = tid & 63;
-  // per head: one workgroup per (b, h); per sequence: one per b, whose
-  // selection is written to every head's rows
-  const int b = m.per_sequence ? blockIdx.x : blockIdx.x / m.n_kv_heads;
-  const int bh = m.per_sequence ? b * m.n_kv_heads : blockIdx.x;
-  const int n_rows = m.per_sequence ? m.n_kv_heads : 1;
+  // one workgroup per (b, h).  Per sequence, every workgroup of sequence b
+  // sums the scores of all its heads in the same order, so all of them find
+  // the same selection; each writes its own head's rows.
+  const int b = blockIdx.x / m.n_kv_heads;
+  const int bh = blockIdx.x;
+  const int n_sum = m.per_sequence ? m.n_kv_heads : 1;
   const int max_blocks = a.max_blocks;
   const int32_t* trow = a.table + (int64_t)b * max_blocks;
-  const uint32_t* krow = a.keys + (int64_t)bh * max_blocks;
+  const uint32_t* krow =
+      a.keys + (int64_t)(m.per_sequence ? b * m.n_kv_heads : bh) * max_blocks;
 
   // --- requests independent of the length ---
   const int lraw = a.lens[b];
@@ -295,7 +298,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelArgs a) {
     tab[i] = in ? trow[j] : -1;
     // scores (raw fp32) -> order keys; per sequence, summed over the heads
     float sc = 0.f;
-    for (int hr = 0; hr < n_rows; ++hr)
+    for (int hr = 0; hr < n_sum; ++hr)
       sc += in ? __uint_as_float(krow[(int64_t)hr * max_blocks + j]) : 0.f;
     key[i] = order_key(sc);
   }
@@ -388,15 +391,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelArgs a) {
       const uint32_t rem = (uint32_t)remaining;
       const uint32_t pos = gt_before + (eq_before < rem ? eq_before : rem);
       if ((gt || (eq && eq_before < rem)) && pos < (uint32_t)k) {
-        for (int hr = 0; hr < n_rows; ++hr) srow[(int64_t)hr * a.k_cap + pos] = j;
+        srow[pos] = j;
         rank1[i] = (int)pos + 1;
       }
       gt_carry += tot & 0xffffu;
       eq_carry += tot >> 16;
     }
   } else {
-    for (int r = tid; r < k; r += kTopkThreads)
-      for (int hr = 0; hr < n_rows; ++hr) srow[(int64_t)hr * a.k_cap + r] = R.n_init + r;
+    for (int r = tid; r < k; r += kTopkThreads) srow[r] = R.n_init + r;
   }
 
   // merged page list from the block-table entries each thread holds
@@ -415,13 +417,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelArgs a) {
       } else if (rank1[i]) {
         dst = R.n_init + rank1[i] - 1;
       }
-      if (dst >= 0)
-        for (int hr = 0; hr < n_rows; ++hr) mrow[(int64_t)hr * a.m_cap + dst] = tab[i];
+      if (dst >= 0) mrow[dst] = tab[i];
     }
-    for (int hr = tid; hr < n_rows; hr += kTopkThreads)
-      a.n_merged[bh + hr] = R.n_init + k + (R.nb - lstart);
+    if (tid == 0) a.n_merged[bh] = R.n_init + k + (R.nb - lstart);
   }
-  for (int hr = tid; hr < n_rows; hr += kTopkThreads) a.n_sel[bh + hr] = k;
+  if (tid == 0) a.n_sel[bh] = k;
 }
 
 // Standalone merge from given selections.  Ids outside the offload range
@@ -494,8 +494,7 @@ hipError_t launch_select(const Method& m, const uint16_t* q, const float* reps,
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_kernel, dim3(m.per_sequence ? batch : groups),
-                     dim3(kTopkThreads), 0, stream, a);
+  hipLaunchKernelGGL(topk_kernel, dim3(groups), dim3(kTopkThreads), 0, stream, a);
   return hipGetLastError();
 }
 
