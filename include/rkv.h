@@ -321,26 +321,39 @@ size_t rkv_stage_workspace_size(const rkv_params* params, int32_t batch,
  * rounds keep many of the same blocks, so a block already held in HBM is
  * not loaded again: the result is that of rkv_stage_blocks followed by
  * rkv_merge_table with the same host table, with fewer bytes over the bus.
- * Staging slot r of (sequence b, KV head h) is the head-h slice of device
- * page stage_page0 + b * k_cap + r.  For every (b, h):
- *   slot_ids [batch][n_kv_heads][k_cap] device int32, IN/OUT: the logical
- *            block each slot holds (-1: none).  Fill it with -1 before the
- *            first call for a sequence (and whenever the host pools, the host
- *            table or the staging pages are changed by anyone else); leave
- *            it untouched between calls.
+ * Staging slot r (0 <= r < slot_cap) of (sequence b, KV head h) is the
+ * head-h slice of device page stage_page0 + b * slot_cap + r.  slot_cap must
+ * be at least the number of host-resident blocks a list keeps in one call
+ * (k_cap always suffices; ceil(n_off * topk_ppm / 10^6) suffices when no
+ * prompt is below the dense boundary).  A list that keeps more gives the
+ * blocks that found no slot page -1 (not attended) and reports
+ * n_staged = -1.
+ * For every (b, h):
+ *   slot_ids [batch][n_kv_heads][slot_cap] device int32, IN/OUT: the
+ *            logical block each slot holds (-1: none);
+ *   slot_cursor [batch][n_kv_heads] device int32, IN/OUT: the next slot to
+ *            fill.  Fill slot_ids with -1 and slot_cursor with 0 before the
+ *            first call for a sequence (and whenever the host pools, the
+ *            host table or the staging pages are changed by anyone else);
+ *            leave both untouched between calls.
  *   A kept host-resident block already held by a slot keeps that slot; the
  *   kept host-resident blocks not held take, in ascending block order, the
- *   slots whose blocks are no longer kept, in ascending slot order, and are
- *   copied there (K and V tiles of head h, 32 KiB each).  A slot not reused
- *   keeps its block, which then costs no copy if kept again later.
+ *   slots holding no kept block, first-in first-out (in slot order from the
+ *   cursor, which then moves past the last slot filled), and are copied
+ *   there (K and V tiles of head h, 32 KiB each).  A slot not reused keeps
+ *   its block, which then costs no copy if kept again later: with slot_cap
+ *   above the number of kept blocks, recently dropped blocks stay resident.
  *   merged / n_merged: as rkv_merge_table (init blocks, kept blocks, local
  *   blocks; kept host-resident blocks at their slot's page, other kept
  *   blocks at their block-table page).
- *   n_staged [batch][n_kv_heads] (optional, may be NULL): blocks copied.
- * host_table, host_k, host_v, n_host_pages, sel_ids, n_sel: as
- * rkv_stage_blocks; lens as rkv_select.  k_cap <= 8192, m_cap >= max_blocks.
+ *   n_staged [batch][n_kv_heads] (optional, may be NULL): blocks copied
+ *   (-1: slot_cap was too small for the kept blocks, see above).
+ * host_table, host_k, host_v, n_host_pages, sel_ids, n_sel, k_cap: as
+ * rkv_stage_blocks; lens as rkv_select.  1 <= slot_cap <= 8192,
+ * m_cap >= max_blocks; pages [stage_page0, stage_page0 + batch * slot_cap)
+ * must lie inside the device pools.
  * Two launches on `stream` (slot planner, then the copies); calls that
- * overlap on one slot_ids / workspace race.
+ * overlap on one slot state / workspace race.
  * Errors: RKV_ERR_INVALID_ARG, RKV_ERR_UNSUPPORTED, RKV_ERR_WORKSPACE,
  * RKV_ERR_HIP.
  */
@@ -350,7 +363,8 @@ rkv_status rkv_stage_resident(const rkv_params* params, const uint16_t* host_k,
                               const int32_t* block_table, int32_t max_blocks,
                               const int32_t* lens, const int32_t* sel_ids,
                               const int32_t* n_sel, int32_t k_cap, int32_t batch,
-                              int32_t* slot_ids, uint16_t* k_pages,
+                              int32_t slot_cap, int32_t* slot_ids,
+                              int32_t* slot_cursor, uint16_t* k_pages,
                               uint16_t* v_pages, int64_t n_pages,
                               int64_t stage_page0, int32_t* merged,
                               int32_t* n_merged, int32_t m_cap, int32_t* n_staged,

@@ -74,8 +74,8 @@ _SIGS = {
                                           _P, _P, _I64, _P]),
     "rkv_stage_workspace_size": (_SZ, [_PP, _I32, _I32]),
     "rkv_stage_resident": (ctypes.c_int, [_PP, _P, _P, _I64, _P, _P, _I32, _P, _P,
-                                          _P, _I32, _I32, _P, _P, _P, _I64, _I64, _P,
-                                          _P, _I32, _P, _P, _SZ, _P]),
+                                          _P, _I32, _I32, _I32, _P, _P, _P, _P, _I64,
+                                          _I64, _P, _P, _I32, _P, _P, _SZ, _P]),
     "rkv_attn_workspace_size": (_SZ, [_PP, _I32, _I32]),
     "rkv_decode_attn": (ctypes.c_int, [_PP, _P, _P, _P, _I64, _P, _P, _I32, _P, _I32,
                                        _P, _P, _SZ, _P]),
@@ -244,8 +244,8 @@ def stage_workspace_size(p: Params, batch: int, k_cap: int) -> int:
 
 
 def stage_resident(p: Params, host_k, host_v, host_table, block_table, lens,
-                   sel_ids, n_sel, slot_ids, k_pages, v_pages, stage_page0: int,
-                   merged, n_merged, workspace, n_staged=None):
+                   sel_ids, n_sel, slot_ids, slot_cursor, k_pages, v_pages,
+                   stage_page0: int, merged, n_merged, workspace, n_staged=None):
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().rkv_stage_resident(
         ctypes.byref(p), _host_ptr(host_k, "host_k"), _host_ptr(host_v, "host_v"),
@@ -253,7 +253,8 @@ def stage_resident(p: Params, host_k, host_v, host_table, block_table, lens,
         _ptr(block_table, torch.int32, "block_table"), block_table.shape[1],
         _ptr(lens, torch.int32, "lens"), _ptr(sel_ids, torch.int32, "sel_ids"),
         _ptr(n_sel, torch.int32, "n_sel"), sel_ids.shape[-1], n_sel.shape[0],
-        _ptr(slot_ids, torch.int32, "slot_ids"),
+        slot_ids.shape[-1], _ptr(slot_ids, torch.int32, "slot_ids"),
+        _ptr(slot_cursor, torch.int32, "slot_cursor"),
         _ptr(k_pages, torch.int16, "k_pages"), _ptr(v_pages, torch.int16, "v_pages"),
         k_pages.shape[0], stage_page0, _ptr(merged, torch.int32, "merged"),
         _ptr(n_merged, torch.int32, "n_merged"), merged.shape[-1],

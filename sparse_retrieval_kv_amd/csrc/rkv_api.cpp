@@ -393,7 +393,8 @@ rkv_status rkv_stage_resident(const rkv_params* params, const uint16_t* host_k,
                               const int32_t* block_table, int32_t max_blocks,
                               const int32_t* lens, const int32_t* sel_ids,
                               const int32_t* n_sel, int32_t k_cap, int32_t batch,
-                              int32_t* slot_ids, uint16_t* k_pages,
+                              int32_t slot_cap, int32_t* slot_ids,
+                              int32_t* slot_cursor, uint16_t* k_pages,
                               uint16_t* v_pages, int64_t n_pages,
                               int64_t stage_page0, int32_t* merged,
                               int32_t* n_merged, int32_t m_cap, int32_t* n_staged,
@@ -407,18 +408,20 @@ rkv_status rkv_stage_resident(const rkv_params* params, const uint16_t* host_k,
   RKV_TRY(check_pool(host_k, n_host_pages, "host_k"));
   RKV_TRY(check_pool(host_v, n_host_pages, "host_v"));
   RKV_REQUIRE(host_table && block_table && lens && sel_ids && n_sel && slot_ids &&
-                  merged && n_merged,
+                  slot_cursor && merged && n_merged,
               RKV_ERR_INVALID_ARG, "a required pointer is NULL");
   RKV_REQUIRE(k_cap >= 1 && k_cap <= RKV_MAX_BLOCKS, RKV_ERR_INVALID_ARG,
               "k_cap %d outside [1, %d]", k_cap, RKV_MAX_BLOCKS);
+  RKV_REQUIRE(slot_cap >= 1 && slot_cap <= RKV_MAX_BLOCKS, RKV_ERR_INVALID_ARG,
+              "slot_cap %d outside [1, %d]", slot_cap, RKV_MAX_BLOCKS);
   RKV_REQUIRE(m_cap >= max_blocks, RKV_ERR_INVALID_ARG,
               "m_cap %d below max_blocks %d", m_cap, max_blocks);
   RKV_REQUIRE(stage_page0 >= 0 &&
-                  stage_page0 + (int64_t)batch * k_cap <= n_pages &&
-                  stage_page0 + (int64_t)batch * k_cap <= (int64_t)INT32_MAX,
+                  stage_page0 + (int64_t)batch * slot_cap <= n_pages &&
+                  stage_page0 + (int64_t)batch * slot_cap <= (int64_t)INT32_MAX,
               RKV_ERR_INVALID_ARG,
               "staging pages [%lld, +%lld) do not fit in the %lld-page pool",
-              (long long)stage_page0, (long long)batch * k_cap,
+              (long long)stage_page0, (long long)batch * slot_cap,
               (long long)n_pages);
   const size_t need = rkv_stage_workspace_size(params, batch, k_cap);
   RKV_REQUIRE(workspace_bytes >= need && (need == 0 || workspace),
@@ -431,7 +434,8 @@ rkv_status rkv_stage_resident(const rkv_params* params, const uint16_t* host_k,
   return hip_status(rkv::launch_stage_resident(
                         m, dev_view[0], dev_view[1], n_host_pages, host_table,
                         block_table, lens, max_blocks, sel_ids, n_sel, k_cap,
-                        batch, slot_ids, k_pages, v_pages, n_pages, stage_page0,
+                        batch, slot_cap, slot_ids, slot_cursor, k_pages, v_pages,
+                        n_pages, stage_page0,
                         merged, n_merged, m_cap, n_staged, workspace, stream),
                     "rkv_stage_resident launch");
 }

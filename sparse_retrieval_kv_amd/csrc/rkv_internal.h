@@ -86,7 +86,8 @@ hipError_t launch_stage_resident(const Method& m, const uint16_t* host_k,
                                  const int32_t* host_table, const int32_t* table,
                                  const int32_t* lens, int max_blocks,
                                  const int32_t* sel_ids, const int32_t* n_sel,
-                                 int k_cap, int batch, int32_t* slot_ids,
+                                 int k_cap, int batch, int slot_cap,
+                                 int32_t* slot_ids, int32_t* slot_cursor,
                                  uint16_t* k_pages, uint16_t* v_pages,
                                  int64_t n_pages, int64_t stage_page0,
                                  int32_t* merged, int32_t* n_merged, int m_cap,

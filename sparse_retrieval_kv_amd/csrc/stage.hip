@@ -81,13 +81,17 @@ __global__ __launch_bounds__(kStageThreads) void stage_kernel(
 
 
 // ---------------------------------------------------------------------------
-// Residency across steps.  Staging slot r of (sequence b, KV head h) is the
-// head-h slice of page stage_page0 + b * k_cap + r; slot_ids[b][h][r] names
-// the logical block whose K/V the slot holds (-1: none).  A kept block that
-// already sits in a slot is not copied again; the blocks new to the kept set
-// take, in ascending order, the slots whose blocks were dropped, in
-// ascending slot order.  Results are those of staging every kept block: the
-// merged table points each kept host-resident block at its slot.
+// Residency across steps.  Staging slot r (of slot_cap >= k_cap) of
+// (sequence b, KV head h) is the head-h slice of page
+// stage_page0 + b * slot_cap + r; slot_ids[b][h][r] names the logical block
+// whose K/V the slot holds (-1: none).  A kept block that already sits in a
+// slot is not copied again; the blocks new to the kept set take, in
+// ascending order, the slots that hold no kept block, first-in first-out:
+// in slot order starting at the list's cursor, which then moves past the
+// last slot filled.  With more slots than kept blocks, a dropped block
+// stays resident for a while and costs no copy if it is kept again.
+// Results are those of staging every kept block: the merged table points
+// each kept host-resident block at its slot.
 // ---------------------------------------------------------------------------
 constexpr int kPlanThreads = 256;
 constexpr int kPlanWaves = kPlanThreads / 64;
@@ -101,7 +105,9 @@ struct ResArgs {
   const int32_t* sel_ids;
   const int32_t* n_sel;
   int k_cap;
+  int slot_cap;
   int32_t* slot_ids;
+  int32_t* slot_cursor;  // [bh]: next slot to fill, first-in first-out
   int2* copies;       // [bh][k_cap]: (block, slot) to copy
   int32_t* n_copies;  // [bh]
   int32_t* n_staged;  // optional copy of n_copies
@@ -144,6 +150,7 @@ __global__ __launch_bounds__(kPlanThreads) void stage_plan_kernel(ResArgs a) {
   const int b = bh / a.n_kv;
   const int max_blocks = a.max_blocks;
   const int k_cap = a.k_cap;
+  const int S = a.slot_cap;
   const int L = clamp_len(a.lens[b], max_blocks * kBlock);
   const Regions R = regions_of(L, a.init_tokens, a.local_tokens);
   int k = a.n_sel[bh];
@@ -153,9 +160,11 @@ __global__ __launch_bounds__(kPlanThreads) void stage_plan_kernel(ResArgs a) {
   const int32_t* trow = a.table + (int64_t)b * max_blocks;
   const int32_t* hrow = a.host_table + (int64_t)b * max_blocks;
   const int32_t* srow = a.sel_ids + (int64_t)bh * k_cap;
-  int32_t* slots = a.slot_ids + (int64_t)bh * k_cap;
+  int32_t* slots = a.slot_ids + (int64_t)bh * S;
   int32_t* mrow = a.merged + (int64_t)bh * a.m_cap;
-  const int64_t page0 = a.stage_page0 + (int64_t)b * k_cap;
+  const int64_t page0 = a.stage_page0 + (int64_t)b * S;
+  int cursor = a.slot_cursor[bh];
+  cursor = (cursor < 0 || cursor >= S) ? 0 : cursor;
   auto in_off = [&](int j) { return j >= R.n_init && j < R.n_init + R.n_off; };
   auto bit = [](const uint32_t* bits, int j) { return (bits[j >> 5] >> (j & 31)) & 1u; };
 
@@ -174,12 +183,13 @@ __global__ __launch_bounds__(kPlanThreads) void stage_plan_kernel(ResArgs a) {
   }
   __syncthreads();
   // slots whose block stays kept keep it (one slot per block); the others
-  // are free, in ascending slot order
+  // are free, listed first-in first-out (slot order from the cursor)
   int n_free = 0;
-  for (int base = 0; base < k_cap; base += kPlanThreads) {
-    const int r = base + tid;
+  for (int base = 0; base < S; base += kPlanThreads) {
+    const int i = base + tid;
+    const int r = i < S ? (cursor + i) % S : 0;
     bool is_free = false;
-    if (r < k_cap) {
+    if (i < S) {
       const int j = slots[r];
       bool keep = j >= 0 && j < max_blocks && in_off(j) && bit(selbits, j) &&
                   hrow[j] >= 0;
@@ -227,16 +237,18 @@ __global__ __launch_bounds__(kPlanThreads) void stage_plan_kernel(ResArgs a) {
     crow[i] = make_int2(j, r);
     mrow[R.n_init + q] = (int32_t)(page0 + r);
   }
-  // (cannot happen with k <= k_cap; kept blocks without a slot are skipped)
+  // more kept host blocks than slots (slot_cap below the kept count): the
+  // blocks without a slot get page -1 and the list reports n_staged = -1
   for (int i = n_cp + tid; i < n_new; i += kPlanThreads)
     mrow[R.n_init + new_ranks[i]] = -1;
   // a free slot that is not reused keeps its block's data and its id, so
   // the block costs no copy if it is kept again later
+  if (tid == 0 && n_cp > 0) a.slot_cursor[bh] = (free_slots[n_cp - 1] + 1) % S;
   const int cnt = write_fixed_entries_stage(R, k, trow, mrow);
   if (tid == 0) {
     a.n_merged[bh] = cnt;
     a.n_copies[bh] = n_cp;
-    if (a.n_staged) a.n_staged[bh] = n_cp;
+    if (a.n_staged) a.n_staged[bh] = n_new > n_cp ? -1 : n_cp;
   }
 }
 
@@ -246,7 +258,7 @@ __global__ __launch_bounds__(kStageThreads) void stage_copy_kernel(
     const uint4* __restrict__ host_k, const uint4* __restrict__ host_v,
     int64_t n_host_pages, const int32_t* __restrict__ host_table,
     int max_blocks, const int2* __restrict__ copies,
-    const int32_t* __restrict__ n_copies, int k_cap, int n_kv,
+    const int32_t* __restrict__ n_copies, int k_cap, int slot_cap, int n_kv,
     uint4* __restrict__ k_pages, uint4* __restrict__ v_pages, int64_t n_pages,
     int64_t stage_page0) {
   const int64_t item = blockIdx.x;  // (bh, i), i fastest
@@ -255,10 +267,10 @@ __global__ __launch_bounds__(kStageThreads) void stage_copy_kernel(
   const int b = bh / n_kv, h = bh - b * n_kv;
   if (i >= n_copies[bh]) return;
   const int2 c = copies[(int64_t)bh * k_cap + i];
-  if (c.x < 0 || c.x >= max_blocks || c.y < 0 || c.y >= k_cap) return;
+  if (c.x < 0 || c.x >= max_blocks || c.y < 0 || c.y >= slot_cap) return;
   const int hp = host_table[(int64_t)b * max_blocks + c.x];
   if ((uint64_t)(int64_t)hp >= (uint64_t)n_host_pages) return;
-  const int64_t dst_page = stage_page0 + (int64_t)b * k_cap + c.y;
+  const int64_t dst_page = stage_page0 + (int64_t)b * slot_cap + c.y;
   if (dst_page < 0 || dst_page >= n_pages) return;
   copy_tiles(host_k, host_v, ((int64_t)hp * n_kv + h) * kTile16, k_pages, v_pages,
              (dst_page * n_kv + h) * kTile16);
@@ -319,7 +331,8 @@ hipError_t launch_stage_resident(const Method& m, const uint16_t* host_k,
                                  const int32_t* host_table, const int32_t* table,
                                  const int32_t* lens, int max_blocks,
                                  const int32_t* sel_ids, const int32_t* n_sel,
-                                 int k_cap, int batch, int32_t* slot_ids,
+                                 int k_cap, int batch, int slot_cap,
+                                 int32_t* slot_ids, int32_t* slot_cursor,
                                  uint16_t* k_pages, uint16_t* v_pages,
                                  int64_t n_pages, int64_t stage_page0,
                                  int32_t* merged, int32_t* n_merged, int m_cap,
@@ -338,7 +351,9 @@ hipError_t launch_stage_resident(const Method& m, const uint16_t* host_k,
   a.sel_ids = sel_ids;
   a.n_sel = n_sel;
   a.k_cap = k_cap;
+  a.slot_cap = slot_cap;
   a.slot_ids = slot_ids;
+  a.slot_cursor = slot_cursor;
   a.copies = static_cast<int2*>(workspace);
   a.n_copies = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
                                           (size_t)lists * k_cap * sizeof(int2));
@@ -354,7 +369,7 @@ hipError_t launch_stage_resident(const Method& m, const uint16_t* host_k,
   hipLaunchKernelGGL(stage_copy_kernel, dim3((unsigned)items), dim3(kStageThreads), 0,
                      stream, reinterpret_cast<const uint4*>(host_k),
                      reinterpret_cast<const uint4*>(host_v), n_host_pages, host_table,
-                     max_blocks, a.copies, a.n_copies, k_cap, m.n_kv_heads,
+                     max_blocks, a.copies, a.n_copies, k_cap, slot_cap, m.n_kv_heads,
                      reinterpret_cast<uint4*>(k_pages), reinterpret_cast<uint4*>(v_pages),
                      n_pages, stage_page0);
   return hipGetLastError();

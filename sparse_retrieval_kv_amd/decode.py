@@ -99,19 +99,33 @@ class HostTierSession(DecodeSession):
     offload blocks from then on."""
 
     def __init__(self, prm: B.Params, k_pages, v_pages, block_table,
-                 prompt_lens=None, side_stream=True, resident=True):
+                 prompt_lens=None, side_stream=True, resident=True, slot_cap=None):
         super().__init__(prm, k_pages, v_pages, block_table, prompt_lens)
         self.host_k = self.host_v = self.host_table = None
-        self.stage_page0 = k_pages.shape[0] - self.batch * self.k_cap
+        # staging slots per (sequence, KV head): k_cap by default (always
+        # enough); a caller that knows its largest kept count (no prompt
+        # below the dense boundary) may size them from that.  The last
+        # batch * max(slot_cap, k_cap) pages of the device pools are the
+        # staging area and must not hold any page the block table uses.
+        self.slot_cap = self.k_cap if slot_cap is None else int(slot_cap)
+        if self.slot_cap < 1:
+            raise ValueError("slot_cap must be >= 1")
+        area = self.batch * max(self.slot_cap, self.k_cap)
+        self.stage_page0 = k_pages.shape[0] - area
         if self.stage_page0 < 0:
             raise ValueError("the device pools have no room for staging pages")
+        used = int(block_table.max().item()) if block_table.numel() else -1
+        if used >= self.stage_page0:
+            raise ValueError(f"staging pages [{self.stage_page0}, {k_pages.shape[0]}) "
+                             f"overlap page {used} of the block table")
         self.side = torch.cuda.Stream(device=k_pages.device) if side_stream else None
         # residency across steps: the block each staging slot holds
         self.resident = resident
         dev = k_pages.device
         n_kv = prm.n_kv_heads
-        self.slot_ids = torch.full((self.batch, n_kv, self.k_cap), -1,
+        self.slot_ids = torch.full((self.batch, n_kv, self.slot_cap), -1,
                                    dtype=torch.int32, device=dev)
+        self.slot_cursor = torch.zeros((self.batch, n_kv), dtype=torch.int32, device=dev)
         self.n_staged = torch.zeros((self.batch, n_kv), dtype=torch.int32, device=dev)
         ws = B.stage_workspace_size(prm, self.batch, self.k_cap)
         self.ws_stage = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
@@ -140,6 +154,7 @@ class HostTierSession(DecodeSession):
     def reset_residency(self):
         """Forget what the staging slots hold (new sequences or host pools)."""
         self.slot_ids.fill_(-1)
+        self.slot_cursor.zero_()
 
     def select(self, q, lens):
         # the selection only: the merged table is built after staging
@@ -150,7 +165,7 @@ class HostTierSession(DecodeSession):
         if self.resident:
             B.stage_resident(self.p, self.host_k, self.host_v, self.host_table,
                              self.block_table, lens, self.sel_ids, self.n_sel,
-                             self.slot_ids, self.k_pages, self.v_pages,
+                             self.slot_ids, self.slot_cursor, self.k_pages, self.v_pages,
                              self.stage_page0, self.merged, self.n_merged,
                              self.ws_stage, self.n_staged)
             return

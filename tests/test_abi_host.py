@@ -143,18 +143,24 @@ def test_stage_resident_validation(L):
     assert need >= 4 * 8 * 100 * 8 + 4 * 8 * 4
 
     def res(stage_page0=0, n_pages=1000, k_cap=100, batch=4, host_k=FAKE,
-            slot_ids=FAKE, m_cap=200, ws_bytes=None, merged=FAKE):
+            slot_ids=FAKE, slot_cursor=FAKE, slot_cap=None, m_cap=200,
+            ws_bytes=None, merged=FAKE):
         ws = need if ws_bytes is None else ws_bytes
+        sc = k_cap if slot_cap is None else slot_cap
         return L.rkv_stage_resident(ctypes.byref(p), host_k, FAKE, 50, FAKE, FAKE,
-                                    200, FAKE, FAKE, FAKE, k_cap, batch, slot_ids,
-                                    FAKE, FAKE, n_pages, stage_page0, merged, FAKE,
-                                    m_cap, None, FAKE, ws, None)
+                                    200, FAKE, FAKE, FAKE, k_cap, batch, sc, slot_ids,
+                                    slot_cursor, FAKE, FAKE, n_pages, stage_page0,
+                                    merged, FAKE, m_cap, None, FAKE, ws, None)
 
     assert res(stage_page0=601) == B.RKV_ERR_INVALID_ARG   # 601 + 400 > 1000
     assert b"staging" in L.rkv_last_error()
+    assert res(slot_cap=200, stage_page0=201) == B.RKV_ERR_INVALID_ARG  # 201 + 800
+    assert res(slot_cap=0) == B.RKV_ERR_INVALID_ARG
+    assert res(slot_cap=8193, n_pages=10**6) == B.RKV_ERR_INVALID_ARG
     assert res(k_cap=0) == B.RKV_ERR_INVALID_ARG
     assert res(k_cap=8193, n_pages=10**6) == B.RKV_ERR_INVALID_ARG
     assert res(slot_ids=None) == B.RKV_ERR_INVALID_ARG
+    assert res(slot_cursor=None) == B.RKV_ERR_INVALID_ARG
     assert res(merged=None) == B.RKV_ERR_INVALID_ARG
     assert res(m_cap=199) == B.RKV_ERR_INVALID_ARG
     assert res(host_k=ODD) == B.RKV_ERR_INVALID_ARG

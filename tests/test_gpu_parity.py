@@ -495,17 +495,19 @@ def test_valu_variant_matches_oracle_and_mfma(hq, hkv):
     assert np.allclose(outs[B.ATTN_MFMA], outs[B.ATTN_VALU], rtol=1e-4, atol=1e-5)
 
 
-def make_host_session(spec, resident=True, **pkw):
+def make_host_session(spec, resident=True, slot_mult=1, slot_cap=None, **pkw):
     """Host-tier session: prefill representations are built with every block
     in HBM, then the offload blocks move to pinned host memory."""
     max_blocks = -(-(max(spec.context) + spec.steps - 1) // 128)
-    batch = synth.make_batch(spec, DEV, extra_pages=spec.batch * max_blocks)
+    batch = synth.make_batch(spec, DEV, extra_pages=slot_mult * spec.batch * max_blocks)
     kw = dict(init_tokens=spec.init_tokens, local_tokens=spec.local_tokens,
               topk_ppm=spec.topk_ppm, dense_boundary=spec.dense_boundary)
     kw.update(pkw)
     prm = B.params(spec.n_q_heads, spec.n_kv_heads, **kw)
+    k_cap = max(1, B.topk_capacity(prm, max_blocks))
     sess = HostTierSession(prm, batch.k_pages, batch.v_pages, batch.block_table,
-                           i32(batch.context), resident=resident)
+                           i32(batch.context), resident=resident,
+                           slot_cap=slot_mult * k_cap if slot_cap is None else slot_cap)
     assert sess.stage_page0 >= batch.n_pages  # staging pages are the extra ones
     prefill(batch, sess)
     torch.cuda.synchronize()
@@ -532,33 +534,42 @@ def test_host_tier_small(resident):
         oracle_full_check(batch, sess, t, host=host)
 
 
-def mirror_residency(slots, kept, on_host):
+def mirror_residency(slots, cursor, kept, on_host):
     """The slot policy of rkv_stage_resident, restated: slots holding a kept
-    host block keep it; the other kept host blocks, ascending, take the
-    remaining slots, ascending.  Returns the blocks copied."""
+    host block keep it; the other kept host blocks, ascending, take the slots
+    holding no kept block in slot order from the cursor, which then moves
+    past the last slot filled.  Returns (blocks copied, new cursor)."""
+    S = len(slots)
     held = {}
     for r, j in enumerate(slots):
         if j >= 0 and j in kept and on_host[j] and j not in held:
             held[j] = r
-    free = [r for r in range(len(slots)) if r not in held.values()]
-    new = [j for j in kept if on_host[j] and j not in held]
-    for j, r in zip(new, free):
+    free = [(cursor + i) % S for i in range(S) if (cursor + i) % S not in held.values()]
+    new = [j for j in sorted(kept) if on_host[j] and j not in held]
+    n = min(len(new), len(free))
+    for j, r in zip(new[:n], free[:n]):
         slots[r] = j
-    return new[:len(free)]
+    if n:
+        cursor = (free[n - 1] + 1) % S
+    return new[:n], cursor
 
 
-def test_host_tier_residency_matches_full_staging():
+@pytest.mark.parametrize("slot_mult", [1, 2])
+def test_host_tier_residency_matches_full_staging(slot_mult):
     """Residency changes which bytes move, not the results: every step's
     output and selection equal those of staging every kept block, and the
-    slot state, copy counts and merged page ids follow the stated policy."""
+    slot state, copy counts and merged page ids follow the stated policy
+    (with k_cap slots, and with twice as many)."""
     spec = synth.scaled(synth.CONFIGS[5], batch=2, context=(20000, 23000), steps=6,
                         plant_range=(8, 90), plant_count=5, local_tokens=7192,
-                        dense_boundary=0, config_id=104)
-    say("host tier residency vs full staging")
-    batch_r, host_r, sess_r = make_host_session(spec, resident=True)
+                        topk_ppm=200_000, dense_boundary=0, config_id=104)
+    say(f"host tier residency vs full staging (slots {slot_mult} x k_cap)")
+    batch_r, host_r, sess_r = make_host_session(spec, resident=True, slot_mult=slot_mult)
     batch_f, _, sess_f = make_host_session(spec, resident=False)
-    k_cap = sess_r.k_cap
-    slots = {(b, h): [-1] * k_cap for b in range(2) for h in range(8)}
+    k_cap, S = sess_r.k_cap, sess_r.slot_cap
+    assert S == slot_mult * k_cap
+    slots = {(b, h): [-1] * S for b in range(2) for h in range(8)}
+    cursors = {(b, h): 0 for b in range(2) for h in range(8)}
     kept_total = copied_total = 0
     for t in range(6):
         step(batch_r, sess_r, t)
@@ -569,6 +580,7 @@ def test_host_tier_residency_matches_full_staging():
         sel = sess_r.sel_ids.cpu().numpy()
         n_sel = sess_r.n_sel.cpu().numpy()
         slot_gpu = sess_r.slot_ids.cpu().numpy()
+        cur_gpu = sess_r.slot_cursor.cpu().numpy()
         staged = sess_r.n_staged.cpu().numpy()
         merged = sess_r.merged.cpu().numpy()
         lens = batch_r.lens_at(t)
@@ -578,19 +590,47 @@ def test_host_tier_residency_matches_full_staging():
             for h in range(8):
                 kept = [int(j) for j in sel[b, h, :n_sel[b, h]]]
                 assert np.array_equal(kept, sess_f.sel_ids.cpu().numpy()[b, h, :n_sel[b, h]])
-                new = mirror_residency(slots[(b, h)], set(kept), on_host)
+                new, cursors[(b, h)] = mirror_residency(slots[(b, h)], cursors[(b, h)],
+                                                        set(kept), on_host)
                 assert slot_gpu[b, h].tolist() == slots[(b, h)], (t, b, h)
+                assert cur_gpu[b, h] == cursors[(b, h)], (t, b, h)
                 assert staged[b, h] == len(new), (t, b, h)
                 for q, j in enumerate(kept):
                     if on_host[j]:
                         r = slots[(b, h)].index(j)
-                        assert merged[b, h, n_init + q] == sess_r.stage_page0 + b * k_cap + r
+                        assert merged[b, h, n_init + q] == sess_r.stage_page0 + b * S + r
                     else:
                         assert merged[b, h, n_init + q] == batch_r.table_np[b, j]
                 if t > 0:
                     kept_total += sum(1 for j in kept if on_host[j])
                     copied_total += len(new)
     assert copied_total < kept_total
+
+
+def test_host_tier_too_few_slots_is_reported():
+    """slot_cap below the kept count: the blocks that find no slot are left
+    out (page -1) and every such list reports n_staged = -1."""
+    spec = synth.scaled(synth.CONFIGS[5], batch=2, context=(20000, 23000), steps=1,
+                        plant_range=(8, 90), plant_count=5, local_tokens=7192,
+                        dense_boundary=0, config_id=109)
+    say("host tier with too few staging slots")
+    batch, host, sess = make_host_session(spec, resident=True, slot_cap=3)
+    step(batch, sess, 0)
+    torch.cuda.synchronize()
+    staged = sess.n_staged.cpu().numpy()
+    merged = sess.merged.cpu().numpy()
+    sel = sess.sel_ids.cpu().numpy()
+    n_sel = sess.n_sel.cpu().numpy()
+    lens = batch.lens_at(0)
+    for b in range(2):
+        on_host = host.host_table_np[b] >= 0
+        n_init = min(8, -(-int(lens[b]) // 128))
+        for h in range(8):
+            kept = [int(j) for j in sel[b, h, :n_sel[b, h]]]
+            n_host = sum(1 for j in kept if on_host[j])
+            assert n_host > 3 and staged[b, h] == -1, (b, h)
+            pages = [int(merged[b, h, n_init + q]) for q, j in enumerate(kept) if on_host[j]]
+            assert sum(p >= 0 for p in pages) == 3 and pages.count(-1) == n_host - 3
 
 
 def test_offload_prefill_native():
