@@ -279,27 +279,32 @@ __global__ __launch_bounds__(kStageThreads) void stage_copy_kernel(
 // Prefill-time offload: item (b, j, h) copies head h of the device page of
 // offload block j of sequence b (blocks [n_init, local_start) for its
 // length) to host page host_table[b][j] of the pinned pools, K and V tiles,
-// every load issued before the first store.
+// every load issued before the first store.  The copies are bound by the
+// host link, so a small grid walks the items: the rest of the GPU stays free
+// for the representation build that runs beside it.
 __global__ __launch_bounds__(kStageThreads) void offload_kernel(
     const uint4* __restrict__ k_pages, const uint4* __restrict__ v_pages,
     int64_t n_pages, const int32_t* __restrict__ table, int max_blocks,
-    const int32_t* __restrict__ lens, int n_kv, int init_tokens, int local_tokens,
-    const int32_t* __restrict__ host_table, uint4* __restrict__ host_k,
-    uint4* __restrict__ host_v, int64_t n_host_pages) {
-  const int64_t item = blockIdx.x;  // (b, j, h), h fastest
-  const int h = (int)(item % n_kv);
-  const int64_t rest = item / n_kv;
-  const int j = (int)(rest % max_blocks);
-  const int b = (int)(rest / max_blocks);
-  const int L = clamp_len(lens[b], max_blocks * kBlock);
-  const Regions R = regions_of(L, init_tokens, local_tokens);
-  if (j < R.n_init || j >= R.n_init + R.n_off) return;
-  const int hp = host_table[(int64_t)b * max_blocks + j];
-  if ((uint64_t)(int64_t)hp >= (uint64_t)n_host_pages) return;
-  const int page = table[(int64_t)b * max_blocks + j];
-  if ((uint64_t)(int64_t)page >= (uint64_t)n_pages) return;
-  copy_tiles(k_pages, v_pages, ((int64_t)page * n_kv + h) * kTile16, host_k, host_v,
-             ((int64_t)hp * n_kv + h) * kTile16);
+    const int32_t* __restrict__ lens, int batch, int n_kv, int init_tokens,
+    int local_tokens, const int32_t* __restrict__ host_table,
+    uint4* __restrict__ host_k, uint4* __restrict__ host_v, int64_t n_host_pages) {
+  const int64_t items = (int64_t)batch * max_blocks * n_kv;
+  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+    // (b, j, h), h fastest
+    const int h = (int)(item % n_kv);
+    const int64_t rest = item / n_kv;
+    const int j = (int)(rest % max_blocks);
+    const int b = (int)(rest / max_blocks);
+    const int L = clamp_len(lens[b], max_blocks * kBlock);
+    const Regions R = regions_of(L, init_tokens, local_tokens);
+    if (j < R.n_init || j >= R.n_init + R.n_off) continue;
+    const int hp = host_table[(int64_t)b * max_blocks + j];
+    if ((uint64_t)(int64_t)hp >= (uint64_t)n_host_pages) continue;
+    const int page = table[(int64_t)b * max_blocks + j];
+    if ((uint64_t)(int64_t)page >= (uint64_t)n_pages) continue;
+    copy_tiles(k_pages, v_pages, ((int64_t)page * n_kv + h) * kTile16, host_k, host_v,
+               ((int64_t)hp * n_kv + h) * kTile16);
+  }
 }
 
 }  // namespace
@@ -383,11 +388,14 @@ hipError_t launch_offload(const Method& m, const uint16_t* k_pages,
                           hipStream_t stream) {
   const int64_t items = (int64_t)batch * max_blocks * m.n_kv_heads;
   if (items == 0) return hipSuccess;
-  hipLaunchKernelGGL(offload_kernel, dim3((unsigned)items), dim3(kStageThreads), 0,
+  // 64 workgroups keep 4 MiB of copies in flight, far more than the host
+  // link needs, and leave the other compute units free
+  const int64_t wgs = items < 64 ? items : 64;
+  hipLaunchKernelGGL(offload_kernel, dim3((unsigned)wgs), dim3(kStageThreads), 0,
                      stream, reinterpret_cast<const uint4*>(k_pages),
                      reinterpret_cast<const uint4*>(v_pages), n_pages, table,
-                     max_blocks, lens, m.n_kv_heads, m.init_tokens, m.local_tokens,
-                     host_table, reinterpret_cast<uint4*>(host_k),
+                     max_blocks, lens, batch, m.n_kv_heads, m.init_tokens,
+                     m.local_tokens, host_table, reinterpret_cast<uint4*>(host_k),
                      reinterpret_cast<uint4*>(host_v), n_host_pages);
   return hipGetLastError();
 }

@@ -134,21 +134,27 @@ class HostTierSession(DecodeSession):
         self.host_k, self.host_v, self.host_table = host_k, host_v, host_table
         self.reset_residency()
 
-    def offload_prefill(self, host_k, host_v, host_table, lens):
-        """Hand a prefilled batch over to the host tier: the offload-region
-        pages go to the pinned pools (rkv_offload_blocks, side stream) while
-        the representations of the complete blocks are built (main stream);
-        the main stream then waits for the copies.  `lens` = tokens
-        prefilled per sequence."""
+    def offload_prefill(self, host_k, host_v, host_table, lens, concurrent=False):
+        """Hand a prefilled batch over to the host tier: the representations
+        of the complete blocks are built, then the offload-region pages go to
+        the pinned pools (rkv_offload_blocks).  `lens` = tokens prefilled per
+        sequence.  With `concurrent`, the copies run on the side stream while
+        the representations are built; that is slower on MI355X (a kernel
+        writing host memory over the bus holds up the HBM reads of the
+        other compute units), so it is off by default."""
         dev = self.k_pages.device
         main = torch.cuda.current_stream(dev)
-        side = self.side if self.side is not None else main
-        side.wait_stream(main)
-        with torch.cuda.stream(side):
+        if concurrent and self.side is not None:
+            self.side.wait_stream(main)
+            with torch.cuda.stream(self.side):
+                B.offload_blocks(self.p, self.k_pages, self.v_pages, self.block_table,
+                                 lens, host_table, host_k, host_v)
+            self.build_reps(lens)
+            main.wait_stream(self.side)
+        else:
+            self.build_reps(lens)
             B.offload_blocks(self.p, self.k_pages, self.v_pages, self.block_table,
                              lens, host_table, host_k, host_v)
-        self.build_reps(lens)
-        main.wait_stream(side)
         self.attach_host(host_k, host_v, host_table)
 
     def reset_residency(self):

@@ -633,7 +633,8 @@ def test_host_tier_too_few_slots_is_reported():
             assert sum(p >= 0 for p in pages) == 3 and pages.count(-1) == n_host - 3
 
 
-def test_offload_prefill_native():
+@pytest.mark.parametrize("concurrent", [False, True])
+def test_offload_prefill_native(concurrent):
     """rkv_offload_blocks copies exactly the offload blocks that have a host
     page (bit-exact), leaves every other host page alone, and the decode
     path then runs from the natively filled pools (oracle check)."""
@@ -662,7 +663,7 @@ def test_offload_prefill_native():
                         i32(batch.context))
     prefill_lens = i32(batch.context - 1)
     ref.build_reps(prefill_lens)
-    sess.offload_prefill(hk, hv, host_table, prefill_lens)
+    sess.offload_prefill(hk, hv, host_table, prefill_lens, concurrent=concurrent)
     torch.cuda.synchronize()
     assert torch.equal(sess.reps, ref.reps)
     kp, vp = batch.k_pages.cpu(), batch.v_pages.cpu()
