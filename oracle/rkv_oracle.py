@@ -22,7 +22,7 @@ What it computes follows these passages (cited by page title and section):
 * CSDN "KV cache" survey, section *Share--KV cache共享*: query heads of one
   group share one K/V head (MQA/GQA).
 
-Readings where the pages are silent (each one is also listed in the design doc):
+Readings where the pages are silent:
 
 * the representation vector of a block is the mean of its 128 keys per KV
   head, and only complete blocks get one;
