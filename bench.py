@@ -336,6 +336,26 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
+    # spread of the step time: the same steps again in chunks of 16 between
+    # HIP event pairs (the pair's own cost, ~10 us, spreads over the chunk)
+    chunk = 16
+    n_chunks = max(1, min(16, args.steps // chunk))
+    ev_pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(n_chunks)]
+    base_idx = args.warmup + args.steps
+    torch.cuda.synchronize()
+    for c_i, (e0, e1) in enumerate(ev_pairs):
+        e0.record()
+        for i in range(chunk):
+            run(base_idx + c_i * chunk + i)
+        e1.record()
+    torch.cuda.synchronize()
+    chunk_us = np.array([a.elapsed_time(b) * 1e3 / chunk for a, b in ev_pairs])
+    step_spread = {"chunk_steps": chunk, "chunks": n_chunks,
+                   "p10_us": float(np.percentile(chunk_us, 10)),
+                   "p50_us": float(np.percentile(chunk_us, 50)),
+                   "p90_us": float(np.percentile(chunk_us, 90))}
+
     # the attention call alone, replayed on every layer copy's current merged
     # tables between one pair of HIP events on its stream (an event pair per
     # launch would add its own overhead to every launch)
@@ -434,6 +454,7 @@ def main():
             "split_waves": args.split,
             "select": args.select,
         },
+        "step_us_spread": step_spread,
         "stream_read_probe_gbs": probe_gbs,
         "host_staging": staging,
         "host_prefill": prefill,
