@@ -63,6 +63,12 @@ extern "C" {
 #define RKV_PPM_ONE 1000000
 #define RKV_MAX_GROUP 16        /* query heads per KV head */
 #define RKV_MAX_BLOCKS 8192     /* blocks per sequence (1M tokens) */
+/* Extent of one call, so that every launch grid fits the 32-bit work-item
+ * count of a dispatch: batch * n_q_heads query rows, and batch * n_kv_heads
+ * lists times the longest per-list row the call takes (max_blocks, m_cap,
+ * k_cap, slot_cap).  Larger calls fail with RKV_ERR_UNSUPPORTED. */
+#define RKV_MAX_QUERY_ROWS (1 << 18)
+#define RKV_MAX_LIST_ENTRIES (1 << 23)
 
 typedef enum rkv_status {
   RKV_OK = 0,

@@ -22,6 +22,9 @@ RKV_OK, RKV_ERR_INVALID_ARG, RKV_ERR_UNSUPPORTED, RKV_ERR_WORKSPACE, RKV_ERR_HIP
 ATTN_AUTO, ATTN_MFMA, ATTN_VALU = 0, 1, 2
 BLOCK = 128
 HEAD_DIM = 128
+RKV_MAX_BLOCKS = 8192
+RKV_MAX_QUERY_ROWS = 1 << 18     # batch * n_q_heads per call
+RKV_MAX_LIST_ENTRIES = 1 << 23   # batch * n_kv_heads * longest per-list row
 
 
 class Params(ctypes.Structure):

@@ -93,6 +93,26 @@ rkv_status check_sizes(int32_t batch, int32_t max_blocks) {
   return RKV_OK;
 }
 
+// Call extent: keeps every grid of the call within a dispatch's 32-bit
+// work-item count (the largest is the staging copy's 256 work-items per
+// list entry: 2^31 at the limit).
+rkv_status check_extent(const rkv_params* p, int32_t batch, int64_t row) {
+  const int64_t rows = (int64_t)batch * p->n_q_heads;
+  const int64_t entries = (int64_t)batch * p->n_kv_heads * (row > 1 ? row : 1);
+  RKV_REQUIRE(rows <= RKV_MAX_QUERY_ROWS, RKV_ERR_UNSUPPORTED,
+              "batch * n_q_heads = %lld above %d", (long long)rows,
+              RKV_MAX_QUERY_ROWS);
+  RKV_REQUIRE(entries <= RKV_MAX_LIST_ENTRIES, RKV_ERR_UNSUPPORTED,
+              "batch * n_kv_heads * %lld = %lld above %d", (long long)row,
+              (long long)entries, RKV_MAX_LIST_ENTRIES);
+  return RKV_OK;
+}
+
+int64_t max3(int64_t a, int64_t b, int64_t c) {
+  const int64_t m = a > b ? a : b;
+  return m > c ? m : c;
+}
+
 rkv_status check_pool(const void* pool, int64_t n_pages, const char* name) {
   RKV_REQUIRE(pool != nullptr, RKV_ERR_INVALID_ARG, "%s is NULL", name);
   RKV_REQUIRE(aligned16(pool), RKV_ERR_INVALID_ARG,
@@ -159,6 +179,7 @@ rkv_status rkv_build_reps(const rkv_params* params, const uint16_t* k_pages,
   rkv::Method m;
   RKV_TRY(check_params(params, &m));
   RKV_TRY(check_sizes(batch, max_blocks));
+  RKV_TRY(check_extent(params, batch, max_blocks));
   RKV_TRY(check_pool(k_pages, n_pages, "k_pages"));
   RKV_REQUIRE(block_table && lens && reps, RKV_ERR_INVALID_ARG,
               "block_table, lens and reps must not be NULL");
@@ -178,6 +199,7 @@ rkv_status rkv_append_kv(const rkv_params* params, const uint16_t* k_new,
   rkv::Method m;
   RKV_TRY(check_params(params, &m));
   RKV_TRY(check_sizes(batch, max_blocks));
+  RKV_TRY(check_extent(params, batch, max_blocks));
   RKV_TRY(check_pool(k_pages, n_pages, "k_pages"));
   RKV_TRY(check_pool(v_pages, n_pages, "v_pages"));
   RKV_REQUIRE(k_new && v_new && block_table && lens, RKV_ERR_INVALID_ARG,
@@ -210,6 +232,7 @@ rkv_status select_common(const rkv_params* params, const uint16_t* q,
   rkv::Method m;
   RKV_TRY(check_params(params, &m));
   RKV_TRY(check_sizes(batch, max_blocks));
+  RKV_TRY(check_extent(params, batch, max_blocks));
   RKV_REQUIRE(q && reps && block_table && lens && n_sel && (sel_ids || k_cap == 0),
               RKV_ERR_INVALID_ARG,
               "q, reps, block_table, lens, sel_ids and n_sel must not be NULL");
@@ -285,6 +308,7 @@ rkv_status rkv_merge_table(const rkv_params* params, const int32_t* block_table,
   RKV_REQUIRE(block_table && lens && sel_ids && n_sel && merged && n_merged,
               RKV_ERR_INVALID_ARG, "a required pointer is NULL");
   RKV_REQUIRE(k_cap >= 0, RKV_ERR_INVALID_ARG, "k_cap %d < 0", k_cap);
+  RKV_TRY(check_extent(params, batch, max3(max_blocks, k_cap, m_cap)));
   RKV_REQUIRE(m_cap >= max_blocks, RKV_ERR_INVALID_ARG,
               "m_cap %d below max_blocks %d", m_cap, max_blocks);
   RKV_REQUIRE(!host_table || (stage_page0 >= 0 &&
@@ -339,6 +363,7 @@ rkv_status rkv_stage_blocks(const rkv_params* params, const uint16_t* host_k,
   RKV_REQUIRE(host_table && sel_ids && n_sel, RKV_ERR_INVALID_ARG,
               "host_table, sel_ids and n_sel must not be NULL");
   RKV_REQUIRE(k_cap >= 1, RKV_ERR_INVALID_ARG, "k_cap %d < 1", k_cap);
+  RKV_TRY(check_extent(params, batch, max3(max_blocks, k_cap, 1)));
   RKV_REQUIRE(stage_page0 >= 0 &&
                   stage_page0 + (int64_t)batch * k_cap <= n_pages &&
                   stage_page0 + (int64_t)batch * k_cap <= (int64_t)INT32_MAX,
@@ -371,6 +396,7 @@ rkv_status rkv_offload_blocks(const rkv_params* params, const uint16_t* k_pages,
   RKV_TRY(check_pool(host_v, n_host_pages, "host_v"));
   RKV_REQUIRE(block_table && lens && host_table, RKV_ERR_INVALID_ARG,
               "block_table, lens and host_table must not be NULL");
+  RKV_TRY(check_extent(params, batch, max_blocks));
   const uint16_t* dev_view[2] = {nullptr, nullptr};
   RKV_TRY(host_views(host_k, host_v, dev_view));
   return hip_status(rkv::launch_offload(m, k_pages, v_pages, n_pages, block_table,
@@ -416,6 +442,7 @@ rkv_status rkv_stage_resident(const rkv_params* params, const uint16_t* host_k,
               "slot_cap %d outside [1, %d]", slot_cap, RKV_MAX_BLOCKS);
   RKV_REQUIRE(m_cap >= max_blocks, RKV_ERR_INVALID_ARG,
               "m_cap %d below max_blocks %d", m_cap, max_blocks);
+  RKV_TRY(check_extent(params, batch, max3(m_cap, k_cap, slot_cap)));
   RKV_REQUIRE(stage_page0 >= 0 &&
                   stage_page0 + (int64_t)batch * slot_cap <= n_pages &&
                   stage_page0 + (int64_t)batch * slot_cap <= (int64_t)INT32_MAX,
@@ -475,8 +502,7 @@ rkv_status rkv_decode_attn(const rkv_params* params, const uint16_t* q,
               RKV_ERR_UNSUPPORTED,
               "the VALU attention variant supports groups 1, 2, 4 and 8 (got %d)",
               m.group);
-  RKV_REQUIRE((int64_t)batch * m.n_kv_heads * m_cap < ((int64_t)1 << 30),
-              RKV_ERR_UNSUPPORTED, "batch * n_kv_heads * m_cap too large");
+  RKV_TRY(check_extent(params, batch, m_cap));
   const rkv::AttnPlan plan = rkv::plan_attention(
       batch, m.n_q_heads, m.n_kv_heads, params->split_waves, m_cap,
       rkv::device_cu_count());

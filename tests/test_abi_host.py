@@ -4,6 +4,7 @@ rejects bad arguments before anything is enqueued."""
 
 import ctypes
 import os
+import re
 
 import pytest
 
@@ -181,6 +182,37 @@ def test_reps_and_append_validation(L):
     p.block_size = 256
     assert L.rkv_append_kv(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 10, FAKE, 8,
                            FAKE, 1, None, None) == B.RKV_ERR_UNSUPPORTED
+
+
+def test_call_extent_limits(L):
+    """Calls whose launch grids would pass a dispatch's 32-bit work-item count
+    are refused up front; at the limits they go on to the next check."""
+    p = L.rkv_params_default(32, 8)
+    rows, entries = B.RKV_MAX_QUERY_ROWS, B.RKV_MAX_LIST_ENTRIES
+    with open(B.HEADER) as f:
+        text = f.read()
+    for name, val in (("RKV_MAX_QUERY_ROWS", rows), ("RKV_MAX_LIST_ENTRIES", entries),
+                      ("RKV_MAX_BLOCKS", B.RKV_MAX_BLOCKS)):
+        m = re.search(r"#define %s \(?1 << (\d+)\)?|#define %s (\d+)" % (name, name), text)
+        assert m, name
+        assert val == (1 << int(m.group(1)) if m.group(1) else int(m.group(2))), name
+    batch = rows // 32                       # batch * n_q_heads at the limit
+    assert _attn(L, p, batch=batch + 1, m_cap=1) == B.RKV_ERR_UNSUPPORTED
+    assert b"n_q_heads" in L.rkv_last_error()
+    assert _attn(L, p, batch=batch, m_cap=1) == B.RKV_ERR_WORKSPACE
+    # batch * n_kv_heads * m_cap: 1024 * 8 * 1024 is the limit
+    assert _attn(L, p, batch=1024, m_cap=1025) == B.RKV_ERR_UNSUPPORTED
+    assert _attn(L, p, batch=1024, m_cap=1024) == B.RKV_ERR_WORKSPACE
+    assert L.rkv_build_reps(ctypes.byref(p), FAKE, 10, FAKE, 1025, FAKE, None, 1024,
+                            FAKE, None) == B.RKV_ERR_UNSUPPORTED
+    assert L.rkv_build_reps(ctypes.byref(p), FAKE, 10, FAKE, 1024, FAKE, None, 1024,
+                            ODD, None) == B.RKV_ERR_INVALID_ARG
+    assert L.rkv_select(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, 1024, 1025,
+                        FAKE, FAKE, 1025, FAKE, FAKE, 1025, FAKE, 0,
+                        None) == B.RKV_ERR_UNSUPPORTED
+    assert L.rkv_stage_blocks(ctypes.byref(p), FAKE, FAKE, 50, FAKE, 200, FAKE, FAKE,
+                              entries // 32 + 1, 4, FAKE, FAKE, 10**9, 0,
+                              None) == B.RKV_ERR_UNSUPPORTED
 
 
 def test_workspace_sizes_are_monotone(L):
