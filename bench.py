@@ -4,7 +4,10 @@ A step is one layer's decode step for the whole batch: rkv_append_select
 (write the token and a just-completed block's representation; inner-product
 scores, per-(sequence, KV head) top-k and the merged block table, in one
 launch) -> rkv_decode_attn (split-K paged attention + log-sum-exp combine).
-The host tier adds rkv_stage_blocks + rkv_merge_table on a side stream.
+The host tier adds the staging of kept host-resident blocks on a side
+stream (rkv_stage_resident, which copies only blocks no staging slot
+holds; copying every kept block, rkv_stage_blocks + rkv_merge_table, is
+timed beside it).
 Inputs are synthetic and already resident in HBM when timing starts.
 
 Consecutive steps cycle over `--layers` independent copies of the layer's
@@ -48,8 +51,8 @@ COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 ATTN_SOURCE = os.path.join(ROOT, "sparse_retrieval_kv_amd", "csrc", "attn.hip")
 MEASURED_TRAFFIC = {
     # config: (sha256 prefix of attn.hip, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    2: ("4acfc0f39d0f2ebf", 40064.1 + 720.0, 1040.0 + 16.0),
-    4: ("4acfc0f39d0f2ebf", 506573.2 + 2391.0, 2080.6 + 256.0),
+    2: ("6f11bc7c0b4218c9", 39989.9 + 719.5, 1040.3 + 16.0),
+    4: ("6f11bc7c0b4218c9", 506478.6 + 2391.5, 2080.6 + 256.0),
 }
 METRIC = "decode attn steps/s and attended-KV HBM GB/s (% of peak) at 64K-128K ctx, 1 GPU"
 

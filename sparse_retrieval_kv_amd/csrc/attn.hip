@@ -17,7 +17,10 @@
 // of slots, numbered along the list, and the wave holding a list's first
 // unit records how many pieces the list has.  T is known only on the
 // device, so every wave derives the partition from n_merged itself: ragged
-// batches stay balanced and no host round trip is needed.  Within a list, a
+// batches stay balanced and no host round trip is needed.  A batch of one
+// sequence (all its lists equally long) instead deals each list's units
+// round robin over a fixed set of waves, so that a wave can request its
+// page ids before it knows the list length (strided_body).  Within a list, a
 // wave's loads are software-pipelined: unit u+1's K tile is requested right
 // after unit u's V tile, so about 32 KiB per wave stay in flight while unit
 // u's softmax and PV products run.
@@ -109,6 +112,7 @@ struct AttnArgs {
   int m_cap, max_len, batch, n_kv, group, n_waves, piece_cap;
   int comb_spec;     // pieces per combine lane requested before the count
   int n_cu;          // compute units of the device
+  int per_list;      // > 0: waves per list of the single-sequence partition
   float scale_log2;  // scale * log2(e)
 };
 
@@ -554,13 +558,94 @@ __device__ __forceinline__ void split_body(const AttnArgs& a) {
   }
 }
 
-__global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
-  split_body<MfmaMath>(a);
+// Single-sequence partition (batch of one: every list has the same length,
+// since the regions and k depend only on the sequence).  Wave w takes list
+// w mod NB and, as piece c = w / NB of P per list, the list's units c,
+// c + P, c + 2P, ...: its units sit at positions that do not depend on the
+// list length, so the page ids of its first 64 units are requested together
+// with the length -- one dependent memory round trip fewer before the first
+// K tile than the range split.  Each list's units are dealt evenly (+-1 per
+// wave) and the pieces are numbered by c.
+template <class Math>
+__device__ __forceinline__ void strided_body(const AttnArgs& a) {
+  const int lane = threadIdx.x;
+  const int col = lane & 15, grp = lane >> 4;
+  const int NB = a.batch * a.n_kv;
+  const int P = a.per_list;
+  const int bh = (int)(blockIdx.x % (unsigned)NB);
+  const int c = (int)(blockIdx.x / (unsigned)NB);
+  const int b = bh / a.n_kv, h = bh - b * a.n_kv;
+  const int32_t* mrow = a.merged + (int64_t)bh * a.m_cap;
+  // --- requests independent of the length ---
+  const int64_t e_lane = ((int64_t)c + (int64_t)lane * P) >> 1;
+  const int pref = e_lane < a.m_cap ? mrow[e_lane] : 0;
+  const int units = units_of(a, bh);
+  const int L = clamp_len(a.lens[b], a.max_len);
+  Math math;
+  math.begin(a, b, h, col, grp);
+  if (c >= units) return;  // uniform over the wave
+  if (c == 0 && lane == 0) a.n_pieces[bh] = units < P ? units : P;
+  const int n_mine = (units - c + P - 1) / P;
+  const int n = units >> 1;
+  const int last_valid = L - (((L + 127) >> 7) - 1) * kBlock;
+  const int64_t head_off = (int64_t)h * (kBlock * kDim);
+  const int64_t page_stride = (int64_t)a.n_kv * (kBlock * kDim);
+  auto page_ok = [&](int p) { return (uint64_t)(int64_t)p < (uint64_t)a.n_pages; };
+  auto tile_of = [&](int p) {
+    return (page_ok(p) ? (int64_t)p * page_stride : 0) + head_off;
+  };
+  auto valid_of = [&](int u) {
+    const int e = u >> 1;
+    const int v = (e == n - 1 ? last_valid : kBlock) - kUnit * (u & 1);
+    return v < 0 ? 0 : (v > kUnit ? kUnit : v);
+  };
+  // page id of this wave's i-th unit: requested above for i < 64
+  auto page_at = [&](int i) {
+    return i < 64 ? __shfl(pref, i) : mrow[(c + (int64_t)i * P) >> 1];
+  };
+
+  int page = page_at(0);
+  int64_t tile = tile_of(page);
+  uint4 kf[4][4];
+  load_k_unit(kf, a.k_pages + tile, c & 1, col, grp);
+  int page_next = n_mine > 1 ? page_at(1) : 0;
+  for (int i = 0; i < n_mine; ++i) {
+    const int u = c + i * P;
+    typename Math::Scores s;
+    math.scores(kf, s);
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 vf[2][8];
+    load_v_unit(vf, a.v_pages + tile, u & 1, col, grp);
+    const bool cur_ok = page_ok(page);
+    const int valid = valid_of(u);
+    if (i + 1 < n_mine) {  // prefetch the next unit's K tile
+      page = page_next;
+      tile = tile_of(page);
+      page_next = i + 2 < n_mine ? page_at(i + 2) : 0;
+      load_k_unit(kf, a.k_pages + tile, (u + P) & 1, col, grp);
+    }
+    if (!cur_ok || valid == 0) continue;
+    math.accumulate(s, vf, valid, a.scale_log2, col, grp);
+  }
+  math.finish(a, (int64_t)bh * a.piece_cap + c, lane, col, grp);
 }
 
-template <int G>
+template <class Math, bool STRIDED>
+__device__ __forceinline__ void attn_body(const AttnArgs& a) {
+  if (STRIDED)
+    strided_body<Math>(a);
+  else
+    split_body<Math>(a);
+}
+
+template <bool STRIDED>
+__global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
+  attn_body<MfmaMath, STRIDED>(a);
+}
+
+template <int G, bool STRIDED>
 __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
-  split_body<ValuMath<G>>(a);
+  attn_body<ValuMath<G>, STRIDED>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -685,6 +770,12 @@ AttnPlan plan_attention(int batch, int n_q_heads, int n_kv_heads, int waves,
   int spec = (int)((avg + 7) / 8);
   p.comb_spec = spec < 1 ? 1 : (spec > 20 ? 20 : spec);
   p.total_bytes = p.partial_bytes + p.ml_bytes + p.count_bytes;
+  // a single sequence takes the length-independent strided partition
+  p.per_list = 0;
+  if (batch == 1 && n_kv_heads > 0) {
+    p.per_list = p.n_waves / n_kv_heads;
+    if (p.per_list < 1) p.per_list = 1;
+  }
   return p;
 }
 
@@ -718,18 +809,33 @@ hipError_t launch_decode_attn(const Method& m, bool use_mfma,
   a.n_kv = m.n_kv_heads;
   a.group = m.group;
   a.n_waves = plan.n_waves;
+  a.per_list = plan.per_list;
   a.scale_log2 = scale * 1.4426950408889634f;
-  const dim3 grid((unsigned)plan.n_waves), block(64);
+  const int64_t waves =
+      plan.per_list > 0 ? (int64_t)batch * m.n_kv_heads * plan.per_list : plan.n_waves;
+  const dim3 grid((unsigned)waves), block(64);
+  const bool strided = plan.per_list > 0;
   if (use_mfma) {
-    hipLaunchKernelGGL(attn_mfma_kernel, grid, block, 0, stream, a);
+    if (strided)
+      hipLaunchKernelGGL(attn_mfma_kernel<true>, grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL(attn_mfma_kernel<false>, grid, block, 0, stream, a);
   } else {
+#define RKV_VALU_CASE(G)                                                        \
+  case G:                                                                       \
+    if (strided)                                                                \
+      hipLaunchKernelGGL((attn_valu_kernel<G, true>), grid, block, 0, stream, a); \
+    else                                                                        \
+      hipLaunchKernelGGL((attn_valu_kernel<G, false>), grid, block, 0, stream, a); \
+    break;
     switch (m.group) {
-      case 1: hipLaunchKernelGGL(attn_valu_kernel<1>, grid, block, 0, stream, a); break;
-      case 2: hipLaunchKernelGGL(attn_valu_kernel<2>, grid, block, 0, stream, a); break;
-      case 4: hipLaunchKernelGGL(attn_valu_kernel<4>, grid, block, 0, stream, a); break;
-      case 8: hipLaunchKernelGGL(attn_valu_kernel<8>, grid, block, 0, stream, a); break;
+      RKV_VALU_CASE(1)
+      RKV_VALU_CASE(2)
+      RKV_VALU_CASE(4)
+      RKV_VALU_CASE(8)
       default: return hipErrorInvalidValue;
     }
+#undef RKV_VALU_CASE
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

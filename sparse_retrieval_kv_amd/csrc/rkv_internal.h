@@ -103,6 +103,7 @@ struct AttnPlan {
   int piece_cap;         // partial slots per (sequence, KV head) list
   int comb_spec;         // combine pieces per lane requested speculatively
   int n_cu;              // compute units of the device
+  int per_list;          // > 0: single-sequence partition, waves per list
   size_t partial_bytes;  // fp32 [lists][piece_cap][group][kDim]
   size_t ml_bytes;       // float2 [lists][piece_cap][group]
   size_t count_bytes;    // int [lists] piece counts (padded)

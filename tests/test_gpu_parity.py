@@ -354,6 +354,36 @@ def test_split_sizes_agree_and_runs_are_deterministic():
         assert np.allclose(o, outs[0], rtol=1e-5, atol=1e-6)
 
 
+def test_single_sequence_partition_split_sizes():
+    """A batch of one takes the strided partition (wave c of P per list takes
+    units c, c + P, ...): from one piece per list (every wave past its 64
+    prefetched page ids) to more waves than units, each run deterministic
+    and equal to the oracle."""
+    spec = synth.custom("strided", batch=1, n_q_heads=32, n_kv_heads=8,
+                        context=(30000,), init_tokens=1024, local_tokens=3000,
+                        dense_boundary=0, shuffle=True, config_id=89)
+    batch = synth.make_batch(spec, DEV)
+    lens = i32(batch.lens_at(0))
+    kn, vn = batch.new_kv_bits(0)
+    outs = []
+    for split in (1, 7, 64, 301, 2048, 5000):
+        prm, sess = make_session(batch, split_waves=split)
+        say("single-sequence split", split)
+        prefill(batch, sess)
+        if split == 1:
+            sess.append(kn, vn, lens)  # once: the pools are shared
+        sess.select(batch.q_bits(0), lens)
+        o1 = sess.attend(batch.q_bits(0), lens).clone()
+        o2 = sess.attend(batch.q_bits(0), lens).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2)
+        outs.append(o1.cpu().numpy())
+        if split in (1, 301, 5000):
+            oracle_full_check(batch, sess, 0)
+    for o in outs[1:]:
+        assert np.allclose(o, outs[0], rtol=1e-5, atol=1e-6)
+
+
 def _permuted_copy(batch, seed=5):
     """Same logical contents at different physical pages."""
     rng = np.random.default_rng(seed)
