@@ -9,9 +9,10 @@
 //
 // Two launches per selection:
 //  1. score_kernel: one wave per 32 representations (16 KiB) of one
-//     (sequence, KV head), so the scan of even one sequence is spread over
-//     most compute units (one compute unit alone streams only a few tens of
-//     GB/s).  The group's query heads are summed once
+//     (sequence, KV head) -- 16 or 8 when that gives too few waves to cover
+//     the compute units twice -- so the scan of even one sequence is spread
+//     over most compute units (one compute unit alone streams only a few
+//     tens of GB/s).  The group's query heads are summed once
 //     (sum_g q_g . r = (sum_g q_g) . r); eight lanes score one
 //     representation; the fp32 scores go to the workspace.  Extra workgroups append the decoded token meanwhile.
 //  2. topk_kernel: one 1024-thread workgroup per (sequence, KV head) -- in
@@ -127,8 +128,7 @@ struct SelArgs {
 };
 
 constexpr int kScoreThreads = 64;
-constexpr int kScoreChunk = 32;  // representations per score wave
-constexpr int kScoreRounds = kScoreChunk / 8;  // 8 representations per round
+constexpr int kScoreMaxRounds = 4;  // 8 representations per round
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kTabRegs = RKV_MAX_BLOCKS / kTopkThreads;  // blocks per thread
@@ -154,12 +154,14 @@ __device__ __forceinline__ Pick pick_of(const Method& m, int lraw, int plen,
 }
 
 // Wave item = (bh, chunk c): representations of blocks
-// [ib + 32c, ib + 32c + 32) of the offload range.  Items past the score
-// grid append the decoded token of sequence-head item - n_bh * n_chunks
-// (one wave).
-template <bool APPEND>
+// [ib + C c, ib + C c + C) of the offload range, C = 8 * ROUNDS.  Items past
+// the score grid append the decoded token of sequence-head item - n_bh *
+// n_chunks (one wave).
+template <bool APPEND, int ROUNDS>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(SelArgs a,
                                                               AppendArgs ap) {
+  constexpr int kScoreRounds = ROUNDS;
+  constexpr int kScoreChunk = 8 * ROUNDS;
   __shared__ float qs[kDim];
   const Method& m = a.m;
   const int tid = threadIdx.x;
@@ -477,20 +479,41 @@ hipError_t launch_select(const Method& m, const uint16_t* q, const float* reps,
   if (groups == 0) return hipSuccess;
   int ib = (int)(((int64_t)m.init_tokens + 127) >> 7);
   ib = ib < max_blocks ? ib : max_blocks;
-  const int n_chunks = (max_blocks - ib + kScoreChunk - 1) / kScoreChunk;
+  // 32 representations per score wave, fewer when that leaves less than
+  // two waves per compute unit: a small scan is latency-bound, and its
+  // share of one compute unit's bandwidth is what its waves wait for
+  const int64_t want = 2 * (int64_t)device_cu_count();
+  int rounds = kScoreMaxRounds;
+  while (rounds > 1 &&
+         (int64_t)groups * ((max_blocks - ib + 8 * rounds - 1) / (8 * rounds)) < want)
+    rounds >>= 1;
+  const int chunk = 8 * rounds;
+  const int n_chunks = (max_blocks - ib + chunk - 1) / chunk;
   SelArgs a{m, q, reps, table, lens, prompt_lens, max_blocks, ib, n_chunks,
             groups, static_cast<uint32_t*>(workspace), sel_ids, n_sel, k_cap,
             merged, n_merged, m_cap};
   const int64_t score_wgs = (int64_t)groups * n_chunks;
-  if (append) {
-    AppendArgs ap{append->k_new, append->v_new, append->k_pages, append->v_pages,
-                  append->n_pages, append->reps};
-    hipLaunchKernelGGL(score_kernel<true>, dim3((unsigned)(score_wgs + groups)),
-                       dim3(kScoreThreads), 0, stream, a, ap);
-  } else if (score_wgs > 0) {
-    AppendArgs ap{};
-    hipLaunchKernelGGL(score_kernel<false>, dim3((unsigned)score_wgs),
-                       dim3(kScoreThreads), 0, stream, a, ap);
+  AppendArgs ap{};
+  if (append)
+    ap = AppendArgs{append->k_new, append->v_new, append->k_pages, append->v_pages,
+                    append->n_pages, append->reps};
+  const dim3 sgrid((unsigned)(score_wgs + (append ? groups : 0)));
+  if (sgrid.x > 0) {
+#define RKV_SCORE_LAUNCH(R)                                                      \
+  if (append)                                                                    \
+    hipLaunchKernelGGL((score_kernel<true, R>), sgrid, dim3(kScoreThreads), 0,   \
+                       stream, a, ap);                                           \
+  else                                                                           \
+    hipLaunchKernelGGL((score_kernel<false, R>), sgrid, dim3(kScoreThreads), 0,  \
+                       stream, a, ap);
+    if (rounds == 1) {
+      RKV_SCORE_LAUNCH(1)
+    } else if (rounds == 2) {
+      RKV_SCORE_LAUNCH(2)
+    } else {
+      RKV_SCORE_LAUNCH(4)
+    }
+#undef RKV_SCORE_LAUNCH
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
