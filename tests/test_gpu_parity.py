@@ -384,6 +384,39 @@ def test_single_sequence_partition_split_sizes():
         assert np.allclose(o, outs[0], rtol=1e-5, atol=1e-6)
 
 
+def _score_rounds(groups, max_blocks, init_tokens, n_cu):
+    """Representations per score wave (8 x rounds) the library picks: 32,
+    halved while the scan would have fewer than two waves per compute unit."""
+    ib = min(-(-init_tokens // 128), max_blocks)
+    rounds = 4
+    while rounds > 1 and groups * -(-(max_blocks - ib) // (8 * rounds)) < 2 * n_cu:
+        rounds //= 2
+    return rounds
+
+
+@pytest.mark.parametrize("batch_n,context,rounds", [
+    (1, (20000,), 1), (2, (76800, 70001), 2), (8, (38400,) * 8, 4)])
+def test_score_chunk_sizes(batch_n, context, rounds):
+    """The scan's three chunk sizes (8, 16 and 32 representations per wave)
+    give the oracle's selections, merged tables and outputs."""
+    spec = synth.custom(f"score chunks {rounds}", batch=batch_n, n_q_heads=32,
+                        n_kv_heads=8, context=context, shuffle=True,
+                        dense_boundary=0, config_id=88)
+    batch = synth.make_batch(spec, DEV)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    mb = batch.table_np.shape[1]
+    got = _score_rounds(batch_n * spec.n_kv_heads, mb, spec.init_tokens, n_cu)
+    if n_cu == 256:
+        assert got == rounds, (got, rounds)
+    say("score chunk", 8 * got, "batch", batch_n, "max_blocks", mb)
+    prm, sess = make_session(batch)
+    prefill(batch, sess)
+    step(batch, sess, 0)
+    torch.cuda.synchronize()
+    seqs = sorted({0, batch_n - 1})
+    oracle_full_check(batch, sess, 0, seqs=seqs, heads=[0, 5])
+
+
 def _permuted_copy(batch, seed=5):
     """Same logical contents at different physical pages."""
     rng = np.random.default_rng(seed)
