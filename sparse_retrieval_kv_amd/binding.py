@@ -127,7 +127,11 @@ def params(n_q_heads: int, n_kv_heads: int, **kw) -> Params:
     return p
 
 
-def _ptr(t, dtype=None, name="tensor"):
+def _ptr(t, dtype=None, name="tensor", shape=None, dev=None):
+    """Device pointer of a contiguous GPU tensor (None for None), after
+    checking its dtype, its exact shape and its device when given: the C
+    ABI takes plain pointers, so a buffer smaller than its declared layout
+    would otherwise be read or written past its end on the device."""
     if t is None:
         return None
     if not isinstance(t, torch.Tensor):
@@ -138,6 +142,10 @@ def _ptr(t, dtype=None, name="tensor"):
         raise ValueError(f"{name} must be contiguous")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, the other buffers on {dev}")
     return t.data_ptr()
 
 
@@ -145,23 +153,38 @@ def _stream(t: torch.Tensor):
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+def _pool_shape(p: Params, pool):
+    """[n_pages][n_kv_heads][128][128] (K token-major, V dim-major)."""
+    return (pool.shape[0], p.n_kv_heads, BLOCK, HEAD_DIM)
+
+
 def build_reps(p: Params, k_pages, block_table, lens, reps, block_begin=None):
+    batch, mb = block_table.shape
+    d = k_pages.device
     _check(lib().rkv_build_reps(
-        ctypes.byref(p), _ptr(k_pages, torch.int16, "k_pages"), k_pages.shape[0],
-        _ptr(block_table, torch.int32, "block_table"), block_table.shape[1],
-        _ptr(lens, torch.int32, "lens"), _ptr(block_begin, torch.int32, "block_begin"),
-        lens.shape[0], _ptr(reps, torch.float32, "reps"), _stream(k_pages)))
+        ctypes.byref(p), _ptr(k_pages, torch.int16, "k_pages", _pool_shape(p, k_pages), d),
+        k_pages.shape[0],
+        _ptr(block_table, torch.int32, "block_table", None, d), mb,
+        _ptr(lens, torch.int32, "lens", (batch,), d),
+        _ptr(block_begin, torch.int32, "block_begin", (batch,), d), batch,
+        _ptr(reps, torch.float32, "reps", (batch, p.n_kv_heads, mb, HEAD_DIM), d),
+        _stream(k_pages)))
 
 
 def append_kv(p: Params, k_new, v_new, k_pages, v_pages, block_table, lens,
               reps=None):
+    batch, mb = block_table.shape
+    d = k_pages.device
+    kv = (batch, p.n_kv_heads, HEAD_DIM)
     _check(lib().rkv_append_kv(
-        ctypes.byref(p), _ptr(k_new, torch.int16, "k_new"),
-        _ptr(v_new, torch.int16, "v_new"), _ptr(k_pages, torch.int16, "k_pages"),
-        _ptr(v_pages, torch.int16, "v_pages"), k_pages.shape[0],
-        _ptr(block_table, torch.int32, "block_table"), block_table.shape[1],
-        _ptr(lens, torch.int32, "lens"), lens.shape[0],
-        _ptr(reps, torch.float32, "reps"), _stream(k_pages)))
+        ctypes.byref(p), _ptr(k_new, torch.int16, "k_new", kv, d),
+        _ptr(v_new, torch.int16, "v_new", kv, d),
+        _ptr(k_pages, torch.int16, "k_pages", _pool_shape(p, k_pages), d),
+        _ptr(v_pages, torch.int16, "v_pages", _pool_shape(p, k_pages), d), k_pages.shape[0],
+        _ptr(block_table, torch.int32, "block_table", None, d), mb,
+        _ptr(lens, torch.int32, "lens", (batch,), d), batch,
+        _ptr(reps, torch.float32, "reps", (batch, p.n_kv_heads, mb, HEAD_DIM), d),
+        _stream(k_pages)))
 
 
 def select_workspace_size(p: Params, batch: int, max_blocks: int) -> int:
@@ -170,76 +193,107 @@ def select_workspace_size(p: Params, batch: int, max_blocks: int) -> int:
 
 def select(p: Params, q, reps, block_table, lens, sel_ids, n_sel,
            merged=None, n_merged=None, prompt_lens=None, workspace=None):
+    batch, mb = block_table.shape
+    d = q.device
+    hkv = p.n_kv_heads
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().rkv_select(
-        ctypes.byref(p), _ptr(q, torch.int16, "q"), _ptr(reps, torch.float32, "reps"),
-        _ptr(block_table, torch.int32, "block_table"), _ptr(lens, torch.int32, "lens"),
-        _ptr(prompt_lens, torch.int32, "prompt_lens"), lens.shape[0],
-        block_table.shape[1], _ptr(sel_ids, torch.int32, "sel_ids"),
-        _ptr(n_sel, torch.int32, "n_sel"), sel_ids.shape[-1],
-        _ptr(merged, torch.int32, "merged"), _ptr(n_merged, torch.int32, "n_merged"),
+        ctypes.byref(p), _ptr(q, torch.int16, "q", (batch, p.n_q_heads, HEAD_DIM), d),
+        _ptr(reps, torch.float32, "reps", (batch, hkv, mb, HEAD_DIM), d),
+        _ptr(block_table, torch.int32, "block_table", None, d),
+        _ptr(lens, torch.int32, "lens", (batch,), d),
+        _ptr(prompt_lens, torch.int32, "prompt_lens", (batch,), d), batch, mb,
+        _ptr(sel_ids, torch.int32, "sel_ids", (batch, hkv, sel_ids.shape[-1]), d),
+        _ptr(n_sel, torch.int32, "n_sel", (batch, hkv), d), sel_ids.shape[-1],
+        _ptr(merged, torch.int32, "merged",
+             None if merged is None else (batch, hkv, merged.shape[-1]), d),
+        _ptr(n_merged, torch.int32, "n_merged", (batch, hkv), d),
         merged.shape[-1] if merged is not None else 0,
-        _ptr(workspace, None, "workspace"), ws_bytes, _stream(q)))
+        _ptr(workspace, None, "workspace", None, d), ws_bytes, _stream(q)))
 
 
 def append_select(p: Params, k_new, v_new, k_pages, v_pages, q, reps, block_table,
                   lens, sel_ids, n_sel, merged=None, n_merged=None,
                   prompt_lens=None, workspace=None):
+    batch, mb = block_table.shape
+    d = q.device
+    hkv = p.n_kv_heads
+    kv = (batch, hkv, HEAD_DIM)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().rkv_append_select(
-        ctypes.byref(p), _ptr(k_new, torch.int16, "k_new"),
-        _ptr(v_new, torch.int16, "v_new"), _ptr(k_pages, torch.int16, "k_pages"),
-        _ptr(v_pages, torch.int16, "v_pages"), k_pages.shape[0],
-        _ptr(q, torch.int16, "q"), _ptr(reps, torch.float32, "reps"),
-        _ptr(block_table, torch.int32, "block_table"), _ptr(lens, torch.int32, "lens"),
-        _ptr(prompt_lens, torch.int32, "prompt_lens"), lens.shape[0],
-        block_table.shape[1], _ptr(sel_ids, torch.int32, "sel_ids"),
-        _ptr(n_sel, torch.int32, "n_sel"), sel_ids.shape[-1],
-        _ptr(merged, torch.int32, "merged"), _ptr(n_merged, torch.int32, "n_merged"),
+        ctypes.byref(p), _ptr(k_new, torch.int16, "k_new", kv, d),
+        _ptr(v_new, torch.int16, "v_new", kv, d),
+        _ptr(k_pages, torch.int16, "k_pages", _pool_shape(p, k_pages), d),
+        _ptr(v_pages, torch.int16, "v_pages", _pool_shape(p, k_pages), d), k_pages.shape[0],
+        _ptr(q, torch.int16, "q", (batch, p.n_q_heads, HEAD_DIM), d),
+        _ptr(reps, torch.float32, "reps", (batch, hkv, mb, HEAD_DIM), d),
+        _ptr(block_table, torch.int32, "block_table", None, d),
+        _ptr(lens, torch.int32, "lens", (batch,), d),
+        _ptr(prompt_lens, torch.int32, "prompt_lens", (batch,), d), batch, mb,
+        _ptr(sel_ids, torch.int32, "sel_ids", (batch, hkv, sel_ids.shape[-1]), d),
+        _ptr(n_sel, torch.int32, "n_sel", (batch, hkv), d), sel_ids.shape[-1],
+        _ptr(merged, torch.int32, "merged",
+             None if merged is None else (batch, hkv, merged.shape[-1]), d),
+        _ptr(n_merged, torch.int32, "n_merged", (batch, hkv), d),
         merged.shape[-1] if merged is not None else 0,
-        _ptr(workspace, None, "workspace"), ws_bytes, _stream(q)))
+        _ptr(workspace, None, "workspace", None, d), ws_bytes, _stream(q)))
 
 
 def merge_table(p: Params, block_table, lens, sel_ids, n_sel, merged, n_merged,
                 host_table=None, stage_page0: int = -1):
+    batch, mb = block_table.shape
+    d = block_table.device
+    hkv = p.n_kv_heads
     _check(lib().rkv_merge_table(
-        ctypes.byref(p), _ptr(block_table, torch.int32, "block_table"),
-        block_table.shape[1], _ptr(lens, torch.int32, "lens"),
-        _ptr(sel_ids, torch.int32, "sel_ids"), _ptr(n_sel, torch.int32, "n_sel"),
-        sel_ids.shape[-1], lens.shape[0],
-        _ptr(host_table, torch.int32, "host_table"), stage_page0,
-        _ptr(merged, torch.int32, "merged"),
-        _ptr(n_merged, torch.int32, "n_merged"), merged.shape[-1], _stream(lens)))
+        ctypes.byref(p), _ptr(block_table, torch.int32, "block_table", None, d), mb,
+        _ptr(lens, torch.int32, "lens", (batch,), d),
+        _ptr(sel_ids, torch.int32, "sel_ids", (batch, hkv, sel_ids.shape[-1]), d),
+        _ptr(n_sel, torch.int32, "n_sel", (batch, hkv), d), sel_ids.shape[-1], batch,
+        _ptr(host_table, torch.int32, "host_table", (batch, mb), d), stage_page0,
+        _ptr(merged, torch.int32, "merged", (batch, hkv, merged.shape[-1]), d),
+        _ptr(n_merged, torch.int32, "n_merged", (batch, hkv), d), merged.shape[-1],
+        _stream(block_table)))
 
 
-def _host_ptr(t, name):
+def _host_ptr(t, name, shape=None):
     if not isinstance(t, torch.Tensor) or t.is_cuda or not t.is_pinned():
         raise ValueError(f"{name} must be a pinned host tensor")
     if t.dtype != torch.int16 or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous int16 tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     return t.data_ptr()
 
 
 def stage_blocks(p: Params, host_k, host_v, host_table, sel_ids, n_sel,
                  k_pages, v_pages, stage_page0: int):
+    batch, mb = host_table.shape
+    d = k_pages.device
+    hkv = p.n_kv_heads
     _check(lib().rkv_stage_blocks(
-        ctypes.byref(p), _host_ptr(host_k, "host_k"), _host_ptr(host_v, "host_v"),
-        host_k.shape[0], _ptr(host_table, torch.int32, "host_table"),
-        host_table.shape[1], _ptr(sel_ids, torch.int32, "sel_ids"),
-        _ptr(n_sel, torch.int32, "n_sel"), sel_ids.shape[-1], n_sel.shape[0],
-        _ptr(k_pages, torch.int16, "k_pages"), _ptr(v_pages, torch.int16, "v_pages"),
+        ctypes.byref(p), _host_ptr(host_k, "host_k", _pool_shape(p, host_k)),
+        _host_ptr(host_v, "host_v", _pool_shape(p, host_k)),
+        host_k.shape[0], _ptr(host_table, torch.int32, "host_table", None, d), mb,
+        _ptr(sel_ids, torch.int32, "sel_ids", (batch, hkv, sel_ids.shape[-1]), d),
+        _ptr(n_sel, torch.int32, "n_sel", (batch, hkv), d), sel_ids.shape[-1], batch,
+        _ptr(k_pages, torch.int16, "k_pages", _pool_shape(p, k_pages), d),
+        _ptr(v_pages, torch.int16, "v_pages", _pool_shape(p, k_pages), d),
         k_pages.shape[0], stage_page0, _stream(k_pages)))
 
 
 def offload_blocks(p: Params, k_pages, v_pages, block_table, lens, host_table,
                    host_k, host_v):
+    batch, mb = block_table.shape
+    d = k_pages.device
     _check(lib().rkv_offload_blocks(
-        ctypes.byref(p), _ptr(k_pages, torch.int16, "k_pages"),
-        _ptr(v_pages, torch.int16, "v_pages"), k_pages.shape[0],
-        _ptr(block_table, torch.int32, "block_table"), block_table.shape[1],
-        _ptr(lens, torch.int32, "lens"), lens.shape[0],
-        _ptr(host_table, torch.int32, "host_table"), _host_ptr(host_k, "host_k"),
-        _host_ptr(host_v, "host_v"), host_k.shape[0], _stream(k_pages)))
+        ctypes.byref(p), _ptr(k_pages, torch.int16, "k_pages", _pool_shape(p, k_pages), d),
+        _ptr(v_pages, torch.int16, "v_pages", _pool_shape(p, k_pages), d), k_pages.shape[0],
+        _ptr(block_table, torch.int32, "block_table", None, d), mb,
+        _ptr(lens, torch.int32, "lens", (batch,), d), batch,
+        _ptr(host_table, torch.int32, "host_table", (batch, mb), d),
+        _host_ptr(host_k, "host_k", _pool_shape(p, host_k)),
+        _host_ptr(host_v, "host_v", _pool_shape(p, host_k)), host_k.shape[0],
+        _stream(k_pages)))
 
 
 def stage_workspace_size(p: Params, batch: int, k_cap: int) -> int:
@@ -249,20 +303,29 @@ def stage_workspace_size(p: Params, batch: int, k_cap: int) -> int:
 def stage_resident(p: Params, host_k, host_v, host_table, block_table, lens,
                    sel_ids, n_sel, slot_ids, slot_cursor, k_pages, v_pages,
                    stage_page0: int, merged, n_merged, workspace, n_staged=None):
+    batch, mb = block_table.shape
+    d = k_pages.device
+    hkv = p.n_kv_heads
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().rkv_stage_resident(
-        ctypes.byref(p), _host_ptr(host_k, "host_k"), _host_ptr(host_v, "host_v"),
-        host_k.shape[0], _ptr(host_table, torch.int32, "host_table"),
-        _ptr(block_table, torch.int32, "block_table"), block_table.shape[1],
-        _ptr(lens, torch.int32, "lens"), _ptr(sel_ids, torch.int32, "sel_ids"),
-        _ptr(n_sel, torch.int32, "n_sel"), sel_ids.shape[-1], n_sel.shape[0],
-        slot_ids.shape[-1], _ptr(slot_ids, torch.int32, "slot_ids"),
-        _ptr(slot_cursor, torch.int32, "slot_cursor"),
-        _ptr(k_pages, torch.int16, "k_pages"), _ptr(v_pages, torch.int16, "v_pages"),
-        k_pages.shape[0], stage_page0, _ptr(merged, torch.int32, "merged"),
-        _ptr(n_merged, torch.int32, "n_merged"), merged.shape[-1],
-        None if n_staged is None else _ptr(n_staged, torch.int32, "n_staged"),
-        _ptr(workspace, None, "workspace"), ws_bytes, _stream(k_pages)))
+        ctypes.byref(p), _host_ptr(host_k, "host_k", _pool_shape(p, host_k)),
+        _host_ptr(host_v, "host_v", _pool_shape(p, host_k)),
+        host_k.shape[0], _ptr(host_table, torch.int32, "host_table", (batch, mb), d),
+        _ptr(block_table, torch.int32, "block_table", None, d), mb,
+        _ptr(lens, torch.int32, "lens", (batch,), d),
+        _ptr(sel_ids, torch.int32, "sel_ids", (batch, hkv, sel_ids.shape[-1]), d),
+        _ptr(n_sel, torch.int32, "n_sel", (batch, hkv), d), sel_ids.shape[-1], batch,
+        slot_ids.shape[-1],
+        _ptr(slot_ids, torch.int32, "slot_ids", (batch, hkv, slot_ids.shape[-1]), d),
+        _ptr(slot_cursor, torch.int32, "slot_cursor", (batch, hkv), d),
+        _ptr(k_pages, torch.int16, "k_pages", _pool_shape(p, k_pages), d),
+        _ptr(v_pages, torch.int16, "v_pages", _pool_shape(p, k_pages), d),
+        k_pages.shape[0], stage_page0,
+        _ptr(merged, torch.int32, "merged", (batch, hkv, merged.shape[-1]), d),
+        _ptr(n_merged, torch.int32, "n_merged", (batch, hkv), d), merged.shape[-1],
+        None if n_staged is None else _ptr(n_staged, torch.int32, "n_staged",
+                                           (batch, hkv), d),
+        _ptr(workspace, None, "workspace", None, d), ws_bytes, _stream(k_pages)))
 
 
 def attn_workspace_size(p: Params, batch: int, m_cap: int) -> int:
@@ -271,23 +334,30 @@ def attn_workspace_size(p: Params, batch: int, m_cap: int) -> int:
 
 def decode_attn(p: Params, q, k_pages, v_pages, merged, n_merged, lens, out,
                 workspace):
+    batch = lens.shape[0]
+    d = q.device
+    hkv = p.n_kv_heads
+    rows = (batch, p.n_q_heads, HEAD_DIM)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().rkv_decode_attn(
-        ctypes.byref(p), _ptr(q, torch.int16, "q"),
-        _ptr(k_pages, torch.int16, "k_pages"), _ptr(v_pages, torch.int16, "v_pages"),
-        k_pages.shape[0], _ptr(merged, torch.int32, "merged"),
-        _ptr(n_merged, torch.int32, "n_merged"), merged.shape[-1],
-        _ptr(lens, torch.int32, "lens"), lens.shape[0],
-        _ptr(out, torch.float32, "out"), _ptr(workspace, None, "workspace"),
+        ctypes.byref(p), _ptr(q, torch.int16, "q", rows, d),
+        _ptr(k_pages, torch.int16, "k_pages", _pool_shape(p, k_pages), d),
+        _ptr(v_pages, torch.int16, "v_pages", _pool_shape(p, k_pages), d),
+        k_pages.shape[0],
+        _ptr(merged, torch.int32, "merged", (batch, hkv, merged.shape[-1]), d),
+        _ptr(n_merged, torch.int32, "n_merged", (batch, hkv), d), merged.shape[-1],
+        _ptr(lens, torch.int32, "lens", (batch,), d), batch,
+        _ptr(out, torch.float32, "out", rows, d), _ptr(workspace, None, "workspace", None, d),
         ws_bytes, _stream(q)))
 
 
-def _dyn(t, dtype, shape, name):
+def _dyn(t, dtype, shape, name, dev):
     """Pointer of a per-step tensor whose dtype / shape / device were fixed
     when the call was prepared (cheap checks only)."""
-    if t.dtype is not dtype or tuple(t.shape) != shape or not t.is_cuda \
+    if t.dtype is not dtype or tuple(t.shape) != shape or t.device != dev \
             or not t.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous GPU {dtype} tensor of shape {shape}")
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {shape} "
+                         f"on {dev}")
     return t.data_ptr()
 
 
@@ -309,22 +379,31 @@ class PreparedStep:
         self._q_shape = (batch, hq, HEAD_DIM)
         self._kv_shape = (batch, hkv, HEAD_DIM)
         self._lens_shape = (batch,)
+        d = self._dev
+        pool = _pool_shape(p, k_pages)
+        if merged is None or n_merged is None:
+            raise ValueError("a prepared step needs the merged table and its counts")
+        m_cap = merged.shape[-1]
         ws_sel = 0 if ws_select is None else ws_select.numel() * ws_select.element_size()
         self._sel_args = (
-            _ptr(k_pages, torch.int16, "k_pages"), _ptr(v_pages, torch.int16, "v_pages"),
-            k_pages.shape[0], _ptr(reps, torch.float32, "reps"),
-            _ptr(block_table, torch.int32, "block_table"),
-            _ptr(prompt_lens, torch.int32, "prompt_lens"), batch, max_blocks,
-            _ptr(sel_ids, torch.int32, "sel_ids"), _ptr(n_sel, torch.int32, "n_sel"),
-            sel_ids.shape[-1], _ptr(merged, torch.int32, "merged"),
-            _ptr(n_merged, torch.int32, "n_merged"),
-            merged.shape[-1] if merged is not None else 0,
-            _ptr(ws_select, None, "workspace"), ws_sel)
+            _ptr(k_pages, torch.int16, "k_pages", pool, d),
+            _ptr(v_pages, torch.int16, "v_pages", pool, d),
+            k_pages.shape[0], _ptr(reps, torch.float32, "reps",
+                                   (batch, hkv, max_blocks, HEAD_DIM), d),
+            _ptr(block_table, torch.int32, "block_table", None, d),
+            _ptr(prompt_lens, torch.int32, "prompt_lens", (batch,), d), batch, max_blocks,
+            _ptr(sel_ids, torch.int32, "sel_ids", (batch, hkv, sel_ids.shape[-1]), d),
+            _ptr(n_sel, torch.int32, "n_sel", (batch, hkv), d),
+            sel_ids.shape[-1], _ptr(merged, torch.int32, "merged", (batch, hkv, m_cap), d),
+            _ptr(n_merged, torch.int32, "n_merged", (batch, hkv), d), m_cap,
+            _ptr(ws_select, None, "workspace", None, d), ws_sel)
         self._attn_args = (
-            _ptr(k_pages, torch.int16, "k_pages"), _ptr(v_pages, torch.int16, "v_pages"),
-            k_pages.shape[0], _ptr(merged, torch.int32, "merged"),
-            _ptr(n_merged, torch.int32, "n_merged"), merged.shape[-1] if merged is not None else 0,
-            batch, _ptr(out, torch.float32, "out"), _ptr(ws_attn, None, "workspace"),
+            _ptr(k_pages, torch.int16, "k_pages", pool, d),
+            _ptr(v_pages, torch.int16, "v_pages", pool, d),
+            k_pages.shape[0], _ptr(merged, torch.int32, "merged", (batch, hkv, m_cap), d),
+            _ptr(n_merged, torch.int32, "n_merged", (batch, hkv), d), m_cap,
+            batch, _ptr(out, torch.float32, "out", (batch, hq, HEAD_DIM), d),
+            _ptr(ws_attn, None, "workspace", None, d),
             ws_attn.numel() * ws_attn.element_size())
         # keep every buffer alive as long as the prepared call
         self._keep = (k_pages, v_pages, reps, block_table, sel_ids, n_sel, merged,
@@ -334,18 +413,20 @@ class PreparedStep:
         (kp, vp, n_pages, reps, bt, plens, batch, max_blocks, sel, nsel, k_cap,
          merged, nmerged, m_cap, ws, ws_bytes) = self._sel_args
         _check(self._L.rkv_append_select(
-            self._pp, _dyn(k_new, torch.int16, self._kv_shape, "k_new"),
-            _dyn(v_new, torch.int16, self._kv_shape, "v_new"), kp, vp, n_pages,
-            _dyn(q, torch.int16, self._q_shape, "q"), reps, bt,
-            _dyn(lens, torch.int32, self._lens_shape, "lens"), plens, batch, max_blocks,
+            self._pp, _dyn(k_new, torch.int16, self._kv_shape, "k_new", self._dev),
+            _dyn(v_new, torch.int16, self._kv_shape, "v_new", self._dev), kp, vp, n_pages,
+            _dyn(q, torch.int16, self._q_shape, "q", self._dev), reps, bt,
+            _dyn(lens, torch.int32, self._lens_shape, "lens", self._dev), plens, batch,
+            max_blocks,
             sel, nsel, k_cap, merged, nmerged, m_cap, ws, ws_bytes,
             torch.cuda.current_stream(self._dev).cuda_stream))
 
     def decode_attn(self, q, lens):
         kp, vp, n_pages, merged, nmerged, m_cap, batch, out, ws, ws_bytes = self._attn_args
         _check(self._L.rkv_decode_attn(
-            self._pp, _dyn(q, torch.int16, self._q_shape, "q"), kp, vp, n_pages,
-            merged, nmerged, m_cap, _dyn(lens, torch.int32, self._lens_shape, "lens"),
+            self._pp, _dyn(q, torch.int16, self._q_shape, "q", self._dev), kp, vp, n_pages,
+            merged, nmerged, m_cap,
+            _dyn(lens, torch.int32, self._lens_shape, "lens", self._dev),
             batch, out, ws, ws_bytes, torch.cuda.current_stream(self._dev).cuda_stream))
 
 

@@ -417,6 +417,37 @@ def test_score_chunk_sizes(batch_n, context, rounds):
     oracle_full_check(batch, sess, 0, seqs=seqs, heads=[0, 5])
 
 
+def test_binding_rejects_mismatched_buffers():
+    """The binding checks every tensor against the layout the C ABI assumes
+    (exact shape, dtype, device) before the call, so an undersized or
+    misplaced buffer raises instead of being read past its end."""
+    spec = synth.custom("binding shapes", batch=2, n_q_heads=8, n_kv_heads=2,
+                        context=(3000, 1000), dense_boundary=0, config_id=87)
+    batch = synth.make_batch(spec, DEV)
+    prm, sess = make_session(batch)
+    lens = i32(batch.lens_at(0))
+    q = batch.q_bits(0)
+    short_out = torch.zeros((2, 7, 128), dtype=torch.float32, device=DEV)
+    with pytest.raises(ValueError, match="out"):
+        B.decode_attn(prm, q, sess.k_pages, sess.v_pages, sess.merged, sess.n_merged,
+                      lens, short_out, sess.ws_attn)
+    with pytest.raises(ValueError, match="reps"):
+        B.select(prm, q, sess.reps[:, :, :-1].contiguous(), sess.block_table, lens,
+                 sess.sel_ids, sess.n_sel, sess.merged, sess.n_merged, None,
+                 sess.ws_select)
+    with pytest.raises(ValueError, match="lens"):
+        B.build_reps(prm, sess.k_pages, sess.block_table, lens[:1], sess.reps)
+    with pytest.raises(ValueError, match="q"):
+        sess.attend(q[:, :4].contiguous(), lens)          # prepared fast path
+    with pytest.raises(ValueError, match="lens"):
+        sess.attend(q, lens.cpu())                       # host tensor
+    # the buffers are untouched and a well-formed step still runs
+    prefill(batch, sess)
+    step(batch, sess, 0)
+    torch.cuda.synchronize()
+    oracle_full_check(batch, sess, 0)
+
+
 def _permuted_copy(batch, seed=5):
     """Same logical contents at different physical pages."""
     rng = np.random.default_rng(seed)
