@@ -448,6 +448,25 @@ def test_binding_rejects_mismatched_buffers():
     oracle_full_check(batch, sess, 0)
 
 
+def test_many_short_lists():
+    """More (sequence, KV head) lists than split waves (96 x 8 = 768 > 512),
+    ragged and short: most waves' ranges cover several whole lists, so the
+    piece numbering, the piece counts and the combine are exercised across
+    many list boundaries.  Sampled sequences against the oracle."""
+    rng = np.random.default_rng(86)
+    ctx = tuple(int(x) for x in rng.integers(1, 3000, size=96))
+    spec = synth.custom("many lists", batch=96, n_q_heads=32, n_kv_heads=8,
+                        context=ctx, init_tokens=128, local_tokens=256,
+                        dense_boundary=0, shuffle=True, config_id=86)
+    batch = synth.make_batch(spec, DEV)
+    prm, sess = make_session(batch)
+    prefill(batch, sess)
+    step(batch, sess, 0)
+    torch.cuda.synchronize()
+    seqs = [0, 1, 47, int(np.argmax(batch.context)), int(np.argmin(batch.context)), 95]
+    oracle_full_check(batch, sess, 0, seqs=sorted(set(seqs)))
+
+
 def _permuted_copy(batch, seed=5):
     """Same logical contents at different physical pages."""
     rng = np.random.default_rng(seed)
