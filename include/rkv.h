@@ -290,8 +290,10 @@ rkv_status rkv_stage_blocks(const rkv_params* params, const uint16_t* host_k,
  * host tier (openGauss page, "Feature Description" and "Configuration
  * Parameters": beyond the offload boundary the offload part of the KV cache
  * is kept in host DDR; "Overall Solution": representations are extracted
- * block by block at prefill, so rkv_build_reps over the same pages can run
- * on another stream meanwhile -- both only read the device pages).
+ * block by block at prefill, so rkv_build_reps over the same pages may run
+ * on another stream meanwhile -- both only read the device pages -- though
+ * on MI355X that is slower than running them one after the other: while a
+ * kernel writes host memory over the bus, HBM reads elsewhere stall).
  * For every sequence b and every block j of its offload range
  * [n_init, local_start) (region rule of rkv_select, from lens[b]) with
  * host_table[b][j] >= 0: copies all KV heads of device page
@@ -395,11 +397,13 @@ size_t rkv_attn_workspace_size(const rkv_params* params, int32_t batch,
  * n_merged = 0 writes zeros.
  * The work is split over the merged blocks (split-K, the Flash-Decoding
  * idiom named in the CSDN survey's references): the 64-token halves of all
- * merged blocks of the batch are spread evenly over split_waves waves, and
- * the partial softmax results are merged by their log-sum-exp (the
- * survey's cascade-inference paragraph: partial results merged the
- * FlashDecoding way) by a second kernel.  batch * n_kv_heads * m_cap must
- * stay below 2^30.
+ * merged blocks of the batch are spread evenly over split_waves waves (for
+ * a batch of one, whose lists are all equally long, each list's halves are
+ * dealt round robin over split_waves / n_kv_heads waves), and the partial
+ * softmax results are merged by their log-sum-exp (the survey's
+ * cascade-inference paragraph: partial results merged the FlashDecoding
+ * way) by a second kernel.  Extent limits: RKV_MAX_QUERY_ROWS and
+ * RKV_MAX_LIST_ENTRIES with m_cap as the row.
  *   merged [batch][n_kv_heads][m_cap], n_merged [batch][n_kv_heads]
  *   out [batch][n_q_heads][128] fp32
  *   workspace >= rkv_attn_workspace_size(params, batch, m_cap) bytes of
