@@ -97,6 +97,15 @@ def attn_traffic(config):
                      rec[2] * COUNTER_SCALE["WRITE_SIZE"])
 
 
+def attn_kernel_label(impl, spec):
+    """The two kernels one rkv_decode_attn call launches; the split kernel is
+    templated on its partition (true: a batch of one sequence)."""
+    strided = "true" if spec.batch == 1 else "false"
+    split = (f"attn_valu_kernel<{spec.group}, {strided}>" if impl == "valu"
+             else f"attn_mfma_kernel<{strided}>")
+    return f"rkv_decode_attn ({split} + attn_combine_kernel)"
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -465,7 +474,7 @@ def main():
         "attended_kv_pct_peak_step": 100.0 * step_gbs / HBM_PEAK_GBS,
         "roofline": {
             "bound": "hbm",
-            "kernel": "rkv_decode_attn (attn_mfma_kernel + attn_combine_kernel)",
+            "kernel": attn_kernel_label(args.impl, spec),
             "achieved": attn_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
