@@ -293,17 +293,39 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelArgs a) {
   const int plen = a.prompt_lens ? a.prompt_lens[b] : lraw;
   int tab[kTabRegs];
   uint32_t key[kTabRegs];
+  float sc[kTabRegs];
+  // table entries and (first) scores in one batch of loads, no loop
+  // between them, so that they share one memory round trip
 #pragma unroll
   for (int i = 0; i < kTabRegs; ++i) {
     const int j = tid + kTopkThreads * i;
     const bool in = j < max_blocks;
     tab[i] = in ? trow[j] : -1;
-    // scores (raw fp32) -> order keys; per sequence, summed over the heads
-    float sc = 0.f;
-    for (int hr = 0; hr < n_sum; ++hr)
-      sc += in ? __uint_as_float(krow[(int64_t)hr * max_blocks + j]) : 0.f;
-    key[i] = order_key(sc);
+    sc[i] = in ? __uint_as_float(krow[j]) : 0.f;
   }
+  // per sequence: the other heads' scores, added in head order; four
+  // heads' loads are issued before any of them is waited for (eight at a
+  // time needs 95 registers and ran slower)
+  for (int h0 = 1; h0 < n_sum; h0 += 4) {
+    float t[4][kTabRegs];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < kTabRegs; ++i) {
+        const int j = tid + kTopkThreads * i;
+        t[u][i] = (h0 + u < n_sum && j < max_blocks)
+                      ? __uint_as_float(krow[(int64_t)(h0 + u) * max_blocks + j])
+                      : 0.f;
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < kTabRegs; ++i)
+        if (h0 + u < n_sum && tid + kTopkThreads * i < max_blocks) sc[i] += t[u][i];
+  }
+  // raw fp32 scores -> order keys
+#pragma unroll
+  for (int i = 0; i < kTabRegs; ++i) key[i] = order_key(sc[i]);
   if (tid < 256) hist[tid] = 0u;
 
   const Pick pk = pick_of(m, lraw, plen, max_blocks);
