@@ -126,6 +126,14 @@ __device__ __forceinline__ int units_of(const AttnArgs& a, int bh) {
   return 2 * n;
 }
 
+// units_of for a lane's list bh, 0 past the last list.  The load is made
+// from a valid index on every lane and masked afterwards: a load under a
+// lane condition makes the compiler wait for it where the branch rejoins.
+__device__ __forceinline__ int units_or_zero(const AttnArgs& a, int bh, int NB) {
+  const int u = units_of(a, bh < NB ? bh : NB - 1);
+  return bh < NB ? u : 0;
+}
+
 // The T units are split evenly over W waves in a virtual order in which the
 // waves that share a compute unit are neighbours: when the grid fills an
 // idle GPU, workgroup w runs on compute unit w mod n_cu (workgroups are
@@ -204,17 +212,23 @@ struct MfmaMath {
   float m_run, l_run;
 
   // Q^T as the B operand: lane (col, grp) holds head col, dims of chunk
-  // 4kk+grp (8 bf16) for kk = 0..3; padded heads are zero.
+  // 4kk+grp (8 bf16) for kk = 0..3; padded heads are zero.  Every lane
+  // loads a valid row (padded lanes the group's last) and the padding is
+  // zeroed after the load: a branch around the loads would make the
+  // compiler wait for them at the branch's end.
   __device__ __forceinline__ void begin(const AttnArgs& a, int b, int h, int col,
                                         int grp) {
     const int G = a.group;
-    const uint16_t* qrow = a.q + ((int64_t)b * a.n_kv * G + h * G + col) * kDim;
+    const int row = col < G ? col : G - 1;
+    const uint16_t* qrow = a.q + ((int64_t)b * a.n_kv * G + h * G + row) * kDim;
+    uint4 v[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (col < G) v = ld16(qrow + (4 * kk + grp) * 8);
-      bq[kk] = as_bf16x8(v);
-    }
+    for (int kk = 0; kk < 4; ++kk) v[kk] = ld16(qrow + (4 * kk + grp) * 8);
+    const uint32_t keep = col < G ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      bq[kk] = as_bf16x8(make_uint4(v[kk].x & keep, v[kk].y & keep, v[kk].z & keep,
+                                    v[kk].w & keep));
 #pragma unroll
     for (int n8 = 0; n8 < 8; ++n8) acc[n8] = (f32x4){0.f, 0.f, 0.f, 0.f};
     m_run = kNegInf;
@@ -518,11 +532,18 @@ __device__ __forceinline__ void split_body(const AttnArgs& a) {
   const int W = a.n_waves;
   const int w = virtual_wave(blockIdx.x, W, a.n_cu);
   const int NB = a.batch * a.n_kv;
+  // the unit counts of the first 4 x 64 lists are requested together and
+  // kept in registers (a loop of loads would wait for each group in turn,
+  // and the walk below would read them again)
+  constexpr int kHeld = 4;
+  int held[kHeld];
+#pragma unroll
+  for (int g = 0; g < kHeld; ++g) held[g] = units_or_zero(a, 64 * g + lane, NB);
   int64_t T = 0;
-  for (int base = 0; base < NB; base += 64) {
-    const int bh = base + lane;
-    T += wave_sum_i(bh < NB ? units_of(a, bh) : 0);
-  }
+#pragma unroll
+  for (int g = 0; g < kHeld; ++g) T += wave_sum_i(held[g]);
+  for (int base = 64 * kHeld; base < NB; base += 64)
+    T += wave_sum_i(units_or_zero(a, base + lane, NB));
   if (T == 0) return;
   const int64_t lo = unit_start(w, T, W), hi = unit_start(w + 1, T, W);
   if (lo >= hi) return;
@@ -530,7 +551,12 @@ __device__ __forceinline__ void split_body(const AttnArgs& a) {
   int64_t run = 0;  // units of the lists before this group of 64
   for (int base = 0; base < NB && run < hi; base += 64) {
     const int bh = base + lane;
-    const int u = bh < NB ? units_of(a, bh) : 0;
+    const int gi = base >> 6;
+    const int u = gi == 0 ? held[0]
+                : gi == 1 ? held[1]
+                : gi == 2 ? held[2]
+                : gi == 3 ? held[3]
+                : units_or_zero(a, bh, NB);
     const int incl = wave_incl_scan(u, lane);
     const int64_t s0 = run + incl - u, s1 = run + incl;
     uint64_t hit = __ballot(u > 0 && s0 < hi && s1 > lo);
@@ -576,13 +602,17 @@ __device__ __forceinline__ void strided_body(const AttnArgs& a) {
   const int c = (int)(blockIdx.x / (unsigned)NB);
   const int b = bh / a.n_kv, h = bh - b * a.n_kv;
   const int32_t* mrow = a.merged + (int64_t)bh * a.m_cap;
-  // --- requests independent of the length ---
-  const int64_t e_lane = ((int64_t)c + (int64_t)lane * P) >> 1;
-  const int pref = e_lane < a.m_cap ? mrow[e_lane] : 0;
+  // --- one memory round trip: the list length, the sequence length, the
+  // page ids of this wave's first 64 units and the query rows ---
   const int units = units_of(a, bh);
   const int L = clamp_len(a.lens[b], a.max_len);
+  const int64_t e_lane = ((int64_t)c + (int64_t)lane * P) >> 1;
+  const int pref = e_lane < a.m_cap ? mrow[e_lane] : 0;
   Math math;
   math.begin(a, b, h, col, grp);
+  // L is used only past the branch below; without this use the compiler
+  // would request it only after n_merged has arrived (a second round trip)
+  __asm__ volatile("" ::"s"(L));
   if (c >= units) return;  // uniform over the wave
   if (c == 0 && lane == 0) a.n_pieces[bh] = units < P ? units : P;
   const int n_mine = (units - c + P - 1) / P;

@@ -162,7 +162,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(SelArgs a,
                                                               AppendArgs ap) {
   constexpr int kScoreRounds = ROUNDS;
   constexpr int kScoreChunk = 8 * ROUNDS;
-  __shared__ float qs[kDim];
+  __shared__ __attribute__((aligned(16))) float qs[kDim];
   const Method& m = a.m;
   const int tid = threadIdx.x;
   const int64_t item = blockIdx.x;
@@ -182,17 +182,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(SelArgs a,
   const int c = (int)(item - (int64_t)bh * a.n_chunks);
   const int b = bh / m.n_kv_heads, h = bh - b * m.n_kv_heads;
 
-  // --- requests independent of the length ---
-  const int lraw = a.lens[b];
-  const int plen = a.prompt_lens ? a.prompt_lens[b] : lraw;
-  float qsum0 = 0.f, qsum1 = 0.f;  // dims tid and tid + 64
-  {
-    const uint16_t* qh = a.q + ((int64_t)b * m.n_q_heads + h * m.group) * kDim;
-    for (int g = 0; g < m.group; ++g) {
-      qsum0 += __uint_as_float((uint32_t)qh[g * kDim + tid] << 16);
-      qsum1 += __uint_as_float((uint32_t)qh[g * kDim + tid + 64] << 16);
-    }
-  }
+  // --- requests independent of the length: representations, the group's
+  // query rows (lane tid holds dims 2 tid and 2 tid + 1 of each) and the
+  // lengths, all issued before any of them is waited for ---
   const int o = tid & 7, slot = tid >> 3;  // lane octet o of slot 0..7
   const int j0 = a.ib + c * kScoreChunk;
   float4 v[kScoreRounds][4];
@@ -205,13 +197,31 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(SelArgs a,
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[u][i] = p[o + 8 * i];
   }
+  const uint32_t* qh = reinterpret_cast<const uint32_t*>(
+      a.q + ((int64_t)b * m.n_q_heads + h * m.group) * kDim);
+  uint32_t qw[RKV_MAX_GROUP];
+#pragma unroll
+  for (int g = 0; g < RKV_MAX_GROUP; ++g)
+    qw[g] = g < m.group ? qh[g * (kDim / 2) + tid] : 0u;
+  const int lraw = a.lens[b];
+  // the pointer is chosen, not the value, so that this load goes out with
+  // the others instead of after the length arrives
+  const int plen = (a.prompt_lens ? a.prompt_lens : a.lens)[b];
+  // the group's query heads summed in head order
+  float qsum0 = 0.f, qsum1 = 0.f;  // dims 2 tid and 2 tid + 1
+#pragma unroll
+  for (int g = 0; g < RKV_MAX_GROUP; ++g) {
+    if (g < m.group) {
+      qsum0 += bf16lo(qw[g]);
+      qsum1 += bf16hi(qw[g]);
+    }
+  }
 
   // --- this chunk's share of the offload range ---
   const Pick pk = pick_of(m, lraw, plen, max_blocks);
   const int ls = pk.R.n_init + pk.R.n_off;  // offload end
   if (!pk.ranked || j0 >= ls) return;  // uniform over the wave
-  qs[tid] = qsum0;
-  qs[tid + 64] = qsum1;
+  *reinterpret_cast<float2*>(&qs[2 * tid]) = make_float2(qsum0, qsum1);
   __syncthreads();
   float4 qv[4];
 #pragma unroll
@@ -290,7 +300,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelArgs a) {
 
   // --- requests independent of the length ---
   const int lraw = a.lens[b];
-  const int plen = a.prompt_lens ? a.prompt_lens[b] : lraw;
+  // the pointer is chosen, not the value, so that this load goes out with
+  // the others instead of after the length arrives
+  const int plen = (a.prompt_lens ? a.prompt_lens : a.lens)[b];
   int tab[kTabRegs];
   uint32_t key[kTabRegs];
   float sc[kTabRegs];
