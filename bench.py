@@ -51,7 +51,7 @@ COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 ATTN_SOURCE = os.path.join(ROOT, "sparse_retrieval_kv_amd", "csrc", "attn.hip")
 MEASURED_TRAFFIC = {
     # config: (sha256 prefix of attn.hip, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    2: ("2f58af364c4097ce", 39989.9 + 719.5, 1040.3 + 16.0),
+    2: ("2f58af364c4097ce", 39970.2 + 719.5, 1040.3 + 16.0),
     4: ("2f58af364c4097ce", 506502.1 + 2391.5, 2080.6 + 256.0),
 }
 METRIC = "decode attn steps/s and attended-KV HBM GB/s (% of peak) at 64K-128K ctx, 1 GPU"
@@ -83,10 +83,15 @@ def step_bytes(spec, context, t):
     return kv * spec.n_kv_heads, reps * spec.n_kv_heads, kept * spec.n_kv_heads
 
 
-def attn_traffic(config):
+def attn_traffic(args):
     """Counter-measured HBM bytes per attention call, or None when no
-    record exists for this config and this attention source."""
-    rec = MEASURED_TRAFFIC.get(config)
+    record exists for this config, launch and attention source.  The records
+    were taken with the default launch (MFMA, automatic split, per-head
+    selection, default layer copies)."""
+    if (args.impl not in ("auto", "mfma") or args.split != 0 or
+            args.select != "per-head" or args.layers != 0):
+        return None
+    rec = MEASURED_TRAFFIC.get(args.config)
     if rec is None:
         return None
     with open(ATTN_SOURCE, "rb") as f:
@@ -274,7 +279,10 @@ def main():
     else:
         base = synth.make_batch(spec, dev)
     layer_bytes = 2 * base.k_pages.numel() * 2
-    n_layers = args.layers or max(1, min(16, math.ceil((1 << 30) / layer_bytes)))
+    # >= 2 GiB of layers between two visits of one layer: nothing of it (pages,
+    # representations, tables) is left in the 256 MB Infinity Cache, as in a
+    # model with many layers (with 1 GiB, ~2% of the 8B step stayed warm)
+    n_layers = args.layers or max(1, min(16, math.ceil((2 << 30) / layer_bytes)))
     impl = {"auto": B.ATTN_AUTO, "mfma": B.ATTN_MFMA, "valu": B.ATTN_VALU}[args.impl]
     prm = B.params(spec.n_q_heads, spec.n_kv_heads, init_tokens=spec.init_tokens,
                    local_tokens=spec.local_tokens, topk_ppm=spec.topk_ppm,
@@ -480,7 +488,7 @@ def main():
             "unit": "GB/s",
             "frac": attn_gbs / HBM_PEAK_GBS,
             "frac_of_read_probe": attn_gbs / probe_gbs,
-            "traffic": attn_traffic(args.config),
+            "traffic": attn_traffic(args),
             "traffic_source": ("rocprofv3 FETCH_SIZE + WRITE_SIZE per call, "
                                "scaled by a 1 GiB copy's readings"),
             "bytes_per_launch": float(kv_attn),
