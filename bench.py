@@ -352,9 +352,13 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         ts.append(run(args.warmup + i))
+    t_enq = time.perf_counter()  # host side done: every step is enqueued
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    # the host's enqueue time per step; well below the step time means the
+    # wall-clock figure is the GPU's
+    host_us_per_step = (t_enq - t0) * 1e6 / args.steps
 
     # spread of the step time: the same steps again in chunks of 16 between
     # HIP event pairs (the pair's own cost, ~10 us, spreads over the chunk)
@@ -475,6 +479,7 @@ def main():
             "select": args.select,
         },
         "step_us_spread": step_spread,
+        "host_enqueue_us_per_step": host_us_per_step,
         "stream_read_probe_gbs": probe_gbs,
         "host_staging": staging,
         "host_prefill": prefill,
