@@ -315,10 +315,27 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelArgs a) {
     tab[i] = in ? trow[j] : -1;
     sc[i] = in ? __uint_as_float(krow[j]) : 0.f;
   }
-  // per sequence: the other heads' scores, added in head order; four
-  // heads' loads are issued before any of them is waited for (eight at a
-  // time needs 95 registers and ran slower)
-  for (int h0 = 1; h0 < n_sum; h0 += 4) {
+  // per sequence: the other heads' scores, added in head order.  When
+  // every block fits one thread (max_blocks <= 1024), heads 1..8 join the
+  // batch above: their loads use a clamped index, so no lane condition
+  // makes the compiler wait for them early.
+  const bool one_reg = max_blocks <= kTopkThreads;
+  int h_rest = 1;
+  if (one_reg && n_sum > 1) {  // uniform
+    const int jc = tid < max_blocks ? tid : max_blocks - 1;
+    float t1[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      t1[u] = 1 + u < n_sum ? __uint_as_float(krow[(int64_t)(1 + u) * max_blocks + jc])
+                            : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (1 + u < n_sum && tid < max_blocks) sc[0] += t1[u];
+    h_rest = 9;
+  }
+  // the rest four heads per round trip (eight at a time over all registers
+  // needs 95 registers and ran slower)
+  for (int h0 = h_rest; h0 < n_sum; h0 += 4) {
     float t[4][kTabRegs];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
