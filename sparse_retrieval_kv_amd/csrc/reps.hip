@@ -59,11 +59,13 @@ __global__ __launch_bounds__(256) void build_reps_kernel(
   const int64_t rest = item / n_kv;
   const int j = (int)(rest % max_blocks);
   const int b = (int)(rest / max_blocks);
+  // the page id is requested together with the lengths (j < max_blocks
+  // always holds), so the tile's loads wait for one round trip, not two
+  const int page = table[(int64_t)b * max_blocks + j];
   const int L = clamp_len(lens[b], max_blocks * kBlock);
   int j0 = block_begin ? block_begin[b] : 0;
   j0 = j0 < 0 ? 0 : j0;
   if (j < j0 || j >= (L >> 7)) return;
-  const int page = table[(int64_t)b * max_blocks + j];
   if ((uint64_t)(int64_t)page >= (uint64_t)n_pages) return;
   const uint16_t* K = k_pages + ((int64_t)page * n_kv + h) * (kBlock * kDim);
   const int c = lane & 15, g = lane >> 4;
