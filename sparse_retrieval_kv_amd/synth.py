@@ -67,9 +67,9 @@ class Spec:
 # The five workloads.  plant_range is the offload block range at step 0,
 # worked out by hand from the region rule (init = ceil(init/128) blocks,
 # local starts at floor((L - local)/128)):
-#   c1: L=4096, init 256, local 512 -> init blocks 2, local start 28 -> [2, 28)
-#   c2: L=65536, 1024/7192 -> 8, floor(58344/128)=455 -> [8, 455)
-#   c5: L=262144 -> 8, floor(254952/128)=1991 -> [8, 1991)
+#   tiny (1 x 4K): L=4096, init 256, local 512 -> init blocks 2, local start 28 -> [2, 28)
+#   8B layer (1 x 64K): L=65536, 1024/7192 -> 8, floor(58344/128)=455 -> [8, 455)
+#   host tier (4 x 256K): L=262144 -> 8, floor(254952/128)=1991 -> [8, 1991)
 CONFIGS = {
     1: Spec("tiny sparse decode, 1 x 4K, 8/2 heads", 1, 8, 2, context=(4096,),
             steps=1, init_tokens=256, local_tokens=512, dense_boundary=0,

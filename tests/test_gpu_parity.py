@@ -213,7 +213,7 @@ def test_append_writes_slots_and_completed_block_rep():
 def test_tiny_config_end_to_end_planted():
     batch = synth.make_batch(synth.CONFIGS[1], DEV)
     prm, sess = make_session(batch)
-    say("config 1")
+    say("tiny workload (1 x 4K, 8/2 heads)")
     prefill(batch, sess)
     step(batch, sess, 0)
     torch.cuda.synchronize()
@@ -550,7 +550,7 @@ def test_invalid_page_ids_are_skipped():
 def test_llama_layer_full_size_steps():
     batch = synth.make_batch(synth.CONFIGS[2], DEV)
     prm, sess = make_session(batch)
-    say("config 2 (64K, 64 steps)")
+    say("8B layer (1 x 64K, 64 steps)")
     prefill(batch, sess)
     for t in range(64):
         step(batch, sess, t)
@@ -564,7 +564,7 @@ def test_llama_layer_full_size_steps():
 def test_batched_ragged_full_size_sampled():
     batch = synth.make_batch(synth.CONFIGS[3], DEV)
     prm, sess = make_session(batch)
-    say("config 3 (16 x 32K-128K, shuffled)", batch.context.tolist())
+    say("batched (16 x 32K-128K, shuffled)", batch.context.tolist())
     prefill(batch, sess)
     for t in range(32):
         step(batch, sess, t)
@@ -577,7 +577,7 @@ def test_batched_ragged_full_size_sampled():
 def test_70b_shared_prefix_full_size_sampled():
     batch = synth.make_batch(synth.CONFIGS[4], DEV)
     prm, sess = make_session(batch)
-    say("config 4 (8 x 128K, 64/8, shared prefix)")
+    say("70B layer (8 x 128K, 64/8, shared prefix)")
     prefill(batch, sess)
     for t in range(16):
         step(batch, sess, t)
@@ -797,7 +797,7 @@ def test_offload_prefill_native(concurrent):
 
 
 def test_host_tier_full_size_sampled():
-    say("config 5 (4 x 256K, host tier)")
+    say("host tier (4 x 256K)")
     batch, host, sess = make_host_session(synth.CONFIGS[5])
     for t in range(16):
         step(batch, sess, t)
@@ -854,7 +854,7 @@ def test_per_sequence_selection_mixed():
 
 
 def test_per_sequence_selection_llama_layer():
-    say("per-sequence selection, config 2 (1 x 64K), steps 0 and 5")
+    say("per-sequence selection, 8B layer (1 x 64K), steps 0 and 5")
     spec = synth.scaled(synth.CONFIGS[2], steps=6)
     batch = synth.make_batch(spec, DEV)
     prm, sess = make_session(batch, select_mode=B.SELECT_PER_SEQUENCE)
