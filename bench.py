@@ -1,10 +1,12 @@
 """Decode-step benchmark of retrieval-sparse paged decode attention on one GPU.
 
-A step is one layer's decode step for the whole batch: rkv_append_select
-(write the token and a just-completed block's representation; inner-product
-scores, per-(sequence, KV head) top-k and the merged block table, in one
-launch) -> rkv_decode_attn (split-K paged attention + log-sum-exp combine).
-The host tier adds the staging of kept host-resident blocks on a side
+A step is one layer's decode step for the whole batch, one rkv_decode_step
+call: write the token and a just-completed block's representation, score the
+offload blocks (one launch), then the per-(sequence, KV head) top-k, the
+merged block table and the split-K paged attention (for a batch of one the
+top-k and merge run inside the attention launch; otherwise a top-k launch
+precedes it), then the log-sum-exp combine.  The host tier's step is
+rkv_append_select -> staging -> rkv_decode_attn, and adds the staging of kept host-resident blocks on a side
 stream (rkv_stage_resident, which copies only blocks no staging slot
 holds; copying every kept block, rkv_stage_blocks + rkv_merge_table, is
 timed beside it).
@@ -40,7 +42,8 @@ from sparse_retrieval_kv_amd.decode import DecodeSession, HostTierSession  # noq
 
 HBM_PEAK_GBS = 8000.0
 
-# HBM bytes moved by one rkv_decode_attn call (both of its kernels), from
+# HBM bytes moved by the timed attention call (both of its kernels:
+# rkv_select_attend for a batch of one, rkv_decode_attn otherwise), from
 # two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE; KiB
 # per dispatch, mean over the dispatches of the timed steps).  Each counter
 # is scaled by what it reads for a plain 1 GiB device-to-device copy:
@@ -51,7 +54,7 @@ COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 ATTN_SOURCE = os.path.join(ROOT, "sparse_retrieval_kv_amd", "csrc", "attn.hip")
 MEASURED_TRAFFIC = {
     # config: (sha256 prefix of attn.hip, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    2: ("2f58af364c4097ce", 39970.2 + 719.5, 1040.3 + 16.0),
+    2: ("215f1d3b0804443e", 40028.2 + 722.0, 1048.9 + 16.0),
     3: ("2f58af364c4097ce", 751608.5 + 1275.5, 1298.4 + 256.0),
     4: ("2f58af364c4097ce", 506502.1 + 2391.5, 2080.6 + 256.0),
 }
@@ -103,9 +106,19 @@ def attn_traffic(args):
                      rec[2] * COUNTER_SCALE["WRITE_SIZE"])
 
 
-def attn_kernel_label(impl, spec):
-    """The two kernels one rkv_decode_attn call launches; the split kernel is
+def fused_select_attend(args, spec, max_blocks):
+    """Whether the library folds the top-k into the attention launch for this
+    launch: a batch of one, MFMA attention, per-head selection, at most 1024
+    blocks per sequence."""
+    return (spec.batch == 1 and args.impl != "valu" and args.select == "per-head"
+            and max_blocks <= 1024)
+
+
+def attn_kernel_label(impl, spec, fused=False):
+    """The kernels the timed attention call launches; the split kernel is
     templated on its partition (true: a batch of one sequence)."""
+    if fused:
+        return "rkv_select_attend (attn_select_mfma_kernel + attn_combine_kernel)"
     strided = "true" if spec.batch == 1 else "false"
     split = (f"attn_valu_kernel<{spec.group}, {strided}>" if impl == "valu"
              else f"attn_mfma_kernel<{strided}>")
@@ -332,13 +345,16 @@ def main():
             # prefill: nothing staged yet (the queries repeat from pass to
             # pass, so kept staging slots would otherwise see them again)
             sess.reset_residency()
+        if host is None:
+            sess.step(qs[t], kn, vn, lens[t])
+            return t
         sess.append_select(qs[t], kn, vn, lens[t])
-        if host is not None:  # stage the kept host blocks on the side stream
-            main = torch.cuda.current_stream(dev)
-            sess.side.wait_stream(main)
-            with torch.cuda.stream(sess.side):
-                sess.stage(lens[t])
-            main.wait_stream(sess.side)
+        # stage the kept host blocks on the side stream
+        main = torch.cuda.current_stream(dev)
+        sess.side.wait_stream(main)
+        with torch.cuda.stream(sess.side):
+            sess.stage(lens[t])
+        main.wait_stream(sess.side)
         sess.attend(qs[t], lens[t])
         return t
 
@@ -381,20 +397,41 @@ def main():
                    "p50_us": float(np.percentile(chunk_us, 50)),
                    "p90_us": float(np.percentile(chunk_us, 90))}
 
-    # the attention call alone, replayed on every layer copy's current merged
-    # tables between one pair of HIP events on its stream (an event pair per
-    # launch would add its own overhead to every launch)
+    # the step's attention call alone, replayed on every layer copy between
+    # one pair of HIP events on its stream (an event pair per launch would
+    # add its own overhead to every launch): for a batch of one the
+    # selection + attention call over the scores the last step left
+    # (rkv_select_attend: one launch with the top-k folded in, + combine),
+    # otherwise rkv_decode_attn over the current merged tables
     reps_attn = max(args.steps, 2 * n_layers)
     t_last = ts[-1]
     ev0, ev1 = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    fused = host is None and fused_select_attend(args, spec, base.table_np.shape[1])
     torch.cuda.synchronize()
     ev0.record()
     for i in range(reps_attn):
-        sessions[i % n_layers].attend(qs[t_last], lens[t_last])
+        if fused:
+            sessions[i % n_layers].select_attend(qs[t_last], lens[t_last])
+        else:
+            sessions[i % n_layers].attend(qs[t_last], lens[t_last])
     ev1.record()
     torch.cuda.synchronize()
     attn_us = ev0.elapsed_time(ev1) * 1e3 / reps_attn
     kv_attn = step_bytes(spec, base.context, t_last)[0]
+    # for context beside the folded call: rkv_decode_attn alone over the
+    # merged tables the replayed calls wrote (no selection work)
+    attn_only = None
+    if fused:
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(reps_attn):
+            sessions[i % n_layers].attend(qs[t_last], lens[t_last])
+        ev1.record()
+        torch.cuda.synchronize()
+        us = ev0.elapsed_time(ev1) * 1e3 / reps_attn
+        attn_only = {"kernel": attn_kernel_label(args.impl, spec), "avg_us": us,
+                     "achieved_gbs": kv_attn / (us * 1e-6) / 1e9,
+                     "frac": kv_attn / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
 
     staging = None
     if host is not None:
@@ -488,7 +525,7 @@ def main():
         "attended_kv_pct_peak_step": 100.0 * step_gbs / HBM_PEAK_GBS,
         "roofline": {
             "bound": "hbm",
-            "kernel": attn_kernel_label(args.impl, spec),
+            "kernel": attn_kernel_label(args.impl, spec, fused),
             "achieved": attn_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -499,8 +536,10 @@ def main():
                                "scaled by a 1 GiB copy's readings"),
             "bytes_per_launch": float(kv_attn),
             "avg_launch_us": float(attn_us),
-            "timing": (f"{reps_attn} back-to-back rkv_decode_attn calls over the "
-                       f"{n_layers} layer copies between one HIP event pair"),
+            "decode_attn_alone": attn_only,
+            "timing": (f"{reps_attn} back-to-back "
+                       f"{'rkv_select_attend' if fused else 'rkv_decode_attn'} calls over "
+                       f"the {n_layers} layer copies between one HIP event pair"),
         },
         "cpu_baseline": cpu,
     }

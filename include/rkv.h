@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define RKV_ABI_VERSION 2
+#define RKV_ABI_VERSION 3
 #define RKV_BLOCK_SIZE 128
 #define RKV_HEAD_DIM 128
 #define RKV_PPM_ONE 1000000
@@ -417,6 +417,74 @@ rkv_status rkv_decode_attn(const rkv_params* params, const uint16_t* q,
                            const int32_t* n_merged, int32_t m_cap,
                            const int32_t* lens, int32_t batch, float* out,
                            void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
+ * rkv_select_attend -- the top-k and merge of rkv_select from given scores,
+ * followed by rkv_decode_attn over the merged table (openGauss page,
+ * "Overall Solution": the top-K blocks by inner product joined with the
+ * initial and window blocks; rkmt.cn ATB article, sections 1.1 and 2.2: the
+ * attention over those pages).  Same results, bit for bit, as those two
+ * steps: sel_ids / n_sel / merged / n_merged as rkv_select writes them and
+ * out as rkv_decode_attn writes it.
+ *   scores [batch][n_kv_heads][max_blocks] device fp32: entry j of (b, h)
+ *          is the inner-product score of block j (the group's query heads
+ *          summed, per-sequence mode: summed over the heads by the top-k as
+ *          in rkv_select); only the offload blocks' entries are read, and
+ *          only for lists with 0 < k < n_off.  rkv_select,
+ *          rkv_append_select and rkv_decode_step leave exactly these scores
+ *          in the first batch * n_kv_heads * max_blocks * 4 bytes of their
+ *          select workspace.
+ * For a batch of one sequence with per-head selection, MFMA attention
+ * (attn_impl != RKV_ATTN_VALU) and max_blocks <= 1024, the top-k and merge
+ * run inside the attention launch: each of the P attention waves of a
+ * (sequence, KV head) list finds the list's selection from the scores
+ * itself (the same set; the list's first wave writes the selection and
+ * merged outputs), so the step has no separate top-k launch.  Other shapes
+ * take the top-k launch and then rkv_decode_attn's launches.
+ * Other arguments as rkv_select (prompt_lens, k_cap, m_cap >= max_blocks,
+ * merged and n_merged required) and rkv_decode_attn (workspace:
+ * rkv_attn_workspace_size(params, batch, m_cap) bytes; calls that overlap
+ * on one workspace race).
+ * Errors: RKV_ERR_INVALID_ARG, RKV_ERR_UNSUPPORTED, RKV_ERR_WORKSPACE,
+ * RKV_ERR_HIP.
+ */
+rkv_status rkv_select_attend(const rkv_params* params, const uint16_t* q,
+                             const uint16_t* k_pages, const uint16_t* v_pages,
+                             int64_t n_pages, const int32_t* block_table,
+                             int32_t max_blocks, const int32_t* lens,
+                             const int32_t* prompt_lens, int32_t batch,
+                             const float* scores, int32_t* sel_ids,
+                             int32_t* n_sel, int32_t k_cap, int32_t* merged,
+                             int32_t* n_merged, int32_t m_cap, float* out,
+                             void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/*
+ * rkv_decode_step -- one decode step of one layer: rkv_append_select
+ * (append the decoded token, score the offload blocks) and then
+ * rkv_select_attend on the scores it left in select_workspace.  Same
+ * results, bit for bit, as rkv_append_select (with the merged table)
+ * followed by rkv_decode_attn.  For a batch of one sequence (see
+ * rkv_select_attend) that is three launches: scoring with the append, the
+ * attention with the selection folded in, the combine.
+ *   select_workspace >= rkv_select_workspace_size(params, batch, max_blocks)
+ *   attn_workspace   >= rkv_attn_workspace_size(params, batch, m_cap),
+ *                       16-byte aligned, not the select workspace.
+ * Other arguments as rkv_append_select and rkv_decode_attn.
+ * Errors: RKV_ERR_INVALID_ARG, RKV_ERR_UNSUPPORTED, RKV_ERR_WORKSPACE,
+ * RKV_ERR_HIP.
+ */
+rkv_status rkv_decode_step(const rkv_params* params, const uint16_t* k_new,
+                           const uint16_t* v_new, uint16_t* k_pages,
+                           uint16_t* v_pages, int64_t n_pages, const uint16_t* q,
+                           float* reps, const int32_t* block_table,
+                           const int32_t* lens, const int32_t* prompt_lens,
+                           int32_t batch, int32_t max_blocks, int32_t* sel_ids,
+                           int32_t* n_sel, int32_t k_cap, int32_t* merged,
+                           int32_t* n_merged, int32_t m_cap, float* out,
+                           void* select_workspace, size_t select_workspace_bytes,
+                           void* attn_workspace, size_t attn_workspace_bytes,
                            hipStream_t stream);
 
 /*

@@ -82,6 +82,12 @@ _SIGS = {
     "rkv_attn_workspace_size": (_SZ, [_PP, _I32, _I32]),
     "rkv_decode_attn": (ctypes.c_int, [_PP, _P, _P, _P, _I64, _P, _P, _I32, _P, _I32,
                                        _P, _P, _SZ, _P]),
+    "rkv_select_attend": (ctypes.c_int, [_PP, _P, _P, _P, _I64, _P, _I32, _P, _P, _I32,
+                                         _P, _P, _P, _I32, _P, _P, _I32, _P, _P, _SZ,
+                                         _P]),
+    "rkv_decode_step": (ctypes.c_int, [_PP, _P, _P, _P, _P, _I64, _P, _P, _P, _P, _P,
+                                       _I32, _I32, _P, _P, _I32, _P, _P, _I32, _P, _P,
+                                       _SZ, _P, _SZ, _P]),
     "rkv_read_probe": (ctypes.c_int, [_P, _SZ, _P, _P]),
 }
 
@@ -419,6 +425,34 @@ class PreparedStep:
             _dyn(lens, torch.int32, self._lens_shape, "lens", self._dev), plens, batch,
             max_blocks,
             sel, nsel, k_cap, merged, nmerged, m_cap, ws, ws_bytes,
+            torch.cuda.current_stream(self._dev).cuda_stream))
+
+    def decode_step(self, q, k_new, v_new, lens):
+        """rkv_decode_step: append + scores, then the selection and the
+        attention (folded into one launch for a batch of one)."""
+        (kp, vp, n_pages, reps, bt, plens, batch, max_blocks, sel, nsel, k_cap,
+         merged, nmerged, m_cap, ws, ws_bytes) = self._sel_args
+        out, wa, wa_bytes = self._attn_args[7:]
+        _check(self._L.rkv_decode_step(
+            self._pp, _dyn(k_new, torch.int16, self._kv_shape, "k_new", self._dev),
+            _dyn(v_new, torch.int16, self._kv_shape, "v_new", self._dev), kp, vp, n_pages,
+            _dyn(q, torch.int16, self._q_shape, "q", self._dev), reps, bt,
+            _dyn(lens, torch.int32, self._lens_shape, "lens", self._dev), plens, batch,
+            max_blocks, sel, nsel, k_cap, merged, nmerged, m_cap, out, ws, ws_bytes,
+            wa, wa_bytes, torch.cuda.current_stream(self._dev).cuda_stream))
+
+    def select_attend(self, q, lens):
+        """rkv_select_attend on the scores the last selection left in the
+        select workspace."""
+        (kp, vp, n_pages, reps, bt, plens, batch, max_blocks, sel, nsel, k_cap,
+         merged, nmerged, m_cap, ws, ws_bytes) = self._sel_args
+        out, wa, wa_bytes = self._attn_args[7:]
+        if ws is None:
+            raise ValueError("no select workspace holds scores")
+        _check(self._L.rkv_select_attend(
+            self._pp, _dyn(q, torch.int16, self._q_shape, "q", self._dev), kp, vp, n_pages,
+            bt, max_blocks, _dyn(lens, torch.int32, self._lens_shape, "lens", self._dev),
+            plens, batch, ws, sel, nsel, k_cap, merged, nmerged, m_cap, out, wa, wa_bytes,
             torch.cuda.current_stream(self._dev).cuda_stream))
 
     def decode_attn(self, q, lens):

@@ -584,35 +584,16 @@ __device__ __forceinline__ void split_body(const AttnArgs& a) {
   }
 }
 
-// Single-sequence partition (batch of one: every list has the same length,
-// since the regions and k depend only on the sequence).  Wave w takes list
-// w mod NB and, as piece c = w / NB of P per list, the list's units c,
-// c + P, c + 2P, ...: its units sit at positions that do not depend on the
-// list length, so the page ids of its first 64 units are requested together
-// with the length -- one dependent memory round trip fewer before the first
-// K tile than the range split.  Each list's units are dealt evenly (+-1 per
-// wave) and the pieces are numbered by c.
-template <class Math>
-__device__ __forceinline__ void strided_body(const AttnArgs& a) {
-  const int lane = threadIdx.x;
-  const int col = lane & 15, grp = lane >> 4;
-  const int NB = a.batch * a.n_kv;
+// The unit loop of the single-sequence partition for wave c of list bh,
+// whose list has `units` units (L: the sequence length); page_at(i) gives
+// the page id of the wave's i-th unit (unit c + i P).
+template <class Math, class PageAt>
+__device__ __forceinline__ void strided_loop(const AttnArgs& a, Math& math, int bh,
+                                             int c, int units, int L,
+                                             PageAt page_at, int lane, int col,
+                                             int grp) {
   const int P = a.per_list;
-  const int bh = (int)(blockIdx.x % (unsigned)NB);
-  const int c = (int)(blockIdx.x / (unsigned)NB);
-  const int b = bh / a.n_kv, h = bh - b * a.n_kv;
-  const int32_t* mrow = a.merged + (int64_t)bh * a.m_cap;
-  // --- one memory round trip: the list length, the sequence length, the
-  // page ids of this wave's first 64 units and the query rows ---
-  const int units = units_of(a, bh);
-  const int L = clamp_len(a.lens[b], a.max_len);
-  const int64_t e_lane = ((int64_t)c + (int64_t)lane * P) >> 1;
-  const int pref = e_lane < a.m_cap ? mrow[e_lane] : 0;
-  Math math;
-  math.begin(a, b, h, col, grp);
-  // L is used only past the branch below; without this use the compiler
-  // would request it only after n_merged has arrived (a second round trip)
-  __asm__ volatile("" ::"s"(L));
+  const int h = bh % a.n_kv;
   if (c >= units) return;  // uniform over the wave
   if (c == 0 && lane == 0) a.n_pieces[bh] = units < P ? units : P;
   const int n_mine = (units - c + P - 1) / P;
@@ -628,10 +609,6 @@ __device__ __forceinline__ void strided_body(const AttnArgs& a) {
     const int e = u >> 1;
     const int v = (e == n - 1 ? last_valid : kBlock) - kUnit * (u & 1);
     return v < 0 ? 0 : (v > kUnit ? kUnit : v);
-  };
-  // page id of this wave's i-th unit: requested above for i < 64
-  auto page_at = [&](int i) {
-    return i < 64 ? __shfl(pref, i) : mrow[(c + (int64_t)i * P) >> 1];
   };
 
   int page = page_at(0);
@@ -658,6 +635,239 @@ __device__ __forceinline__ void strided_body(const AttnArgs& a) {
     math.accumulate(s, vf, valid, a.scale_log2, col, grp);
   }
   math.finish(a, (int64_t)bh * a.piece_cap + c, lane, col, grp);
+}
+
+// Single-sequence partition (batch of one: every list has the same length,
+// since the regions and k depend only on the sequence).  Wave w takes list
+// w mod NB and, as piece c = w / NB of P per list, the list's units c,
+// c + P, c + 2P, ...: its units sit at positions that do not depend on the
+// list length, so the page ids of its first 64 units are requested together
+// with the length -- one dependent memory round trip fewer before the first
+// K tile than the range split.  Each list's units are dealt evenly (+-1 per
+// wave) and the pieces are numbered by c.
+template <class Math>
+__device__ __forceinline__ void strided_body(const AttnArgs& a) {
+  const int lane = threadIdx.x;
+  const int col = lane & 15, grp = lane >> 4;
+  const int NB = a.batch * a.n_kv;
+  const int P = a.per_list;
+  const int bh = (int)(blockIdx.x % (unsigned)NB);
+  const int c = (int)(blockIdx.x / (unsigned)NB);
+  const int b = bh / a.n_kv, h = bh - b * a.n_kv;
+  const int32_t* mrow = a.merged + (int64_t)bh * a.m_cap;
+  // --- one memory round trip: the list length, the sequence length, the
+  // page ids of this wave's first 64 units and the query rows ---
+  const int units = units_of(a, bh);
+  const int L = clamp_len(a.lens[b], a.max_len);
+  const int64_t e_lane = ((int64_t)c + (int64_t)lane * P) >> 1;
+  const int pref = e_lane < a.m_cap ? mrow[e_lane] : 0;
+  Math math;
+  math.begin(a, b, h, col, grp);
+  // L is used only past the branch in strided_loop; without this use the
+  // compiler would request it only after n_merged has arrived (a second
+  // round trip)
+  __asm__ volatile("" ::"s"(L));
+  // page id of this wave's i-th unit: requested above for i < 64
+  auto page_at = [&](int i) {
+    return i < 64 ? __shfl(pref, i) : mrow[(c + (int64_t)i * P) >> 1];
+  };
+  strided_loop(a, math, bh, c, units, L, page_at, lane, col, grp);
+}
+
+// ---------------------------------------------------------------------------
+// Top-k and merge inside the attention launch (batch of one).
+//
+// The selection of a (sequence, KV head) list depends only on the list's
+// scores, the sequence length and the parameters, and fits one wave when
+// max_blocks <= 1024 (16 blocks per lane).  So instead of a separate top-k
+// launch, every one of the list's P attention waves finds the selection
+// itself from the same inputs -- the same set, since the set is defined by
+// its values alone -- builds the merged page list in its own LDS and then
+// runs the single-sequence unit loop on it.  The list's first wave also
+// writes sel_ids, n_sel, merged and n_merged, as the top-k launch would.
+//
+// Selection (openGauss page, "Overall Solution": the top-K blocks by
+// inner product): scores become order keys (unsigned order = float order);
+// the k-th largest key T is found by deciding its bits from the top, one
+// count of keys >= candidate per bit (ballots over the wave), stopping as
+// soon as exactly k keys are >= T.  Kept: every key > T and, when the
+// search ran to the last bit, the lowest-index keys == T up to k.  Lane l
+// holds blocks l, l + 64, ..., so ascending (register, lane) is ascending
+// block order.
+// ---------------------------------------------------------------------------
+constexpr int kFusedRegs = kFusedMaxBlocks / 64;
+
+struct SelectIn {
+  const int32_t* table;      // [1][max_blocks]
+  const uint32_t* scores;    // [n_kv][max_blocks] raw fp32 bits
+  const int32_t* prompt_lens;  // [1] or null (then lens)
+  int max_blocks;
+  int init_tokens, local_tokens, topk_ppm, dense_boundary;
+  int32_t* sel_ids;   // [n_kv][k_cap]
+  int32_t* n_sel;     // [n_kv]
+  int k_cap;
+  int32_t* merged;    // [n_kv][m_cap]
+  int32_t* n_merged;  // [n_kv]
+};
+
+// The kept offload blocks of one list as per-lane bit masks (bit i: block
+// lane + 64 i), for lists whose offload range ends within the first NR
+// registers; cbits marks the offload blocks, 0 < k < n_off.
+template <int NR>
+__device__ __forceinline__ uint32_t kept_blocks(const uint32_t (&key)[kFusedRegs],
+                                                uint32_t cbits, int k, int n_off,
+                                                int lane) {
+  // non-offload blocks as key 0: every threshold tried below is >= 1, so
+  // they are never counted (an offload block whose key is 0, a NaN score,
+  // is the lowest key and is not counted either, correctly)
+  uint32_t keyc[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) keyc[i] = ((cbits >> i) & 1u) ? key[i] : 0u;
+  uint32_t T = 0;
+  int cT = n_off;  // offload keys >= T
+  for (int bit = 31; bit >= 0; --bit) {
+    if (cT == k) break;  // exactly k keys >= T: they are the top k
+    const uint32_t t = T | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) cnt += __popcll(__ballot(keyc[i] >= t));
+    if (cnt >= k) {
+      T = t;
+      cT = cnt;
+    }
+  }
+  uint32_t kbits = 0;
+  if (cT == k) {  // here T >= 1 (k < n_off)
+#pragma unroll
+    for (int i = 0; i < NR; ++i) kbits |= keyc[i] >= T ? 1u << i : 0u;
+    return kbits;
+  }
+  // T is the k-th largest key: keys > T, then the lowest blocks with key T
+  int g = 0;
+#pragma unroll
+  for (int i = 0; i < NR; ++i)
+    g += __popcll(__ballot(((cbits >> i) & 1u) && key[i] > T));
+  const int need = k - g;
+  int eq_before = 0;
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const bool c = ((cbits >> i) & 1u) != 0u;
+    const bool eq = c && key[i] == T;
+    const uint64_t em = __ballot(eq);
+    const bool take = (c && key[i] > T) || (eq && eq_before + lanes_below(em) < need);
+    kbits |= take ? 1u << i : 0u;
+    eq_before += __popcll(em);
+  }
+  return kbits;
+}
+
+template <class Math>
+__device__ __forceinline__ void select_strided_body(const AttnArgs& a,
+                                                    const SelectIn& f) {
+  __shared__ int mlist[kFusedMaxBlocks];
+  const int lane = threadIdx.x;
+  const int col = lane & 15, grp = lane >> 4;
+  const int NB = a.n_kv;  // one sequence
+  const int bh = (int)(blockIdx.x % (unsigned)NB);
+  const int c = (int)(blockIdx.x / (unsigned)NB);
+  const int mb = f.max_blocks;
+  const uint32_t* srow_in = f.scores + (int64_t)bh * mb;
+
+  // --- one memory round trip: lengths, the block-table row, the list's
+  // scores and the query rows (clamped indexes, no lane conditions) ---
+  const int lraw_v = a.lens[0];
+  const int plen_v = (f.prompt_lens ? f.prompt_lens : a.lens)[0];
+  int tab[kFusedRegs];
+  uint32_t raw[kFusedRegs];
+#pragma unroll
+  for (int i = 0; i < kFusedRegs; ++i) {
+    int j = lane + 64 * i;
+    j = j < mb ? j : mb - 1;
+    tab[i] = f.table[j];
+    raw[i] = srow_in[j];
+  }
+  Math math;
+  math.begin(a, 0, bh, col, grp);
+  // the lengths are the same on every lane: scalar registers from here on,
+  // so the region arithmetic and the selection's branches stay scalar
+  const int lraw = __builtin_amdgcn_readfirstlane(lraw_v);
+  const int plen = __builtin_amdgcn_readfirstlane(plen_v);
+
+  // --- regions and k, as the top-k launch takes them ---
+  const int Ls = clamp_len(lraw, mb * kBlock);
+  const Regions R = regions_of(Ls, f.init_tokens, f.local_tokens);
+  const bool dense = plen < f.dense_boundary || f.topk_ppm >= kPpmOne;
+  int k = dense ? R.n_off : topk_of(R.n_off, f.topk_ppm);
+  k = k < R.n_off ? k : R.n_off;
+  const bool ranked = k > 0 && k < R.n_off;
+  const int ls = R.n_init + R.n_off;  // offload end (= first local block)
+
+  // per-lane bit masks over the registers (bit i: block lane + 64 i): the
+  // list's offload blocks and the kept ones
+  uint32_t cbits = 0, kbits = 0;
+#pragma unroll
+  for (int i = 0; i < kFusedRegs; ++i) {
+    const int j = lane + 64 * i;
+    cbits |= (j >= R.n_init && j < ls) ? 1u << i : 0u;
+  }
+  if (ranked) {  // uniform
+    uint32_t key[kFusedRegs];
+#pragma unroll
+    for (int i = 0; i < kFusedRegs; ++i) key[i] = order_key(__uint_as_float(raw[i]));
+    kbits = (ls + 63) >> 6 <= 8 ? kept_blocks<8>(key, cbits, k, R.n_off, lane)
+                                : kept_blocks<16>(key, cbits, k, R.n_off, lane);
+  }
+
+  // --- merged page list (init blocks, kept blocks, local blocks) ---
+  const int lstart = R.local_start > R.n_init ? R.local_start : R.n_init;
+  const int n_m = R.n_init + k + (R.nb - lstart);
+  const bool writer = c == 0;
+  int32_t* sel_out = f.sel_ids + (int64_t)bh * f.k_cap;
+  int32_t* m_out = f.merged + (int64_t)bh * a.m_cap;
+  int pos_before = 0;
+#pragma unroll
+  for (int i = 0; i < kFusedRegs; ++i) {
+    if (64 * i < R.nb) {  // uniform
+      const int j = lane + 64 * i;
+      const bool kj = ((kbits >> i) & 1u) != 0u;
+      const uint64_t km = __ballot(kj);
+      const int pos = pos_before + lanes_below(km);
+      int dst = -1;
+      if (j < R.nb) {
+        if (j < R.n_init)
+          dst = j;
+        else if (j >= lstart)
+          dst = R.n_init + k + (j - lstart);
+        else if (k == R.n_off)
+          dst = j;
+        else if (kj)
+          dst = R.n_init + pos;
+      }
+      if (dst >= 0) {
+        mlist[dst] = tab[i];
+        if (writer) m_out[dst] = tab[i];
+      }
+      if (writer && kj) sel_out[pos] = j;
+      pos_before += __popcll(km);
+    }
+  }
+  if (writer && !ranked)
+    for (int r = lane; r < k; r += 64) sel_out[r] = R.n_init + r;
+  if (writer && lane == 0) {
+    f.n_sel[bh] = k;
+    f.n_merged[bh] = n_m;
+  }
+  __syncthreads();  // the list in LDS is complete (one wave per workgroup)
+
+  const int L = clamp_len(lraw, a.max_len);
+  const int P = a.per_list;
+  auto page_at = [&](int i) { return mlist[(c + i * P) >> 1]; };
+  strided_loop(a, math, bh, c, 2 * n_m, L, page_at, lane, col, grp);
+}
+
+__global__ __launch_bounds__(64) void attn_select_mfma_kernel(AttnArgs a,
+                                                              SelectIn f) {
+  select_strided_body<MfmaMath>(a, f);
 }
 
 template <class Math, bool STRIDED>
@@ -809,14 +1019,13 @@ AttnPlan plan_attention(int batch, int n_q_heads, int n_kv_heads, int waves,
   return p;
 }
 
-hipError_t launch_decode_attn(const Method& m, bool use_mfma,
-                              const AttnPlan& plan, float scale,
-                              const uint16_t* q, const uint16_t* k_pages,
-                              const uint16_t* v_pages, int64_t n_pages,
-                              const int32_t* merged, const int32_t* n_merged,
-                              int m_cap, const int32_t* lens, int batch,
-                              float* out, void* workspace, hipStream_t stream) {
-  if (batch == 0) return hipSuccess;
+namespace {
+
+AttnArgs attn_args(const Method& m, const AttnPlan& plan, float scale,
+                   const uint16_t* q, const uint16_t* k_pages,
+                   const uint16_t* v_pages, int64_t n_pages,
+                   const int32_t* merged, const int32_t* n_merged, int m_cap,
+                   const int32_t* lens, int batch, void* workspace) {
   AttnArgs a;
   a.q = q;
   a.k_pages = k_pages;
@@ -841,6 +1050,29 @@ hipError_t launch_decode_attn(const Method& m, bool use_mfma,
   a.n_waves = plan.n_waves;
   a.per_list = plan.per_list;
   a.scale_log2 = scale * 1.4426950408889634f;
+  return a;
+}
+
+hipError_t launch_combine(const Method& m, const AttnArgs& a, int batch,
+                          float* out, hipStream_t stream) {
+  hipLaunchKernelGGL(attn_combine_kernel,
+                     dim3((unsigned)(batch * m.n_q_heads * kCombSlices)), dim3(64), 0,
+                     stream, a, out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_attn(const Method& m, bool use_mfma,
+                              const AttnPlan& plan, float scale,
+                              const uint16_t* q, const uint16_t* k_pages,
+                              const uint16_t* v_pages, int64_t n_pages,
+                              const int32_t* merged, const int32_t* n_merged,
+                              int m_cap, const int32_t* lens, int batch,
+                              float* out, void* workspace, hipStream_t stream) {
+  if (batch == 0) return hipSuccess;
+  const AttnArgs a = attn_args(m, plan, scale, q, k_pages, v_pages, n_pages, merged,
+                               n_merged, m_cap, lens, batch, workspace);
   const int64_t waves =
       plan.per_list > 0 ? (int64_t)batch * m.n_kv_heads * plan.per_list : plan.n_waves;
   const dim3 grid((unsigned)waves), block(64);
@@ -869,10 +1101,46 @@ hipError_t launch_decode_attn(const Method& m, bool use_mfma,
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel,
-                     dim3((unsigned)(batch * m.n_q_heads * kCombSlices)), dim3(64), 0,
-                     stream, a, out);
-  return hipGetLastError();
+  return launch_combine(m, a, batch, out, stream);
+}
+
+bool fused_select_attn_ok(const Method& m, bool use_mfma, const AttnPlan& plan,
+                          int batch, int max_blocks) {
+  return batch == 1 && use_mfma && !m.per_sequence && plan.per_list > 0 &&
+         max_blocks <= kFusedMaxBlocks;
+}
+
+hipError_t launch_select_attn(const Method& m, bool use_mfma, const AttnPlan& plan,
+                              float scale, const uint16_t* q,
+                              const uint16_t* k_pages, const uint16_t* v_pages,
+                              int64_t n_pages, const int32_t* table, int max_blocks,
+                              const int32_t* lens, const int32_t* prompt_lens,
+                              const uint32_t* scores, int32_t* sel_ids,
+                              int32_t* n_sel, int k_cap, int32_t* merged,
+                              int32_t* n_merged, int m_cap, float* out,
+                              void* workspace, hipStream_t stream) {
+  if (!fused_select_attn_ok(m, use_mfma, plan, 1, max_blocks)) return hipErrorInvalidValue;
+  const AttnArgs a = attn_args(m, plan, scale, q, k_pages, v_pages, n_pages, merged,
+                               n_merged, m_cap, lens, 1, workspace);
+  SelectIn f;
+  f.table = table;
+  f.scores = scores;
+  f.prompt_lens = prompt_lens;
+  f.max_blocks = max_blocks;
+  f.init_tokens = m.init_tokens;
+  f.local_tokens = m.local_tokens;
+  f.topk_ppm = m.topk_ppm;
+  f.dense_boundary = m.dense_boundary;
+  f.sel_ids = sel_ids;
+  f.n_sel = n_sel;
+  f.k_cap = k_cap;
+  f.merged = merged;
+  f.n_merged = n_merged;
+  const dim3 grid((unsigned)((int64_t)m.n_kv_heads * plan.per_list)), block(64);
+  hipLaunchKernelGGL(attn_select_mfma_kernel, grid, block, 0, stream, a, f);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_combine(m, a, 1, out, stream);
 }
 
 }  // namespace rkv

@@ -520,6 +520,152 @@ rkv_status rkv_decode_attn(const rkv_params* params, const uint16_t* q,
       "rkv_decode_attn launch");
 }
 
+namespace {
+
+// Checks of rkv_select_attend (also the attention half of rkv_decode_step).
+rkv_status select_attend_checks(const rkv_params* params, rkv::Method* m,
+                                const uint16_t* q, const uint16_t* k_pages,
+                                const uint16_t* v_pages, int64_t n_pages,
+                                const int32_t* block_table, int32_t max_blocks,
+                                const int32_t* lens, int32_t batch,
+                                const int32_t* sel_ids, const int32_t* n_sel,
+                                int32_t k_cap, const int32_t* merged,
+                                const int32_t* n_merged, int32_t m_cap,
+                                const float* out, const void* workspace,
+                                size_t workspace_bytes, rkv::AttnPlan* plan) {
+  RKV_TRY(check_params(params, m));
+  RKV_TRY(check_sizes(batch, max_blocks));
+  RKV_REQUIRE(k_cap >= 0, RKV_ERR_INVALID_ARG, "k_cap %d < 0", k_cap);
+  RKV_REQUIRE(m_cap >= max_blocks && m_cap <= RKV_MAX_BLOCKS, RKV_ERR_INVALID_ARG,
+              "m_cap %d outside [max_blocks %d, %d]", m_cap, max_blocks,
+              RKV_MAX_BLOCKS);
+  RKV_TRY(check_extent(params, batch, max3(max_blocks, k_cap, m_cap)));
+  RKV_TRY(check_pool(k_pages, n_pages, "k_pages"));
+  RKV_TRY(check_pool(v_pages, n_pages, "v_pages"));
+  RKV_REQUIRE(q && block_table && lens && n_sel && (sel_ids || k_cap == 0) &&
+                  merged && n_merged && out,
+              RKV_ERR_INVALID_ARG,
+              "q, block_table, lens, sel_ids, n_sel, merged, n_merged and out "
+              "must not be NULL");
+  RKV_REQUIRE(aligned16(q) && aligned16(out), RKV_ERR_INVALID_ARG,
+              "q and out must be 16-byte aligned");
+  RKV_REQUIRE(k_cap >= topk_cap(params, max_blocks), RKV_ERR_INVALID_ARG,
+              "k_cap %d below the required %lld", k_cap,
+              (long long)topk_cap(params, max_blocks));
+  const bool use_mfma = params->attn_impl != RKV_ATTN_VALU;
+  RKV_REQUIRE(use_mfma || m->group == 1 || m->group == 2 || m->group == 4 ||
+                  m->group == 8,
+              RKV_ERR_UNSUPPORTED,
+              "the VALU attention variant supports groups 1, 2, 4 and 8 (got %d)",
+              m->group);
+  *plan = rkv::plan_attention(batch, m->n_q_heads, m->n_kv_heads,
+                              params->split_waves, m_cap, rkv::device_cu_count());
+  RKV_REQUIRE(workspace_bytes >= plan->total_bytes &&
+                  (plan->total_bytes == 0 || workspace != nullptr),
+              RKV_ERR_WORKSPACE, "attention workspace %zu bytes, need %zu",
+              workspace_bytes, plan->total_bytes);
+  RKV_REQUIRE(aligned16(workspace), RKV_ERR_INVALID_ARG,
+              "attention workspace is not 16-byte aligned");
+  return RKV_OK;
+}
+
+// Top-k + merge from the scores, then attention: one fused launch where
+// fused_select_attn_ok holds, else the top-k launch and rkv_decode_attn's.
+hipError_t select_attend_launch(const rkv_params* params, const rkv::Method& m,
+                                const rkv::AttnPlan& plan, const uint16_t* q,
+                                const uint16_t* k_pages, const uint16_t* v_pages,
+                                int64_t n_pages, const int32_t* block_table,
+                                int32_t max_blocks, const int32_t* lens,
+                                const int32_t* prompt_lens, int32_t batch,
+                                const uint32_t* scores, int32_t* sel_ids,
+                                int32_t* n_sel, int32_t k_cap, int32_t* merged,
+                                int32_t* n_merged, int32_t m_cap, float* out,
+                                void* workspace, hipStream_t stream) {
+  if (batch == 0) return hipSuccess;
+  const bool use_mfma = params->attn_impl != RKV_ATTN_VALU;
+  if (rkv::fused_select_attn_ok(m, use_mfma, plan, batch, max_blocks))
+    return rkv::launch_select_attn(m, use_mfma, plan, params->scale, q, k_pages,
+                                   v_pages, n_pages, block_table, max_blocks, lens,
+                                   prompt_lens, scores, sel_ids, n_sel, k_cap,
+                                   merged, n_merged, m_cap, out, workspace, stream);
+  hipError_t e = rkv::launch_topk(m, block_table, lens, prompt_lens, batch,
+                                  max_blocks, scores, sel_ids, n_sel, k_cap,
+                                  merged, n_merged, m_cap, stream);
+  if (e != hipSuccess) return e;
+  return rkv::launch_decode_attn(m, use_mfma, plan, params->scale, q, k_pages,
+                                 v_pages, n_pages, merged, n_merged, m_cap, lens,
+                                 batch, out, workspace, stream);
+}
+
+}  // namespace
+
+rkv_status rkv_select_attend(const rkv_params* params, const uint16_t* q,
+                             const uint16_t* k_pages, const uint16_t* v_pages,
+                             int64_t n_pages, const int32_t* block_table,
+                             int32_t max_blocks, const int32_t* lens,
+                             const int32_t* prompt_lens, int32_t batch,
+                             const float* scores, int32_t* sel_ids,
+                             int32_t* n_sel, int32_t k_cap, int32_t* merged,
+                             int32_t* n_merged, int32_t m_cap, float* out,
+                             void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  rkv::Method m;
+  rkv::AttnPlan plan;
+  RKV_TRY(select_attend_checks(params, &m, q, k_pages, v_pages, n_pages, block_table,
+                               max_blocks, lens, batch, sel_ids, n_sel, k_cap,
+                               merged, n_merged, m_cap, out, workspace,
+                               workspace_bytes, &plan));
+  RKV_REQUIRE(scores != nullptr, RKV_ERR_INVALID_ARG, "scores must not be NULL");
+  return hip_status(
+      select_attend_launch(params, m, plan, q, k_pages, v_pages, n_pages, block_table,
+                           max_blocks, lens, prompt_lens, batch,
+                           reinterpret_cast<const uint32_t*>(scores), sel_ids,
+                           n_sel, k_cap, merged, n_merged, m_cap, out, workspace,
+                           stream),
+      "rkv_select_attend launch");
+}
+
+rkv_status rkv_decode_step(const rkv_params* params, const uint16_t* k_new,
+                           const uint16_t* v_new, uint16_t* k_pages,
+                           uint16_t* v_pages, int64_t n_pages, const uint16_t* q,
+                           float* reps, const int32_t* block_table,
+                           const int32_t* lens, const int32_t* prompt_lens,
+                           int32_t batch, int32_t max_blocks, int32_t* sel_ids,
+                           int32_t* n_sel, int32_t k_cap, int32_t* merged,
+                           int32_t* n_merged, int32_t m_cap, float* out,
+                           void* select_workspace, size_t select_workspace_bytes,
+                           void* attn_workspace, size_t attn_workspace_bytes,
+                           hipStream_t stream) {
+  rkv::Method m;
+  rkv::AttnPlan plan;
+  RKV_TRY(select_attend_checks(params, &m, q, k_pages, v_pages, n_pages, block_table,
+                               max_blocks, lens, batch, sel_ids, n_sel, k_cap,
+                               merged, n_merged, m_cap, out, attn_workspace,
+                               attn_workspace_bytes, &plan));
+  RKV_REQUIRE(reps != nullptr && aligned16(reps), RKV_ERR_INVALID_ARG,
+              "reps must be a 16-byte aligned, non-NULL pointer");
+  RKV_REQUIRE(k_new && v_new, RKV_ERR_INVALID_ARG, "k_new and v_new must not be NULL");
+  RKV_REQUIRE(aligned16(k_new) && aligned16(v_new), RKV_ERR_INVALID_ARG,
+              "k_new and v_new must be 16-byte aligned");
+  const size_t need = rkv_select_workspace_size(params, batch, max_blocks);
+  RKV_REQUIRE(select_workspace_bytes >= need && (need == 0 || select_workspace),
+              RKV_ERR_WORKSPACE, "select workspace %zu bytes, need %zu",
+              select_workspace_bytes, need);
+  RKV_REQUIRE(select_workspace != attn_workspace || need == 0, RKV_ERR_INVALID_ARG,
+              "the select and attention workspaces must not be the same buffer");
+  uint32_t* scores = static_cast<uint32_t*>(select_workspace);
+  const rkv::AppendOp op{k_new, v_new, k_pages, v_pages, n_pages, reps};
+  hipError_t e = rkv::launch_score(m, q, reps, block_table, lens, prompt_lens, batch,
+                                   max_blocks, scores, &op, stream);
+  if (e != hipSuccess) return hip_status(e, "rkv_decode_step launch");
+  return hip_status(
+      select_attend_launch(params, m, plan, q, k_pages, v_pages, n_pages, block_table,
+                           max_blocks, lens, prompt_lens, batch, scores, sel_ids,
+                           n_sel, k_cap, merged, n_merged, m_cap, out,
+                           attn_workspace, stream),
+      "rkv_decode_step launch");
+}
+
 rkv_status rkv_read_probe(const void* buffer, size_t bytes, uint32_t* sink,
                           hipStream_t stream) {
   RKV_REQUIRE(buffer && sink, RKV_ERR_INVALID_ARG, "buffer and sink must not be NULL");

@@ -49,6 +49,19 @@ __device__ __forceinline__ int topk_of(int n_off, int ppm) {
   return (int)(((int64_t)n_off * ppm + 999999) / 1000000);
 }
 
+// fp32 -> uint32 whose unsigned order is the float order (-0 taken as +0).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  f = f + 0.0f;  // -0 + +0 = +0 under round-to-nearest
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Set bits of a wave mask in the lanes below this one.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
 // Wave-wide sum / max over all 64 lanes.
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

@@ -56,6 +56,21 @@ hipError_t launch_select(const Method& m, const uint16_t* q, const float* reps,
                          void* workspace, const AppendOp* append,
                          hipStream_t stream);
 
+// The two launches of launch_select on their own: fp32 inner-product
+// scores of the offload blocks (raw bits, [batch][n_kv_heads][max_blocks];
+// entries outside a list's offload range are not written), with the
+// optional decode-token append; then the top-k and merge from such scores.
+hipError_t launch_score(const Method& m, const uint16_t* q, const float* reps,
+                        const int32_t* table, const int32_t* lens,
+                        const int32_t* prompt_lens, int batch, int max_blocks,
+                        uint32_t* scores, const AppendOp* append,
+                        hipStream_t stream);
+hipError_t launch_topk(const Method& m, const int32_t* table, const int32_t* lens,
+                       const int32_t* prompt_lens, int batch, int max_blocks,
+                       const uint32_t* scores, int32_t* sel_ids, int32_t* n_sel,
+                       int k_cap, int32_t* merged, int32_t* n_merged, int m_cap,
+                       hipStream_t stream);
+
 hipError_t launch_merge(const Method& m, const int32_t* table, int max_blocks,
                         const int32_t* lens, const int32_t* sel_ids,
                         const int32_t* n_sel, int k_cap, int batch,
@@ -122,6 +137,26 @@ hipError_t launch_decode_attn(const Method& m, bool use_mfma,
                               const int32_t* merged, const int32_t* n_merged,
                               int m_cap, const int32_t* lens, int batch,
                               float* out, void* workspace, hipStream_t stream);
+
+// Top-k + merge folded into the attention launch, for the shapes
+// fused_select_attn_ok accepts (a batch of one, MFMA, per-head selection,
+// max_blocks <= kFusedMaxBlocks): every wave of a list finds the list's
+// selection from the scores itself (the list's first wave also writes
+// sel_ids / n_sel / merged / n_merged), then attends exactly as
+// launch_decode_attn's single-sequence partition does; then the combine.
+constexpr int kFusedMaxBlocks = 1024;
+bool fused_select_attn_ok(const Method& m, bool use_mfma, const AttnPlan& plan,
+                          int batch, int max_blocks);
+hipError_t launch_select_attn(const Method& m, bool use_mfma, const AttnPlan& plan,
+                              float scale,
+                              const uint16_t* q, const uint16_t* k_pages,
+                              const uint16_t* v_pages, int64_t n_pages,
+                              const int32_t* table, int max_blocks,
+                              const int32_t* lens, const int32_t* prompt_lens,
+                              const uint32_t* scores, int32_t* sel_ids,
+                              int32_t* n_sel, int k_cap, int32_t* merged,
+                              int32_t* n_merged, int m_cap, float* out,
+                              void* workspace, hipStream_t stream);
 
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
                              int n_cu, hipStream_t stream);

@@ -32,12 +32,6 @@ namespace rkv {
 namespace {
 
 
-// fp32 -> uint32 whose unsigned order is the float order (-0 taken as +0).
-__device__ __forceinline__ uint32_t order_key(float f) {
-  f = f + 0.0f;  // -0 + +0 = +0 under round-to-nearest
-  const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 // Merged page list: init blocks, the given kept offload blocks (written by
 // the caller), then local blocks.  Returns the entry count.
@@ -276,10 +270,6 @@ __device__ __forceinline__ uint32_t waves_before(uint32_t x, uint32_t* sh,
   return before;
 }
 
-__device__ __forceinline__ int lanes_below(uint64_t mask) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
 
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelArgs a) {
   __shared__ uint32_t hist[256];
@@ -519,13 +509,11 @@ size_t select_keys_bytes(int batch, int n_kv_heads, int max_blocks) {
   return (size_t)batch * n_kv_heads * max_blocks * sizeof(uint32_t);
 }
 
-hipError_t launch_select(const Method& m, const uint16_t* q, const float* reps,
-                         const int32_t* table, const int32_t* lens,
-                         const int32_t* prompt_lens, int batch, int max_blocks,
-                         int32_t* sel_ids, int32_t* n_sel, int k_cap,
-                         int32_t* merged, int32_t* n_merged, int m_cap,
-                         void* workspace, const AppendOp* append,
-                         hipStream_t stream) {
+hipError_t launch_score(const Method& m, const uint16_t* q, const float* reps,
+                        const int32_t* table, const int32_t* lens,
+                        const int32_t* prompt_lens, int batch, int max_blocks,
+                        uint32_t* scores, const AppendOp* append,
+                        hipStream_t stream) {
   const int groups = batch * m.n_kv_heads;
   if (groups == 0) return hipSuccess;
   int ib = (int)(((int64_t)m.init_tokens + 127) >> 7);
@@ -541,8 +529,7 @@ hipError_t launch_select(const Method& m, const uint16_t* q, const float* reps,
   const int chunk = 8 * rounds;
   const int n_chunks = (max_blocks - ib + chunk - 1) / chunk;
   SelArgs a{m, q, reps, table, lens, prompt_lens, max_blocks, ib, n_chunks,
-            groups, static_cast<uint32_t*>(workspace), sel_ids, n_sel, k_cap,
-            merged, n_merged, m_cap};
+            groups, scores, nullptr, nullptr, 0, nullptr, nullptr, 0};
   const int64_t score_wgs = (int64_t)groups * n_chunks;
   AppendArgs ap{};
   if (append)
@@ -566,10 +553,37 @@ hipError_t launch_select(const Method& m, const uint16_t* q, const float* reps,
     }
 #undef RKV_SCORE_LAUNCH
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const Method& m, const int32_t* table, const int32_t* lens,
+                       const int32_t* prompt_lens, int batch, int max_blocks,
+                       const uint32_t* scores, int32_t* sel_ids, int32_t* n_sel,
+                       int k_cap, int32_t* merged, int32_t* n_merged, int m_cap,
+                       hipStream_t stream) {
+  const int groups = batch * m.n_kv_heads;
+  if (groups == 0) return hipSuccess;
+  // the top-k only reads the scores
+  SelArgs a{m, nullptr, nullptr, table, lens, prompt_lens, max_blocks, 0, 0,
+            groups, const_cast<uint32_t*>(scores), sel_ids, n_sel, k_cap,
+            merged, n_merged, m_cap};
   hipLaunchKernelGGL(topk_kernel, dim3(groups), dim3(kTopkThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_select(const Method& m, const uint16_t* q, const float* reps,
+                         const int32_t* table, const int32_t* lens,
+                         const int32_t* prompt_lens, int batch, int max_blocks,
+                         int32_t* sel_ids, int32_t* n_sel, int k_cap,
+                         int32_t* merged, int32_t* n_merged, int m_cap,
+                         void* workspace, const AppendOp* append,
+                         hipStream_t stream) {
+  uint32_t* scores = static_cast<uint32_t*>(workspace);
+  hipError_t e = launch_score(m, q, reps, table, lens, prompt_lens, batch,
+                              max_blocks, scores, append, stream);
+  if (e != hipSuccess) return e;
+  return launch_topk(m, table, lens, prompt_lens, batch, max_blocks, scores,
+                     sel_ids, n_sel, k_cap, merged, n_merged, m_cap, stream);
 }
 
 hipError_t launch_merge(const Method& m, const int32_t* table, int max_blocks,

@@ -10,7 +10,9 @@ sequence on the current stream:
                     the merged block table
     rkv_decode_attn split-K paged attention and the log-sum-exp combine
 
-PyTorch only allocates memory and provides the stream here.
+A step issues them as rkv_decode_step (the append folded into the scoring
+launch; for a batch of one the top-k and merge folded into the attention
+launch).  PyTorch only allocates memory and provides the stream here.
 """
 
 from __future__ import annotations
@@ -78,9 +80,21 @@ class DecodeSession:
         """The append folded into the selection's launches."""
         self._prepared().append_select(q, k_new, v_new, lens)
 
+    def select_attend(self, q, lens):
+        """Selection from the scores the last selection left in the select
+        workspace, then attention (rkv_select_attend)."""
+        self._prepared().select_attend(q, lens)
+        return self.out
+
     def step(self, q, k_new, v_new, lens):
-        """append + select (one launch) -> attend for one decode step;
-        returns `out`."""
+        """One decode step (rkv_decode_step: append + scores, then selection
+        and attention; for a batch of one the selection runs inside the
+        attention launch); returns `out`."""
+        self._prepared().decode_step(q, k_new, v_new, lens)
+        return self.out
+
+    def step_separate(self, q, k_new, v_new, lens):
+        """The same step as rkv_append_select + rkv_decode_attn."""
         self.append_select(q, k_new, v_new, lens)
         return self.attend(q, lens)
 

@@ -26,7 +26,7 @@ def test_every_declared_function_is_exported(L):
     assert len(names) >= 11
     for n in names:
         assert hasattr(L, n), n
-    assert L.rkv_abi_version() == 2
+    assert L.rkv_abi_version() == 3
 
 
 def test_defaults_follow_the_page(L):

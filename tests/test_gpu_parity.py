@@ -993,3 +993,180 @@ def test_append_select_equals_append_then_select():
         assert torch.equal(x, y)
     # sequence 0 completed block 5 at step 1: its representation exists
     assert results[1][2][0, :, 5].abs().sum() > 0
+
+
+# ---------------------------------------------------------------------------
+# rkv_decode_step (for a batch of one: the top-k and merge inside the
+# attention launch) against rkv_append_select + rkv_decode_attn.  Every
+# selection, merged table, pool, representation and output must be
+# bit-identical: both attend the same pages in the same order with the same
+# arithmetic, and the selection is defined by its values alone.
+# ---------------------------------------------------------------------------
+
+def _valid_rows(sel, n):
+    return [sel[i, :int(n[i])].tolist() for i in range(n.shape[0])]
+
+
+def _snapshot(sess):
+    n_sel = sess.n_sel.cpu().numpy()
+    n_m = sess.n_merged.cpu().numpy()
+    sel = sess.sel_ids.cpu().numpy()
+    mer = sess.merged.cpu().numpy()
+    return (sess.out.cpu().numpy().copy(), n_sel.copy(), n_m.copy(),
+            [_valid_rows(sel[b], n_sel[b]) for b in range(sel.shape[0])],
+            [_valid_rows(mer[b], n_m[b]) for b in range(mer.shape[0])])
+
+
+def fused_vs_separate(spec, launch=None, steps=None, zero_q=False, mutate=None,
+                      oracle_check=False):
+    launch = launch or {}
+    steps = spec.steps if steps is None else steps
+    runs = []
+    for mode in ("step", "separate"):
+        batch = synth.make_batch(spec, DEV)
+        if mutate is not None:
+            mutate(batch)
+        prm, sess = make_session(batch, **launch)
+        prefill(batch, sess)
+        rec = []
+        for t in range(steps):
+            lens = i32(batch.lens_at(t))
+            kn, vn = batch.new_kv_bits(t)
+            q = batch.q_bits(t)
+            if zero_q:
+                q = torch.zeros_like(q)
+            if mode == "step":
+                sess.step(q, kn, vn, lens)
+            else:
+                sess.step_separate(q, kn, vn, lens)
+            torch.cuda.synchronize()
+            rec.append(_snapshot(sess))
+            if mode == "step" and oracle_check and not zero_q:
+                oracle_full_check(batch, sess, t)
+        rec.append((u16(batch.k_pages), u16(batch.v_pages), sess.reps.cpu().numpy()))
+        runs.append(rec)
+        del batch, sess
+    for t, (a, b) in enumerate(zip(runs[0][:-1], runs[1][:-1])):
+        assert np.array_equal(a[0], b[0]), f"out differs at step {t}"
+        assert np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2]), t
+        assert a[3] == b[3], f"selection differs at step {t}"
+        assert a[4] == b[4], f"merged table differs at step {t}"
+    for x, y in zip(runs[0][-1], runs[1][-1]):
+        assert np.array_equal(x, y)
+    return runs
+
+
+def test_decode_step_llama_layer_equals_separate_calls():
+    say("decode step vs separate calls, 8B layer (1 x 64K), 3 steps")
+    fused_vs_separate(synth.CONFIGS[2], steps=3)
+
+
+def test_decode_step_tiny_planted_against_oracle():
+    say("decode step, tiny workload (1 x 4K), against the oracle and separate calls")
+    fused_vs_separate(synth.CONFIGS[1], oracle_check=True)
+
+
+def test_decode_step_all_scores_tied():
+    """q = 0: every score is 0 (or -0), so the k-th largest key ties with
+    every other key and the lowest blocks are kept."""
+    spec = synth.custom("tied", batch=1, n_q_heads=16, n_kv_heads=4, context=(40000,),
+                        steps=2, dense_boundary=0, config_id=120)
+    say("decode step, all scores tied")
+    runs = fused_vs_separate(spec, zero_q=True)
+    n_init = 8
+    n_sel = runs[0][0][1][0]
+    sel = runs[0][0][3][0]
+    for h in range(4):
+        assert sel[h] == list(range(n_init, n_init + int(n_sel[h])))
+
+
+def test_decode_step_partial_ties_at_the_threshold():
+    spec = synth.custom("ties2", batch=1, n_q_heads=8, n_kv_heads=2, context=(30000,),
+                        steps=2, init_tokens=128, local_tokens=256, dense_boundary=0,
+                        config_id=121)
+
+    def dup(batch):
+        t = batch.table_np[0]
+        for j in range(30, 230, 2):  # 100 copies of block 20 -> ties around k
+            batch.k_pages[t[j]] = batch.k_pages[t[20]]
+
+    say("decode step, duplicated blocks (ties)")
+    for ppm in (50_000, 200_000, 500_000):
+        fused_vs_separate(spec, dict(topk_ppm=ppm), mutate=dup)
+
+
+@pytest.mark.parametrize("ctx,expect_fused", [(131071, True), (131072, False)])
+def test_decode_step_block_limit(ctx, expect_fused):
+    """1024 blocks (the last shape the folded selection takes) and 1025."""
+    spec = synth.custom(f"limit{ctx}", batch=1, n_q_heads=8, n_kv_heads=1,
+                        context=(ctx,), steps=2, dense_boundary=0, config_id=122)
+    say("decode step at the block limit", ctx, "fused" if expect_fused else "two launches")
+    fused_vs_separate(spec)
+
+
+def random_batch1_case(seed):
+    rng = np.random.default_rng(9100 + seed)
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    L = int(rng.choice([int(rng.integers(1, 3000)), int(rng.integers(3000, 131000))]))
+    spec = synth.custom(f"b1random{seed}", batch=1, n_q_heads=G * hkv, n_kv_heads=hkv,
+                        context=(L,), steps=2,
+                        init_tokens=int(rng.choice([0, 128, 256, 1000, 1024])),
+                        local_tokens=int(rng.choice([0, 1, 128, 1000, 7192])),
+                        topk_ppm=int(rng.choice([0, 1, 50_000, 200_000, 999_999,
+                                                 1_000_000])),
+                        dense_boundary=int(rng.choice([0, 0, 5000, 32768])),
+                        shuffle=bool(rng.integers(0, 2)), config_id=500 + seed)
+    launch = dict(split_waves=int(rng.choice([0, 0, 7, 64, 512, 1000])))
+    return spec, launch
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_decode_step_random_single_sequence(seed):
+    spec, launch = random_batch1_case(seed)
+    say(f"decode step random single sequence {seed}: L {spec.context[0]}, "
+        f"{spec.n_q_heads}/{spec.n_kv_heads}, init {spec.init_tokens}, "
+        f"local {spec.local_tokens}, ppm {spec.topk_ppm}, "
+        f"dense {spec.dense_boundary}, {launch}")
+    fused_vs_separate(spec, launch, oracle_check=seed < 4)
+
+
+def test_decode_step_batch_and_valu_take_the_two_launch_path():
+    spec = synth.custom("b3", batch=3, n_q_heads=16, n_kv_heads=4,
+                        context=(767, 9000, 20480), steps=2, init_tokens=256,
+                        local_tokens=1000, dense_boundary=0, config_id=123)
+    say("decode step, batch of three and VALU")
+    fused_vs_separate(spec)
+    spec1 = synth.custom("b1valu", batch=1, n_q_heads=16, n_kv_heads=4,
+                         context=(20000,), steps=2, dense_boundary=0, config_id=124)
+    fused_vs_separate(spec1, dict(attn_impl=B.ATTN_VALU))
+    fused_vs_separate(spec1, dict(select_mode=B.SELECT_PER_SEQUENCE))
+
+
+def test_select_attend_from_the_select_workspace():
+    """rkv_select_attend over the scores a selection left in its workspace
+    repeats that selection and attention bit for bit."""
+    for spec in (synth.custom("sa1", batch=1, n_q_heads=32, n_kv_heads=8,
+                              context=(50000,), steps=1, dense_boundary=0,
+                              config_id=125),
+                 synth.custom("sa2", batch=2, n_q_heads=32, n_kv_heads=8,
+                              context=(50000, 20000), steps=1, dense_boundary=0,
+                              config_id=126)):
+        say("select_attend from the workspace", spec.name)
+        batch = synth.make_batch(spec, DEV)
+        prm, sess = make_session(batch)
+        prefill(batch, sess)
+        lens = i32(batch.lens_at(0))
+        kn, vn = batch.new_kv_bits(0)
+        q = batch.q_bits(0)
+        sess.step_separate(q, kn, vn, lens)
+        torch.cuda.synchronize()
+        ref = _snapshot(sess)
+        sess.out.zero_()
+        sess.merged.zero_()
+        sess.sel_ids.zero_()
+        sess.select_attend(q, lens)
+        torch.cuda.synchronize()
+        got = _snapshot(sess)
+        assert np.array_equal(got[0], ref[0])
+        assert got[3] == ref[3] and got[4] == ref[4]
