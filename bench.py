@@ -54,9 +54,9 @@ COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 ATTN_SOURCE = os.path.join(ROOT, "sparse_retrieval_kv_amd", "csrc", "attn.hip")
 MEASURED_TRAFFIC = {
     # config: (sha256 prefix of attn.hip, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    2: ("215f1d3b0804443e", 40028.2 + 722.0, 1048.9 + 16.0),
-    3: ("215f1d3b0804443e", 751676.6 + 1278.0, 1298.4 + 256.0),
-    4: ("215f1d3b0804443e", 506483.2 + 2394.0, 2080.6 + 256.0),
+    2: ("a838123a715d96a0", 40030.2 + 721.5, 1048.9 + 16.0),
+    3: ("a838123a715d96a0", 751658.3 + 1277.5, 1298.4 + 256.0),
+    4: ("a838123a715d96a0", 506489.0 + 2393.5, 2080.6 + 256.0),
 }
 METRIC = "decode attn steps/s and attended-KV HBM GB/s (% of peak) at 64K-128K ctx, 1 GPU"
 

@@ -42,6 +42,12 @@
 //   V: lane (col, g) reads dim 16n+col, tokens 32pp+8g..+7 (one 16-byte
 //   piece of the dim-major V tile).
 // Every (page, head) K and V tile is read exactly once.
+//
+// For a batch of one, attn_select_mfma_kernel also takes over the top-k and
+// the merge (openGauss DataVec page, "Overall Solution"): each wave of a
+// list finds the list's selection from the inner-product scores itself and
+// builds the merged page list in its LDS, so a decode step needs no
+// separate top-k launch (see select_strided_body).
 #include "rkv_device.h"
 #include "rkv_internal.h"
 
@@ -728,9 +734,15 @@ __device__ __forceinline__ uint32_t kept_blocks(const uint32_t (&key)[kFusedRegs
   for (int bit = 31; bit >= 0; --bit) {
     if (cT == k) break;  // exactly k keys >= T: they are the top k
     const uint32_t t = T | (1u << bit);
+    // every compare of the pass first, then the counts: a count read
+    // right after its compare waits for the vector unit's mask write
+    uint64_t m[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) m[i] = __ballot(keyc[i] >= t);
+    __builtin_amdgcn_sched_barrier(0);
     int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < NR; ++i) cnt += __popcll(__ballot(keyc[i] >= t));
+    for (int i = 0; i < NR; ++i) cnt += __popcll(m[i]);
     if (cnt >= k) {
       T = t;
       cT = cnt;
