@@ -122,6 +122,56 @@ def test_select_and_merge_capacity_rules(L):
                              FAKE, -1, FAKE, FAKE, 100, None) == B.RKV_ERR_INVALID_ARG
 
 
+def test_select_attend_and_decode_step_validation(L):
+    """Every case breaks exactly one rule; nothing is enqueued."""
+    p = L.rkv_params_default(32, 8)
+    big = L.rkv_attn_workspace_size(ctypes.byref(p), 1, 100)
+    assert big > 0
+
+    def sa(**kw):
+        a = dict(q=FAKE, table=FAKE, max_blocks=100, lens=FAKE, scores=FAKE,
+                 sel=FAKE, k_cap=100, merged=FAKE, n_merged=FAKE, m_cap=100,
+                 out=FAKE, ws=FAKE, ws_bytes=big)
+        a.update(kw)
+        return L.rkv_select_attend(ctypes.byref(p), a["q"], FAKE, FAKE, 1000,
+                                   a["table"], a["max_blocks"], a["lens"], None, 1,
+                                   a["scores"], a["sel"], FAKE, a["k_cap"],
+                                   a["merged"], a["n_merged"], a["m_cap"], a["out"],
+                                   a["ws"], a["ws_bytes"], None)
+
+    assert sa(scores=None) == B.RKV_ERR_INVALID_ARG
+    assert b"scores" in L.rkv_last_error()
+    assert sa(merged=None) == B.RKV_ERR_INVALID_ARG
+    assert sa(n_merged=None) == B.RKV_ERR_INVALID_ARG
+    assert sa(k_cap=99) == B.RKV_ERR_INVALID_ARG     # dense switch possible
+    assert sa(m_cap=99) == B.RKV_ERR_INVALID_ARG
+    assert sa(max_blocks=0) == B.RKV_ERR_INVALID_ARG
+    assert sa(q=ODD) == B.RKV_ERR_INVALID_ARG
+    assert sa(ws_bytes=big - 1) == B.RKV_ERR_WORKSPACE
+    assert sa(ws=ODD) == B.RKV_ERR_INVALID_ARG
+
+    sel_need = L.rkv_select_workspace_size(ctypes.byref(p), 1, 100)
+    assert sel_need == 8 * 100 * 4
+
+    def step(**kw):
+        a = dict(k_new=FAKE, reps=FAKE, sel_ws=FAKE, sel_bytes=sel_need,
+                 attn_ws=FAKE + 0x100000, attn_bytes=big, k_cap=100)
+        a.update(kw)
+        return L.rkv_decode_step(ctypes.byref(p), a["k_new"], FAKE, FAKE, FAKE, 1000,
+                                 FAKE, a["reps"], FAKE, FAKE, None, 1, 100, FAKE,
+                                 FAKE, a["k_cap"], FAKE, FAKE, 100, FAKE,
+                                 a["sel_ws"], a["sel_bytes"], a["attn_ws"],
+                                 a["attn_bytes"], None)
+
+    assert step(k_new=None) == B.RKV_ERR_INVALID_ARG
+    assert step(reps=ODD) == B.RKV_ERR_INVALID_ARG
+    assert step(sel_bytes=sel_need - 4) == B.RKV_ERR_WORKSPACE
+    assert b"select workspace" in L.rkv_last_error()
+    assert step(attn_bytes=big - 1) == B.RKV_ERR_WORKSPACE
+    assert step(attn_ws=FAKE) == B.RKV_ERR_INVALID_ARG   # same buffer as select
+    assert step(k_cap=99) == B.RKV_ERR_INVALID_ARG
+
+
 def test_stage_validation(L):
     p = L.rkv_params_default(32, 8)
 
