@@ -430,8 +430,9 @@ rkv_status rkv_decode_attn(const rkv_params* params, const uint16_t* q,
  *   scores [batch][n_kv_heads][max_blocks] device fp32: entry j of (b, h)
  *          is the inner-product score of block j (the group's query heads
  *          summed, per-sequence mode: summed over the heads by the top-k as
- *          in rkv_select); only the offload blocks' entries are read, and
- *          only for lists with 0 < k < n_off.  rkv_select,
+ *          in rkv_select); the whole [max_blocks] row of a list may be
+ *          read, but only its offload blocks' entries affect the result,
+ *          and only for lists with 0 < k < n_off.  rkv_select,
  *          rkv_append_select and rkv_decode_step leave exactly these scores
  *          in the first batch * n_kv_heads * max_blocks * 4 bytes of their
  *          select workspace.
