@@ -57,6 +57,7 @@ MEASURED_TRAFFIC = {
     2: ("a838123a715d96a0", 40030.2 + 721.5, 1048.9 + 16.0),
     3: ("a838123a715d96a0", 751658.3 + 1277.5, 1298.4 + 256.0),
     4: ("a838123a715d96a0", 506489.0 + 2393.5, 2080.6 + 256.0),
+    5: ("a838123a715d96a0", 474770.3 + 947.6, 1040.2 + 64.0),
 }
 METRIC = "decode attn steps/s and attended-KV HBM GB/s (% of peak) at 64K-128K ctx, 1 GPU"
 
