@@ -1170,3 +1170,16 @@ def test_select_attend_from_the_select_workspace():
         got = _snapshot(sess)
         assert np.array_equal(got[0], ref[0])
         assert got[3] == ref[3] and got[4] == ref[4]
+
+
+@pytest.mark.parametrize("ctx", [72727, 72728, 72856, 72857])
+def test_decode_step_search_register_edge(ctx):
+    """The folded search runs over 8 registers while the offload range ends
+    at or before block 512 and over 16 past it: contexts around that edge
+    (local 7192 tokens: the offload range ends at block 512 for
+    L in [72728, 72855])."""
+    spec = synth.custom(f"edge{ctx}", batch=1, n_q_heads=32, n_kv_heads=8,
+                        context=(ctx,), steps=2, dense_boundary=0,
+                        config_id=130 + ctx % 97)
+    say("decode step at the 8/16-register edge", ctx)
+    fused_vs_separate(spec, oracle_check=ctx in (72728, 72857))
