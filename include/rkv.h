@@ -427,10 +427,10 @@ rkv_status rkv_decode_attn(const rkv_params* params, const uint16_t* q,
  * attention over those pages).  Same results, bit for bit, as those two
  * steps: sel_ids / n_sel / merged / n_merged as rkv_select writes them and
  * out as rkv_decode_attn writes it.
- *   scores [batch][n_kv_heads][max_blocks] device fp32: entry j of (b, h)
- *          is the inner-product score of block j (the group's query heads
- *          summed, per-sequence mode: summed over the heads by the top-k as
- *          in rkv_select); the whole [max_blocks] row of a list may be
+ *   scores [batch][n_kv_heads][max_blocks] device fp32, 4-byte aligned:
+ *          entry j of (b, h) is the inner-product score of block j (the
+ *          group's query heads summed; per-sequence mode: summed over the
+ *          heads by the top-k as in rkv_select); the whole [max_blocks] row of a list may be
  *          read, but only its offload blocks' entries affect the result,
  *          and only for lists with 0 < k < n_off.  rkv_select,
  *          rkv_append_select and rkv_decode_step leave exactly these scores

@@ -615,7 +615,8 @@ rkv_status rkv_select_attend(const rkv_params* params, const uint16_t* q,
                                max_blocks, lens, batch, sel_ids, n_sel, k_cap,
                                merged, n_merged, m_cap, out, workspace,
                                workspace_bytes, &plan));
-  RKV_REQUIRE(scores != nullptr, RKV_ERR_INVALID_ARG, "scores must not be NULL");
+  RKV_REQUIRE(scores != nullptr && (reinterpret_cast<uintptr_t>(scores) & 3u) == 0,
+              RKV_ERR_INVALID_ARG, "scores must be a 4-byte aligned, non-NULL pointer");
   return hip_status(
       select_attend_launch(params, m, plan, q, k_pages, v_pages, n_pages, block_table,
                            max_blocks, lens, prompt_lens, batch,

@@ -141,6 +141,7 @@ def test_select_attend_and_decode_step_validation(L):
 
     assert sa(scores=None) == B.RKV_ERR_INVALID_ARG
     assert b"scores" in L.rkv_last_error()
+    assert sa(scores=FAKE + 2) == B.RKV_ERR_INVALID_ARG
     assert sa(merged=None) == B.RKV_ERR_INVALID_ARG
     assert sa(n_merged=None) == B.RKV_ERR_INVALID_ARG
     assert sa(k_cap=99) == B.RKV_ERR_INVALID_ARG     # dense switch possible
