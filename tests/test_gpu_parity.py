@@ -22,13 +22,13 @@ import oracle as O
 from sparse_retrieval_kv_amd import binding as B
 from sparse_retrieval_kv_amd import synth
 from sparse_retrieval_kv_amd.decode import DecodeSession, HostTierSession
-from tests.helpers import (close_report, logical_at_step, oracle_params,
-                           q_f64, seq_pages_host, u16)
+from tests.helpers import (GAP, check_merged, check_selection, close_report,
+                           gpu_merged_logical, gpu_selection, logical_at_step,
+                           oracle_params, q_f64, seq_pages_host, u16)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 REL_L2 = 1e-4
-GAP = 1e-3
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -68,59 +68,20 @@ def step(batch, sess, t):
     return sess.step(batch.q_bits(t), kn, vn, lens)
 
 
-def check_selection(sel_gpu, hr, n_init, ctx):
-    ref = hr.selected
-    assert len(sel_gpu) == len(ref) == hr.k, ctx
-    if hr.gap_rel > GAP:
-        assert np.array_equal(sel_gpu, ref), (ctx, hr.gap_rel)
-        return
-    # near tie: the GPU set only has to be a valid top-k of the oracle scores
-    s = hr.scores
-    mask = np.zeros(len(s), bool)
-    mask[np.asarray(sel_gpu) - n_init] = True
-    assert np.all(np.diff(sel_gpu) > 0), ctx
-    if mask.all() or not mask.any():
-        return
-    tol = GAP * abs(np.sort(s)[::-1][hr.k - 1])
-    assert s[mask].min() >= s[~mask].max() - tol, ctx
-
-
-def gpu_selection(sess, b, h):
-    n = int(sess.n_sel[b, h])
-    return sess.sel_ids[b, h, :n].cpu().numpy()
-
-
-def gpu_merged_logical(sess, batch, b, h, staged=False):
-    """The GPU's merged list of (b, h) as logical blocks (and page ids).
-    Staging page stage_page0 + b*k_cap + r stands for the block slot r holds:
-    the r-th kept block without residency, slot_ids[b][h][r] with it."""
-    n = int(sess.n_merged[b, h])
-    pages = sess.merged[b, h, :n].cpu().numpy()
-    inv = {int(p): j for j, p in enumerate(batch.table_np[b]) if p >= 0}
-    if staged:
-        if getattr(sess, "resident", False):
-            held = sess.slot_ids[b, h].cpu().numpy()
-        else:
-            held = gpu_selection(sess, b, h)
-        for r, j in enumerate(held):
-            if j >= 0:
-                inv[int(sess.stage_page0 + b * sess.k_cap + r)] = int(j)
-    return np.array([inv[int(p)] for p in pages], dtype=np.int64), pages
-
-
 def check_head_output(out_gpu, ref, ctx):
     ok, mx, rl2 = close_report(out_gpu, ref)
     assert ok, (ctx, mx, rl2)
     assert rl2 <= REL_L2, (ctx, mx, rl2)
 
 
-def oracle_full_check(batch, sess, t, seqs=None, heads=None, host=None):
+def oracle_full_check(batch, sess, t, seqs=None, heads=None, host=None, q=None):
     """Check selections, merged tables and outputs of step t for the given
-    sequences / KV heads against the oracle."""
+    sequences / KV heads (default: all) against the oracle.  `q` replaces the
+    step's queries (bf16 bits on the device) when the step ran on others."""
     spec = batch.spec
     G = spec.group
     out = sess.out.cpu().numpy()
-    qall = q_f64(batch, t)
+    qall = q_f64(batch, t) if q is None else O.bf16_to_f64(u16(q))
     for b in (range(spec.batch) if seqs is None else seqs):
         hs = list(range(spec.n_kv_heads)) if heads is None else heads
         pages = seq_pages_host(batch, b, hs, host)
@@ -130,22 +91,19 @@ def oracle_full_check(batch, sess, t, seqs=None, heads=None, host=None):
                         prm1.dense_boundary)
         for i, h in enumerate(hs):
             ctx = f"{spec.name} step {t} seq {b} head {h}"
-            q = qall[b, h * G:(h + 1) * G]
-            res = O.decode_step(q, K[i:i + 1], V[i:i + 1], L,
+            qh = qall[b, h * G:(h + 1) * G]
+            res = O.decode_step(qh, K[i:i + 1], V[i:i + 1], L,
                                 int(batch.context[b]), prm1)
             hr = res.heads[0]
             sel = gpu_selection(sess, b, h)
             check_selection(sel, hr, res.regions.n_init, ctx)
-            mlog, mpages = gpu_merged_logical(sess, batch, b, h, host is not None)
+            expect = check_merged(sess, batch, b, h, res.regions, sel, host, ctx)
             if np.array_equal(sel, hr.selected):
-                assert np.array_equal(mlog, hr.merged), ctx
-                if host is None:
-                    assert np.array_equal(mpages, batch.table_np[b, hr.merged]), ctx
                 ref = res.out
-            else:
-                ref = O.decode_step(q, K[i:i + 1], V[i:i + 1], L,
+            else:  # a valid near-tie selection: attention over its blocks
+                ref = O.decode_step(qh, K[i:i + 1], V[i:i + 1], L,
                                     int(batch.context[b]), prm1,
-                                    merged_override=[mlog]).out
+                                    merged_override=[expect]).out
             check_head_output(out[b, h * G:(h + 1) * G], ref, ctx)
 
 
@@ -309,22 +267,22 @@ def test_ties_go_to_lower_block_index():
     (smaller logical block first) decides the selection exactly."""
     spec = synth.custom("ties", batch=1, n_q_heads=8, n_kv_heads=2,
                         context=(6000,), init_tokens=128, local_tokens=256,
-                        dense_boundary=0, config_id=97)
+                        topk_ppm=100_000, dense_boundary=0, config_id=97)
     batch = synth.make_batch(spec, DEV)
     t = batch.table_np[0]
     src = t[10]
     for j in (3, 7, 12, 20, 33, 40):  # six copies of block 10 -> 7 equal reps
         batch.k_pages[t[j]] = batch.k_pages[src]
-    prm, sess = make_session(batch, topk_ppm=100_000)
+    prm, sess = make_session(batch)
     say("ties")
     prefill(batch, sess)
     step(batch, sess, 0)
     torch.cuda.synchronize()
     K, V, L = logical_at_step(batch, 0, 0)
-    res = O.decode_step(q_f64(batch, 0)[0], K, V, L, L,
-                        oracle_params(spec, topk_ppm=100_000))
+    res = O.decode_step(q_f64(batch, 0)[0], K, V, L, L, oracle_params(spec))
     for h in range(2):
         assert np.array_equal(gpu_selection(sess, 0, h), res.heads[h].selected)
+    oracle_full_check(batch, sess, 0)
 
 
 def test_split_sizes_agree_and_runs_are_deterministic():
@@ -554,36 +512,54 @@ def test_llama_layer_full_size_steps():
     prefill(batch, sess)
     for t in range(64):
         step(batch, sess, t)
-        if t in (0, 24, 63):
+        if t in (0, 31, 63):
             torch.cuda.synchronize()
             for h in range(8):
                 assert set(batch.planted[0]) <= set(gpu_selection(sess, 0, h).tolist())
             oracle_full_check(batch, sess, t)
 
 
-def test_batched_ragged_full_size_sampled():
+def run_to_step(batch, sess, t_check):
+    """Prefill, then decode steps 0 .. t_check (every step through the
+    library, so the pools and representations evolve as in a real decode)."""
+    prefill(batch, sess)
+    for t in range(t_check + 1):
+        step(batch, sess, t)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("t_check", [0, 15, 31])
+def test_batched_ragged_full_size(t_check):
+    """Batched workload (16 x U[32K, 128K], shuffled pool): every sequence
+    and KV head against the oracle at the first, middle and last step."""
     batch = synth.make_batch(synth.CONFIGS[3], DEV)
     prm, sess = make_session(batch)
-    say("batched (16 x 32K-128K, shuffled)", batch.context.tolist())
-    prefill(batch, sess)
-    for t in range(32):
-        step(batch, sess, t)
-        if t in (0, 31):
-            torch.cuda.synchronize()
-            lo, hi = int(np.argmin(batch.context)), int(np.argmax(batch.context))
-            oracle_full_check(batch, sess, t, seqs=[lo, hi, 7], heads=[0, 5])
+    say("batched (16 x 32K-128K, shuffled)", batch.context.tolist(), "step", t_check)
+    run_to_step(batch, sess, t_check)
+    oracle_full_check(batch, sess, t_check)
 
 
-def test_70b_shared_prefix_full_size_sampled():
+@pytest.mark.parametrize("t_check", [0, 7, 15])
+def test_70b_shared_prefix_full_size(t_check):
+    """70B-shaped layer (8 x 128K, 64/8 heads, 16K shared prefix): every
+    sequence and KV head against the oracle at the first, middle and last
+    step."""
     batch = synth.make_batch(synth.CONFIGS[4], DEV)
     prm, sess = make_session(batch)
-    say("70B layer (8 x 128K, 64/8, shared prefix)")
-    prefill(batch, sess)
-    for t in range(16):
-        step(batch, sess, t)
-        if t in (0, 15):
-            torch.cuda.synchronize()
-            oracle_full_check(batch, sess, t, seqs=[0, 6], heads=[1, 7])
+    say("70B layer (8 x 128K, 64/8, shared prefix) step", t_check)
+    run_to_step(batch, sess, t_check)
+    oracle_full_check(batch, sess, t_check)
+
+
+@pytest.mark.parametrize("t_check", [0, 15])
+def test_70b_shared_prefix_full_size_per_sequence(t_check):
+    """The per-sequence selection reading on the 70B-shaped layer at full
+    size: every sequence against the head-summed oracle step."""
+    batch = synth.make_batch(synth.CONFIGS[4], DEV)
+    prm, sess = make_session(batch, select_mode=B.SELECT_PER_SEQUENCE)
+    say("70B layer, per-sequence selection, step", t_check)
+    run_to_step(batch, sess, t_check)
+    per_sequence_check(batch, sess, t_check)
 
 
 @pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (16, 4), (64, 8)])
@@ -796,20 +772,24 @@ def test_offload_prefill_native(concurrent):
         oracle_full_check(batch, sess, t, host=pools)
 
 
-def test_host_tier_full_size_sampled():
-    say("host tier (4 x 256K)")
+@pytest.mark.parametrize("t_check", [0, 7, 15])
+def test_host_tier_full_size(t_check):
+    """Host tier (4 x 256K, offload blocks in pinned host memory, residency):
+    every sequence and KV head against the oracle at the first, middle and
+    last step."""
+    say("host tier (4 x 256K) step", t_check)
     batch, host, sess = make_host_session(synth.CONFIGS[5])
-    for t in range(16):
+    for t in range(t_check + 1):
         step(batch, sess, t)
-        if t in (0, 15):
-            torch.cuda.synchronize()
-            oracle_full_check(batch, sess, t, seqs=[0, 3], heads=[2, 6], host=host)
+    torch.cuda.synchronize()
+    oracle_full_check(batch, sess, t_check, host=host)
 
 
 def per_sequence_check(batch, sess, t, seqs=None, host=None):
     """Per-sequence selection mode: one oracle step over all KV heads of each
     sequence (scores summed over the heads), every head's GPU selection equal
-    to the others' and checked against it, and outputs per head."""
+    to the others' and checked against it, merged tables and outputs per
+    head."""
     spec = batch.spec
     G = spec.group
     out = sess.out.cpu().numpy()
@@ -826,16 +806,15 @@ def per_sequence_check(batch, sess, t, seqs=None, host=None):
             assert np.array_equal(sel, sel0), ctx
             hr = res.heads[h]
             check_selection(sel, hr, res.regions.n_init, ctx)
-            mlog, _ = gpu_merged_logical(sess, batch, b, h, host is not None)
+            expect = check_merged(sess, batch, b, h, res.regions, sel, host, ctx)
             q = qall[b, h * G:(h + 1) * G]
             if np.array_equal(sel, hr.selected):
-                assert np.array_equal(mlog, hr.merged), ctx
                 ref = res.out[h * G:(h + 1) * G]
             else:
                 prm1 = O.Params(G, 1, prm.init_tokens, prm.local_tokens, prm.topk_ppm,
                                 prm.dense_boundary)
                 ref = O.decode_step(q, K[h:h + 1], V[h:h + 1], L, int(batch.context[b]),
-                                    prm1, merged_override=[mlog]).out
+                                    prm1, merged_override=[expect]).out
             check_head_output(out[b, h * G:(h + 1) * G], ref, ctx)
 
 
@@ -1041,8 +1020,8 @@ def fused_vs_separate(spec, launch=None, steps=None, zero_q=False, mutate=None,
                 sess.step_separate(q, kn, vn, lens)
             torch.cuda.synchronize()
             rec.append(_snapshot(sess))
-            if mode == "step" and oracle_check and not zero_q:
-                oracle_full_check(batch, sess, t)
+            if mode == "step" and oracle_check:
+                oracle_full_check(batch, sess, t, q=q if zero_q else None)
         rec.append((u16(batch.k_pages), u16(batch.v_pages), sess.reps.cpu().numpy()))
         runs.append(rec)
         del batch, sess
@@ -1072,7 +1051,7 @@ def test_decode_step_all_scores_tied():
     spec = synth.custom("tied", batch=1, n_q_heads=16, n_kv_heads=4, context=(40000,),
                         steps=2, dense_boundary=0, config_id=120)
     say("decode step, all scores tied")
-    runs = fused_vs_separate(spec, zero_q=True)
+    runs = fused_vs_separate(spec, zero_q=True, oracle_check=True)
     n_init = 8
     n_sel = runs[0][0][1][0]
     sel = runs[0][0][3][0]
@@ -1092,7 +1071,8 @@ def test_decode_step_partial_ties_at_the_threshold():
 
     say("decode step, duplicated blocks (ties)")
     for ppm in (50_000, 200_000, 500_000):
-        fused_vs_separate(spec, dict(topk_ppm=ppm), mutate=dup)
+        fused_vs_separate(synth.scaled(spec, topk_ppm=ppm), mutate=dup,
+                          oracle_check=True)
 
 
 @pytest.mark.parametrize("ctx,expect_fused", [(131071, True), (131072, False)])
