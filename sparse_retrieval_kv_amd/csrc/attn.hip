@@ -13,9 +13,11 @@
 // waves (default two per compute unit), taken in a virtual order that puts
 // the waves sharing a compute unit next to each other, so every compute
 // unit streams the same share.  A wave's range meets one or a few lists;
-// for each list it writes one partial (m, l, acc) into that list's own run
-// of slots, numbered along the list, and the wave holding a list's first
-// unit records how many pieces the list has.  T is known only on the
+// for each list it writes one partial (m, l, acc) into slot v + list (v: the
+// wave's virtual index).  Walking the range, every step to the next piece
+// moves to the next wave or the next list or both, so v + list never repeats
+// and a list's pieces sit in consecutive slots; the wave holding a list's
+// first unit records the first slot and the piece count.  T is known only on the
 // device, so every wave derives the partition from n_merged itself: ragged
 // batches stay balanced and no host round trip is needed.  A batch of one
 // sequence (all its lists equally long) instead deals each list's units
@@ -112,10 +114,11 @@ struct AttnArgs {
   const int32_t* merged;
   const int32_t* n_merged;
   const int32_t* lens;
-  float* part_acc;   // [batch * n_kv][piece_cap][group][128]
-  float2* part_ml;   // [batch * n_kv][piece_cap][group]
+  float* part_acc;   // [n_slots][group][128]
+  float2* part_ml;   // [n_slots][group]
   int* n_pieces;     // [batch * n_kv]: pieces of each non-empty list
-  int m_cap, max_len, batch, n_kv, group, n_waves, piece_cap;
+  int* first_slot;   // [batch * n_kv]: slot of a list's first piece (range split)
+  int m_cap, max_len, batch, n_kv, group, n_waves, n_slots;
   int comb_spec;     // pieces per combine lane requested before the count
   int n_cu;          // compute units of the device
   int per_list;      // > 0: waves per list of the single-sequence partition
@@ -153,14 +156,19 @@ __device__ __forceinline__ int virtual_wave(int w, int W, int n_cu) {
   return (w % n_cu) * (W / n_cu) + w / n_cu;
 }
 
+// With at least as many units as waves, wave v takes units
+// [v T / W, (v+1) T / W); with fewer, wave v < T takes unit v alone (so the
+// waves holding units are consecutive in both cases).
 __device__ __forceinline__ int64_t unit_start(int v, int64_t T, int W) {
-  return (int64_t)v * T / W;
+  if (T >= W) return (int64_t)v * T / W;
+  return v < T ? v : T;
 }
 
 // The virtual wave whose range holds unit u (0 <= u < T): the largest v
 // with unit_start(v) <= u.
 __device__ __forceinline__ int wave_of(int64_t u, int64_t T, int W) {
-  return (int)(((u + 1) * W - 1) / T);
+  if (T >= W) return (int)(((u + 1) * W - 1) / T);
+  return (int)u;
 }
 
 __device__ __forceinline__ int wave_sum_i(int x) {
@@ -574,17 +582,16 @@ __device__ __forceinline__ void split_body(const AttnArgs& a) {
       const int pu = __shfl(u, src);
       const int64_t a0 = lo > ps ? lo : ps;
       const int64_t a1 = hi < ps + pu ? hi : ps + pu;
-      // pieces of a list are numbered along it: with T >= W every wave
-      // has units, so piece = w - w0; otherwise every non-empty wave has
-      // one unit, so piece = that unit's index in the list.  The wave that
-      // holds the list's first unit records the count.
-      const int w0 = wave_of(ps, T, W);
-      const bool dense_waves = T >= W;
-      const int piece = dense_waves ? w - w0 : (int)(a0 - ps);
-      if (a0 == ps && lane == 0)
-        a.n_pieces[pbh] = dense_waves ? wave_of(ps + pu - 1, T, W) - w0 + 1 : pu;
-      run_piece(a, math, pbh, (int)(a0 - ps), (int)(a1 - ps),
-                (int64_t)pbh * a.piece_cap + piece, lane, col, grp);
+      // the list's pieces are those of waves wave_of(ps) .. wave_of(ps +
+      // pu - 1), in slots wave + list; the wave holding the list's first
+      // unit records where they start and how many there are
+      if (a0 == ps && lane == 0) {
+        const int w0 = wave_of(ps, T, W);
+        a.first_slot[pbh] = w0 + pbh;
+        a.n_pieces[pbh] = wave_of(ps + pu - 1, T, W) - w0 + 1;
+      }
+      run_piece(a, math, pbh, (int)(a0 - ps), (int)(a1 - ps), (int64_t)w + pbh,
+                lane, col, grp);
     }
     run += __shfl(incl, 63);
   }
@@ -640,7 +647,7 @@ __device__ __forceinline__ void strided_loop(const AttnArgs& a, Math& math, int 
     if (!cur_ok || valid == 0) continue;
     math.accumulate(s, vf, valid, a.scale_log2, col, grp);
   }
-  math.finish(a, (int64_t)bh * a.piece_cap + c, lane, col, grp);
+  math.finish(a, (int64_t)bh * P + c, lane, col, grp);
 }
 
 // Single-sequence partition (batch of one: every list has the same length,
@@ -903,10 +910,13 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // Combine: one wave per (sequence, query head, 32-dim slice), so that even a
 // batch of one sequence spreads the partial reads over many compute units.
-// A list's pieces sit in its own run of piece_cap slots.  Lane (pg, d4)
-// takes pieces pg, pg + 8, ... (up to 16 requested at once) over the float4
-// d4 of the slice and folds them with a running maximum; the eight piece
-// groups are then merged by log-sum-exp in a fixed butterfly order.
+// A list's pieces sit in consecutive slots: from slot list * P in the
+// single-sequence partition (known up front, so the first pieces are
+// requested together with the piece count), from the recorded first slot in
+// the range split.  Lane (pg, d4) takes pieces pg, pg + 8, ... (up to 16
+// requested at once) over the float4 d4 of the slice and folds them with a
+// running maximum; the eight piece groups are then merged by log-sum-exp in
+// a fixed butterfly order.
 // ---------------------------------------------------------------------------
 constexpr int kCombSlices = 4;   // 32-dim slices per query head
 constexpr int kCombGroups = 8;   // piece groups per wave
@@ -935,13 +945,16 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a,
   const int Hq = a.n_kv * G;
   const int b = bq / Hq, qh = bq - b * Hq;
   const int bh = b * a.n_kv + qh / G, hh = qh - (qh / G) * G;
-  const int P = a.piece_cap;
-  const int64_t slot0 = (int64_t)bh * P;
+  const bool strided = a.per_list > 0;  // uniform
   const int dim0 = 32 * slice + 4 * d4;
   float4* dst = reinterpret_cast<float4*>(out + (int64_t)bq * kDim + dim0);
 
-  // the first `spec` pieces per lane are requested together with the
-  // piece count (spec is sized by the host for lists of average length)
+  // single-sequence partition: the first `spec` pieces per lane are
+  // requested together with the piece count (spec: the host's estimate of a
+  // list's pieces per lane; 0 in the range split, whose slots are known
+  // only from first_slot)
+  const int P = strided ? a.per_list : a.n_slots;
+  const int64_t sslot0 = strided ? (int64_t)bh * P : 0;
   const int spec = a.comb_spec;
   float2 ml0[kCombSpecMax];
   float4 v0[kCombSpecMax];
@@ -949,14 +962,21 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a,
   for (int u = 0; u < kCombSpecMax; ++u) {
     if (u < spec) {
       const int i = pg + u * kCombGroups;
-      const int64_t slot = slot0 + (i < P ? i : P - 1);
+      const int64_t slot = sslot0 + (i < P ? i : P - 1);
       ml0[u] = a.part_ml[slot * G + hh];
       v0[u] = *reinterpret_cast<const float4*>(a.part_acc + (slot * G + hh) * kDim + dim0);
     }
   }
   const int units = units_of(a, bh);
   int np = a.n_pieces[bh];
-  np = units == 0 ? 0 : (np < 1 ? 1 : (np > P ? P : np));
+  int fs = a.first_slot[bh];
+  int64_t slot0 = sslot0;
+  if (!strided) {  // uniform
+    fs = fs < 0 ? 0 : (fs > a.n_slots - 1 ? a.n_slots - 1 : fs);
+    slot0 = fs;
+  }
+  const int np_cap = strided ? P : a.n_slots - fs;
+  np = units == 0 ? 0 : (np < 1 ? 1 : (np > np_cap ? np_cap : np));
   float m = kNegInf, l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -1003,31 +1023,31 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a,
 AttnPlan plan_attention(int batch, int n_q_heads, int n_kv_heads, int waves,
                         int m_cap, int n_cu) {
   AttnPlan p;
+  (void)m_cap;
   // two waves per compute unit (one per SIMD pair): the whole split runs in
   // one round, each wave streaming its own run of units
   p.n_cu = n_cu > 0 ? n_cu : 256;
   p.n_waves = waves > 0 ? waves : 2 * p.n_cu;
-  // a list of at most 2 * m_cap units meets at most min(W, 2 m_cap) + 1 waves
-  const int units_cap = 2 * (m_cap > 0 ? m_cap : 1);
-  p.piece_cap = (p.n_waves < units_cap ? p.n_waves : units_cap) + 1;
-  const int group = n_kv_heads > 0 ? n_q_heads / n_kv_heads : 0;
-  const size_t slots = (size_t)batch * n_kv_heads * p.piece_cap;
-  p.partial_bytes = slots * group * kDim * sizeof(float);
-  p.ml_bytes = slots * group * 2 * sizeof(float);
-  p.count_bytes = ((size_t)batch * n_kv_heads * sizeof(int) + 255) / 256 * 256;
-  // lists of average length meet about W / lists + 1 waves; the combine's
-  // eight lanes per slice request that many pieces before knowing the count
-  const int64_t lists = (int64_t)batch * n_kv_heads;
-  const int64_t avg = lists > 0 ? p.n_waves / lists + 2 : 1;
-  int spec = (int)((avg + 7) / 8);
-  p.comb_spec = spec < 1 ? 1 : (spec > 20 ? 20 : spec);
-  p.total_bytes = p.partial_bytes + p.ml_bytes + p.count_bytes;
-  // a single sequence takes the length-independent strided partition
+  const int64_t lists = (int64_t)batch * (n_kv_heads > 0 ? n_kv_heads : 0);
+  // a single sequence takes the length-independent strided partition: P
+  // waves per list, slot list * P + c for wave c of a list; the range split
+  // writes slot v + list for virtual wave v, at most W + lists slots
   p.per_list = 0;
   if (batch == 1 && n_kv_heads > 0) {
     p.per_list = p.n_waves / n_kv_heads;
     if (p.per_list < 1) p.per_list = 1;
   }
+  p.n_slots = p.per_list > 0 ? lists * p.per_list : p.n_waves + lists;
+  const int group = n_kv_heads > 0 ? n_q_heads / n_kv_heads : 0;
+  p.partial_bytes = (size_t)p.n_slots * group * kDim * sizeof(float);
+  p.ml_bytes = (size_t)p.n_slots * group * 2 * sizeof(float);
+  // piece counts, then first slots
+  p.count_bytes = ((size_t)lists * 2 * sizeof(int) + 255) / 256 * 256;
+  // single-sequence partition: a list has per_list pieces at most; the
+  // combine's eight lanes per slice request them before knowing the count
+  int spec = (p.per_list + 7) / 8;
+  p.comb_spec = p.per_list > 0 ? (spec < 1 ? 1 : (spec > 20 ? 20 : spec)) : 0;
+  p.total_bytes = p.partial_bytes + p.ml_bytes + p.count_bytes;
   return p;
 }
 
@@ -1051,7 +1071,8 @@ AttnArgs attn_args(const Method& m, const AttnPlan& plan, float scale,
                                         plan.partial_bytes);
   a.n_pieces = reinterpret_cast<int*>(static_cast<char*>(workspace) +
                                       plan.partial_bytes + plan.ml_bytes);
-  a.piece_cap = plan.piece_cap;
+  a.first_slot = a.n_pieces + (int64_t)batch * m.n_kv_heads;
+  a.n_slots = plan.n_slots;
   a.comb_spec = plan.comb_spec;
   a.n_cu = plan.n_cu;
   a.m_cap = m_cap;

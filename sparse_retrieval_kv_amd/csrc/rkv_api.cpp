@@ -637,34 +637,11 @@ rkv_status rkv_decode_step(const rkv_params* params, const uint16_t* k_new,
                            void* select_workspace, size_t select_workspace_bytes,
                            void* attn_workspace, size_t attn_workspace_bytes,
                            hipStream_t stream) {
-  rkv::Method m;
-  rkv::AttnPlan plan;
-  RKV_TRY(select_attend_checks(params, &m, q, k_pages, v_pages, n_pages, block_table,
-                               max_blocks, lens, batch, sel_ids, n_sel, k_cap,
-                               merged, n_merged, m_cap, out, attn_workspace,
-                               attn_workspace_bytes, &plan));
-  RKV_REQUIRE(reps != nullptr && aligned16(reps), RKV_ERR_INVALID_ARG,
-              "reps must be a 16-byte aligned, non-NULL pointer");
-  RKV_REQUIRE(k_new && v_new, RKV_ERR_INVALID_ARG, "k_new and v_new must not be NULL");
-  RKV_REQUIRE(aligned16(k_new) && aligned16(v_new), RKV_ERR_INVALID_ARG,
-              "k_new and v_new must be 16-byte aligned");
-  const size_t need = rkv_select_workspace_size(params, batch, max_blocks);
-  RKV_REQUIRE(select_workspace_bytes >= need && (need == 0 || select_workspace),
-              RKV_ERR_WORKSPACE, "select workspace %zu bytes, need %zu",
-              select_workspace_bytes, need);
-  RKV_REQUIRE(select_workspace != attn_workspace || need == 0, RKV_ERR_INVALID_ARG,
-              "the select and attention workspaces must not be the same buffer");
-  uint32_t* scores = static_cast<uint32_t*>(select_workspace);
-  const rkv::AppendOp op{k_new, v_new, k_pages, v_pages, n_pages, reps};
-  hipError_t e = rkv::launch_score(m, q, reps, block_table, lens, prompt_lens, batch,
-                                   max_blocks, scores, &op, stream);
-  if (e != hipSuccess) return hip_status(e, "rkv_decode_step launch");
-  return hip_status(
-      select_attend_launch(params, m, plan, q, k_pages, v_pages, n_pages, block_table,
-                           max_blocks, lens, prompt_lens, batch, scores, sel_ids,
-                           n_sel, k_cap, merged, n_merged, m_cap, out,
-                           attn_workspace, stream),
-      "rkv_decode_step launch");
+  return rkv::decode_step_impl(params, k_new, v_new, k_pages, v_pages, n_pages, q,
+                               reps, block_table, lens, prompt_lens, batch,
+                               max_blocks, sel_ids, n_sel, k_cap, merged, n_merged,
+                               m_cap, out, select_workspace, select_workspace_bytes,
+                               attn_workspace, attn_workspace_bytes, stream);
 }
 
 rkv_status rkv_read_probe(const void* buffer, size_t bytes, uint32_t* sink,
@@ -682,6 +659,57 @@ rkv_status rkv_read_probe(const void* buffer, size_t bytes, uint32_t* sink,
 }  // extern "C"
 
 namespace rkv {
+
+rkv_status decode_step_impl(const rkv_params* params, const uint16_t* k_new,
+                           const uint16_t* v_new, uint16_t* k_pages,
+                           uint16_t* v_pages, int64_t n_pages, const uint16_t* q,
+                           float* reps, const int32_t* block_table,
+                           const int32_t* lens, const int32_t* prompt_lens,
+                           int32_t batch, int32_t max_blocks, int32_t* sel_ids,
+                           int32_t* n_sel, int32_t k_cap, int32_t* merged,
+                           int32_t* n_merged, int32_t m_cap, float* out,
+                           void* select_workspace, size_t select_workspace_bytes,
+                           void* attn_workspace, size_t attn_workspace_bytes,
+                           hipStream_t stream) {
+  rkv::Method m;
+  rkv::AttnPlan plan;
+  RKV_TRY(select_attend_checks(params, &m, q, k_pages, v_pages, n_pages, block_table,
+                               max_blocks, lens, batch, sel_ids, n_sel, k_cap,
+                               merged, n_merged, m_cap, out, attn_workspace,
+                               attn_workspace_bytes, &plan));
+  RKV_REQUIRE(reps != nullptr && aligned16(reps), RKV_ERR_INVALID_ARG,
+              "reps must be a 16-byte aligned, non-NULL pointer");
+  RKV_REQUIRE(k_new && v_new, RKV_ERR_INVALID_ARG, "k_new and v_new must not be NULL");
+  RKV_REQUIRE(aligned16(k_new) && aligned16(v_new), RKV_ERR_INVALID_ARG,
+              "k_new and v_new must be 16-byte aligned");
+  const size_t need = rkv_select_workspace_size(params, batch, max_blocks);
+  RKV_REQUIRE(select_workspace_bytes >= need && (need == 0 || select_workspace),
+              RKV_ERR_WORKSPACE, "select workspace %zu bytes, need %zu",
+              select_workspace_bytes, need);
+  {
+    // the two workspaces must not overlap: the attention waves of a list
+    // read the scores while other waves write partials
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(select_workspace);
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(attn_workspace);
+    const bool disjoint = need == 0 || plan.total_bytes == 0 ||
+                          s0 + need <= a0 || a0 + plan.total_bytes <= s0;
+    RKV_REQUIRE(disjoint, RKV_ERR_INVALID_ARG,
+                "the select workspace [%p, +%zu) and the attention workspace "
+                "[%p, +%zu) overlap", select_workspace, need, attn_workspace,
+                plan.total_bytes);
+  }
+  uint32_t* scores = static_cast<uint32_t*>(select_workspace);
+  const rkv::AppendOp op{k_new, v_new, k_pages, v_pages, n_pages, reps};
+  hipError_t e = rkv::launch_score(m, q, reps, block_table, lens, prompt_lens, batch,
+                                   max_blocks, scores, &op, stream);
+  if (e != hipSuccess) return hip_status(e, "rkv_decode_step launch");
+  return hip_status(
+      select_attend_launch(params, m, plan, q, k_pages, v_pages, n_pages, block_table,
+                           max_blocks, lens, prompt_lens, batch, scores, sel_ids,
+                           n_sel, k_cap, merged, n_merged, m_cap, out,
+                           attn_workspace, stream),
+      "rkv_decode_step launch");
+}
 
 int device_cu_count() {
   static std::atomic<int> cache[64];  // 0: not queried yet

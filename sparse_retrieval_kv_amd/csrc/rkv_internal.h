@@ -9,6 +9,8 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include "rkv.h"
+
 namespace rkv {
 
 constexpr int kBlock = 128;   // tokens per block / page
@@ -111,17 +113,18 @@ hipError_t launch_stage_resident(const Method& m, const uint16_t* host_k,
 
 // Split-K decode attention over a fixed number of waves: the 64-token units
 // of all merged lists are spread evenly over `n_waves` waves; the workspace
-// holds one partial per (wave, list) piece, n_waves + batch * n_kv_heads
-// slots of `group` heads.
+// holds one partial per (wave, list) piece: n_waves + lists slots of
+// `group` heads for the range split, lists * per_list for the
+// single-sequence partition.
 struct AttnPlan {
   int n_waves;
-  int piece_cap;         // partial slots per (sequence, KV head) list
+  int n_slots;           // partial slots
   int comb_spec;         // combine pieces per lane requested speculatively
   int n_cu;              // compute units of the device
   int per_list;          // > 0: single-sequence partition, waves per list
-  size_t partial_bytes;  // fp32 [lists][piece_cap][group][kDim]
-  size_t ml_bytes;       // float2 [lists][piece_cap][group]
-  size_t count_bytes;    // int [lists] piece counts (padded)
+  size_t partial_bytes;  // fp32 [n_slots][group][kDim]
+  size_t ml_bytes;       // float2 [n_slots][group]
+  size_t count_bytes;    // int [lists] piece counts, int [lists] first slots (padded)
   size_t total_bytes;
 };
 AttnPlan plan_attention(int batch, int n_q_heads, int n_kv_heads, int waves,
@@ -160,5 +163,20 @@ hipError_t launch_select_attn(const Method& m, bool use_mfma, const AttnPlan& pl
 
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
                              int n_cu, hipStream_t stream);
+
+// Body of rkv_decode_step (validation, then the launches) with the two
+// workspaces as given; also behind the entry point that takes them from the
+// library's static scratch.
+rkv_status decode_step_impl(const rkv_params* params, const uint16_t* k_new,
+                            const uint16_t* v_new, uint16_t* k_pages,
+                            uint16_t* v_pages, int64_t n_pages, const uint16_t* q,
+                            float* reps, const int32_t* block_table,
+                            const int32_t* lens, const int32_t* prompt_lens,
+                            int32_t batch, int32_t max_blocks, int32_t* sel_ids,
+                            int32_t* n_sel, int32_t k_cap, int32_t* merged,
+                            int32_t* n_merged, int32_t m_cap, float* out,
+                            void* select_workspace, size_t select_workspace_bytes,
+                            void* attn_workspace, size_t attn_workspace_bytes,
+                            hipStream_t stream);
 
 }  // namespace rkv

@@ -170,6 +170,11 @@ def test_select_attend_and_decode_step_validation(L):
     assert b"select workspace" in L.rkv_last_error()
     assert step(attn_bytes=big - 1) == B.RKV_ERR_WORKSPACE
     assert step(attn_ws=FAKE) == B.RKV_ERR_INVALID_ARG   # same buffer as select
+    # overlapping byte ranges, either way round
+    assert step(attn_ws=FAKE + 16) == B.RKV_ERR_INVALID_ARG
+    assert b"overlap" in L.rkv_last_error()
+    assert step(sel_ws=FAKE + 0x100000 + 256) == B.RKV_ERR_INVALID_ARG
+    assert step(sel_ws=FAKE + 0x100000 - sel_need + 16) == B.RKV_ERR_INVALID_ARG
     assert step(k_cap=99) == B.RKV_ERR_INVALID_ARG
 
 
