@@ -17,7 +17,8 @@
  *  - Pointers are DEVICE pointers unless a parameter says "host".  The caller
  *    owns every buffer; the library allocates nothing and keeps no state
  *    between calls except the calling thread's last error text and, per
- *    device, its compute-unit count (queried once).
+ *    device, its compute-unit count (queried once) and the address of the
+ *    static scratch array of rkv_decode_step_static.
  *  - bf16 values travel as their 16-bit patterns (uint16_t).
  *  - All work is enqueued asynchronously on the given HIP stream; a call
  *    returns once the work is enqueued.  Arguments are validated on the host
@@ -487,6 +488,35 @@ rkv_status rkv_decode_step(const rkv_params* params, const uint16_t* k_new,
                            void* select_workspace, size_t select_workspace_bytes,
                            void* attn_workspace, size_t attn_workspace_bytes,
                            hipStream_t stream);
+
+/*
+ * rkv_decode_step_static -- for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): rkv_decode_step with both workspaces taken from a scratch
+ * array the library keeps in device memory, RKV_STATIC_SCRATCH_BYTES per
+ * GPU, held from the library's first use on that GPU until the process ends.
+ * The call allocates nothing and gives the same results as rkv_decode_step,
+ * bit for bit (the same kernels run).  The select workspace takes the first
+ * rkv_select_workspace_size bytes (rounded up to 256), the attention
+ * workspace the following rkv_attn_workspace_size bytes; a shape that needs
+ * more than RKV_STATIC_SCRATCH_BYTES in all fails with RKV_ERR_UNSUPPORTED
+ * before anything is enqueued.  Nothing in the scratch has to start at zero.
+ * Every call on one GPU uses that GPU's one scratch array and leaves its
+ * contents there, so calls that overlap on one GPU (other streams, other
+ * host threads) race: the caller must order them.
+ * Other arguments and errors as rkv_decode_step.
+ */
+#define RKV_STATIC_SCRATCH_BYTES (64u << 20)
+rkv_status rkv_decode_step_static(const rkv_params* params, const uint16_t* k_new,
+                                  const uint16_t* v_new, uint16_t* k_pages,
+                                  uint16_t* v_pages, int64_t n_pages,
+                                  const uint16_t* q, float* reps,
+                                  const int32_t* block_table, const int32_t* lens,
+                                  const int32_t* prompt_lens, int32_t batch,
+                                  int32_t max_blocks, int32_t* sel_ids,
+                                  int32_t* n_sel, int32_t k_cap, int32_t* merged,
+                                  int32_t* n_merged, int32_t m_cap, float* out,
+                                  hipStream_t stream);
 
 /*
  * rkv_read_probe -- measurement helper, not part of the method: reads

@@ -88,8 +88,12 @@ _SIGS = {
     "rkv_decode_step": (ctypes.c_int, [_PP, _P, _P, _P, _P, _I64, _P, _P, _P, _P, _P,
                                        _I32, _I32, _P, _P, _I32, _P, _P, _I32, _P, _P,
                                        _SZ, _P, _SZ, _P]),
+    "rkv_decode_step_static": (ctypes.c_int, [_PP, _P, _P, _P, _P, _I64, _P, _P, _P,
+                                              _P, _P, _I32, _I32, _P, _P, _I32, _P,
+                                              _P, _I32, _P, _P]),
     "rkv_read_probe": (ctypes.c_int, [_P, _SZ, _P, _P]),
 }
+RKV_STATIC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -462,6 +466,34 @@ class PreparedStep:
             merged, nmerged, m_cap,
             _dyn(lens, torch.int32, self._lens_shape, "lens", self._dev),
             batch, out, ws, ws_bytes, torch.cuda.current_stream(self._dev).cuda_stream))
+
+
+def decode_step_static(p: Params, q, k_new, v_new, k_pages, v_pages, reps,
+                       block_table, lens, sel_ids, n_sel, merged, n_merged, out,
+                       prompt_lens=None):
+    """rkv_decode_step_static: the decode step with the library's static
+    scratch as its workspaces (no allocation behind the call)."""
+    batch, mb = block_table.shape
+    d = q.device
+    hkv = p.n_kv_heads
+    kv = (batch, hkv, HEAD_DIM)
+    pool = _pool_shape(p, k_pages)
+    _check(lib().rkv_decode_step_static(
+        ctypes.byref(p), _ptr(k_new, torch.int16, "k_new", kv, d),
+        _ptr(v_new, torch.int16, "v_new", kv, d),
+        _ptr(k_pages, torch.int16, "k_pages", pool, d),
+        _ptr(v_pages, torch.int16, "v_pages", pool, d), k_pages.shape[0],
+        _ptr(q, torch.int16, "q", (batch, p.n_q_heads, HEAD_DIM), d),
+        _ptr(reps, torch.float32, "reps", (batch, hkv, mb, HEAD_DIM), d),
+        _ptr(block_table, torch.int32, "block_table", None, d),
+        _ptr(lens, torch.int32, "lens", (batch,), d),
+        _ptr(prompt_lens, torch.int32, "prompt_lens", (batch,), d), batch, mb,
+        _ptr(sel_ids, torch.int32, "sel_ids", (batch, hkv, sel_ids.shape[-1]), d),
+        _ptr(n_sel, torch.int32, "n_sel", (batch, hkv), d), sel_ids.shape[-1],
+        _ptr(merged, torch.int32, "merged", (batch, hkv, merged.shape[-1]), d),
+        _ptr(n_merged, torch.int32, "n_merged", (batch, hkv), d), merged.shape[-1],
+        _ptr(out, torch.float32, "out", (batch, p.n_q_heads, HEAD_DIM), d),
+        _stream(q)))
 
 
 def read_probe(buf, sink):

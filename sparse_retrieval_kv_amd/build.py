@@ -16,7 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "librkv.so")
-SOURCES = ["rkv_api.cpp", "reps.hip", "select.hip", "attn.hip", "stage.hip"]
+SOURCES = ["rkv_api.cpp", "reps.hip", "select.hip", "attn.hip", "stage.hip",
+           "static_scratch.hip"]
 ARCH = "gfx950"
 
 

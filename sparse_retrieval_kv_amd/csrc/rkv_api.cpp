@@ -660,6 +660,16 @@ rkv_status rkv_read_probe(const void* buffer, size_t bytes, uint32_t* sink,
 
 namespace rkv {
 
+rkv_status report(rkv_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
 rkv_status decode_step_impl(const rkv_params* params, const uint16_t* k_new,
                            const uint16_t* v_new, uint16_t* k_pages,
                            uint16_t* v_pages, int64_t n_pages, const uint16_t* q,

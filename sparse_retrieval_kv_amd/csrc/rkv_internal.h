@@ -164,6 +164,9 @@ hipError_t launch_select_attn(const Method& m, bool use_mfma, const AttnPlan& pl
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
                              int n_cu, hipStream_t stream);
 
+// Sets the calling thread's error text (rkv_last_error) and returns s.
+rkv_status report(rkv_status s, const char* fmt, ...);
+
 // Body of rkv_decode_step (validation, then the launches) with the two
 // workspaces as given; also behind the entry point that takes them from the
 // library's static scratch.

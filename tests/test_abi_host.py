@@ -271,6 +271,27 @@ def test_call_extent_limits(L):
                               None) == B.RKV_ERR_UNSUPPORTED
 
 
+def test_static_scratch_limit(L):
+    """rkv_decode_step_static refuses, before touching the device, a shape
+    whose workspaces do not fit the static scratch (65536 split waves of 16
+    query heads: 65538 partial slots of 16 x 520 bytes)."""
+    assert B.RKV_STATIC_SCRATCH_BYTES == 64 << 20
+    p = L.rkv_params_default(16, 1)
+    p.split_waves = 1 << 16
+    p.dense_boundary = 0
+    need = (L.rkv_attn_workspace_size(ctypes.byref(p), 2, 100) +
+            L.rkv_select_workspace_size(ctypes.byref(p), 2, 100))
+    assert need > B.RKV_STATIC_SCRATCH_BYTES
+    st = L.rkv_decode_step_static(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 1000, FAKE,
+                                  FAKE, FAKE, FAKE, None, 2, 100, FAKE, FAKE, 100, FAKE,
+                                  FAKE, 100, FAKE, None)
+    assert st == B.RKV_ERR_UNSUPPORTED
+    assert b"static" in L.rkv_last_error()
+    assert L.rkv_decode_step_static(None, FAKE, FAKE, FAKE, FAKE, 1000, FAKE, FAKE, FAKE,
+                                    FAKE, None, 2, 100, FAKE, FAKE, 100, FAKE, FAKE, 100,
+                                    FAKE, None) == B.RKV_ERR_INVALID_ARG
+
+
 def test_workspace_sizes_are_monotone(L):
     p = L.rkv_params_default(32, 8)
     a = L.rkv_attn_workspace_size(ctypes.byref(p), 1, 513)
