@@ -55,6 +55,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace rkv {
 namespace {
 
@@ -598,13 +600,18 @@ __device__ __forceinline__ void split_body(const AttnArgs& a) {
 }
 
 // The unit loop of the single-sequence partition for wave c of list bh,
-// whose list has `units` units (L: the sequence length); page_at(i) gives
-// the page id of the wave's i-th unit (unit c + i P).
-template <class Math, class PageAt>
+// whose list has `units` units (L: the sequence length).  The wave's units
+// are c, c + P, c + 2P, ...; it takes them last first, so that its first unit
+// lies in the list's tail (the window blocks), whose page the folded
+// selection knows before it has found the kept blocks.  page_at(i) gives the
+// page id of the wave's i-th unit (unit c + i P).  With PRE, the first unit's
+// K and V tiles (page pre_page) were requested by the caller into kf / vf.
+template <bool PRE, class Math, class PageAt>
 __device__ __forceinline__ void strided_loop(const AttnArgs& a, Math& math, int bh,
                                              int c, int units, int L,
                                              PageAt page_at, int lane, int col,
-                                             int grp) {
+                                             int grp, uint4 (&kf)[4][4],
+                                             uint4 (&vf)[2][8], int pre_page) {
   const int P = a.per_list;
   const int h = bh % a.n_kv;
   if (c >= units) return;  // uniform over the wave
@@ -624,29 +631,34 @@ __device__ __forceinline__ void strided_loop(const AttnArgs& a, Math& math, int 
     return v < 0 ? 0 : (v > kUnit ? kUnit : v);
   };
 
-  int page = page_at(0);
+  int i = n_mine - 1;
+  int page = PRE ? pre_page : page_at(i);
   int64_t tile = tile_of(page);
-  uint4 kf[4][4];
-  load_k_unit(kf, a.k_pages + tile, c & 1, col, grp);
-  int page_next = n_mine > 1 ? page_at(1) : 0;
-  for (int i = 0; i < n_mine; ++i) {
+  if (!PRE) load_k_unit(kf, a.k_pages + tile, (c + i * P) & 1, col, grp);
+  int page_next = i > 0 ? page_at(i - 1) : 0;
+  // one unit: its scores, its V tile (unless requested ahead), the next
+  // unit's K tile, then its softmax and PV products
+  auto unit = [&](auto load_v) {
     const int u = c + i * P;
     typename Math::Scores s;
     math.scores(kf, s);
     __builtin_amdgcn_sched_barrier(0);
-    uint4 vf[2][8];
-    load_v_unit(vf, a.v_pages + tile, u & 1, col, grp);
+    if (decltype(load_v)::value) load_v_unit(vf, a.v_pages + tile, u & 1, col, grp);
     const bool cur_ok = page_ok(page);
     const int valid = valid_of(u);
-    if (i + 1 < n_mine) {  // prefetch the next unit's K tile
+    if (i > 0) {  // prefetch the next unit's K tile
       page = page_next;
       tile = tile_of(page);
-      page_next = i + 2 < n_mine ? page_at(i + 2) : 0;
-      load_k_unit(kf, a.k_pages + tile, (u + P) & 1, col, grp);
+      page_next = i > 1 ? page_at(i - 2) : 0;
+      load_k_unit(kf, a.k_pages + tile, (u - P) & 1, col, grp);
     }
-    if (!cur_ok || valid == 0) continue;
-    math.accumulate(s, vf, valid, a.scale_log2, col, grp);
+    if (cur_ok && valid > 0) math.accumulate(s, vf, valid, a.scale_log2, col, grp);
+  };
+  if (PRE) {
+    unit(std::false_type());
+    --i;
   }
+  for (; i >= 0; --i) unit(std::true_type());
   math.finish(a, (int64_t)bh * P + c, lane, col, grp);
 }
 
@@ -684,7 +696,9 @@ __device__ __forceinline__ void strided_body(const AttnArgs& a) {
   auto page_at = [&](int i) {
     return i < 64 ? __shfl(pref, i) : mrow[(c + (int64_t)i * P) >> 1];
   };
-  strided_loop(a, math, bh, c, units, L, page_at, lane, col, grp);
+  uint4 kf[4][4];
+  uint4 vf[2][8];
+  strided_loop<false>(a, math, bh, c, units, L, page_at, lane, col, grp, kf, vf, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -783,7 +797,7 @@ __device__ __forceinline__ uint32_t kept_blocks(const uint32_t (&key)[kFusedRegs
 template <class Math>
 __device__ __forceinline__ void select_strided_body(const AttnArgs& a,
                                                     const SelectIn& f) {
-  __shared__ int mlist[kFusedMaxBlocks];
+  __shared__ int mlist[kFusedMaxBlocks + 1];  // + a spare slot
   const int lane = threadIdx.x;
   const int col = lane & 15, grp = lane >> 4;
   const int NB = a.n_kv;  // one sequence
@@ -796,6 +810,8 @@ __device__ __forceinline__ void select_strided_body(const AttnArgs& a,
   // scores and the query rows (clamped indexes, no lane conditions) ---
   const int lraw_v = a.lens[0];
   const int plen_v = (f.prompt_lens ? f.prompt_lens : a.lens)[0];
+  // (the whole table row first: the first tile's page needs only it, and
+  // loads arrive in the order they were requested)
   int tab[kFusedRegs];
   uint32_t raw[kFusedRegs];
 #pragma unroll
@@ -803,6 +819,11 @@ __device__ __forceinline__ void select_strided_body(const AttnArgs& a,
     int j = lane + 64 * i;
     j = j < mb ? j : mb - 1;
     tab[i] = f.table[j];
+  }
+#pragma unroll
+  for (int i = 0; i < kFusedRegs; ++i) {
+    int j = lane + 64 * i;
+    j = j < mb ? j : mb - 1;
     raw[i] = srow_in[j];
   }
   Math math;
@@ -820,27 +841,63 @@ __device__ __forceinline__ void select_strided_body(const AttnArgs& a,
   k = k < R.n_off ? k : R.n_off;
   const bool ranked = k > 0 && k < R.n_off;
   const int ls = R.n_init + R.n_off;  // offload end (= first local block)
+  const int lstart = R.local_start > R.n_init ? R.local_start : R.n_init;
+  const int n_m = R.n_init + k + (R.nb - lstart);
+
+  // --- the wave's first unit (its last in list order) is requested now,
+  // before the selection, when its block does not depend on it: an init
+  // block, a window block, or any block when every offload block is kept.
+  // Entry e of the merged list is block e below n_init + k and block
+  // lstart + (e - n_init - k) from there on.  A wave whose first unit is a
+  // kept block (or that has no unit) requests block 0's tile instead and
+  // does not use it: the code stays straight, since a load under a branch
+  // would make the selection below wait for it where the branch rejoins. ---
+  const int P = a.per_list;
+  const int units = 2 * n_m;
+  const int n_first = c < units ? (units - c + P - 1) / P : 0;
+  const int u_first = c + (n_first - 1) * P;
+  const int e_first = u_first >> 1;
+  const bool early = n_first > 0 && (!ranked || e_first < R.n_init || e_first >= R.n_init + k);
+  int j0 = e_first < R.n_init + k ? e_first : lstart + (e_first - R.n_init - k);
+  j0 = early ? j0 : 0;
+  int t0 = tab[0];
+#pragma unroll
+  for (int i = 1; i < kFusedRegs; ++i) t0 = (j0 >> 6) == i ? tab[i] : t0;
+  const int early_page = __shfl(t0, j0 & 63);
+  const int64_t early_tile =
+      ((uint64_t)(int64_t)early_page < (uint64_t)a.n_pages
+           ? (int64_t)early_page * a.n_kv * (kBlock * kDim) : 0) +
+      (int64_t)bh * (kBlock * kDim);
+  uint4 kf[4][4];
+  uint4 vf[2][8];
+  // only the K tile now: a compute unit keeps about one unit's K and V
+  // (32 KiB) per wave pair in flight, and a wave asking for more stalls at
+  // the request until earlier data returns -- the selection would then
+  // start only after that.  The V tile follows the selection.
+  load_k_unit(kf, a.k_pages + early_tile, u_first & 1, col, grp);
+  __builtin_amdgcn_sched_barrier(0);
 
   // per-lane bit masks over the registers (bit i: block lane + 64 i): the
   // list's offload blocks and the kept ones
+  uint32_t key[kFusedRegs];
+#pragma unroll
+  for (int i = 0; i < kFusedRegs; ++i) key[i] = order_key(__uint_as_float(raw[i]));
   uint32_t cbits = 0, kbits = 0;
 #pragma unroll
   for (int i = 0; i < kFusedRegs; ++i) {
     const int j = lane + 64 * i;
     cbits |= (j >= R.n_init && j < ls) ? 1u << i : 0u;
   }
-  if (ranked) {  // uniform
-    uint32_t key[kFusedRegs];
-#pragma unroll
-    for (int i = 0; i < kFusedRegs; ++i) key[i] = order_key(__uint_as_float(raw[i]));
+  if (ranked)  // uniform
     kbits = (ls + 63) >> 6 <= 8 ? kept_blocks<8>(key, cbits, k, R.n_off, lane)
                                 : kept_blocks<16>(key, cbits, k, R.n_off, lane);
-  }
+  load_v_unit(vf, a.v_pages + early_tile, u_first & 1, col, grp);
 
-  // --- merged page list (init blocks, kept blocks, local blocks) ---
-  const int lstart = R.local_start > R.n_init ? R.local_start : R.n_init;
-  const int n_m = R.n_init + k + (R.nb - lstart);
+  // --- merged page list (init blocks, kept blocks, local blocks), with
+  // selects only: entry dst of block j, -1 when j is not attended (its LDS
+  // write then goes to a spare slot) ---
   const bool writer = c == 0;
+  const bool all_kept = k == R.n_off;
   int32_t* sel_out = f.sel_ids + (int64_t)bh * f.k_cap;
   int32_t* m_out = f.merged + (int64_t)bh * a.m_cap;
   int pos_before = 0;
@@ -851,22 +908,15 @@ __device__ __forceinline__ void select_strided_body(const AttnArgs& a,
       const bool kj = ((kbits >> i) & 1u) != 0u;
       const uint64_t km = __ballot(kj);
       const int pos = pos_before + lanes_below(km);
-      int dst = -1;
-      if (j < R.nb) {
-        if (j < R.n_init)
-          dst = j;
-        else if (j >= lstart)
-          dst = R.n_init + k + (j - lstart);
-        else if (k == R.n_off)
-          dst = j;
-        else if (kj)
-          dst = R.n_init + pos;
+      const bool offl = j >= R.n_init && j < lstart;
+      int dst = j >= lstart ? R.n_init + k + (j - lstart) : j;
+      dst = (offl && !all_kept) ? (kj ? R.n_init + pos : -1) : dst;
+      dst = j < R.nb ? dst : -1;
+      mlist[dst >= 0 ? dst : kFusedMaxBlocks] = tab[i];
+      if (writer) {  // uniform
+        if (dst >= 0) m_out[dst] = tab[i];
+        if (kj) sel_out[pos] = j;
       }
-      if (dst >= 0) {
-        mlist[dst] = tab[i];
-        if (writer) m_out[dst] = tab[i];
-      }
-      if (writer && kj) sel_out[pos] = j;
       pos_before += __popcll(km);
     }
   }
@@ -879,9 +929,12 @@ __device__ __forceinline__ void select_strided_body(const AttnArgs& a,
   __syncthreads();  // the list in LDS is complete (one wave per workgroup)
 
   const int L = clamp_len(lraw, a.max_len);
-  const int P = a.per_list;
   auto page_at = [&](int i) { return mlist[(c + i * P) >> 1]; };
-  strided_loop(a, math, bh, c, 2 * n_m, L, page_at, lane, col, grp);
+  if (early)
+    strided_loop<true>(a, math, bh, c, 2 * n_m, L, page_at, lane, col, grp, kf, vf,
+                       early_page);
+  else
+    strided_loop<false>(a, math, bh, c, 2 * n_m, L, page_at, lane, col, grp, kf, vf, 0);
 }
 
 __global__ __launch_bounds__(64) void attn_select_mfma_kernel(AttnArgs a,
