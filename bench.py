@@ -16,12 +16,19 @@ Consecutive steps cycle over `--layers` independent copies of the layer's
 KV cache (as a model's layers would), so a step never finds the previous
 step's pages in the 256 MB Infinity Cache.
 
+After the headline workload (`--config`, default the Llama-3-8B-shaped
+layer) the same run measures the other workloads of the metric's 64K-128K
+range and the host tier (`--also`, default 3,4,5): each with its own steps/s,
+the roofline of its attention call and the CPU oracle on a bounded sample,
+under "configs" in the JSON line.
+
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
 
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import math
@@ -88,7 +95,7 @@ def step_bytes(spec, context, t):
     return kv * spec.n_kv_heads, reps * spec.n_kv_heads, kept * spec.n_kv_heads
 
 
-def attn_traffic(args):
+def attn_traffic(args, config):
     """Counter-measured HBM bytes per attention call, or None when no
     record exists for this config, launch and attention source.  The records
     were taken with the default launch (MFMA, automatic split, per-head
@@ -96,7 +103,7 @@ def attn_traffic(args):
     if (args.impl not in ("auto", "mfma") or args.split != 0 or
             args.select != "per-head" or args.layers != 0):
         return None
-    rec = MEASURED_TRAFFIC.get(args.config)
+    rec = MEASURED_TRAFFIC.get(config)
     if rec is None:
         return None
     with open(ATTN_SOURCE, "rb") as f:
@@ -241,51 +248,13 @@ def stream_read_probe(dev, gib=2, reps=5):
     return (gib << 30) / (sorted(ms)[len(ms) // 2] * 1e-3) / 1e9
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=256)
-    ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--layers", type=int, default=0,
-                    help="KV-cache copies cycled over (0: enough to exceed 1 GiB)")
-    ap.add_argument("--impl", default="auto", choices=["auto", "mfma", "valu"])
-    ap.add_argument("--split", type=int, default=0)
-    ap.add_argument("--slots", type=float, default=2.0,
-                    help="host tier: staging slots per (sequence, KV head), as a "
-                         "multiple of the kept-block capacity")
-    ap.add_argument("--select", default="per-head", choices=["per-head", "per-sequence"],
-                    help="selection per (sequence, KV head) or once per sequence")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="run one plain 1 GiB device-to-device copy first "
-                         "(a known-size reference for HBM byte counters)")
-    args = ap.parse_args()
-
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
-              "this path has no multi-GPU mode.", file=sys.stderr)
-        sys.exit(2)
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(2)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    B.lib()
-
-    if args.calibrate_copy:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-        log("calibration copy: 1 GiB read + 1 GiB written")
-
-    probe_gbs = stream_read_probe(dev)
-    log(f"streaming-read probe: {probe_gbs:.0f} GB/s")
-
-    spec = synth.CONFIGS[args.config]
-    log("config", args.config, spec.name)
+def run_workload(args, config, steps, warmup, cpu_budget, probe_gbs, dev,
+                 spread_budget=None):
+    """Build one workload, time `steps` decode steps after `warmup`, the
+    attention call alone, the host tier's staging (host-tier workload) and
+    the CPU oracle on a bounded sample.  Returns the workload's record."""
+    spec = synth.CONFIGS[config]
+    log("config", config, spec.name)
     host = None
     prefill = None
     if spec.host_offload:
@@ -359,32 +328,32 @@ def main():
         sess.attend(qs[t], lens[t])
         return t
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         run(i)
     torch.cuda.synchronize()
-    log(f"warmup {args.warmup} done; timing {args.steps} steps")
+    log(f"warmup {warmup} done; timing {steps} steps")
 
     # timed region: K whole steps, nothing else on the stream
     ts = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        ts.append(run(args.warmup + i))
+    for i in range(steps):
+        ts.append(run(warmup + i))
     t_enq = time.perf_counter()  # host side done: every step is enqueued
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = wall * 1e3 / steps
     # the host's enqueue time per step; well below the step time means the
     # wall-clock figure is the GPU's
-    host_us_per_step = (t_enq - t0) * 1e6 / args.steps
+    host_us_per_step = (t_enq - t0) * 1e6 / steps
 
     # spread of the step time: the same steps again in chunks of 16 between
     # HIP event pairs (the pair's own cost, ~10 us, spreads over the chunk)
     chunk = 16
-    n_chunks = max(1, min(16, args.steps // chunk))
+    n_chunks = max(1, min(16, steps // chunk, (spread_budget or steps) // chunk))
     ev_pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 for _ in range(n_chunks)]
-    base_idx = args.warmup + args.steps
+    base_idx = warmup + steps
     torch.cuda.synchronize()
     for c_i, (e0, e1) in enumerate(ev_pairs):
         e0.record()
@@ -393,10 +362,15 @@ def main():
         e1.record()
     torch.cuda.synchronize()
     chunk_us = np.array([a.elapsed_time(b) * 1e3 / chunk for a, b in ev_pairs])
-    step_spread = {"chunk_steps": chunk, "chunks": n_chunks,
-                   "p10_us": float(np.percentile(chunk_us, 10)),
-                   "p50_us": float(np.percentile(chunk_us, 50)),
-                   "p90_us": float(np.percentile(chunk_us, 90))}
+    step_spread = {"chunk_steps": chunk, "chunks": n_chunks}
+    if n_chunks >= 3:
+        step_spread.update({"p10_us": float(np.percentile(chunk_us, 10)),
+                            "p50_us": float(np.percentile(chunk_us, 50)),
+                            "p90_us": float(np.percentile(chunk_us, 90))})
+    else:  # percentiles of one or two chunks would say nothing
+        step_spread.update({"chunk_us": [float(x) for x in chunk_us],
+                            "note": f"{n_chunks} chunk(s) of {chunk} steps: too few "
+                                    "for percentiles"})
 
     # the step's attention call alone, replayed on every layer copy between
     # one pair of HIP events on its stream (an event pair per launch would
@@ -404,7 +378,7 @@ def main():
     # selection + attention call over the scores the last step left
     # (rkv_select_attend: one launch with the top-k folded in, + combine),
     # otherwise rkv_decode_attn over the current merged tables
-    reps_attn = max(args.steps, 2 * n_layers)
+    reps_attn = max(steps, 2 * n_layers)
     t_last = ts[-1]
     ev0, ev1 = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     fused = host is None and fused_select_attend(args, spec, base.table_np.shape[1])
@@ -489,37 +463,22 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(base, host)
+        cpu = cpu_baseline(base, host, budget_s=cpu_budget)
 
-    res = {
-        "metric": METRIC,
-        "value": args.steps / wall,
-        "unit": "steps/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+    return {
+        "workload": spec.name,
+        "config_id": config,
+        "steps": steps,
+        "warmup": warmup,
+        "steps_per_s": steps / wall,
         "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "dtype_detail": "bf16 K/V/q on MFMA, fp32 accumulation, softmax and output",
-        "data": "synthetic (seeded N(0,1) bf16 K/V/q, planted blocks per config)",
-        "config": {
-            "workload": spec.name,
-            "config_id": args.config,
-            "batch": spec.batch,
-            "context": [int(x) for x in base.context[:4]],
-            "heads_q_kv": [spec.n_q_heads, spec.n_kv_heads],
-            "init_local_topk_ppm": [spec.init_tokens, spec.local_tokens, spec.topk_ppm],
-            "layer_copies": n_layers,
-            "attn_impl": args.impl,
-            "split_waves": args.split,
-            "select": args.select,
-        },
+        "batch": spec.batch,
+        "context": [int(x) for x in base.context[:4]],
+        "heads_q_kv": [spec.n_q_heads, spec.n_kv_heads],
+        "init_local_topk_ppm": [spec.init_tokens, spec.local_tokens, spec.topk_ppm],
+        "layer_copies": n_layers,
         "step_us_spread": step_spread,
         "host_enqueue_us_per_step": host_us_per_step,
-        "stream_read_probe_gbs": probe_gbs,
         "host_staging": staging,
         "host_prefill": prefill,
         "attended_kv_gbs_step": step_gbs,
@@ -532,7 +491,7 @@ def main():
             "unit": "GB/s",
             "frac": attn_gbs / HBM_PEAK_GBS,
             "frac_of_read_probe": attn_gbs / probe_gbs,
-            "traffic": attn_traffic(args),
+            "traffic": attn_traffic(args, config),
             "traffic_source": ("rocprofv3 FETCH_SIZE + WRITE_SIZE per call, "
                                "scaled by a 1 GiB copy's readings"),
             "bytes_per_launch": float(kv_attn),
@@ -543,6 +502,106 @@ def main():
                        f"the {n_layers} layer copies between one HIP event pair"),
         },
         "cpu_baseline": cpu,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--layers", type=int, default=0,
+                    help="KV-cache copies cycled over (0: enough to exceed 1 GiB)")
+    ap.add_argument("--impl", default="auto", choices=["auto", "mfma", "valu"])
+    ap.add_argument("--split", type=int, default=0)
+    ap.add_argument("--slots", type=float, default=2.0,
+                    help="host tier: staging slots per (sequence, KV head), as a "
+                         "multiple of the kept-block capacity")
+    ap.add_argument("--select", default="per-head", choices=["per-head", "per-sequence"],
+                    help="selection per (sequence, KV head) or once per sequence")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--also", default="3,4,5",
+                    help="other workloads measured after the headline one in the "
+                         "same run (comma-separated config ids; empty: none)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one plain 1 GiB device-to-device copy first "
+                         "(a known-size reference for HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "this path has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B.lib()
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("calibration copy: 1 GiB read + 1 GiB written")
+
+    probe_gbs = stream_read_probe(dev)
+    log(f"streaming-read probe: {probe_gbs:.0f} GB/s")
+
+    head = run_workload(args, args.config, args.steps, args.warmup, 12.0, probe_gbs, dev)
+    others = {}
+    extra = [int(x) for x in args.also.split(",") if x.strip()] if args.also else []
+    for c in extra:
+        if c == args.config:
+            continue
+        gc.collect()
+        torch.cuda.empty_cache()
+        steps_c = synth.CONFIGS[c].steps * (2 if synth.CONFIGS[c].steps < 32 else 1)
+        others[str(c)] = run_workload(args, c, steps_c, 16, 4.0, probe_gbs, dev,
+                                      spread_budget=steps_c)
+
+    res = {
+        "metric": METRIC,
+        "value": head["steps_per_s"],
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "dtype_detail": "bf16 K/V/q on MFMA, fp32 accumulation, softmax and output",
+        "data": "synthetic (seeded N(0,1) bf16 K/V/q, planted blocks per config)",
+        "config": {
+            "workload": head["workload"],
+            "config_id": args.config,
+            "batch": head["batch"],
+            "context": head["context"],
+            "heads_q_kv": head["heads_q_kv"],
+            "init_local_topk_ppm": head["init_local_topk_ppm"],
+            "layer_copies": head["layer_copies"],
+            "attn_impl": args.impl,
+            "split_waves": args.split,
+            "select": args.select,
+        },
+        "step_us_spread": head["step_us_spread"],
+        "host_enqueue_us_per_step": head["host_enqueue_us_per_step"],
+        "stream_read_probe_gbs": probe_gbs,
+        "host_staging": head["host_staging"],
+        "host_prefill": head["host_prefill"],
+        "attended_kv_gbs_step": head["attended_kv_gbs_step"],
+        "attended_kv_pct_peak_step": head["attended_kv_pct_peak_step"],
+        "roofline": head["roofline"],
+        "cpu_baseline": head["cpu_baseline"],
+        # the other workloads of the metric's 64K-128K range (and the host
+        # tier), each measured in this same run: steps/s, roofline of its
+        # attention call, CPU oracle on a bounded sample
+        "configs": others,
     }
     print(json.dumps(res), flush=True)
 
