@@ -229,6 +229,93 @@ def measure_prefill(sess, host, lens, spec):
     return out
 
 
+def measure_copy_engines(sess, spec, qs, news, lens, T, t_last, kept, gather_us, dev):
+    """Host tier through the copy engines (rkv_stage_*_async: coalesced
+    hipMemcpy2DAsync / hipMemcpyAsync on the side stream) beside the gather
+    kernel: every kept block staged per call, decode steps with residency,
+    and the HBM read rate another stream gets while each mode stages.
+    Leaves the session in the gather-kernel mode with empty slots."""
+    out = {}
+    n_st = 4
+    # every kept block, wall clock per call (the call waits for the kept ids
+    # on the host, then issues the copies; the time runs until they are done)
+    sess.copy_mode, sess.resident = "memcpy", False
+    sess.stage(lens[t_last])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_st):
+        sess.stage(lens[t_last])
+    torch.cuda.synchronize()
+    full_us = (time.perf_counter() - t0) * 1e6 / n_st
+    out["full"] = {"bytes_per_step": float(kept), "avg_us": full_us,
+                   "gbs": kept / (full_us * 1e-6) / 1e9}
+    # decode steps with residency from empty slots, as the timed steps run
+    sess.resident = True
+    sess.reset_residency()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(T):
+        kn, vn = news[t]
+        sess.step(qs[t], kn, vn, lens[t])
+    torch.cuda.synchronize()
+    step_us = (time.perf_counter() - t0) * 1e6 / T
+    out["resident_step_us"] = step_us
+    out["resident_steps_per_s"] = 1e6 / step_us
+    log(f"copy engines: full staging {full_us:.0f} us ({out['full']['gbs']:.1f} GB/s); "
+        f"steps with residency {step_us:.0f} us (gather kernel: full {gather_us:.0f} us)")
+
+    # HBM readers beside staging: rkv_read_probe over 1 GiB on its own
+    # stream, alone and while every kept block is staged by either mode
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    ps = torch.cuda.Stream(device=dev)
+
+    def probe_rate(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(ps):
+            e0.record()
+            for _ in range(n):
+                B.read_probe(buf, sink)
+            e1.record()
+        return n, e0, e1
+
+    def finish(ev):
+        torch.cuda.synchronize()
+        n, e0, e1 = ev
+        return n * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+    torch.cuda.synchronize()
+    out["read_probe_alone_gbs"] = finish(probe_rate(8))
+    probe_us = (1 << 30) / (out["read_probe_alone_gbs"] * 1e9) * 1e6
+    main = torch.cuda.current_stream(dev)
+    for mode, mode_us in (("kernel", gather_us), ("memcpy", full_us)):
+        sess.copy_mode, sess.resident = mode, False
+        torch.cuda.synchronize()
+        # probes first (they start at once), then the staging: probes covering
+        # about half the staging time all run beside it
+        ev = probe_rate(max(4, int(0.5 * mode_us / probe_us)))
+        if mode == "kernel":
+            sess.side.wait_stream(main)
+            with torch.cuda.stream(sess.side):
+                sess.stage(lens[t_last])
+        else:
+            sess.stage(lens[t_last])  # copies queued on the side stream
+        out[f"read_probe_beside_{mode}_gbs"] = finish(ev)
+    del buf
+    log(f"HBM read probe: alone {out['read_probe_alone_gbs']:.0f} GB/s, beside the "
+        f"gather kernel {out['read_probe_beside_kernel_gbs']:.0f} GB/s, beside the copy "
+        f"engines {out['read_probe_beside_memcpy_gbs']:.0f} GB/s")
+    sess.copy_mode, sess.resident = "kernel", True
+    sess.reset_residency()
+    torch.cuda.synchronize()
+    out["path"] = ("kept ids (or the residency planner's copy list) to pinned host "
+                   "memory, then one hipMemcpy2DAsync per run of consecutive blocks "
+                   "and KV head (whole pages in the per-sequence mode) on the side "
+                   "stream; the main stream waits on an event")
+    return out
+
+
 def stream_read_probe(dev, gib=2, reps=5):
     """Achievable streaming-read bandwidth: rkv_read_probe over a buffer
     larger than the Infinity Cache, median of `reps` timed launches."""
@@ -452,6 +539,8 @@ def run_workload(args, config, steps, warmup, cpu_budget, probe_gbs, dev,
         log(f"full staging {st_us:.0f} us ({staging['full']['gbs']:.1f} GB/s); "
             f"residency copies {staging['resident']['fraction_of_full'] * 100:.0f}% "
             "of the kept bytes per step")
+        staging["copy_engines"] = measure_copy_engines(sess, spec, qs, news, lens, T,
+                                                       t_last, kept, st_us, dev)
 
     kv_b = np.array([step_bytes(spec, base.context, t)[0] for t in ts], dtype=np.float64)
     rep_b = np.array([step_bytes(spec, base.context, t)[1] for t in ts], dtype=np.float64)

@@ -381,6 +381,73 @@ rkv_status rkv_stage_resident(const rkv_params* params, const uint16_t* host_k,
                               hipStream_t stream);
 
 /*
+ * Bytes of pinned host memory (host_list) the copy-engine staging calls
+ * below need for these sizes.
+ */
+size_t rkv_stage_host_list_size(const rkv_params* params, int32_t batch,
+                                int32_t k_cap);
+
+/*
+ * rkv_stage_blocks_async -- rkv_stage_blocks through the copy engines (same
+ * source, page and staging-page rules, same results): the kept ids and
+ * counts (device sel_ids / n_sel as rkv_select wrote them) are copied to the
+ * pinned host buffer host_list on `stream`, the calling thread waits for
+ * them, and the K and V tiles of every kept host-resident block are copied
+ * with hipMemcpy2DAsync / hipMemcpyAsync on `side`: one copy per run of
+ * consecutive blocks on consecutive host pages going to consecutive staging
+ * pages (per KV head, a 2-D copy with a one-page pitch; in the per-sequence
+ * selection mode, where every head keeps the same blocks, whole pages in one
+ * contiguous copy).  `done` (may be NULL) is recorded on `side` after the
+ * last copy: make the attention's stream wait for it.  The merged table
+ * comes from rkv_merge_table with the device host table, as for
+ * rkv_stage_blocks.  The call blocks the calling thread until the ids are
+ * on the host, so it cannot be captured in a graph.
+ *   host_table_host [batch][max_blocks] HOST int32: the same table as the
+ *                   device host_table of rkv_stage_blocks
+ *   host_list       pinned host memory, >= rkv_stage_host_list_size bytes
+ * Other arguments as rkv_stage_blocks.
+ * Errors: RKV_ERR_INVALID_ARG (including host pools or host_list that are
+ * not pinned host memory), RKV_ERR_UNSUPPORTED, RKV_ERR_WORKSPACE,
+ * RKV_ERR_HIP.
+ */
+rkv_status rkv_stage_blocks_async(const rkv_params* params, const uint16_t* host_k,
+                                  const uint16_t* host_v, int64_t n_host_pages,
+                                  const int32_t* host_table_host, int32_t max_blocks,
+                                  const int32_t* sel_ids, const int32_t* n_sel,
+                                  int32_t k_cap, int32_t batch, uint16_t* k_pages,
+                                  uint16_t* v_pages, int64_t n_pages,
+                                  int64_t stage_page0, void* host_list,
+                                  size_t host_list_bytes, hipStream_t stream,
+                                  hipStream_t side, hipEvent_t done);
+
+/*
+ * rkv_stage_resident_async -- rkv_stage_resident with the copies through the
+ * copy engines (same slot policy, slot state, merged table and results): the
+ * slot planner runs on `stream`, its (block, slot) copy list and counts go
+ * to the pinned host buffer host_list, the calling thread waits for them,
+ * and the copies are issued on `side` as for rkv_stage_blocks_async (runs
+ * of consecutive blocks, host pages and slots; whole pages in the
+ * per-sequence mode).  `done` (may be NULL) is recorded on `side` after the
+ * last copy.  Blocks the calling thread until the list is on the host.
+ *   host_table      [batch][max_blocks] DEVICE int32 (read by the planner)
+ *   host_table_host the same table in HOST memory (read by the copy issue)
+ *   host_list       pinned host memory, >= rkv_stage_host_list_size bytes
+ * Other arguments as rkv_stage_resident.
+ * Errors: as rkv_stage_resident, and RKV_ERR_INVALID_ARG / RKV_ERR_WORKSPACE
+ * for host_list.
+ */
+rkv_status rkv_stage_resident_async(
+    const rkv_params* params, const uint16_t* host_k, const uint16_t* host_v,
+    int64_t n_host_pages, const int32_t* host_table, const int32_t* host_table_host,
+    const int32_t* block_table, int32_t max_blocks, const int32_t* lens,
+    const int32_t* sel_ids, const int32_t* n_sel, int32_t k_cap, int32_t batch,
+    int32_t slot_cap, int32_t* slot_ids, int32_t* slot_cursor, uint16_t* k_pages,
+    uint16_t* v_pages, int64_t n_pages, int64_t stage_page0, int32_t* merged,
+    int32_t* n_merged, int32_t m_cap, int32_t* n_staged, void* workspace,
+    size_t workspace_bytes, void* host_list, size_t host_list_bytes,
+    hipStream_t stream, hipStream_t side, hipEvent_t done);
+
+/*
  * Workspace bytes rkv_decode_attn needs for these sizes.
  */
 size_t rkv_attn_workspace_size(const rkv_params* params, int32_t batch,

@@ -79,6 +79,14 @@ _SIGS = {
     "rkv_stage_resident": (ctypes.c_int, [_PP, _P, _P, _I64, _P, _P, _I32, _P, _P,
                                           _P, _I32, _I32, _I32, _P, _P, _P, _P, _I64,
                                           _I64, _P, _P, _I32, _P, _P, _SZ, _P]),
+    "rkv_stage_host_list_size": (_SZ, [_PP, _I32, _I32]),
+    "rkv_stage_blocks_async": (ctypes.c_int, [_PP, _P, _P, _I64, _P, _I32, _P, _P, _I32,
+                                              _I32, _P, _P, _I64, _I64, _P, _SZ, _P, _P,
+                                              _P]),
+    "rkv_stage_resident_async": (ctypes.c_int, [_PP, _P, _P, _I64, _P, _P, _P, _I32, _P,
+                                                _P, _P, _I32, _I32, _I32, _P, _P, _P, _P,
+                                                _I64, _I64, _P, _P, _I32, _P, _P, _SZ, _P,
+                                                _SZ, _P, _P, _P]),
     "rkv_attn_workspace_size": (_SZ, [_PP, _I32, _I32]),
     "rkv_decode_attn": (ctypes.c_int, [_PP, _P, _P, _P, _I64, _P, _P, _I32, _P, _I32,
                                        _P, _P, _SZ, _P]),
@@ -336,6 +344,84 @@ def stage_resident(p: Params, host_k, host_v, host_table, block_table, lens,
         None if n_staged is None else _ptr(n_staged, torch.int32, "n_staged",
                                            (batch, hkv), d),
         _ptr(workspace, None, "workspace", None, d), ws_bytes, _stream(k_pages)))
+
+
+def stage_host_list_size(p: Params, batch: int, k_cap: int) -> int:
+    return lib().rkv_stage_host_list_size(ctypes.byref(p), batch, k_cap)
+
+
+def _host_i32(t, name, shape):
+    if not isinstance(t, torch.Tensor) or t.is_cuda or t.dtype != torch.int32 \
+            or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous int32 host tensor of shape {shape}")
+    return t.data_ptr()
+
+
+def _pinned_buf(t, name, nbytes):
+    if not isinstance(t, torch.Tensor) or t.is_cuda or not t.is_pinned() \
+            or not t.is_contiguous() or t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} must be a pinned host tensor of at least {nbytes} bytes")
+    return t.data_ptr(), t.numel() * t.element_size()
+
+
+def _event(ev):
+    return None if ev is None else ev.cuda_event
+
+
+def stage_blocks_async(p: Params, host_k, host_v, host_table_host, sel_ids, n_sel,
+                       k_pages, v_pages, stage_page0: int, host_list, side, done=None):
+    """rkv_stage_blocks_async: kept ids to the host, then copy-engine copies
+    of the kept host blocks on `side` (a torch stream); `done` an event."""
+    batch, mb = host_table_host.shape
+    d = k_pages.device
+    hkv = p.n_kv_heads
+    k_cap = sel_ids.shape[-1]
+    lp, lb = _pinned_buf(host_list, "host_list", stage_host_list_size(p, batch, k_cap))
+    _check(lib().rkv_stage_blocks_async(
+        ctypes.byref(p), _host_ptr(host_k, "host_k", _pool_shape(p, host_k)),
+        _host_ptr(host_v, "host_v", _pool_shape(p, host_k)), host_k.shape[0],
+        _host_i32(host_table_host, "host_table_host", (batch, mb)), mb,
+        _ptr(sel_ids, torch.int32, "sel_ids", (batch, hkv, k_cap), d),
+        _ptr(n_sel, torch.int32, "n_sel", (batch, hkv), d), k_cap, batch,
+        _ptr(k_pages, torch.int16, "k_pages", _pool_shape(p, k_pages), d),
+        _ptr(v_pages, torch.int16, "v_pages", _pool_shape(p, k_pages), d),
+        k_pages.shape[0], stage_page0, lp, lb, _stream(k_pages), side.cuda_stream,
+        _event(done)))
+
+
+def stage_resident_async(p: Params, host_k, host_v, host_table, host_table_host,
+                         block_table, lens, sel_ids, n_sel, slot_ids, slot_cursor,
+                         k_pages, v_pages, stage_page0: int, merged, n_merged, workspace,
+                         host_list, side, done=None, n_staged=None):
+    """rkv_stage_resident_async: the residency planner on the current stream,
+    its copy list to the host, copy-engine copies on `side`."""
+    batch, mb = block_table.shape
+    d = k_pages.device
+    hkv = p.n_kv_heads
+    k_cap = sel_ids.shape[-1]
+    ws_bytes = workspace.numel() * workspace.element_size()
+    lp, lb = _pinned_buf(host_list, "host_list", stage_host_list_size(p, batch, k_cap))
+    _check(lib().rkv_stage_resident_async(
+        ctypes.byref(p), _host_ptr(host_k, "host_k", _pool_shape(p, host_k)),
+        _host_ptr(host_v, "host_v", _pool_shape(p, host_k)), host_k.shape[0],
+        _ptr(host_table, torch.int32, "host_table", (batch, mb), d),
+        _host_i32(host_table_host, "host_table_host", (batch, mb)),
+        _ptr(block_table, torch.int32, "block_table", None, d), mb,
+        _ptr(lens, torch.int32, "lens", (batch,), d),
+        _ptr(sel_ids, torch.int32, "sel_ids", (batch, hkv, k_cap), d),
+        _ptr(n_sel, torch.int32, "n_sel", (batch, hkv), d), k_cap, batch,
+        slot_ids.shape[-1],
+        _ptr(slot_ids, torch.int32, "slot_ids", (batch, hkv, slot_ids.shape[-1]), d),
+        _ptr(slot_cursor, torch.int32, "slot_cursor", (batch, hkv), d),
+        _ptr(k_pages, torch.int16, "k_pages", _pool_shape(p, k_pages), d),
+        _ptr(v_pages, torch.int16, "v_pages", _pool_shape(p, k_pages), d),
+        k_pages.shape[0], stage_page0,
+        _ptr(merged, torch.int32, "merged", (batch, hkv, merged.shape[-1]), d),
+        _ptr(n_merged, torch.int32, "n_merged", (batch, hkv), d), merged.shape[-1],
+        None if n_staged is None else _ptr(n_staged, torch.int32, "n_staged",
+                                           (batch, hkv), d),
+        _ptr(workspace, None, "workspace", None, d), ws_bytes, lp, lb,
+        _stream(k_pages), side.cuda_stream, _event(done)))
 
 
 def attn_workspace_size(p: Params, batch: int, m_cap: int) -> int:

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "librkv.so")
 SOURCES = ["rkv_api.cpp", "reps.hip", "select.hip", "attn.hip", "stage.hip",
-           "static_scratch.hip"]
+           "static_scratch.hip", "stage_copy.cpp"]
 ARCH = "gfx950"
 
 

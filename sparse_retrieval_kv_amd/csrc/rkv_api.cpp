@@ -467,6 +467,181 @@ rkv_status rkv_stage_resident(const rkv_params* params, const uint16_t* host_k,
                     "rkv_stage_resident launch");
 }
 
+size_t rkv_stage_host_list_size(const rkv_params* params, int32_t batch,
+                                int32_t k_cap) {
+  if (!params || params->n_kv_heads <= 0 || batch <= 0 || k_cap <= 0) return 0;
+  const size_t lists = (size_t)batch * params->n_kv_heads;
+  return lists * k_cap * 2 * sizeof(int32_t) + lists * sizeof(int32_t);
+}
+
+namespace {
+
+// The host list of the copy-engine staging calls must be pinned host memory
+// (the device writes it with an asynchronous copy).
+rkv_status check_host_list(const void* host_list, size_t bytes, size_t need) {
+  RKV_REQUIRE(host_list != nullptr, RKV_ERR_INVALID_ARG, "host_list is NULL");
+  RKV_REQUIRE(bytes >= need, RKV_ERR_WORKSPACE, "host_list %zu bytes, need %zu",
+              bytes, need);
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, host_list) != hipSuccess ||
+      attr.type != hipMemoryTypeHost) {
+    (void)hipGetLastError();
+    return fail(RKV_ERR_INVALID_ARG, "host_list is not pinned host memory");
+  }
+  return RKV_OK;
+}
+
+rkv_status copy_issue(const rkv::StageCopyArgs& a, int64_t* tiles, hipEvent_t done,
+                      const char* what) {
+  hipError_t e = rkv::issue_stage_copies(a, tiles);
+  if (e == hipSuccess && done) e = hipEventRecord(done, a.side);
+  return hip_status(e, what);
+}
+
+}  // namespace
+
+rkv_status rkv_stage_blocks_async(const rkv_params* params, const uint16_t* host_k,
+                                  const uint16_t* host_v, int64_t n_host_pages,
+                                  const int32_t* host_table_host, int32_t max_blocks,
+                                  const int32_t* sel_ids, const int32_t* n_sel,
+                                  int32_t k_cap, int32_t batch, uint16_t* k_pages,
+                                  uint16_t* v_pages, int64_t n_pages,
+                                  int64_t stage_page0, void* host_list,
+                                  size_t host_list_bytes, hipStream_t stream,
+                                  hipStream_t side, hipEvent_t done) {
+  rkv::Method m;
+  RKV_TRY(check_params(params, &m));
+  RKV_TRY(check_sizes(batch, max_blocks));
+  RKV_TRY(check_pool(k_pages, n_pages, "k_pages"));
+  RKV_TRY(check_pool(v_pages, n_pages, "v_pages"));
+  RKV_TRY(check_pool(host_k, n_host_pages, "host_k"));
+  RKV_TRY(check_pool(host_v, n_host_pages, "host_v"));
+  RKV_REQUIRE(host_table_host && sel_ids && n_sel, RKV_ERR_INVALID_ARG,
+              "host_table_host, sel_ids and n_sel must not be NULL");
+  RKV_REQUIRE(k_cap >= 1, RKV_ERR_INVALID_ARG, "k_cap %d < 1", k_cap);
+  RKV_TRY(check_extent(params, batch, max3(max_blocks, k_cap, 1)));
+  RKV_REQUIRE(stage_page0 >= 0 &&
+                  stage_page0 + (int64_t)batch * k_cap <= n_pages &&
+                  stage_page0 + (int64_t)batch * k_cap <= (int64_t)INT32_MAX,
+              RKV_ERR_INVALID_ARG,
+              "staging pages [%lld, +%lld) do not fit in the %lld-page pool",
+              (long long)stage_page0, (long long)batch * k_cap,
+              (long long)n_pages);
+  const uint16_t* dev_view[2] = {nullptr, nullptr};
+  RKV_TRY(host_views(host_k, host_v, dev_view));
+  const size_t lists = (size_t)batch * m.n_kv_heads;
+  const size_t ids_bytes = lists * k_cap * sizeof(int32_t);
+  RKV_TRY(check_host_list(host_list, host_list_bytes, ids_bytes + lists * sizeof(int32_t)));
+  if (lists == 0) return RKV_OK;
+  int32_t* ids = static_cast<int32_t*>(host_list);
+  int32_t* counts = reinterpret_cast<int32_t*>(static_cast<char*>(host_list) + ids_bytes);
+  hipError_t e = hipMemcpyAsync(ids, sel_ids, ids_bytes, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(counts, n_sel, lists * sizeof(int32_t), hipMemcpyDeviceToHost,
+                       stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_status(e, "rkv_stage_blocks_async: kept ids to the host");
+  rkv::StageCopyArgs a;
+  a.host_k = host_k;
+  a.host_v = host_v;
+  a.n_host_pages = n_host_pages;
+  a.k_pages = k_pages;
+  a.v_pages = v_pages;
+  a.n_pages = n_pages;
+  a.host_table = host_table_host;
+  a.max_blocks = max_blocks;
+  a.batch = batch;
+  a.n_kv = m.n_kv_heads;
+  a.stage_page0 = stage_page0;
+  a.slots_per_seq = k_cap;
+  a.whole_pages = m.per_sequence;
+  a.ids = ids;
+  a.pairs = nullptr;
+  a.counts = counts;
+  a.row = k_cap;
+  a.side = side;
+  return copy_issue(a, nullptr, done, "rkv_stage_blocks_async copies");
+}
+
+rkv_status rkv_stage_resident_async(
+    const rkv_params* params, const uint16_t* host_k, const uint16_t* host_v,
+    int64_t n_host_pages, const int32_t* host_table, const int32_t* host_table_host,
+    const int32_t* block_table, int32_t max_blocks, const int32_t* lens,
+    const int32_t* sel_ids, const int32_t* n_sel, int32_t k_cap, int32_t batch,
+    int32_t slot_cap, int32_t* slot_ids, int32_t* slot_cursor, uint16_t* k_pages,
+    uint16_t* v_pages, int64_t n_pages, int64_t stage_page0, int32_t* merged,
+    int32_t* n_merged, int32_t m_cap, int32_t* n_staged, void* workspace,
+    size_t workspace_bytes, void* host_list, size_t host_list_bytes,
+    hipStream_t stream, hipStream_t side, hipEvent_t done) {
+  rkv::Method m;
+  RKV_TRY(check_params(params, &m));
+  RKV_TRY(check_sizes(batch, max_blocks));
+  RKV_TRY(check_pool(k_pages, n_pages, "k_pages"));
+  RKV_TRY(check_pool(v_pages, n_pages, "v_pages"));
+  RKV_TRY(check_pool(host_k, n_host_pages, "host_k"));
+  RKV_TRY(check_pool(host_v, n_host_pages, "host_v"));
+  RKV_REQUIRE(host_table && host_table_host && block_table && lens && sel_ids && n_sel &&
+                  slot_ids && slot_cursor && merged && n_merged,
+              RKV_ERR_INVALID_ARG, "a required pointer is NULL");
+  RKV_REQUIRE(k_cap >= 1 && k_cap <= RKV_MAX_BLOCKS, RKV_ERR_INVALID_ARG,
+              "k_cap %d outside [1, %d]", k_cap, RKV_MAX_BLOCKS);
+  RKV_REQUIRE(slot_cap >= 1 && slot_cap <= RKV_MAX_BLOCKS, RKV_ERR_INVALID_ARG,
+              "slot_cap %d outside [1, %d]", slot_cap, RKV_MAX_BLOCKS);
+  RKV_REQUIRE(m_cap >= max_blocks, RKV_ERR_INVALID_ARG,
+              "m_cap %d below max_blocks %d", m_cap, max_blocks);
+  RKV_TRY(check_extent(params, batch, max3(m_cap, k_cap, slot_cap)));
+  RKV_REQUIRE(stage_page0 >= 0 &&
+                  stage_page0 + (int64_t)batch * slot_cap <= n_pages &&
+                  stage_page0 + (int64_t)batch * slot_cap <= (int64_t)INT32_MAX,
+              RKV_ERR_INVALID_ARG,
+              "staging pages [%lld, +%lld) do not fit in the %lld-page pool",
+              (long long)stage_page0, (long long)batch * slot_cap,
+              (long long)n_pages);
+  const size_t need = rkv_stage_workspace_size(params, batch, k_cap);
+  RKV_REQUIRE(workspace_bytes >= need && (need == 0 || workspace),
+              RKV_ERR_WORKSPACE, "staging workspace %zu bytes, need %zu",
+              workspace_bytes, need);
+  RKV_REQUIRE(aligned16(workspace), RKV_ERR_INVALID_ARG,
+              "workspace is not 16-byte aligned");
+  const uint16_t* dev_view[2] = {nullptr, nullptr};
+  RKV_TRY(host_views(host_k, host_v, dev_view));
+  const size_t lists = (size_t)batch * m.n_kv_heads;
+  const size_t pair_bytes = lists * k_cap * 2 * sizeof(int32_t);
+  const size_t list_bytes = pair_bytes + lists * sizeof(int32_t);
+  RKV_TRY(check_host_list(host_list, host_list_bytes, list_bytes));
+  if (lists == 0) return RKV_OK;
+  // the planner on the device; its (block, slot) list and counts to the host
+  hipError_t e = rkv::launch_stage_plan(m, host_table, block_table, lens, max_blocks,
+                                        sel_ids, n_sel, k_cap, batch, slot_cap,
+                                        slot_ids, slot_cursor, stage_page0, merged,
+                                        n_merged, m_cap, n_staged, workspace, stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(host_list, workspace, list_bytes, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess)
+    return hip_status(e, "rkv_stage_resident_async: planner and its list to the host");
+  rkv::StageCopyArgs a;
+  a.host_k = host_k;
+  a.host_v = host_v;
+  a.n_host_pages = n_host_pages;
+  a.k_pages = k_pages;
+  a.v_pages = v_pages;
+  a.n_pages = n_pages;
+  a.host_table = host_table_host;
+  a.max_blocks = max_blocks;
+  a.batch = batch;
+  a.n_kv = m.n_kv_heads;
+  a.stage_page0 = stage_page0;
+  a.slots_per_seq = slot_cap;
+  a.whole_pages = m.per_sequence;
+  a.ids = nullptr;
+  a.pairs = static_cast<const int32_t*>(host_list);
+  a.counts = reinterpret_cast<const int32_t*>(static_cast<char*>(host_list) + pair_bytes);
+  a.row = k_cap;
+  a.side = side;
+  return copy_issue(a, nullptr, done, "rkv_stage_resident_async copies");
+}
+
 size_t rkv_attn_workspace_size(const rkv_params* params, int32_t batch,
                                int32_t m_cap) {
   if (!params || params->n_q_heads <= 0 || params->n_kv_heads <= 0 ||

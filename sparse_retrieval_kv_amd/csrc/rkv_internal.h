@@ -111,6 +111,53 @@ hipError_t launch_stage_resident(const Method& m, const uint16_t* host_k,
                                  int32_t* n_staged, void* workspace,
                                  hipStream_t stream);
 
+// The residency planner alone (the first launch of launch_stage_resident):
+// slot state, merged table and the (block, slot) copy list in the workspace
+// ([batch * n_kv][k_cap] int32 pairs, then [batch * n_kv] counts).
+hipError_t launch_stage_plan(const Method& m, const int32_t* host_table,
+                             const int32_t* table, const int32_t* lens,
+                             int max_blocks, const int32_t* sel_ids,
+                             const int32_t* n_sel, int k_cap, int batch,
+                             int slot_cap, int32_t* slot_ids, int32_t* slot_cursor,
+                             int64_t stage_page0, int32_t* merged,
+                             int32_t* n_merged, int m_cap, int32_t* n_staged,
+                             void* workspace, hipStream_t stream);
+
+// Copy-engine staging from a host copy of a list: kept ids (pairs null; the
+// r-th kept block goes to slot r) or (block, slot) pairs, rows of `row`
+// entries per (sequence, KV head), with counts.  Slot s of sequence b is page
+// stage_page0 + b * slots_per_seq + s.  Issues the copies on `side` and
+// returns the number of (page, head) tiles copied.
+struct StageCopyArgs {
+  const uint16_t* host_k;
+  const uint16_t* host_v;
+  int64_t n_host_pages;
+  uint16_t* k_pages;
+  uint16_t* v_pages;
+  int64_t n_pages;
+  const int32_t* host_table;  // HOST [batch][max_blocks]
+  int max_blocks, batch, n_kv;
+  int64_t stage_page0;
+  int slots_per_seq;
+  bool whole_pages;  // copy whole pages when all heads of a sequence agree
+  const int32_t* ids;     // [lists][row] kept ids, or null
+  const int32_t* pairs;   // [lists][row][2] (block, slot), or null
+  const int32_t* counts;  // [lists]
+  int row;
+  hipStream_t side;
+  int count(int bh) const {
+    const int n = counts[bh];
+    return n < 0 ? 0 : (n > row ? row : n);
+  }
+  int block(int bh, int i) const {
+    return pairs ? pairs[2 * ((int64_t)bh * row + i)] : ids[(int64_t)bh * row + i];
+  }
+  int slot(int bh, int i) const {
+    return pairs ? pairs[2 * ((int64_t)bh * row + i) + 1] : i;
+  }
+};
+hipError_t issue_stage_copies(const StageCopyArgs& a, int64_t* tiles_copied);
+
 // Split-K decode attention over a fixed number of waves: the 64-token units
 // of all merged lists are spread evenly over `n_waves` waves; the workspace
 // holds one partial per (wave, list) piece: n_waves + lists slots of

@@ -331,20 +331,15 @@ size_t resident_workspace_bytes(int batch, int n_kv, int k_cap) {
   return lists * k_cap * sizeof(int2) + (lists * sizeof(int32_t) + 255) / 256 * 256;
 }
 
-hipError_t launch_stage_resident(const Method& m, const uint16_t* host_k,
-                                 const uint16_t* host_v, int64_t n_host_pages,
-                                 const int32_t* host_table, const int32_t* table,
-                                 const int32_t* lens, int max_blocks,
-                                 const int32_t* sel_ids, const int32_t* n_sel,
-                                 int k_cap, int batch, int slot_cap,
-                                 int32_t* slot_ids, int32_t* slot_cursor,
-                                 uint16_t* k_pages, uint16_t* v_pages,
-                                 int64_t n_pages, int64_t stage_page0,
-                                 int32_t* merged, int32_t* n_merged, int m_cap,
-                                 int32_t* n_staged, void* workspace,
-                                 hipStream_t stream) {
+namespace {
+
+ResArgs resident_args(const Method& m, const int32_t* host_table, const int32_t* table,
+                      const int32_t* lens, int max_blocks, const int32_t* sel_ids,
+                      const int32_t* n_sel, int k_cap, int batch, int slot_cap,
+                      int32_t* slot_ids, int32_t* slot_cursor, int64_t stage_page0,
+                      int32_t* merged, int32_t* n_merged, int m_cap,
+                      int32_t* n_staged, void* workspace) {
   const int lists = batch * m.n_kv_heads;
-  if (lists == 0) return hipSuccess;
   ResArgs a;
   a.n_kv = m.n_kv_heads;
   a.init_tokens = m.init_tokens;
@@ -367,9 +362,52 @@ hipError_t launch_stage_resident(const Method& m, const uint16_t* host_k,
   a.merged = merged;
   a.n_merged = n_merged;
   a.m_cap = m_cap;
+  return a;
+}
+
+}  // namespace
+
+hipError_t launch_stage_plan(const Method& m, const int32_t* host_table,
+                             const int32_t* table, const int32_t* lens,
+                             int max_blocks, const int32_t* sel_ids,
+                             const int32_t* n_sel, int k_cap, int batch,
+                             int slot_cap, int32_t* slot_ids, int32_t* slot_cursor,
+                             int64_t stage_page0, int32_t* merged,
+                             int32_t* n_merged, int m_cap, int32_t* n_staged,
+                             void* workspace, hipStream_t stream) {
+  const int lists = batch * m.n_kv_heads;
+  if (lists == 0) return hipSuccess;
+  const ResArgs a = resident_args(m, host_table, table, lens, max_blocks, sel_ids, n_sel,
+                                  k_cap, batch, slot_cap, slot_ids, slot_cursor,
+                                  stage_page0, merged, n_merged, m_cap, n_staged,
+                                  workspace);
   hipLaunchKernelGGL(stage_plan_kernel, dim3(lists), dim3(kPlanThreads), 0, stream, a);
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_stage_resident(const Method& m, const uint16_t* host_k,
+                                 const uint16_t* host_v, int64_t n_host_pages,
+                                 const int32_t* host_table, const int32_t* table,
+                                 const int32_t* lens, int max_blocks,
+                                 const int32_t* sel_ids, const int32_t* n_sel,
+                                 int k_cap, int batch, int slot_cap,
+                                 int32_t* slot_ids, int32_t* slot_cursor,
+                                 uint16_t* k_pages, uint16_t* v_pages,
+                                 int64_t n_pages, int64_t stage_page0,
+                                 int32_t* merged, int32_t* n_merged, int m_cap,
+                                 int32_t* n_staged, void* workspace,
+                                 hipStream_t stream) {
+  const int lists = batch * m.n_kv_heads;
+  if (lists == 0) return hipSuccess;
+  hipError_t e = launch_stage_plan(m, host_table, table, lens, max_blocks, sel_ids,
+                                   n_sel, k_cap, batch, slot_cap, slot_ids, slot_cursor,
+                                   stage_page0, merged, n_merged, m_cap, n_staged,
+                                   workspace, stream);
   if (e != hipSuccess) return e;
+  const ResArgs a = resident_args(m, host_table, table, lens, max_blocks, sel_ids, n_sel,
+                                  k_cap, batch, slot_cap, slot_ids, slot_cursor,
+                                  stage_page0, merged, n_merged, m_cap, n_staged,
+                                  workspace);
   const int64_t items = (int64_t)lists * k_cap;
   hipLaunchKernelGGL(stage_copy_kernel, dim3((unsigned)items), dim3(kStageThreads), 0,
                      stream, reinterpret_cast<const uint4*>(host_k),

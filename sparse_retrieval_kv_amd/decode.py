@@ -108,12 +108,20 @@ class HostTierSession(DecodeSession):
     copied again (rkv_stage_resident); otherwise every kept block is copied
     each step (rkv_stage_blocks + rkv_merge_table).
 
+    With `copy_mode="memcpy"` the copies go through the copy engines
+    (rkv_stage_resident_async / rkv_stage_blocks_async: the kept ids or the
+    residency planner's copy list go to the host, which issues coalesced
+    hipMemcpy2DAsync / hipMemcpyAsync calls on the side stream and records an
+    event the main stream waits for); the default "kernel" mode copies with a
+    gather kernel that reads the pinned host pools directly.
+
     Representations are built while every block is still in HBM (after
     prefill); `attach_host` then hands over the host pools that hold the
     offload blocks from then on."""
 
     def __init__(self, prm: B.Params, k_pages, v_pages, block_table,
-                 prompt_lens=None, side_stream=True, resident=True, slot_cap=None):
+                 prompt_lens=None, side_stream=True, resident=True, slot_cap=None,
+                 copy_mode="kernel"):
         super().__init__(prm, k_pages, v_pages, block_table, prompt_lens)
         self.host_k = self.host_v = self.host_table = None
         # staging slots per (sequence, KV head): k_cap by default (always
@@ -143,9 +151,26 @@ class HostTierSession(DecodeSession):
         self.n_staged = torch.zeros((self.batch, n_kv), dtype=torch.int32, device=dev)
         ws = B.stage_workspace_size(prm, self.batch, self.k_cap)
         self.ws_stage = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
+        self.host_table_host = None
+        self.host_list = self.done = None
+        self.copy_mode = copy_mode
+        self._check_copy_mode()
+
+    def _check_copy_mode(self):
+        if self.copy_mode not in ("kernel", "memcpy"):
+            raise ValueError("copy_mode must be 'kernel' or 'memcpy'")
+        if self.copy_mode == "memcpy" and self.host_list is None:
+            if self.side is None:
+                raise ValueError("the memcpy staging mode needs the side stream")
+            n = B.stage_host_list_size(self.p, self.batch, self.k_cap)
+            self.host_list = torch.empty(max(n, 16), dtype=torch.uint8, pin_memory=True)
+            self.done = torch.cuda.Event()
+            self.done.record(self.side)  # creates the event the library records
 
     def attach_host(self, host_k, host_v, host_table):
         self.host_k, self.host_v, self.host_table = host_k, host_v, host_table
+        # the copy-engine mode issues its copies from a host copy of the table
+        self.host_table_host = host_table.to("cpu").contiguous()
         self.reset_residency()
 
     def offload_prefill(self, host_k, host_v, host_table, lens, concurrent=False):
@@ -182,6 +207,28 @@ class HostTierSession(DecodeSession):
                  self.n_sel, None, None, self.prompt_lens, self.ws_select)
 
     def stage(self, lens):
+        self._check_copy_mode()
+        if self.copy_mode == "memcpy":
+            # the planner (or the kept ids) on the current stream, the copies
+            # on the side stream; the current stream then waits for them
+            main = torch.cuda.current_stream(self.k_pages.device)
+            if self.resident:
+                B.stage_resident_async(self.p, self.host_k, self.host_v, self.host_table,
+                                       self.host_table_host, self.block_table, lens,
+                                       self.sel_ids, self.n_sel, self.slot_ids,
+                                       self.slot_cursor, self.k_pages, self.v_pages,
+                                       self.stage_page0, self.merged, self.n_merged,
+                                       self.ws_stage, self.host_list, self.side, self.done,
+                                       self.n_staged)
+            else:
+                B.stage_blocks_async(self.p, self.host_k, self.host_v, self.host_table_host,
+                                     self.sel_ids, self.n_sel, self.k_pages, self.v_pages,
+                                     self.stage_page0, self.host_list, self.side, self.done)
+                B.merge_table(self.p, self.block_table, lens, self.sel_ids, self.n_sel,
+                              self.merged, self.n_merged, self.host_table,
+                              self.stage_page0)
+            main.wait_event(self.done)
+            return
         if self.resident:
             B.stage_resident(self.p, self.host_k, self.host_v, self.host_table,
                              self.block_table, lens, self.sel_ids, self.n_sel,
@@ -202,7 +249,7 @@ class HostTierSession(DecodeSession):
 
     def step(self, q, k_new, v_new, lens):
         self.append_select(q, k_new, v_new, lens)
-        if self.side is None:
+        if self.side is None or self.copy_mode == "memcpy":
             self.stage(lens)
         else:
             main = torch.cuda.current_stream(self.k_pages.device)

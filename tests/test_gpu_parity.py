@@ -584,7 +584,8 @@ def test_valu_variant_matches_oracle_and_mfma(hq, hkv):
     assert np.allclose(outs[B.ATTN_MFMA], outs[B.ATTN_VALU], rtol=1e-4, atol=1e-5)
 
 
-def make_host_session(spec, resident=True, slot_mult=1, slot_cap=None, **pkw):
+def make_host_session(spec, resident=True, slot_mult=1, slot_cap=None,
+                      copy_mode="kernel", **pkw):
     """Host-tier session: prefill representations are built with every block
     in HBM, then the offload blocks move to pinned host memory."""
     max_blocks = -(-(max(spec.context) + spec.steps - 1) // 128)
@@ -596,7 +597,8 @@ def make_host_session(spec, resident=True, slot_mult=1, slot_cap=None, **pkw):
     k_cap = max(1, B.topk_capacity(prm, max_blocks))
     sess = HostTierSession(prm, batch.k_pages, batch.v_pages, batch.block_table,
                            i32(batch.context), resident=resident,
-                           slot_cap=slot_mult * k_cap if slot_cap is None else slot_cap)
+                           slot_cap=slot_mult * k_cap if slot_cap is None else slot_cap,
+                           copy_mode=copy_mode)
     assert sess.stage_page0 >= batch.n_pages  # staging pages are the extra ones
     prefill(batch, sess)
     torch.cuda.synchronize()
@@ -605,15 +607,16 @@ def make_host_session(spec, resident=True, slot_mult=1, slot_cap=None, **pkw):
     return batch, host, sess
 
 
+@pytest.mark.parametrize("copy_mode", ["kernel", "memcpy"])
 @pytest.mark.parametrize("resident", [True, False])
-def test_host_tier_small(resident):
+def test_host_tier_small(resident, copy_mode):
     # host blocks [8, 90) of the offload range [8, 100): blocks 90..99 stay in
     # HBM and are read in place when kept
     spec = synth.scaled(synth.CONFIGS[5], batch=2, context=(20000, 20000), steps=3,
                         plant_range=(8, 90), plant_count=5, local_tokens=7192,
                         dense_boundary=0, config_id=102)
-    say(f"host tier small (resident={resident})")
-    batch, host, sess = make_host_session(spec, resident=resident)
+    say(f"host tier small (resident={resident}, copies by {copy_mode})")
+    batch, host, sess = make_host_session(spec, resident=resident, copy_mode=copy_mode)
     for t in range(3):
         step(batch, sess, t)
         torch.cuda.synchronize()
@@ -694,6 +697,33 @@ def test_host_tier_residency_matches_full_staging(slot_mult):
                     kept_total += sum(1 for j in kept if on_host[j])
                     copied_total += len(new)
     assert copied_total < kept_total
+
+
+@pytest.mark.parametrize("select_mode", [B.SELECT_PER_HEAD, B.SELECT_PER_SEQUENCE])
+def test_host_tier_copy_engine_equals_gather_kernel(select_mode):
+    """The copy engines and the gather kernel stage the same bytes to the
+    same slots: pools, slot state, merged tables and outputs bit-identical
+    over steps with residency (2x slots)."""
+    spec = synth.scaled(synth.CONFIGS[5], batch=2, context=(20000, 23000), steps=4,
+                        plant_range=(8, 90), plant_count=5, local_tokens=7192,
+                        dense_boundary=0, config_id=110)
+    say(f"host tier: copy engines vs gather kernel, select mode {select_mode}")
+    runs = {}
+    for mode in ("kernel", "memcpy"):
+        batch, host, sess = make_host_session(spec, resident=True, slot_mult=2,
+                                              copy_mode=mode, select_mode=select_mode)
+        rec = []
+        for t in range(4):
+            step(batch, sess, t)
+            torch.cuda.synchronize()
+            rec.append((sess.out.clone(), sess.merged.clone(), sess.n_merged.clone(),
+                        sess.slot_ids.clone(), sess.n_staged.clone()))
+        rec.append((batch.k_pages.clone(), batch.v_pages.clone()))
+        runs[mode] = rec
+        del batch, host, sess
+    for a, b in zip(runs["kernel"], runs["memcpy"]):
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
 
 
 def test_host_tier_too_few_slots_is_reported():
@@ -888,12 +918,15 @@ def test_decode_step_replays_from_a_hip_graph():
         assert torch.equal(sess.sel_ids, eager[3]), r
 
 
-def test_per_sequence_selection_with_resident_host_tier():
+@pytest.mark.parametrize("copy_mode", ["kernel", "memcpy"])
+def test_per_sequence_selection_with_resident_host_tier(copy_mode):
+    """Per-sequence selection: every KV head keeps the same blocks, so the
+    copy-engine mode copies whole pages."""
     spec = synth.scaled(synth.CONFIGS[5], batch=2, context=(20000, 23000), steps=3,
                         plant_range=(8, 90), plant_count=5, local_tokens=7192,
                         dense_boundary=0, config_id=108)
-    say("per-sequence selection + resident host tier")
-    batch, host, sess = make_host_session(spec, resident=True,
+    say(f"per-sequence selection + resident host tier, copies by {copy_mode}")
+    batch, host, sess = make_host_session(spec, resident=True, copy_mode=copy_mode,
                                           select_mode=B.SELECT_PER_SEQUENCE)
     for t in range(3):
         step(batch, sess, t)
