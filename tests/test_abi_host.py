@@ -227,6 +227,41 @@ def test_stage_resident_validation(L):
     assert b"pinned" in L.rkv_last_error()
 
 
+def test_copy_engine_staging_validation(L):
+    """The copy-engine staging calls check their host-side arguments before
+    anything is enqueued (fake pools are not pinned host memory)."""
+    p = L.rkv_params_default(32, 8)
+    n = L.rkv_stage_host_list_size(ctypes.byref(p), 4, 100)
+    assert n == 4 * 8 * 100 * 8 + 4 * 8 * 4
+    assert L.rkv_stage_host_list_size(None, 4, 100) == 0
+
+    def blocks(host_table_host=FAKE, stage_page0=0, k_cap=100):
+        return L.rkv_stage_blocks_async(ctypes.byref(p), FAKE, FAKE, 50, host_table_host,
+                                        200, FAKE, FAKE, k_cap, 4, FAKE, FAKE, 1000,
+                                        stage_page0, FAKE, n, None, None, None)
+
+    assert blocks(host_table_host=None) == B.RKV_ERR_INVALID_ARG
+    assert blocks(stage_page0=601) == B.RKV_ERR_INVALID_ARG
+    assert b"staging" in L.rkv_last_error()
+    assert blocks(k_cap=0) == B.RKV_ERR_INVALID_ARG
+    assert blocks() == B.RKV_ERR_INVALID_ARG
+    assert b"pinned" in L.rkv_last_error()
+
+    need = L.rkv_stage_workspace_size(ctypes.byref(p), 4, 100)
+
+    def resident(host_table_host=FAKE, ws_bytes=need, slot_cap=100):
+        return L.rkv_stage_resident_async(
+            ctypes.byref(p), FAKE, FAKE, 50, FAKE, host_table_host, FAKE, 200, FAKE, FAKE,
+            FAKE, 100, 4, slot_cap, FAKE, FAKE, FAKE, FAKE, 1000, 0, FAKE, FAKE, 200, None,
+            FAKE, ws_bytes, FAKE, n, None, None, None)
+
+    assert resident(host_table_host=None) == B.RKV_ERR_INVALID_ARG
+    assert resident(ws_bytes=need - 1) == B.RKV_ERR_WORKSPACE
+    assert resident(slot_cap=0) == B.RKV_ERR_INVALID_ARG
+    assert resident() == B.RKV_ERR_INVALID_ARG
+    assert b"pinned" in L.rkv_last_error()
+
+
 def test_reps_and_append_validation(L):
     p = L.rkv_params_default(8, 2)
     assert L.rkv_build_reps(ctypes.byref(p), None, 10, FAKE, 8, FAKE, None, 1,
