@@ -28,6 +28,8 @@
 #include "rkv_device.h"
 #include "rkv_internal.h"
 
+#include <type_traits>
+
 namespace rkv {
 namespace {
 
@@ -111,6 +113,7 @@ struct SelArgs {
   int max_blocks;
   int ib;        // first offload block: min(ceil(init / 128), max_blocks)
   int n_chunks;  // score chunks per (sequence, KV head)
+  int spec_end;  // chunks ending at or below this block load before the length
   int n_bh;      // batch * n_kv_heads
   uint32_t* keys;  // workspace [batch][n_kv_heads][max_blocks]
   int32_t* sel_ids;
@@ -176,64 +179,80 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(SelArgs a,
   const int c = (int)(item - (int64_t)bh * a.n_chunks);
   const int b = bh / m.n_kv_heads, h = bh - b * m.n_kv_heads;
 
-  // --- requests independent of the length: representations, the group's
-  // query rows (lane tid holds dims 2 tid and 2 tid + 1 of each) and the
-  // lengths, all issued before any of them is waited for ---
+  // --- requests independent of the length: the group's query rows (lane
+  // tid holds dims 2 tid and 2 tid + 1 of each) and the lengths; and, for a
+  // chunk inside every possible offload range (below spec_end), its
+  // representations, all issued before any of them is waited for.  A chunk
+  // past spec_end waits for the length and loads only if it is in range: in
+  // a batch of ragged lengths most of those chunks lie past their
+  // sequence's offload end. ---
   const int o = tid & 7, slot = tid >> 3;  // lane octet o of slot 0..7
   const int j0 = a.ib + c * kScoreChunk;
+  const bool spec = j0 + kScoreChunk <= a.spec_end;  // uniform
   float4 v[kScoreRounds][4];
+  auto load_reps = [&]() {
 #pragma unroll
-  for (int u = 0; u < kScoreRounds; ++u) {
-    int j = j0 + u * 8 + slot;
-    j = j < max_blocks ? j : max_blocks - 1;
-    const float4* p = reinterpret_cast<const float4*>(
-        a.reps + ((int64_t)bh * max_blocks + j) * kDim);
+    for (int u = 0; u < kScoreRounds; ++u) {
+      int j = j0 + u * 8 + slot;
+      j = j < max_blocks ? j : max_blocks - 1;
+      const float4* p = reinterpret_cast<const float4*>(
+          a.reps + ((int64_t)bh * max_blocks + j) * kDim);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[u][i] = p[o + 8 * i];
-  }
-  const uint32_t* qh = reinterpret_cast<const uint32_t*>(
-      a.q + ((int64_t)b * m.n_q_heads + h * m.group) * kDim);
-  uint32_t qw[RKV_MAX_GROUP];
-#pragma unroll
-  for (int g = 0; g < RKV_MAX_GROUP; ++g)
-    qw[g] = g < m.group ? qh[g * (kDim / 2) + tid] : 0u;
-  const int lraw = a.lens[b];
-  // the pointer is chosen, not the value, so that this load goes out with
-  // the others instead of after the length arrives
-  const int plen = (a.prompt_lens ? a.prompt_lens : a.lens)[b];
-  // the group's query heads summed in head order
-  float qsum0 = 0.f, qsum1 = 0.f;  // dims 2 tid and 2 tid + 1
-#pragma unroll
-  for (int g = 0; g < RKV_MAX_GROUP; ++g) {
-    if (g < m.group) {
-      qsum0 += bf16lo(qw[g]);
-      qsum1 += bf16hi(qw[g]);
+      for (int i = 0; i < 4; ++i) v[u][i] = p[o + 8 * i];
     }
-  }
-
-  // --- this chunk's share of the offload range ---
-  const Pick pk = pick_of(m, lraw, plen, max_blocks);
-  const int ls = pk.R.n_init + pk.R.n_off;  // offload end
-  if (!pk.ranked || j0 >= ls) return;  // uniform over the wave
-  *reinterpret_cast<float2*>(&qs[2 * tid]) = make_float2(qsum0, qsum1);
-  __syncthreads();
-  float4 qv[4];
+  };
+  // the rest of the item once the representations are requested: the
+  // group's query heads summed in head order, this chunk's share of the
+  // offload range, the scores
+  auto finish = [&](auto early) {
+    const uint32_t* qh = reinterpret_cast<const uint32_t*>(
+        a.q + ((int64_t)b * m.n_q_heads + h * m.group) * kDim);
+    uint32_t qw[RKV_MAX_GROUP];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    qv[i] = *reinterpret_cast<const float4*>(&qs[4 * (o + 8 * i)]);
-  uint32_t* krow = a.keys + (int64_t)bh * max_blocks;
+    for (int g = 0; g < RKV_MAX_GROUP; ++g)
+      qw[g] = g < m.group ? qh[g * (kDim / 2) + tid] : 0u;
+    const int lraw = a.lens[b];
+    // the pointer is chosen, not the value, so that this load goes out with
+    // the others instead of after the length arrives
+    const int plen = (a.prompt_lens ? a.prompt_lens : a.lens)[b];
+    float qsum0 = 0.f, qsum1 = 0.f;  // dims 2 tid and 2 tid + 1
 #pragma unroll
-  for (int u = 0; u < kScoreRounds; ++u) {
-    const int j = j0 + u * 8 + slot;
-    float part = 0.f;
+    for (int g = 0; g < RKV_MAX_GROUP; ++g) {
+      if (g < m.group) {
+        qsum0 += bf16lo(qw[g]);
+        qsum1 += bf16hi(qw[g]);
+      }
+    }
+    const Pick pk = pick_of(m, lraw, plen, max_blocks);
+    const int ls = pk.R.n_init + pk.R.n_off;  // offload end
+    if (!pk.ranked || j0 >= ls) return;  // uniform over the wave
+    if (!decltype(early)::value) load_reps();
+    *reinterpret_cast<float2*>(&qs[2 * tid]) = make_float2(qsum0, qsum1);
+    __syncthreads();
+    float4 qv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      part += v[u][i].x * qv[i].x + v[u][i].y * qv[i].y +
-              v[u][i].z * qv[i].z + v[u][i].w * qv[i].w;
-    part += __shfl_xor(part, 1);
-    part += __shfl_xor(part, 2);
-    part += __shfl_xor(part, 4);
-    if (o == 0 && j < ls) krow[j] = __float_as_uint(part);
+      qv[i] = *reinterpret_cast<const float4*>(&qs[4 * (o + 8 * i)]);
+    uint32_t* krow = a.keys + (int64_t)bh * max_blocks;
+#pragma unroll
+    for (int u = 0; u < kScoreRounds; ++u) {
+      const int j = j0 + u * 8 + slot;
+      float part = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        part += v[u][i].x * qv[i].x + v[u][i].y * qv[i].y +
+                v[u][i].z * qv[i].z + v[u][i].w * qv[i].w;
+      part += __shfl_xor(part, 1);
+      part += __shfl_xor(part, 2);
+      part += __shfl_xor(part, 4);
+      if (o == 0 && j < ls) krow[j] = __float_as_uint(part);
+    }
+  };
+  if (spec) {
+    load_reps();
+    finish(std::true_type());
+  } else {
+    finish(std::false_type());
   }
 }
 
@@ -528,7 +547,19 @@ hipError_t launch_score(const Method& m, const uint16_t* q, const float* reps,
     rounds >>= 1;
   const int chunk = 8 * rounds;
   const int n_chunks = (max_blocks - ib + chunk - 1) / chunk;
-  SelArgs a{m, q, reps, table, lens, prompt_lens, max_blocks, ib, n_chunks,
+  // A batch of one requests every chunk's representations with the length
+  // (only the window's chunks are read in vain).  In a batch, only chunks
+  // inside every ranked list's offload range: a list needs scores only when
+  // its prompt is not below the dense boundary, so L >= dense_boundary and
+  // its offload range reaches at least block (dense_boundary - local) / 128.
+  int spec_end = max_blocks;
+  if (batch > 1) {
+    const int64_t lo = m.dense_boundary > m.local_tokens
+                           ? ((int64_t)m.dense_boundary - m.local_tokens) / kBlock
+                           : 0;
+    spec_end = (int)(lo < ib ? ib : (lo > max_blocks ? max_blocks : lo));
+  }
+  SelArgs a{m, q, reps, table, lens, prompt_lens, max_blocks, ib, n_chunks, spec_end,
             groups, scores, nullptr, nullptr, 0, nullptr, nullptr, 0};
   const int64_t score_wgs = (int64_t)groups * n_chunks;
   AppendArgs ap{};
@@ -564,7 +595,7 @@ hipError_t launch_topk(const Method& m, const int32_t* table, const int32_t* len
   const int groups = batch * m.n_kv_heads;
   if (groups == 0) return hipSuccess;
   // the top-k only reads the scores
-  SelArgs a{m, nullptr, nullptr, table, lens, prompt_lens, max_blocks, 0, 0,
+  SelArgs a{m, nullptr, nullptr, table, lens, prompt_lens, max_blocks, 0, 0, 0,
             groups, const_cast<uint32_t*>(scores), sel_ids, n_sel, k_cap,
             merged, n_merged, m_cap};
   hipLaunchKernelGGL(topk_kernel, dim3(groups), dim3(kTopkThreads), 0, stream, a);
