@@ -28,7 +28,8 @@
  *    by the kernels so that bad values never cause an out-of-bounds access:
  *    a length above max_blocks * 128 is treated as max_blocks * 128, a
  *    negative length as 0, and a page id outside [0, n_pages) makes its block
- *    contribute nothing.
+ *    contribute nothing.  The debug build of the library (built with
+ *    RKV_DEBUG) also reports the first such value: see rkv_debug_check.
  *
  * Memory layouts (part of the ABI):
  *  - k_pages: [n_pages][n_kv_heads][128 tokens][128 dims] bf16.  Each
@@ -76,7 +77,9 @@ typedef enum rkv_status {
   RKV_ERR_INVALID_ARG = 1,  /* null pointer, negative size, bad value */
   RKV_ERR_UNSUPPORTED = 2,  /* block/head size != 128, group > 16, ... */
   RKV_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
-  RKV_ERR_HIP = 4           /* a HIP launch or copy failed; see rkv_last_error */
+  RKV_ERR_HIP = 4,          /* a HIP launch or copy failed; see rkv_last_error */
+  RKV_ERR_BOUNDS = 5        /* debug builds: a kernel met an out-of-range device
+                               value (see rkv_debug_check) */
 } rkv_status;
 
 /* Selection modes (rkv_params.select_mode, see rkv_select). */
@@ -584,6 +587,26 @@ rkv_status rkv_decode_step_static(const rkv_params* params, const uint16_t* k_ne
                                   int32_t* n_sel, int32_t k_cap, int32_t* merged,
                                   int32_t* n_merged, int32_t m_cap, float* out,
                                   hipStream_t stream);
+
+/*
+ * Bounds reports (memory isolation of the pages one sequence may touch:
+ * rkmt.cn ATB article, section 3.3).  In a library built with RKV_DEBUG,
+ * every kernel that clamps or skips an out-of-range device value -- a
+ * length outside [0, max_blocks * 128], a page id outside the device pool
+ * (other than the merge's own -1 for a block it leaves out), a kept block id
+ * outside its list's offload range or [0, max_blocks), a count above its
+ * list's capacity, a host page id outside the host pool -- records the first
+ * one into *word (device uint64_t, zero-filled by the caller) and goes on as
+ * the release build does, so every kernel still exits normally.
+ *   rkv_debug_set_report(word): route the reports of kernels launched from
+ *     now on, on the current device, to word (NULL: stop reporting).  A
+ *     release build returns RKV_ERR_UNSUPPORTED.
+ *   rkv_debug_check(word, stream): waits for `stream`, reads and clears
+ *     *word; RKV_OK if nothing was reported, else RKV_ERR_BOUNDS with the
+ *     kind and value in rkv_last_error.
+ */
+rkv_status rkv_debug_set_report(uint64_t* word);
+rkv_status rkv_debug_check(uint64_t* word, hipStream_t stream);
 
 /*
  * rkv_read_probe -- measurement helper, not part of the method: reads

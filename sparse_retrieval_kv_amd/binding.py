@@ -15,10 +15,14 @@ import re
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.environ.get("RKV_LIB") or os.path.join(HERE, "librkv.so")
+DEFAULT_LIB_PATH = os.path.join(HERE, "librkv.so")
+# the same library built with RKV_DEBUG: kernels report out-of-range values
+DEBUG_LIB_PATH = os.path.join(HERE, "librkv_debug.so")
+LIB_PATH = os.environ.get("RKV_LIB") or DEFAULT_LIB_PATH
 HEADER = os.path.join(os.path.dirname(HERE), "include", "rkv.h")
 
-RKV_OK, RKV_ERR_INVALID_ARG, RKV_ERR_UNSUPPORTED, RKV_ERR_WORKSPACE, RKV_ERR_HIP = range(5)
+(RKV_OK, RKV_ERR_INVALID_ARG, RKV_ERR_UNSUPPORTED, RKV_ERR_WORKSPACE, RKV_ERR_HIP,
+ RKV_ERR_BOUNDS) = range(6)
 ATTN_AUTO, ATTN_MFMA, ATTN_VALU = 0, 1, 2
 BLOCK = 128
 HEAD_DIM = 128
@@ -100,10 +104,23 @@ _SIGS = {
                                               _P, _P, _I32, _I32, _P, _P, _I32, _P,
                                               _P, _I32, _P, _P]),
     "rkv_read_probe": (ctypes.c_int, [_P, _SZ, _P, _P]),
+    "rkv_debug_set_report": (ctypes.c_int, [_P]),
+    "rkv_debug_check": (ctypes.c_int, [_P, _P]),
 }
 RKV_STATIC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
+
+
+def use_library(path: str) -> None:
+    """Load the library at `path` for the calls made from now on (the
+    RKV_DEBUG build, DEBUG_LIB_PATH, or back to DEFAULT_LIB_PATH).  Prepared
+    calls keep the library they were prepared with."""
+    global _lib, LIB_PATH
+    if path != LIB_PATH:
+        LIB_PATH = path
+        _lib = None
+    lib()
 
 
 def lib() -> ctypes.CDLL:
@@ -580,6 +597,20 @@ def decode_step_static(p: Params, q, k_new, v_new, k_pages, v_pages, reps,
         _ptr(n_merged, torch.int32, "n_merged", (batch, hkv), d), merged.shape[-1],
         _ptr(out, torch.float32, "out", (batch, p.n_q_heads, HEAD_DIM), d),
         _stream(q)))
+
+
+def debug_set_report(word):
+    """RKV_DEBUG builds: kernels launched from now on record the first
+    out-of-range device value into `word` (an int64 device tensor of one
+    element, zero-filled); None stops it."""
+    _check(lib().rkv_debug_set_report(
+        None if word is None else _ptr(word, torch.int64, "word", (1,))))
+
+
+def debug_check(word):
+    """Waits for the current stream, reads and clears `word`; raises
+    RkvError(RKV_ERR_BOUNDS) when a kernel reported a value."""
+    _check(lib().rkv_debug_check(_ptr(word, torch.int64, "word", (1,)), _stream(word)))
 
 
 def read_probe(buf, sink):

@@ -16,6 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "librkv.so")
+# the same sources built with RKV_DEBUG: kernels report out-of-range values
+DEBUG_LIB = os.path.join(HERE, "librkv_debug.so")
 SOURCES = ["rkv_api.cpp", "reps.hip", "select.hip", "attn.hip", "stage.hip",
            "static_scratch.hip", "stage_copy.cpp"]
 ARCH = "gfx950"
@@ -29,17 +31,20 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build librkv.so)")
 
 
-def compile_flags() -> list:
+def compile_flags(debug: bool = False) -> list:
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+            *(["-DRKV_DEBUG=1"] if debug else []),
             # packed fp32 VALU forms are kept out of the generated code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-Wno-unused-command-line-argument",
             "-I", INCLUDE, "-I", CSRC]
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
-    """Compile every source to an object, link librkv.so, return its path."""
+def build(verbose: bool = False, jobs: int = 4, debug: bool = False) -> str:
+    """Compile every source to an object, link librkv.so (librkv_debug.so
+    with `debug`: RKV_DEBUG bounds reports), return its path."""
     cc = hipcc()
+    out_lib = DEBUG_LIB if debug else LIB
     with tempfile.TemporaryDirectory(prefix="rkv_build_") as tmp:
         procs = []
         objs = []
@@ -47,7 +52,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
             obj = os.path.join(tmp, src + ".o")
             objs.append(obj)
             lang = ["-x", "hip"] if src.endswith(".hip") else []
-            cmd = [cc] + compile_flags() + lang + ["-c", os.path.join(CSRC, src),
+            cmd = [cc] + compile_flags(debug) + lang + ["-c", os.path.join(CSRC, src),
                                                    "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
@@ -66,10 +71,57 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
                            text=True)
         if r.returncode != 0:
             raise RuntimeError("linking librkv.so failed:\n" + r.stdout)
-        staged = LIB + ".tmp"
+        staged = out_lib + ".tmp"
         shutil.copyfile(tmp_lib, staged)
-        os.replace(staged, LIB)
-    return LIB
+        os.replace(staged, out_lib)
+    return out_lib
+
+
+# The host C++ layer (argument checks, workspace sizing, the copy-engine
+# staging) built with AddressSanitizer for the CPU ABI tests: the .cpp
+# sources by g++ with the sanitizer, the kernel files by hipcc as usual.
+ASAN_LIB = os.path.join(HERE, "librkv_asan.so")
+HOST_SOURCES = [s for s in SOURCES if s.endswith(".cpp")]
+
+
+def asan_runtime() -> str:
+    """The g++ AddressSanitizer runtime a process must preload to load
+    librkv_asan.so."""
+    return subprocess.run(["g++", "-print-file-name=libasan.so"], check=True,
+                          stdout=subprocess.PIPE, text=True).stdout.strip()
+
+
+def build_asan(verbose: bool = False) -> str:
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    with tempfile.TemporaryDirectory(prefix="rkv_asan_") as tmp:
+        objs, procs = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src + ".o")
+            objs.append(obj)
+            if src in HOST_SOURCES:
+                cmd = ["g++", "-fsanitize=address", "-fno-omit-frame-pointer", "-g",
+                       "-O1", "-std=c++17", "-fPIC", "-D__HIP_PLATFORM_AMD__",
+                       "-I", os.path.join(rocm, "include"), "-I", INCLUDE, "-I", CSRC,
+                       "-c", os.path.join(CSRC, src), "-o", obj]
+            else:
+                cmd = [hipcc()] + compile_flags() + ["-x", "hip", "-c",
+                                                     os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                stderr=subprocess.STDOUT, text=True)))
+        for item in procs:
+            _wait(item)
+        tmp_lib = os.path.join(tmp, "librkv_asan.so")
+        cmd = (["g++", "-shared", "-fsanitize=address", "-o", tmp_lib] + objs +
+               ["-L", os.path.join(rocm, "lib"), "-lamdhip64",
+                "-Wl,-rpath," + os.path.join(rocm, "lib")])
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("linking librkv_asan.so failed:\n" + r.stdout)
+        shutil.copyfile(tmp_lib, ASAN_LIB + ".tmp")
+        os.replace(ASAN_LIB + ".tmp", ASAN_LIB)
+    return ASAN_LIB
 
 
 def _wait(item):

@@ -133,8 +133,15 @@ struct AttnArgs {
 
 __device__ __forceinline__ int units_of(const AttnArgs& a, int bh) {
   int n = a.n_merged[bh];
+  if (n < 0 || n > a.m_cap) report_bounds(kBoundsCount, n);
   n = n < 0 ? 0 : (n > a.m_cap ? a.m_cap : n);
   return 2 * n;
+}
+
+// A merged entry's page id outside the pool contributes nothing; -1 is the
+// merge's own mark for a block it left out and is not reported.
+__device__ __forceinline__ void report_page(int page) {
+  if (page != -1) report_bounds(kBoundsPage, page);
 }
 
 // units_of for a lane's list bh, 0 past the last list.  The load is made
@@ -525,6 +532,7 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, Math& math, int bh,
     uint4 vf[2][8];
     load_v_unit(vf, a.v_pages + tile, u & 1, col, grp);
     const bool cur_ok = page_ok(page);
+    if (!cur_ok) report_page(page);
     const int valid = valid_of(u);
     if (u + 1 < u1) {  // prefetch the next unit's K tile
       if (u & 1) {     // the next unit starts the next entry
@@ -645,6 +653,7 @@ __device__ __forceinline__ void strided_loop(const AttnArgs& a, Math& math, int 
     __builtin_amdgcn_sched_barrier(0);
     if (decltype(load_v)::value) load_v_unit(vf, a.v_pages + tile, u & 1, col, grp);
     const bool cur_ok = page_ok(page);
+    if (!cur_ok) report_page(page);
     const int valid = valid_of(u);
     if (i > 0) {  // prefetch the next unit's K tile
       page = page_next;
@@ -1228,5 +1237,7 @@ hipError_t launch_select_attn(const Method& m, bool use_mfma, const AttnPlan& pl
   if (e != hipSuccess) return e;
   return launch_combine(m, a, 1, out, stream);
 }
+
+RKV_BOUNDS_SETTER(set_bounds_word_attn)
 
 }  // namespace rkv

@@ -66,7 +66,10 @@ __global__ __launch_bounds__(256) void build_reps_kernel(
   int j0 = block_begin ? block_begin[b] : 0;
   j0 = j0 < 0 ? 0 : j0;
   if (j < j0 || j >= (L >> 7)) return;
-  if ((uint64_t)(int64_t)page >= (uint64_t)n_pages) return;
+  if ((uint64_t)(int64_t)page >= (uint64_t)n_pages) {
+    report_bounds(kBoundsPage, page);
+    return;
+  }
   const uint16_t* K = k_pages + ((int64_t)page * n_kv + h) * (kBlock * kDim);
   const int c = lane & 15, g = lane >> 4;
   // all 32 loads of the tile in flight at once, then summed in row order
@@ -96,7 +99,10 @@ __global__ __launch_bounds__(64) void append_kv_kernel(
   if (L <= 0) return;
   const int pos = L - 1, j = pos >> 7, slot = pos & 127;
   const int page = table[(int64_t)b * max_blocks + j];
-  if ((uint64_t)(int64_t)page >= (uint64_t)n_pages) return;
+  if ((uint64_t)(int64_t)page >= (uint64_t)n_pages) {
+    report_bounds(kBoundsPage, page);
+    return;
+  }
   const int64_t base = ((int64_t)page * n_kv + h) * (kBlock * kDim);
   const uint16_t* kn = k_new + (int64_t)bh * kDim;
   const uint16_t* vn = v_new + (int64_t)bh * kDim;
@@ -186,5 +192,7 @@ hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
                      static_cast<const uint4*>(buf), n16, sink);
   return hipGetLastError();
 }
+
+RKV_BOUNDS_SETTER(set_bounds_word_reps)
 
 }  // namespace rkv

@@ -165,6 +165,7 @@ const char* rkv_status_string(rkv_status s) {
     case RKV_ERR_UNSUPPORTED: return "unsupported";
     case RKV_ERR_WORKSPACE: return "workspace too small";
     case RKV_ERR_HIP: return "HIP error";
+    case RKV_ERR_BOUNDS: return "out-of-range device value";
   }
   return "unknown status";
 }
@@ -817,6 +818,39 @@ rkv_status rkv_decode_step(const rkv_params* params, const uint16_t* k_new,
                                max_blocks, sel_ids, n_sel, k_cap, merged, n_merged,
                                m_cap, out, select_workspace, select_workspace_bytes,
                                attn_workspace, attn_workspace_bytes, stream);
+}
+
+rkv_status rkv_debug_set_report(uint64_t* word) {
+  RKV_REQUIRE(word == nullptr || (reinterpret_cast<uintptr_t>(word) & 7u) == 0,
+              RKV_ERR_INVALID_ARG, "word must be 8-byte aligned");
+  unsigned long long* w = reinterpret_cast<unsigned long long*>(word);
+  hipError_t e = rkv::set_bounds_word_attn(w);
+  if (e == hipErrorNotSupported) {
+    (void)hipGetLastError();
+    return fail(RKV_ERR_UNSUPPORTED, "this library was built without RKV_DEBUG");
+  }
+  if (e == hipSuccess) e = rkv::set_bounds_word_reps(w);
+  if (e == hipSuccess) e = rkv::set_bounds_word_select(w);
+  if (e == hipSuccess) e = rkv::set_bounds_word_stage(w);
+  return hip_status(e, "rkv_debug_set_report");
+}
+
+rkv_status rkv_debug_check(uint64_t* word, hipStream_t stream) {
+  RKV_REQUIRE(word != nullptr && (reinterpret_cast<uintptr_t>(word) & 7u) == 0,
+              RKV_ERR_INVALID_ARG, "word must be a non-NULL, 8-byte aligned pointer");
+  hipError_t e = hipStreamSynchronize(stream);
+  uint64_t v = 0;
+  if (e == hipSuccess) e = hipMemcpy(&v, word, sizeof(v), hipMemcpyDeviceToHost);
+  const uint64_t zero = 0;
+  if (e == hipSuccess && v != 0)
+    e = hipMemcpy(word, &zero, sizeof(zero), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_status(e, "rkv_debug_check");
+  if (v == 0) return RKV_OK;
+  static const char* const kinds[] = {"?", "length", "page id", "block id", "count",
+                                      "host page id"};
+  const unsigned kind = (unsigned)(v >> 56);
+  return fail(RKV_ERR_BOUNDS, "out-of-range %s %d met by a kernel (clamped or skipped)",
+              kinds[kind < 6 ? kind : 0], (int)(int32_t)(uint32_t)v);
 }
 
 rkv_status rkv_read_probe(const void* buffer, size_t bytes, uint32_t* sink,

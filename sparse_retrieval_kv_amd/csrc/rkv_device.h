@@ -14,8 +14,38 @@ __device__ __forceinline__ float bf16hi(uint32_t w) {
   return __uint_as_float(w & 0xffff0000u);
 }
 
+// Out-of-range device values the kernels clamp or skip.  Debug builds
+// (RKV_DEBUG) record the first one into a caller-given device word (kind in
+// the top byte, the value in the low 32 bits; see rkv_debug_set_report);
+// other builds compile the reports out.
+constexpr unsigned kBoundsLength = 1;    // a length outside [0, max]
+constexpr unsigned kBoundsPage = 2;      // a page id outside the device pool
+constexpr unsigned kBoundsBlock = 3;     // a block id outside the list's range
+constexpr unsigned kBoundsCount = 4;     // a list count above its capacity
+constexpr unsigned kBoundsHostPage = 5;  // a host page id outside the host pool
+
+#ifdef RKV_DEBUG
+// one per code object; set by this file's RKV_BOUNDS_SETTER function
+static __device__ unsigned long long* rkv_bounds_word;
+__device__ __forceinline__ void report_bounds(unsigned kind, int64_t value) {
+  unsigned long long* w = rkv_bounds_word;
+  if (w != nullptr)
+    atomicCAS(w, 0ull, ((unsigned long long)kind << 56) |
+                           (unsigned long long)(uint32_t)value);
+}
+#define RKV_BOUNDS_SETTER(name)                                              \
+  hipError_t name(unsigned long long* word) {                                \
+    return hipMemcpyToSymbol(HIP_SYMBOL(rkv_bounds_word), &word, sizeof(word)); \
+  }
+#else
+__device__ __forceinline__ void report_bounds(unsigned, int64_t) {}
+#define RKV_BOUNDS_SETTER(name) \
+  hipError_t name(unsigned long long*) { return hipErrorNotSupported; }
+#endif
+
 // Current length of sequence b, clamped to [0, max_len].
 __device__ __forceinline__ int clamp_len(int L, int max_len) {
+  if (L < 0 || L > max_len) report_bounds(kBoundsLength, L);
   return L < 0 ? 0 : (L > max_len ? max_len : L);
 }
 

@@ -211,6 +211,13 @@ hipError_t launch_select_attn(const Method& m, bool use_mfma, const AttnPlan& pl
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
                              int n_cu, hipStream_t stream);
 
+// Debug builds: point each kernel file's bounds-report word at `word` (null:
+// off) for the current device.  Other builds: hipErrorNotSupported.
+hipError_t set_bounds_word_attn(unsigned long long* word);
+hipError_t set_bounds_word_reps(unsigned long long* word);
+hipError_t set_bounds_word_select(unsigned long long* word);
+hipError_t set_bounds_word_stage(unsigned long long* word);
+
 // Sets the calling thread's error text (rkv_last_error) and returns s.
 rkv_status report(rkv_status s, const char* fmt, ...);
 

@@ -68,7 +68,10 @@ __device__ __forceinline__ void append_in_wave(const AppendArgs& ap, int bh, int
   if (L <= 0) return;
   const int pos = L - 1, j = pos >> 7, slot = pos & 127;
   const int page = trow[j];
-  if ((uint64_t)(int64_t)page >= (uint64_t)ap.n_pages) return;
+  if ((uint64_t)(int64_t)page >= (uint64_t)ap.n_pages) {
+    report_bounds(kBoundsPage, page);
+    return;
+  }
   const int64_t base = ((int64_t)page * n_kv + h) * (kBlock * kDim);
   const uint16_t* kn = ap.k_new + (int64_t)bh * kDim;
   const uint16_t* vn = ap.v_new + (int64_t)bh * kDim;
@@ -502,6 +505,7 @@ __global__ __launch_bounds__(256) void merge_kernel(
   const int L = clamp_len(lens[b], max_blocks * kBlock);
   const Regions R = regions_of(L, m.init_tokens, m.local_tokens);
   int k = n_sel[bh];
+  if (k < 0 || k > R.n_off || k > k_cap) report_bounds(kBoundsCount, k);
   k = k < 0 ? 0 : k;
   k = k < R.n_off ? k : R.n_off;
   k = k < k_cap ? k : k_cap;
@@ -511,6 +515,7 @@ __global__ __launch_bounds__(256) void merge_kernel(
   for (int r = threadIdx.x; r < k; r += blockDim.x) {
     const int j = srow[r];
     const bool ok = j >= R.n_init && j < R.n_init + R.n_off;
+    if (!ok) report_bounds(kBoundsBlock, j);
     int page = -1;
     if (ok) {
       const bool on_host = host_table && host_table[(int64_t)b * max_blocks + j] >= 0;
@@ -630,5 +635,7 @@ hipError_t launch_merge(const Method& m, const int32_t* table, int max_blocks,
                      stage_page0, merged, n_merged, m_cap);
   return hipGetLastError();
 }
+
+RKV_BOUNDS_SETTER(set_bounds_word_select)
 
 }  // namespace rkv

@@ -67,12 +67,19 @@ __global__ __launch_bounds__(kStageThreads) void stage_kernel(
   const int bh = (int)(item / k_cap);
   const int b = bh / n_kv, h = bh - b * n_kv;
   int ns = n_sel[bh];
+  if (r == 0 && (ns < 0 || ns > k_cap)) report_bounds(kBoundsCount, ns);
   ns = ns < k_cap ? ns : k_cap;
   if (r >= ns) return;
   const int j = sel_ids[(int64_t)bh * k_cap + r];
-  if (j < 0 || j >= max_blocks) return;
+  if (j < 0 || j >= max_blocks) {
+    report_bounds(kBoundsBlock, j);
+    return;
+  }
   const int hp = host_table[(int64_t)b * max_blocks + j];
-  if ((uint64_t)(int64_t)hp >= (uint64_t)n_host_pages) return;
+  if ((uint64_t)(int64_t)hp >= (uint64_t)n_host_pages) {
+    if (hp != -1) report_bounds(kBoundsHostPage, hp);  // -1: block in HBM
+    return;
+  }
   const int64_t dst_page = stage_page0 + (int64_t)b * k_cap + r;
   if (dst_page < 0 || dst_page >= n_pages) return;
   copy_tiles(host_k, host_v, ((int64_t)hp * n_kv + h) * kTile16, k_pages, v_pages,
@@ -154,6 +161,7 @@ __global__ __launch_bounds__(kPlanThreads) void stage_plan_kernel(ResArgs a) {
   const int L = clamp_len(a.lens[b], max_blocks * kBlock);
   const Regions R = regions_of(L, a.init_tokens, a.local_tokens);
   int k = a.n_sel[bh];
+  if (tid == 0 && (k < 0 || k > R.n_off || k > k_cap)) report_bounds(kBoundsCount, k);
   k = k < 0 ? 0 : k;
   k = k < R.n_off ? k : R.n_off;
   k = k < k_cap ? k : k_cap;
@@ -269,7 +277,10 @@ __global__ __launch_bounds__(kStageThreads) void stage_copy_kernel(
   const int2 c = copies[(int64_t)bh * k_cap + i];
   if (c.x < 0 || c.x >= max_blocks || c.y < 0 || c.y >= slot_cap) return;
   const int hp = host_table[(int64_t)b * max_blocks + c.x];
-  if ((uint64_t)(int64_t)hp >= (uint64_t)n_host_pages) return;
+  if ((uint64_t)(int64_t)hp >= (uint64_t)n_host_pages) {
+    report_bounds(kBoundsHostPage, hp);
+    return;
+  }
   const int64_t dst_page = stage_page0 + (int64_t)b * slot_cap + c.y;
   if (dst_page < 0 || dst_page >= n_pages) return;
   copy_tiles(host_k, host_v, ((int64_t)hp * n_kv + h) * kTile16, k_pages, v_pages,
@@ -299,9 +310,15 @@ __global__ __launch_bounds__(kStageThreads) void offload_kernel(
     const Regions R = regions_of(L, init_tokens, local_tokens);
     if (j < R.n_init || j >= R.n_init + R.n_off) continue;
     const int hp = host_table[(int64_t)b * max_blocks + j];
-    if ((uint64_t)(int64_t)hp >= (uint64_t)n_host_pages) continue;
+    if ((uint64_t)(int64_t)hp >= (uint64_t)n_host_pages) {
+      if (hp != -1) report_bounds(kBoundsHostPage, hp);  // -1: block stays in HBM
+      continue;
+    }
     const int page = table[(int64_t)b * max_blocks + j];
-    if ((uint64_t)(int64_t)page >= (uint64_t)n_pages) continue;
+    if ((uint64_t)(int64_t)page >= (uint64_t)n_pages) {
+      report_bounds(kBoundsPage, page);
+      continue;
+    }
     copy_tiles(k_pages, v_pages, ((int64_t)page * n_kv + h) * kTile16, host_k, host_v,
                ((int64_t)hp * n_kv + h) * kTile16);
   }
@@ -437,5 +454,7 @@ hipError_t launch_offload(const Method& m, const uint16_t* k_pages,
                      reinterpret_cast<uint4*>(host_v), n_host_pages);
   return hipGetLastError();
 }
+
+RKV_BOUNDS_SETTER(set_bounds_word_stage)
 
 }  // namespace rkv

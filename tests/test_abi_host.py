@@ -262,6 +262,22 @@ def test_copy_engine_staging_validation(L):
     assert b"pinned" in L.rkv_last_error()
 
 
+def test_release_build_has_no_bounds_reports(L):
+    assert L.rkv_debug_set_report(None) == B.RKV_ERR_UNSUPPORTED
+    assert b"RKV_DEBUG" in L.rkv_last_error()
+    assert L.rkv_debug_set_report(ODD) == B.RKV_ERR_INVALID_ARG
+    assert L.rkv_debug_check(None, None) == B.RKV_ERR_INVALID_ARG
+    assert L.rkv_status_string(B.RKV_ERR_BOUNDS) == b"out-of-range device value"
+
+
+def test_debug_build_exports_the_same_calls():
+    if not os.path.exists(B.DEBUG_LIB_PATH):
+        pytest.skip("debug library not built")
+    D = ctypes.CDLL(B.DEBUG_LIB_PATH)
+    for n in B.header_functions():
+        assert hasattr(D, n), n
+
+
 def test_reps_and_append_validation(L):
     p = L.rkv_params_default(8, 2)
     assert L.rkv_build_reps(ctypes.byref(p), None, 10, FAKE, 8, FAKE, None, 1,
