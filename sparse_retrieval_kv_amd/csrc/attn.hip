@@ -754,8 +754,10 @@ __device__ __forceinline__ uint32_t kept_blocks(const uint32_t (&key)[kFusedRegs
                                                 uint32_t cbits, int k, int n_off,
                                                 int lane) {
   // non-offload blocks as key 0: every threshold tried below is >= 1, so
-  // they are never counted (an offload block whose key is 0, a NaN score,
-  // is the lowest key and is not counted either, correctly)
+  // they are never counted.  An offload block has key 0 only for the score
+  // bit pattern 0xffffffff (a negative NaN): it ranks below every other
+  // key, and if T stays 0 the tie pass below takes such blocks lowest index
+  // first, as for any tied key.
   uint32_t keyc[NR];
 #pragma unroll
   for (int i = 0; i < NR; ++i) keyc[i] = ((cbits >> i) & 1u) ? key[i] : 0u;

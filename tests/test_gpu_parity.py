@@ -342,6 +342,43 @@ def test_single_sequence_partition_split_sizes():
         assert np.allclose(o, outs[0], rtol=1e-5, atol=1e-6)
 
 
+def test_attention_workspace_reused_across_shapes():
+    """One zero-filled attention workspace serves calls of different shapes
+    in turn (a ragged batch on the range split, a single sequence on the
+    strided partition with its per-list hand-off counters, then the batch
+    again): the combine waves leave the counters at rest, so every call
+    gives, bit for bit, what the same call gives with a fresh workspace."""
+    specs = [
+        synth.custom("ws reuse batch", batch=3, n_q_heads=32, n_kv_heads=8,
+                     context=(40000, 9000, 70001), dense_boundary=0, shuffle=True,
+                     config_id=142),
+        synth.custom("ws reuse single", batch=1, n_q_heads=16, n_kv_heads=4,
+                     context=(20000,), dense_boundary=0, config_id=143),
+    ]
+    cases = []
+    for spec in specs:
+        batch = synth.make_batch(spec, DEV)
+        prm, sess = make_session(batch)
+        prefill(batch, sess)
+        lens = i32(batch.lens_at(0))
+        kn, vn = batch.new_kv_bits(0)
+        sess.append(kn, vn, lens)
+        sess.select(batch.q_bits(0), lens)
+        ref = sess.attend(batch.q_bits(0), lens).clone()
+        cases.append((spec, batch, prm, sess, lens, ref))
+    size = max(B.attn_workspace_size(c[2], c[1].spec.batch, c[3].merged.shape[-1])
+               for c in cases)
+    ws = torch.zeros(size, dtype=torch.uint8, device=DEV)
+    for i in (0, 1, 0, 1, 1, 0):
+        spec, batch, prm, sess, lens, ref = cases[i]
+        say("shared attention workspace:", spec.name)
+        out = torch.full_like(ref, float("nan"))
+        B.decode_attn(prm, batch.q_bits(0), sess.k_pages, sess.v_pages, sess.merged,
+                      sess.n_merged, lens, out, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), spec.name
+
+
 def _score_rounds(groups, max_blocks, init_tokens, n_cu):
     """Representations per score wave (8 x rounds) the library picks: 32,
     halved while the scan would have fewer than two waves per compute unit."""
