@@ -335,6 +335,54 @@ def stream_read_probe(dev, gib=2, reps=5):
     return (gib << 30) / (sorted(ms)[len(ms) // 2] * 1e-3) / 1e9
 
 
+def measure_cascade(sessions, spec, q, lens, reps, plain_us, context, t):
+    """The attention call with the shared-prefix cascade (each attended tile
+    of the shared prefix read once per group of sequences) against the
+    plain call over the same merged tables; tiles counted from the session's
+    selections."""
+    S = spec.shared_prefix_pages
+    n_layers = len(sessions)
+    for s_ in sessions:  # sizes each session's cascade workspace once
+        s_.attend_cascade(q, lens, S)
+    ev0, ev1 = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(reps):
+        sessions[i % n_layers].attend_cascade(q, lens, S)
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / reps
+    # attended shared tiles: per list (plain reads) and per group of 16 / G
+    # sequences (cascade reads); init blocks plus kept blocks below the
+    # prefix end (the window lies past it at these lengths)
+    sess = sessions[0]
+    sel, ns = sess.sel_ids.cpu().numpy(), sess.n_sel.cpu().numpy()
+    G = spec.group
+    Q = min(max(16 // G, 1), spec.batch)
+    n_init = -(-spec.init_tokens // 128)
+    per_list, per_group = 0, 0
+    for h in range(spec.n_kv_heads):
+        for g0 in range(0, spec.batch, Q):
+            union = set()
+            for b in range(g0, min(g0 + Q, spec.batch)):
+                L = int(context[b]) + t
+                se = min(S, (L - 1) // 128)
+                att = set(range(min(n_init, se))) | {int(j) for j in sel[b, h, :ns[b, h]]
+                                                     if j < se}
+                per_list += len(att)
+                union |= att
+            per_group += len(union)
+    tile = 2 * 128 * 128 * 2  # K and V of one (page, KV head)
+    log(f"cascade: {us:.1f} us per call vs {plain_us:.1f} us plain; shared tiles "
+        f"{per_group} read vs {per_list}")
+    return {"call": ("rkv_decode_attn_cascade (cascade_prep_kernel, attn_mfma_kernel<false> "
+                     "with cascade waves, attn_combine_kernel)"),
+            "avg_us": us, "plain_avg_us": plain_us, "speedup": plain_us / us,
+            "shared_blocks": S, "sequences_per_tile_read": Q,
+            "shared_tiles_plain": per_list, "shared_tiles_cascade": per_group,
+            "bytes_saved": (per_list - per_group) * tile}
+
+
 def run_workload(args, config, steps, warmup, cpu_budget, probe_gbs, dev,
                  spread_budget=None):
     """Build one workload, time `steps` decode steps after `warmup`, the
@@ -495,6 +543,12 @@ def run_workload(args, config, steps, warmup, cpu_budget, probe_gbs, dev,
                      "achieved_gbs": kv_attn / (us * 1e-6) / 1e9,
                      "frac": kv_attn / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
 
+    cascade = None
+    if host is None and spec.shared_prefix_pages > 0 and spec.batch > 1 \
+            and args.impl != "valu":
+        cascade = measure_cascade(sessions, spec, qs[t_last], lens[t_last], reps_attn,
+                                  attn_us, base.context, t_last)
+
     staging = None
     if host is not None:
         sess = sessions[0]
@@ -586,6 +640,7 @@ def run_workload(args, config, steps, warmup, cpu_budget, probe_gbs, dev,
             "bytes_per_launch": float(kv_attn),
             "avg_launch_us": float(attn_us),
             "decode_attn_alone": attn_only,
+            "cascade": cascade,
             "timing": (f"{reps_attn} back-to-back "
                        f"{'rkv_select_attend' if fused else 'rkv_decode_attn'} calls over "
                        f"the {n_layers} layer copies between one HIP event pair"),

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define RKV_ABI_VERSION 3
+#define RKV_ABI_VERSION 4
 #define RKV_BLOCK_SIZE 128
 #define RKV_HEAD_DIM 128
 #define RKV_PPM_ONE 1000000
@@ -489,6 +489,52 @@ rkv_status rkv_decode_attn(const rkv_params* params, const uint16_t* q,
                            const int32_t* lens, int32_t batch, float* out,
                            void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
+/*
+ * rkv_decode_attn_cascade -- rkv_decode_attn for a batch whose sequences
+ * share a prefix of pages (CSDN survey, section "Share--KV cache共享":
+ * cascade inference attends a shared prefix once for all requests and
+ * merges its partial results with each request's own part the
+ * FlashDecoding way; ATB article, section 2.1: pages shared by reference
+ * count).  The first shared_blocks logical blocks of every sequence are
+ * taken to sit on sequence 0's pages (block_table[b][j] == block_table[0][j]);
+ * a sequence's shared range also ends before its last block (which holds
+ * the decoded token) and at its first block whose page is not sequence
+ * 0's.  Every (page, KV head) tile of the shared range that some sequence
+ * attends (an init, kept or window block of its merged list) is read once
+ * for a group of 16 / group sequences, whose query heads fill the MFMA tile
+ * together (a sequence that did not keep the block is masked out), instead
+ * of once per sequence; the rest of each list is attended as by
+ * rkv_decode_attn, and the partial results of both parts are merged by
+ * log-sum-exp.  The result is rkv_decode_attn's up to floating-point
+ * rounding (the partials are merged in another grouping).  Launches: one
+ * preparation (shared-block masks and private merged tables, in the
+ * workspace), the split, the combine.  With shared_blocks = 0 or a batch of
+ * one, exactly rkv_decode_attn's launches.
+ *   merged, n_merged, m_cap  as rkv_decode_attn, over device pages (not the
+ *                            host tier's staging pages)
+ *   sel_ids [batch][n_kv_heads][k_cap], n_sel [batch][n_kv_heads]
+ *                            the kept ids that merged was built from
+ *   block_table [batch][max_blocks], shared_blocks in [0, max_blocks]
+ *   workspace >= rkv_attn_cascade_workspace_size(params, batch, m_cap,
+ *                shared_blocks) bytes, 16-byte aligned; calls that overlap on
+ *                one workspace race.
+ * MFMA only: attn_impl = RKV_ATTN_VALU gives RKV_ERR_UNSUPPORTED.
+ * Errors: RKV_ERR_INVALID_ARG, RKV_ERR_UNSUPPORTED, RKV_ERR_WORKSPACE,
+ * RKV_ERR_HIP.
+ */
+size_t rkv_attn_cascade_workspace_size(const rkv_params* params, int32_t batch,
+                                       int32_t m_cap, int32_t shared_blocks);
+rkv_status rkv_decode_attn_cascade(const rkv_params* params, const uint16_t* q,
+                                   const uint16_t* k_pages, const uint16_t* v_pages,
+                                   int64_t n_pages, const int32_t* merged,
+                                   const int32_t* n_merged, int32_t m_cap,
+                                   const int32_t* sel_ids, const int32_t* n_sel,
+                                   int32_t k_cap, const int32_t* block_table,
+                                   int32_t max_blocks, int32_t shared_blocks,
+                                   const int32_t* lens, int32_t batch, float* out,
+                                   void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
 
 /*
  * rkv_select_attend -- the top-k and merge of rkv_select from given scores,

@@ -94,6 +94,10 @@ _SIGS = {
     "rkv_attn_workspace_size": (_SZ, [_PP, _I32, _I32]),
     "rkv_decode_attn": (ctypes.c_int, [_PP, _P, _P, _P, _I64, _P, _P, _I32, _P, _I32,
                                        _P, _P, _SZ, _P]),
+    "rkv_attn_cascade_workspace_size": (_SZ, [_PP, _I32, _I32, _I32]),
+    "rkv_decode_attn_cascade": (ctypes.c_int, [_PP, _P, _P, _P, _I64, _P, _P, _I32, _P,
+                                               _P, _I32, _P, _I32, _I32, _P, _I32, _P,
+                                               _P, _SZ, _P]),
     "rkv_select_attend": (ctypes.c_int, [_PP, _P, _P, _P, _I64, _P, _I32, _P, _P, _I32,
                                          _P, _P, _P, _I32, _P, _P, _I32, _P, _P, _SZ,
                                          _P]),
@@ -459,6 +463,36 @@ def decode_attn(p: Params, q, k_pages, v_pages, merged, n_merged, lens, out,
         k_pages.shape[0],
         _ptr(merged, torch.int32, "merged", (batch, hkv, merged.shape[-1]), d),
         _ptr(n_merged, torch.int32, "n_merged", (batch, hkv), d), merged.shape[-1],
+        _ptr(lens, torch.int32, "lens", (batch,), d), batch,
+        _ptr(out, torch.float32, "out", rows, d), _ptr(workspace, None, "workspace", None, d),
+        ws_bytes, _stream(q)))
+
+
+def attn_cascade_workspace_size(p: Params, batch: int, m_cap: int,
+                                shared_blocks: int) -> int:
+    return lib().rkv_attn_cascade_workspace_size(ctypes.byref(p), batch, m_cap,
+                                                 shared_blocks)
+
+
+def decode_attn_cascade(p: Params, q, k_pages, v_pages, merged, n_merged, sel_ids,
+                        n_sel, block_table, shared_blocks: int, lens, out, workspace):
+    batch = lens.shape[0]
+    d = q.device
+    hkv = p.n_kv_heads
+    rows = (batch, p.n_q_heads, HEAD_DIM)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    max_blocks = block_table.shape[-1]
+    _check(lib().rkv_decode_attn_cascade(
+        ctypes.byref(p), _ptr(q, torch.int16, "q", rows, d),
+        _ptr(k_pages, torch.int16, "k_pages", _pool_shape(p, k_pages), d),
+        _ptr(v_pages, torch.int16, "v_pages", _pool_shape(p, k_pages), d),
+        k_pages.shape[0],
+        _ptr(merged, torch.int32, "merged", (batch, hkv, merged.shape[-1]), d),
+        _ptr(n_merged, torch.int32, "n_merged", (batch, hkv), d), merged.shape[-1],
+        _ptr(sel_ids, torch.int32, "sel_ids", (batch, hkv, sel_ids.shape[-1]), d),
+        _ptr(n_sel, torch.int32, "n_sel", (batch, hkv), d), sel_ids.shape[-1],
+        _ptr(block_table, torch.int32, "block_table", (batch, max_blocks), d),
+        max_blocks, shared_blocks,
         _ptr(lens, torch.int32, "lens", (batch,), d), batch,
         _ptr(out, torch.float32, "out", rows, d), _ptr(workspace, None, "workspace", None, d),
         ws_bytes, _stream(q)))

@@ -125,6 +125,19 @@ struct AttnArgs {
   int n_cu;          // compute units of the device
   int per_list;      // > 0: waves per list of the single-sequence partition
   float scale_log2;  // scale * log2(e)
+  // shared-prefix cascade (c_waves > 0): waves n_waves .. n_waves + c_waves - 1
+  // of the range-split launch attend the shared blocks, c_q sequences per
+  // wave; merged / n_merged then hold each list's private entries only
+  const int32_t* c_table;  // block-table row of sequence 0: the shared pages
+  const uint32_t* c_mask;  // [batch * n_kv][c_words]: attended shared blocks
+  int c_words;             // mask words per list
+  int c_q;                 // sequences per cascade wave (16 / group, <= batch)
+  int c_groups;            // sequence groups: ceil(batch / c_q)
+  int c_chunks;            // chunks of shared blocks per (KV head, group)
+  int c_chunk_blocks;      // shared blocks per chunk (<= 64)
+  int c_shared;            // shared blocks named by the caller
+  int c_waves;             // n_kv * c_groups * c_chunks, or 0
+  int64_t c_slot0;         // first cascade slot; wave cw writes c_q slots
 };
 
 // ---------------------------------------------------------------------------
@@ -711,6 +724,197 @@ __device__ __forceinline__ void strided_body(const AttnArgs& a) {
 }
 
 // ---------------------------------------------------------------------------
+// Shared-prefix cascade (CSDN survey, section "Share--KV cache共享": cascade
+// inference attends a prefix shared by several requests once for all of
+// them and merges the partial results with the private suffix's the
+// FlashDecoding way; ATB article, section 2.1: pages shared by reference
+// count).  When the first c_shared logical blocks of every sequence sit on
+// the same pages, a (page, KV head) tile of that prefix is read once for a
+// group of c_q = 16 / group sequences, whose query heads fill the 16 MFMA
+// columns together; a column whose sequence did not keep the block is
+// masked out.  Each cascade wave takes one chunk of the prefix for one (KV
+// head, group) and leaves one piece per sequence of the group.
+// ---------------------------------------------------------------------------
+struct CascadeMath : MfmaMath {
+  // columns c = q * G + hh: query head hh of sequence b0 + q (zero padding
+  // past the group or the batch); every lane loads a valid row
+  __device__ __forceinline__ void begin_group(const AttnArgs& a, int b0, int h,
+                                              int col, int grp) {
+    const int G = a.group;
+    const int q = col / G, hh = col - q * G;
+    const bool ok = q < a.c_q && b0 + q < a.batch;
+    const int b = ok ? b0 + q : b0;
+    const uint16_t* qrow = a.q + ((int64_t)b * a.n_kv * G + h * G + (ok ? hh : 0)) * kDim;
+    uint4 v[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) v[kk] = ld16(qrow + (4 * kk + grp) * 8);
+    const uint32_t keep = ok ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      bq[kk] = as_bf16x8(make_uint4(v[kk].x & keep, v[kk].y & keep, v[kk].z & keep,
+                                    v[kk].w & keep));
+#pragma unroll
+    for (int n8 = 0; n8 < 8; ++n8) acc[n8] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    m_run = kNegInf;
+    l_run = 0.f;
+  }
+
+  // One full 64-token unit; col_ok: this lane's column attends the block.
+  // A column with no logit yet keeps m = -inf and l = 0 (exponents are
+  // taken against 0 then, so no -inf - -inf appears).
+  __device__ __forceinline__ void accumulate_cols(Scores& s, uint4 (&vf)[2][8],
+                                                  bool col_ok, float sl2, int grp) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = col_ok ? s[t][r] * sl2 : kNegInf;
+        s[t][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_base = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_base);
+    float psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = fast_exp2(s[t][r] - m_base);
+        s[t][r] = p;
+        psum += p;
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float ar = __shfl(alpha, 4 * grp + r);
+#pragma unroll
+      for (int n8 = 0; n8 < 8; ++n8) acc[n8][r] *= ar;
+    }
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      const float p8[8] = {s[2 * pp][0],     s[2 * pp][1],     s[2 * pp][2],
+                           s[2 * pp][3],     s[2 * pp + 1][0], s[2 * pp + 1][1],
+                           s[2 * pp + 1][2], s[2 * pp + 1][3]};
+      bf16x8 ph, pl;
+      split_hi_lo(p8, ph, pl);
+#pragma unroll
+      for (int n8 = 0; n8 < 8; ++n8) {
+        const bf16x8 v = as_bf16x8(vf[pp][n8]);
+        acc[n8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, v, acc[n8], 0, 0, 0);
+        acc[n8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, v, acc[n8], 0, 0, 0);
+      }
+    }
+  }
+
+  // Column c's rows go to slot slot0 + c / G, row c mod G (a piece per
+  // sequence of the group, in the ordinary G-row layout).
+  __device__ __forceinline__ void finish_group(const AttnArgs& a, int64_t slot0,
+                                               int lane, int col, int grp) {
+    const int G = a.group;
+    const int QG = a.c_q * G;
+    float lt = l_run + __shfl_xor(l_run, 16);
+    lt += __shfl_xor(lt, 32);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int c = 4 * grp + r;
+      if (c < QG) {
+        const int q = c / G;
+        float* dst = a.part_acc + ((slot0 + q) * G + (c - q * G)) * kDim + col;
+#pragma unroll
+        for (int n8 = 0; n8 < 8; ++n8) dst[16 * n8] = acc[n8][r];
+      }
+    }
+    if (lane < QG) {
+      const int q = lane / G;
+      a.part_ml[(slot0 + q) * G + (lane - q * G)] = make_float2(m_run, lt);
+    }
+  }
+};
+
+__device__ __forceinline__ void cascade_body(const AttnArgs& a) {
+  __shared__ int cpage[64];      // the chunk's attended blocks: pages
+  __shared__ uint32_t cqm[64];   // ... and which sequences of the group attend
+  const int lane = threadIdx.x;
+  const int col = lane & 15, grp = lane >> 4;
+  const int cw = (int)blockIdx.x - a.n_waves;
+  const int chunk = cw % a.c_chunks;
+  const int hg = cw / a.c_chunks;
+  const int g = hg % a.c_groups, h = hg / a.c_groups;
+  const int Q = a.c_q;
+  const int b0 = g * Q;
+  const int j0 = chunk * a.c_chunk_blocks;
+  int j1 = j0 + a.c_chunk_blocks;
+  j1 = j1 < a.c_shared ? j1 : a.c_shared;
+
+  // --- one round trip: block j0 + lane's page (table row 0) and, per
+  // sequence of the group, its attended bit (clamped indexes, masked) ---
+  const int j = j0 + lane;
+  const int jc = j < a.c_shared ? j : a.c_shared - 1;
+  const int page_raw = a.c_table[jc];
+  uint32_t words[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int b = b0 + q < a.batch ? b0 + q : a.batch - 1;
+    words[q] = a.c_mask[((int64_t)b * a.n_kv + h) * a.c_words + (jc >> 5)];
+  }
+  uint32_t qm = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const bool in = q < Q && b0 + q < a.batch;
+    qm |= (in && ((words[q] >> (jc & 31)) & 1u)) ? 1u << q : 0u;
+  }
+  const bool any = j < j1 && qm != 0u;
+  const uint64_t am = __ballot(any);
+  const int n_att = __popcll(am);
+  const int pos = lanes_below(am);
+  // lanes without a block write slot 63, which is an entry only when every
+  // lane has one
+  cpage[any ? pos : 63] = page_raw;
+  cqm[any ? pos : 63] = qm;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  CascadeMath math;
+  math.begin_group(a, b0, h, col, grp);
+  const int q_col = col / a.group;
+  const int64_t head_off = (int64_t)h * (kBlock * kDim);
+  const int64_t page_stride = (int64_t)a.n_kv * (kBlock * kDim);
+  auto page_ok = [&](int p) { return (uint64_t)(int64_t)p < (uint64_t)a.n_pages; };
+  auto tile_of = [&](int p) { return (page_ok(p) ? (int64_t)p * page_stride : 0) + head_off; };
+  const int n_u = 2 * n_att;
+  uint4 kf[4][4];
+  uint4 vf[2][8];
+  if (n_u > 0) {  // uniform
+    int page = cpage[0];
+    int64_t tile = tile_of(page);
+    load_k_unit(kf, a.k_pages + tile, 0, col, grp);
+    for (int u = 0; u < n_u; ++u) {
+      typename CascadeMath::Scores sc;
+      math.scores(kf, sc);
+      __builtin_amdgcn_sched_barrier(0);
+      load_v_unit(vf, a.v_pages + tile, u & 1, col, grp);
+      const bool cur_ok = page_ok(page);
+      if (!cur_ok) report_page(page);
+      const uint32_t m_cur = cqm[u >> 1];
+      if (u + 1 < n_u) {  // the next unit's K tile
+        page = cpage[(u + 1) >> 1];
+        tile = tile_of(page);
+        load_k_unit(kf, a.k_pages + tile, (u + 1) & 1, col, grp);
+      }
+      const bool col_ok = q_col < 16 && ((m_cur >> q_col) & 1u) != 0u;
+      if (cur_ok) math.accumulate_cols(sc, vf, col_ok, a.scale_log2, grp);
+    }
+  }
+  math.finish_group(a, a.c_slot0 + (int64_t)cw * Q, lane, col, grp);
+}
+
+// ---------------------------------------------------------------------------
 // Top-k and merge inside the attention launch (batch of one).
 //
 // The selection of a (sequence, KV head) list depends only on the list's
@@ -955,10 +1159,17 @@ __global__ __launch_bounds__(64) void attn_select_mfma_kernel(AttnArgs a,
 
 template <class Math, bool STRIDED>
 __device__ __forceinline__ void attn_body(const AttnArgs& a) {
-  if (STRIDED)
+  if constexpr (STRIDED) {
     strided_body<Math>(a);
-  else
+  } else {
+    if constexpr (std::is_same<Math, MfmaMath>::value) {
+      if (blockIdx.x >= (unsigned)a.n_waves) {  // shared-prefix cascade waves
+        cascade_body(a);
+        return;
+      }
+    }
     split_body<Math>(a);
+  }
 }
 
 template <bool STRIDED>
@@ -1066,6 +1277,20 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a,
     for (int u = 0; u < kCombDepth; ++u)
       if (ml[u].y > 0.f) lse_fold(m, l, acc, ml[u].x, ml[u].y, v[u]);
   }
+  // shared-prefix cascade: the pieces the (KV head, group) chunk waves left
+  // for this sequence (chunk c's in slot c_slot0 + (wave * c_q + q))
+  if (a.c_waves > 0) {  // uniform
+    const int g = b / a.c_q, q = b - g * a.c_q;
+    const int64_t cbase =
+        a.c_slot0 + (int64_t)((qh / G) * a.c_groups + g) * a.c_chunks * a.c_q + q;
+    for (int c = pg; c < a.c_chunks; c += kCombGroups) {
+      const int64_t slot = cbase + (int64_t)c * a.c_q;
+      const float2 mlc = a.part_ml[slot * G + hh];
+      const float4 vc =
+          *reinterpret_cast<const float4*>(a.part_acc + (slot * G + hh) * kDim + dim0);
+      if (mlc.y > 0.f) lse_fold(m, l, acc, mlc.x, mlc.y, vc);
+    }
+  }
 #pragma unroll
   for (int off = 8; off < 64; off <<= 1) {
     const float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
@@ -1080,6 +1305,97 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a,
     const float inv = l > 0.f ? 1.f / l : 0.f;
     *dst = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
+}
+
+// Shared-prefix cascade, first launch: per (sequence, KV head) list, the
+// shared blocks it attends as a bit mask and its merged table without them.
+// A sequence's shared end is the caller's count of shared blocks, cut before
+// its last block (the decoded token's, never shared) and at its first block
+// whose page is not sequence 0's.  Below that end the list attends its init
+// blocks, its kept blocks and its window blocks; those entries are always a
+// prefix of the merged list (init, kept, window blocks, each ascending), so
+// the private table is the rest of the row.
+struct CascadePrep {
+  const int32_t* table;  // [batch][max_blocks]
+  int max_blocks;
+  const int32_t* lens;
+  const int32_t* merged;
+  const int32_t* n_merged;
+  int m_cap;
+  const int32_t* sel_ids;  // the kept ids the merged table was built from
+  const int32_t* n_sel;
+  int k_cap;
+  int shared, words, n_kv, init_tokens, local_tokens;
+  uint32_t* mask;          // [lists][words]
+  int32_t* merged_priv;    // [lists][m_cap]
+  int32_t* n_priv;         // [lists]
+};
+
+constexpr int kMaxSharedWords = RKV_MAX_BLOCKS / 32;
+
+__global__ __launch_bounds__(64) void cascade_prep_kernel(CascadePrep c) {
+  __shared__ uint32_t bits[kMaxSharedWords];
+  const int lane = threadIdx.x;
+  const int bh = blockIdx.x;
+  const int b = bh / c.n_kv;
+  const int L = clamp_len(c.lens[b], c.max_blocks * kBlock);
+  const Regions R = regions_of(L, c.init_tokens, c.local_tokens);
+  const int lstart = R.local_start > R.n_init ? R.local_start : R.n_init;
+  int se = L > 0 ? (L - 1) >> 7 : 0;
+  se = se < c.shared ? se : c.shared;
+  const int32_t* row = c.table + (int64_t)b * c.max_blocks;
+  for (int j0 = 0; j0 < se; j0 += 64) {  // uniform
+    const int j = j0 + lane;
+    const int jc = j < se ? j : se - 1;
+    const uint64_t dm = __ballot(j < se && row[jc] != c.table[jc]);
+    if (dm != 0) {
+      se = j0 + __builtin_ctzll(dm);
+      break;
+    }
+  }
+  for (int w = lane; w < c.words; w += 64) bits[w] = 0u;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // kept ids below the shared end (ascending: stop at the first chunk that
+  // reaches it)
+  int ns = c.n_sel[bh];
+  if (ns < 0 || ns > c.k_cap) report_bounds(kBoundsCount, ns);
+  ns = ns < 0 ? 0 : (ns > c.k_cap ? c.k_cap : ns);
+  const int32_t* srow = c.sel_ids + (int64_t)bh * c.k_cap;
+  int n_kept_sh = 0;
+  for (int r0 = 0; r0 < ns; r0 += 64) {  // uniform
+    const int r = r0 + lane;
+    const int id = srow[r < ns ? r : ns - 1];
+    const bool in = r < ns && id >= 0 && id < se;
+    if (in) atomicOr(&bits[id >> 5], 1u << (id & 31));
+    n_kept_sh += __popcll(__ballot(in));
+    if (__ballot(r < ns && id >= se) != 0) break;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // init blocks [0, min(n_init, se)) and window blocks [lstart, se)
+  const int init_end = R.n_init < se ? R.n_init : se;
+  auto range_bits = [](int lo, int a0, int a1) {  // bits of [a0, a1) in word [lo, lo + 32)
+    const int s0 = a0 > lo ? a0 - lo : 0;
+    const int s1 = a1 < lo + 32 ? a1 - lo : 32;
+    if (s1 <= s0) return 0u;
+    const uint32_t hi = s1 >= 32 ? 0xffffffffu : (1u << s1) - 1u;
+    return hi & ~((1u << s0) - 1u);
+  };
+  uint32_t* mrow = c.mask + (int64_t)bh * c.words;
+  for (int w = lane; w < c.words; w += 64)
+    mrow[w] = bits[w] | range_bits(32 * w, 0, init_end) | range_bits(32 * w, lstart, se);
+  int n_m = c.n_merged[bh];
+  if (n_m < 0 || n_m > c.m_cap) report_bounds(kBoundsCount, n_m);
+  n_m = n_m < 0 ? 0 : (n_m > c.m_cap ? c.m_cap : n_m);
+  int n_sh = init_end + n_kept_sh + (se > lstart ? se - lstart : 0);
+  n_sh = n_sh < n_m ? n_sh : n_m;
+  const int32_t* src = c.merged + (int64_t)bh * c.m_cap + n_sh;
+  int32_t* dst = c.merged_priv + (int64_t)bh * c.m_cap;
+  for (int e = lane; e < n_m - n_sh; e += 64) dst[e] = src[e];
+  if (lane == 0) c.n_priv[bh] = n_m - n_sh;
 }
 
 }  // namespace
@@ -1147,6 +1463,11 @@ AttnArgs attn_args(const Method& m, const AttnPlan& plan, float scale,
   a.n_waves = plan.n_waves;
   a.per_list = plan.per_list;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.c_table = nullptr;
+  a.c_mask = nullptr;
+  a.c_words = a.c_q = a.c_groups = a.c_chunks = a.c_chunk_blocks = 0;
+  a.c_shared = a.c_waves = 0;
+  a.c_slot0 = 0;
   return a;
 }
 
@@ -1197,6 +1518,111 @@ hipError_t launch_decode_attn(const Method& m, bool use_mfma,
 #undef RKV_VALU_CASE
   }
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_combine(m, a, batch, out, stream);
+}
+
+namespace {
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+}  // namespace
+
+CascadePlan plan_cascade(int batch, int n_q_heads, int n_kv_heads, int waves,
+                         int m_cap, int n_cu, int shared_blocks) {
+  CascadePlan c;
+  c.attn = plan_attention(batch, n_q_heads, n_kv_heads, waves, m_cap, n_cu);
+  c.q = c.groups = c.chunks = c.chunk_blocks = c.waves = c.words = 0;
+  c.shared = shared_blocks;
+  c.slot0 = c.attn.n_slots;
+  c.mask_off = c.priv_off = c.npriv_off = c.attn.total_bytes;
+  c.total_bytes = c.attn.total_bytes;
+  // nothing to share with fewer than two sequences (a batch of one takes the
+  // single-sequence partition)
+  if (batch < 2 || shared_blocks <= 0 || n_kv_heads <= 0 || c.attn.per_list > 0) return c;
+  const int group = n_q_heads / n_kv_heads;
+  c.q = 16 / group > 1 ? 16 / group : 1;
+  c.q = c.q < batch ? c.q : batch;
+  c.groups = (batch + c.q - 1) / c.q;
+  // about one cascade wave per compute unit, chunks of at most 64 blocks
+  const int combos = n_kv_heads * c.groups;
+  int chunks = c.attn.n_cu / combos;
+  const int min_chunks = (shared_blocks + 63) / 64;
+  chunks = chunks < min_chunks ? min_chunks : chunks;
+  chunks = chunks > shared_blocks ? shared_blocks : chunks;
+  c.chunk_blocks = (shared_blocks + chunks - 1) / chunks;
+  c.chunks = (shared_blocks + c.chunk_blocks - 1) / c.chunk_blocks;
+  c.waves = combos * c.chunks;
+  c.words = (shared_blocks + 31) / 32;
+  // cascade slots after the range split's, c_q per cascade wave
+  AttnPlan& p = c.attn;
+  c.slot0 = p.n_slots;
+  p.n_slots += c.waves * c.q;
+  p.partial_bytes = (size_t)p.n_slots * group * kDim * sizeof(float);
+  p.ml_bytes = (size_t)p.n_slots * group * 2 * sizeof(float);
+  p.total_bytes = p.partial_bytes + p.ml_bytes + p.count_bytes;
+  const size_t lists = (size_t)batch * n_kv_heads;
+  c.mask_off = round256(p.total_bytes);
+  c.priv_off = c.mask_off + round256(lists * c.words * sizeof(uint32_t));
+  c.npriv_off = c.priv_off + round256(lists * (size_t)m_cap * sizeof(int32_t));
+  c.total_bytes = c.npriv_off + round256(lists * sizeof(int32_t));
+  return c;
+}
+
+hipError_t launch_decode_attn_cascade(const Method& m, const CascadePlan& plan,
+                                      float scale, const uint16_t* q,
+                                      const uint16_t* k_pages, const uint16_t* v_pages,
+                                      int64_t n_pages, const int32_t* merged,
+                                      const int32_t* n_merged, int m_cap,
+                                      const int32_t* sel_ids, const int32_t* n_sel,
+                                      int k_cap, const int32_t* table, int max_blocks,
+                                      const int32_t* lens, int batch, float* out,
+                                      void* workspace, hipStream_t stream) {
+  if (batch == 0) return hipSuccess;
+  if (plan.waves == 0)
+    return launch_decode_attn(m, true, plan.attn, scale, q, k_pages, v_pages, n_pages,
+                              merged, n_merged, m_cap, lens, batch, out, workspace,
+                              stream);
+  char* ws = static_cast<char*>(workspace);
+  uint32_t* mask = reinterpret_cast<uint32_t*>(ws + plan.mask_off);
+  int32_t* merged_priv = reinterpret_cast<int32_t*>(ws + plan.priv_off);
+  int32_t* n_priv = reinterpret_cast<int32_t*>(ws + plan.npriv_off);
+  CascadePrep c;
+  c.table = table;
+  c.max_blocks = max_blocks;
+  c.lens = lens;
+  c.merged = merged;
+  c.n_merged = n_merged;
+  c.m_cap = m_cap;
+  c.sel_ids = sel_ids;
+  c.n_sel = n_sel;
+  c.k_cap = k_cap;
+  c.shared = plan.shared;
+  c.words = plan.words;
+  c.n_kv = m.n_kv_heads;
+  c.init_tokens = m.init_tokens;
+  c.local_tokens = m.local_tokens;
+  c.mask = mask;
+  c.merged_priv = merged_priv;
+  c.n_priv = n_priv;
+  hipLaunchKernelGGL(cascade_prep_kernel, dim3((unsigned)(batch * m.n_kv_heads)),
+                     dim3(64), 0, stream, c);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  AttnArgs a = attn_args(m, plan.attn, scale, q, k_pages, v_pages, n_pages, merged_priv,
+                         n_priv, m_cap, lens, batch, workspace);
+  a.c_table = table;
+  a.c_mask = mask;
+  a.c_words = plan.words;
+  a.c_q = plan.q;
+  a.c_groups = plan.groups;
+  a.c_chunks = plan.chunks;
+  a.c_chunk_blocks = plan.chunk_blocks;
+  a.c_shared = plan.shared;
+  a.c_waves = plan.waves;
+  a.c_slot0 = plan.slot0;
+  hipLaunchKernelGGL(attn_mfma_kernel<false>,
+                     dim3((unsigned)(plan.attn.n_waves + plan.waves)), dim3(64), 0,
+                     stream, a);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_combine(m, a, batch, out, stream);
 }

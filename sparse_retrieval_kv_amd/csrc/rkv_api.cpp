@@ -696,6 +696,67 @@ rkv_status rkv_decode_attn(const rkv_params* params, const uint16_t* q,
       "rkv_decode_attn launch");
 }
 
+size_t rkv_attn_cascade_workspace_size(const rkv_params* params, int32_t batch,
+                                       int32_t m_cap, int32_t shared_blocks) {
+  if (!params || params->n_q_heads <= 0 || params->n_kv_heads <= 0 ||
+      batch < 0 || m_cap < 1 || params->split_waves < 0 || shared_blocks < 0)
+    return 0;
+  const rkv::CascadePlan p = rkv::plan_cascade(
+      batch, params->n_q_heads, params->n_kv_heads, params->split_waves, m_cap,
+      rkv::device_cu_count(), shared_blocks);
+  return p.total_bytes;
+}
+
+rkv_status rkv_decode_attn_cascade(const rkv_params* params, const uint16_t* q,
+                                   const uint16_t* k_pages, const uint16_t* v_pages,
+                                   int64_t n_pages, const int32_t* merged,
+                                   const int32_t* n_merged, int32_t m_cap,
+                                   const int32_t* sel_ids, const int32_t* n_sel,
+                                   int32_t k_cap, const int32_t* block_table,
+                                   int32_t max_blocks, int32_t shared_blocks,
+                                   const int32_t* lens, int32_t batch, float* out,
+                                   void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  rkv::Method m;
+  RKV_TRY(check_params(params, &m));
+  RKV_REQUIRE(batch >= 0, RKV_ERR_INVALID_ARG, "batch %d < 0", batch);
+  RKV_REQUIRE(m_cap >= 1 && m_cap <= RKV_MAX_BLOCKS, RKV_ERR_INVALID_ARG,
+              "m_cap %d outside [1, %d]", m_cap, RKV_MAX_BLOCKS);
+  RKV_REQUIRE(max_blocks >= 1 && max_blocks <= RKV_MAX_BLOCKS, RKV_ERR_INVALID_ARG,
+              "max_blocks %d outside [1, %d]", max_blocks, RKV_MAX_BLOCKS);
+  RKV_REQUIRE(k_cap >= 1 && k_cap <= RKV_MAX_BLOCKS, RKV_ERR_INVALID_ARG,
+              "k_cap %d outside [1, %d]", k_cap, RKV_MAX_BLOCKS);
+  RKV_REQUIRE(shared_blocks >= 0 && shared_blocks <= max_blocks, RKV_ERR_INVALID_ARG,
+              "shared_blocks %d outside [0, max_blocks = %d]", shared_blocks,
+              max_blocks);
+  RKV_TRY(check_pool(k_pages, n_pages, "k_pages"));
+  RKV_TRY(check_pool(v_pages, n_pages, "v_pages"));
+  RKV_REQUIRE(q && merged && n_merged && sel_ids && n_sel && block_table && lens && out,
+              RKV_ERR_INVALID_ARG,
+              "q, merged, n_merged, sel_ids, n_sel, block_table, lens and out must "
+              "not be NULL");
+  RKV_REQUIRE(aligned16(q) && aligned16(out), RKV_ERR_INVALID_ARG,
+              "q and out must be 16-byte aligned");
+  RKV_REQUIRE(params->attn_impl != RKV_ATTN_VALU, RKV_ERR_UNSUPPORTED,
+              "the shared-prefix cascade runs on the MFMA attention only");
+  RKV_TRY(check_extent(params, batch, max3(m_cap, k_cap, max_blocks)));
+  const rkv::CascadePlan plan = rkv::plan_cascade(
+      batch, m.n_q_heads, m.n_kv_heads, params->split_waves, m_cap,
+      rkv::device_cu_count(), shared_blocks);
+  const size_t need = plan.total_bytes;
+  RKV_REQUIRE(workspace_bytes >= need && (need == 0 || workspace != nullptr),
+              RKV_ERR_WORKSPACE, "cascade attention workspace %zu bytes, need %zu",
+              workspace_bytes, need);
+  RKV_REQUIRE(aligned16(workspace), RKV_ERR_INVALID_ARG,
+              "workspace is not 16-byte aligned");
+  return hip_status(
+      rkv::launch_decode_attn_cascade(m, plan, params->scale, q, k_pages, v_pages,
+                                      n_pages, merged, n_merged, m_cap, sel_ids, n_sel,
+                                      k_cap, block_table, max_blocks, lens, batch, out,
+                                      workspace, stream),
+      "rkv_decode_attn_cascade launch");
+}
+
 namespace {
 
 // Checks of rkv_select_attend (also the attention half of rkv_decode_step).

@@ -208,6 +208,30 @@ hipError_t launch_select_attn(const Method& m, bool use_mfma, const AttnPlan& pl
                               int32_t* n_merged, int m_cap, float* out,
                               void* workspace, hipStream_t stream);
 
+// Shared-prefix cascade decode: the range split over each list's private
+// entries plus cascade waves over the shared prefix, after a preparation
+// launch (shared-block masks and private merged tables), then the combine.
+// Workspace: the range split's (with c_waves * c_q more slots), then the
+// masks, the private merged tables and their counts.
+struct CascadePlan {
+  AttnPlan attn;         // n_slots includes the cascade slots
+  int q, groups, chunks, chunk_blocks, waves, words, shared;
+  int64_t slot0;         // first cascade slot
+  size_t mask_off, priv_off, npriv_off;  // byte offsets in the workspace
+  size_t total_bytes;
+};
+CascadePlan plan_cascade(int batch, int n_q_heads, int n_kv_heads, int waves,
+                         int m_cap, int n_cu, int shared_blocks);
+hipError_t launch_decode_attn_cascade(const Method& m, const CascadePlan& plan,
+                                      float scale, const uint16_t* q,
+                                      const uint16_t* k_pages, const uint16_t* v_pages,
+                                      int64_t n_pages, const int32_t* merged,
+                                      const int32_t* n_merged, int m_cap,
+                                      const int32_t* sel_ids, const int32_t* n_sel,
+                                      int k_cap, const int32_t* table, int max_blocks,
+                                      const int32_t* lens, int batch, float* out,
+                                      void* workspace, hipStream_t stream);
+
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
                              int n_cu, hipStream_t stream);
 

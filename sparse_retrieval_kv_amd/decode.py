@@ -49,6 +49,7 @@ class DecodeSession:
             if ws else None
         wa = B.attn_workspace_size(prm, self.batch, self.m_cap)
         self.ws_attn = torch.empty(max(wa, 16), dtype=torch.uint8, device=dev)
+        self.ws_cascade = None  # sized on the first cascade call
         self._fast = None  # per-step calls with the session buffers bound once
 
     def _prepared(self) -> B.PreparedStep:
@@ -97,6 +98,28 @@ class DecodeSession:
         """The same step as rkv_append_select + rkv_decode_attn."""
         self.append_select(q, k_new, v_new, lens)
         return self.attend(q, lens)
+
+    def attend_cascade(self, q, lens, shared_blocks: int):
+        """Attention with the shared-prefix cascade (rkv_decode_attn_cascade):
+        the first `shared_blocks` blocks of every sequence sit on sequence
+        0's pages, and each attended tile of that prefix is read once per
+        group of sequences.  Uses the merged tables and kept ids of the last
+        selection."""
+        need = B.attn_cascade_workspace_size(self.p, self.batch, self.m_cap,
+                                             shared_blocks)
+        if self.ws_cascade is None or self.ws_cascade.numel() < need:
+            self.ws_cascade = torch.empty(max(need, 16), dtype=torch.uint8,
+                                          device=self.k_pages.device)
+        B.decode_attn_cascade(self.p, q, self.k_pages, self.v_pages, self.merged,
+                              self.n_merged, self.sel_ids, self.n_sel,
+                              self.block_table, shared_blocks, lens, self.out,
+                              self.ws_cascade)
+        return self.out
+
+    def step_cascade(self, q, k_new, v_new, lens, shared_blocks: int):
+        """rkv_append_select, then the cascade attention."""
+        self.append_select(q, k_new, v_new, lens)
+        return self.attend_cascade(q, lens, shared_blocks)
 
 
 class HostTierSession(DecodeSession):

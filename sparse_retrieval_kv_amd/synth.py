@@ -220,6 +220,10 @@ def make_batch(spec: Spec, device="cpu", poison_tail: bool = True,
     nblk = -(-final_len // BLOCK)
     max_blocks = int(nblk.max())
     shared = spec.shared_prefix_pages
+    # every sequence extends past the shared prefix: its decoded tokens (and
+    # the padding after its end) go to pages of its own, never to a shared one
+    assert shared == 0 or int(context.min()) > shared * BLOCK, \
+        "every context must extend past the shared prefix"
     n_pages = int(shared + (nblk - shared).sum())
 
     order = None

@@ -26,7 +26,7 @@ def test_every_declared_function_is_exported(L):
     assert len(names) >= 11
     for n in names:
         assert hasattr(L, n), n
-    assert L.rkv_abi_version() == 3
+    assert L.rkv_abi_version() == 4
 
 
 def test_defaults_follow_the_page(L):
@@ -384,3 +384,49 @@ def test_bench_refuses_more_than_one_gpu():
                          capture_output=True, text=True, timeout=300)
     assert out.returncode == 2
     assert "one GPU" in out.stderr
+
+
+def _cascade(L, p, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, n_pages=10, merged=FAKE, n_merged=FAKE, m_cap=16,
+             sel=FAKE, n_sel=FAKE, k_cap=16, table=FAKE, max_blocks=16, shared=8,
+             lens=FAKE, batch=2, out=FAKE, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return L.rkv_decode_attn_cascade(
+        ctypes.byref(p), a["q"], a["k"], a["v"], a["n_pages"], a["merged"],
+        a["n_merged"], a["m_cap"], a["sel"], a["n_sel"], a["k_cap"], a["table"],
+        a["max_blocks"], a["shared"], a["lens"], a["batch"], a["out"], a["ws"],
+        a["ws_bytes"], None)
+
+
+def test_cascade_attention_validation(L):
+    """rkv_decode_attn_cascade rejects bad arguments before enqueuing."""
+    p = L.rkv_params_default(32, 8)
+    for name in ("q", "merged", "n_merged", "sel", "n_sel", "table", "lens", "out"):
+        assert _cascade(L, p, **{name: None}) == B.RKV_ERR_INVALID_ARG, name
+    assert _cascade(L, p, shared=17) == B.RKV_ERR_INVALID_ARG
+    assert _cascade(L, p, shared=-1) == B.RKV_ERR_INVALID_ARG
+    assert _cascade(L, p, max_blocks=0) == B.RKV_ERR_INVALID_ARG
+    assert _cascade(L, p, k_cap=0) == B.RKV_ERR_INVALID_ARG
+    assert _cascade(L, p, batch=-1) == B.RKV_ERR_INVALID_ARG
+    assert _cascade(L, p, q=FAKE + 4) == B.RKV_ERR_INVALID_ARG
+    assert _cascade(L, p, ws_bytes=16) == B.RKV_ERR_WORKSPACE
+    assert _cascade(L, p, ws=FAKE + 8) == B.RKV_ERR_INVALID_ARG
+    valu = L.rkv_params_default(32, 8)
+    valu.attn_impl = B.ATTN_VALU
+    assert _cascade(L, valu) == B.RKV_ERR_UNSUPPORTED
+    assert _cascade(L, p, batch=1 << 20) == B.RKV_ERR_UNSUPPORTED
+
+
+def test_cascade_workspace_size(L):
+    """The cascade workspace adds the cascade pieces, masks and private tables
+    to the plain attention workspace; with nothing shared, or a single
+    sequence, it is the plain one."""
+    p = L.rkv_params_default(64, 8)
+    plain = L.rkv_attn_workspace_size(ctypes.byref(p), 8, 1025)
+    assert L.rkv_attn_cascade_workspace_size(ctypes.byref(p), 8, 1025, 0) == plain
+    one = L.rkv_attn_workspace_size(ctypes.byref(p), 1, 1025)
+    assert L.rkv_attn_cascade_workspace_size(ctypes.byref(p), 1, 1025, 128) == one
+    big = L.rkv_attn_cascade_workspace_size(ctypes.byref(p), 8, 1025, 128)
+    # at least the private tables (lists x m_cap int32) and masks on top
+    assert big >= plain + 64 * 1025 * 4 + 64 * 4 * 4
+    assert L.rkv_attn_cascade_workspace_size(ctypes.byref(p), 8, 1025, -1) == 0

@@ -379,6 +379,60 @@ def test_attention_workspace_reused_across_shapes():
         assert torch.equal(out, ref), spec.name
 
 
+@pytest.mark.parametrize("hq,hkv,dense_boundary,extra", [
+    (8, 2, 0, 0),        # group 4: four sequences per cascade wave
+    (16, 2, 0, 0),       # group 8: two
+    (4, 2, 0, 6),        # group 2: eight; shared count named 6 past the truth
+    (32, 2, 0, 0),       # group 16: one (no reuse, same results)
+    (16, 2, 12000, 0),   # one prompt below the dense boundary
+])
+def test_cascade_matches_oracle_and_plain_attention(hq, hkv, dense_boundary, extra):
+    """rkv_decode_attn_cascade over a batch with a shared prefix: outputs
+    against the oracle (selections and merged tables are the plain path's,
+    checked too) and against rkv_decode_attn over the same tables.  The
+    batch has a sequence whose last block is the first one past the shared
+    prefix and sequences in a partly filled last group."""
+    S = 40
+    spec = synth.custom(f"cascade {hq}/{hkv}", batch=5, n_q_heads=hq, n_kv_heads=hkv,
+                        context=(20000, 9000, S * 128 + 1, 14001, 11111), steps=2,
+                        init_tokens=1024, local_tokens=3000,
+                        dense_boundary=dense_boundary, shared_prefix_pages=S,
+                        shuffle=True, config_id=144)
+    batch = synth.make_batch(spec, DEV)
+    prm, sess = make_session(batch)
+    prefill(batch, sess)
+    for t in range(spec.steps):
+        say("cascade", spec.name, "step", t)
+        lens = i32(batch.lens_at(t))
+        kn, vn = batch.new_kv_bits(t)
+        sess.append_select(batch.q_bits(t), kn, vn, lens)
+        plain = sess.attend(batch.q_bits(t), lens).clone()
+        sess.out.fill_(float("nan"))
+        got = sess.attend_cascade(batch.q_bits(t), lens, S + extra).clone()
+        torch.cuda.synchronize()
+        assert torch.isfinite(got).all()
+        scale = float(plain.abs().max())
+        assert float((got - plain).abs().max()) <= 1e-5 * scale + 1e-7
+        oracle_full_check(batch, sess, t)
+
+
+def test_cascade_without_shared_blocks_is_plain_attention():
+    """shared_blocks = 0 takes rkv_decode_attn's launches: bit-identical."""
+    spec = synth.custom("cascade none", batch=3, n_q_heads=16, n_kv_heads=2,
+                        context=(20000, 9000, 14001), steps=1, dense_boundary=0,
+                        shared_prefix_pages=20, config_id=145)
+    batch = synth.make_batch(spec, DEV)
+    prm, sess = make_session(batch)
+    prefill(batch, sess)
+    lens = i32(batch.lens_at(0))
+    kn, vn = batch.new_kv_bits(0)
+    sess.append_select(batch.q_bits(0), kn, vn, lens)
+    plain = sess.attend(batch.q_bits(0), lens).clone()
+    got = sess.attend_cascade(batch.q_bits(0), lens, 0).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(plain, got)
+
+
 def _score_rounds(groups, max_blocks, init_tokens, n_cu):
     """Representations per score wave (8 x rounds) the library picks: 32,
     halved while the scan would have fewer than two waves per compute unit."""
@@ -585,6 +639,31 @@ def test_70b_shared_prefix_full_size(t_check):
     prm, sess = make_session(batch)
     say("70B layer (8 x 128K, 64/8, shared prefix) step", t_check)
     run_to_step(batch, sess, t_check)
+    oracle_full_check(batch, sess, t_check)
+
+
+@pytest.mark.parametrize("t_check", [0, 15])
+def test_70b_shared_prefix_cascade_full_size(t_check):
+    """The 70B-shaped layer (8 x 128K, 64/8 heads, 128 shared prefix pages)
+    with the cascade attention: every sequence and KV head against the
+    oracle at the first and last step, and within rounding of
+    rkv_decode_attn."""
+    spec = synth.CONFIGS[4]
+    batch = synth.make_batch(spec, DEV)
+    prm, sess = make_session(batch)
+    prefill(batch, sess)
+    for t in range(t_check + 1):
+        lens = i32(batch.lens_at(t))
+        kn, vn = batch.new_kv_bits(t)
+        sess.append_select(batch.q_bits(t), kn, vn, lens)
+        got = sess.attend_cascade(batch.q_bits(t), lens, spec.shared_prefix_pages)
+    say("70B cascade step", t_check)
+    got = got.clone()
+    plain = sess.attend(batch.q_bits(t_check), i32(batch.lens_at(t_check))).clone()
+    torch.cuda.synchronize()
+    scale = float(plain.abs().max())
+    assert float((got - plain).abs().max()) <= 1e-5 * scale + 1e-7
+    sess.out.copy_(got)
     oracle_full_check(batch, sess, t_check)
 
 
