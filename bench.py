@@ -18,9 +18,11 @@ step's pages in the 256 MB Infinity Cache.
 
 After the headline workload (`--config`, default the Llama-3-8B-shaped
 layer) the same run measures the other workloads of the metric's 64K-128K
-range and the host tier (`--also`, default 3,4,5): each with its own steps/s,
-the roofline of its attention call and the CPU oracle on a bounded sample,
-under "configs" in the JSON line.
+range and the host tier (`--also`, default 3,4,5), each in a child process
+of its own (a workload measured after another in one process runs a few
+percent slower): each with its own steps/s, the roofline of its attention
+call and the CPU oracle on a bounded sample, under "configs" in the JSON
+line.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -34,6 +36,7 @@ import json
 import math
 import os
 import platform
+import subprocess
 import sys
 import time
 
@@ -669,6 +672,16 @@ def main():
     ap.add_argument("--also", default="3,4,5",
                     help="other workloads measured after the headline one in the "
                          "same run (comma-separated config ids; empty: none)")
+    ap.add_argument("--record-only", action="store_true",
+                    help="measure --config alone and print its record as one JSON "
+                         "line (how the --also workloads are run, each in a process "
+                         "of its own)")
+    ap.add_argument("--probe-gbs", type=float, default=0.0,
+                    help="streaming-read probe figure to report (0: measure it)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of CPU oracle steps for the cpu_baseline sample")
+    ap.add_argument("--spread-budget", type=int, default=0,
+                    help="steps timed for step_us_spread (0: up to 16 chunks of 16)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device-to-device copy first "
                          "(a known-size reference for HBM byte counters)")
@@ -693,20 +706,46 @@ def main():
         del src, dst
         log("calibration copy: 1 GiB read + 1 GiB written")
 
-    probe_gbs = stream_read_probe(dev)
-    log(f"streaming-read probe: {probe_gbs:.0f} GB/s")
+    if args.probe_gbs > 0:
+        probe_gbs = args.probe_gbs
+    else:
+        probe_gbs = stream_read_probe(dev)
+        log(f"streaming-read probe: {probe_gbs:.0f} GB/s")
 
-    head = run_workload(args, args.config, args.steps, args.warmup, 12.0, probe_gbs, dev)
+    if args.record_only:
+        rec = run_workload(args, args.config, args.steps, args.warmup, args.cpu_budget,
+                           probe_gbs, dev, spread_budget=args.spread_budget or None)
+        print(json.dumps(rec), flush=True)
+        return
+
+    head = run_workload(args, args.config, args.steps, args.warmup, args.cpu_budget,
+                        probe_gbs, dev, spread_budget=args.spread_budget or None)
+    gc.collect()
+    torch.cuda.empty_cache()
+    # each further workload in a process of its own: a workload measured
+    # after another in the same process ran 3-4% slower (the batched and 70B
+    # attention calls, in either order)
     others = {}
     extra = [int(x) for x in args.also.split(",") if x.strip()] if args.also else []
     for c in extra:
         if c == args.config:
             continue
-        gc.collect()
-        torch.cuda.empty_cache()
         steps_c = synth.CONFIGS[c].steps * (2 if synth.CONFIGS[c].steps < 32 else 1)
-        others[str(c)] = run_workload(args, c, steps_c, 16, 4.0, probe_gbs, dev,
-                                      spread_budget=steps_c)
+        cmd = [sys.executable, os.path.abspath(__file__), "--config", str(c), "--also", "",
+               "--steps", str(steps_c), "--warmup", "16", "--record-only",
+               "--probe-gbs", repr(probe_gbs), "--cpu-budget", "4.0",
+               "--spread-budget", str(steps_c), "--impl", args.impl,
+               "--split", str(args.split), "--slots", repr(args.slots),
+               "--select", args.select, "--layers", str(args.layers)]
+        if args.no_cpu_baseline:
+            cmd.append("--no-cpu-baseline")
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
+        lines = [x for x in r.stdout.splitlines() if x.startswith("{")]
+        if r.returncode != 0 or not lines:
+            log(f"config {c} failed (exit status {r.returncode})")
+            others[str(c)] = {"error": f"exit status {r.returncode}"}
+        else:
+            others[str(c)] = json.loads(lines[-1])
 
     res = {
         "metric": METRIC,
