@@ -384,6 +384,43 @@ rkv_status rkv_stage_resident(const rkv_params* params, const uint16_t* host_k,
                               hipStream_t stream);
 
 /*
+ * rkv_stage_plan / rkv_stage_copy -- rkv_stage_resident's two launches as
+ * separate calls, so that the copies can run on a side stream while the
+ * attention over the blocks already in HBM runs on the main one (the
+ * openGauss page, "Overall Solution": each round loads the retrieved blocks
+ * into HBM; here the round's attention starts on the blocks that are
+ * there).  rkv_stage_plan is the residency planner: slot state, merged table
+ * and the copy list in `workspace`.  With merged_new non-NULL (split mode)
+ * the merged table keeps only the entries whose pages are in HBM before
+ * this call's copies -- init and window blocks, kept blocks on device or
+ * already held in a slot -- in order, and merged_new [batch][n_kv_heads]
+ * [k_cap] receives, n_new [batch][n_kv_heads] per list, the staging pages
+ * of the blocks this call copies (whole blocks; attend them with
+ * rkv_decode_attn_lse and lengths that are multiples of 128).  Kept host
+ * blocks left without a slot (n_staged = -1) are in neither table.
+ * rkv_stage_copy copies the list the last rkv_stage_plan left in the same
+ * workspace (the caller orders it after that call).  Arguments, workspace
+ * (rkv_stage_workspace_size) and errors as rkv_stage_resident; n_pages is
+ * the device pool's page count.
+ */
+rkv_status rkv_stage_plan(const rkv_params* params, const int32_t* host_table,
+                          const int32_t* block_table, int32_t max_blocks,
+                          const int32_t* lens, const int32_t* sel_ids,
+                          const int32_t* n_sel, int32_t k_cap, int32_t batch,
+                          int32_t slot_cap, int32_t* slot_ids, int32_t* slot_cursor,
+                          int64_t n_pages, int64_t stage_page0, int32_t* merged,
+                          int32_t* n_merged, int32_t m_cap, int32_t* merged_new,
+                          int32_t* n_new, int32_t* n_staged, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+rkv_status rkv_stage_copy(const rkv_params* params, const uint16_t* host_k,
+                          const uint16_t* host_v, int64_t n_host_pages,
+                          const int32_t* host_table, int32_t max_blocks, int32_t k_cap,
+                          int32_t batch, int32_t slot_cap, uint16_t* k_pages,
+                          uint16_t* v_pages, int64_t n_pages, int64_t stage_page0,
+                          const void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/*
  * Bytes of pinned host memory (host_list) the copy-engine staging calls
  * below need for these sizes.
  */
@@ -489,6 +526,36 @@ rkv_status rkv_decode_attn(const rkv_params* params, const uint16_t* q,
                            const int32_t* lens, int32_t batch, float* out,
                            void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
+
+/*
+ * rkv_decode_attn_lse -- rkv_decode_attn for one part of each row's tokens,
+ * merged with a part attended before (prev_out / prev_lse) and leaving the
+ * row's log-sum-exp for a part after it.  Softmax over a union of token
+ * sets merges exactly from each set's normalized output and log-sum-exp
+ * (the CSDN survey's cascade-inference paragraph: partial results merged
+ * the FlashDecoding way), so a step's attention can start on the blocks
+ * already in HBM while the rest are still being copied (rkv_stage_plan in
+ * split mode): out = softmax over (this call's tokens and the previous
+ * part's) of V.
+ *   prev_out [batch][n_q_heads][128] fp32, prev_lse [batch][n_q_heads]: a
+ *            previous call's out and lse, or both NULL; must not be out
+ *   lse      [batch][n_q_heads] fp32 or NULL: log2 of sum_t e^{z_t} over
+ *            every token folded into out (z_t = scale * q . K_t), -inf
+ *            for none
+ *   lens     as rkv_decode_attn: the last entry of a list holds
+ *            L - 128 (ceil(L/128) - 1) tokens; to attend every entry as a
+ *            whole block (the newly staged part of a split table), pass
+ *            lengths that are multiples of 128 (e.g. 128 * m_cap)
+ * Other arguments, workspace and errors as rkv_decode_attn.
+ */
+rkv_status rkv_decode_attn_lse(const rkv_params* params, const uint16_t* q,
+                               const uint16_t* k_pages, const uint16_t* v_pages,
+                               int64_t n_pages, const int32_t* merged,
+                               const int32_t* n_merged, int32_t m_cap,
+                               const int32_t* lens, int32_t batch,
+                               const float* prev_out, const float* prev_lse,
+                               float* out, float* lse, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
 /*
  * rkv_decode_attn_cascade -- rkv_decode_attn for a batch whose sequences
  * share a prefix of pages (CSDN survey, section "Share--KV cache共享":

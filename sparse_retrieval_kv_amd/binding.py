@@ -83,6 +83,11 @@ _SIGS = {
     "rkv_stage_resident": (ctypes.c_int, [_PP, _P, _P, _I64, _P, _P, _I32, _P, _P,
                                           _P, _I32, _I32, _I32, _P, _P, _P, _P, _I64,
                                           _I64, _P, _P, _I32, _P, _P, _SZ, _P]),
+    "rkv_stage_plan": (ctypes.c_int, [_PP, _P, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _P,
+                                      _P, _I64, _I64, _P, _P, _I32, _P, _P, _P, _P, _SZ,
+                                      _P]),
+    "rkv_stage_copy": (ctypes.c_int, [_PP, _P, _P, _I64, _P, _I32, _I32, _I32, _I32, _P,
+                                      _P, _I64, _I64, _P, _SZ, _P]),
     "rkv_stage_host_list_size": (_SZ, [_PP, _I32, _I32]),
     "rkv_stage_blocks_async": (ctypes.c_int, [_PP, _P, _P, _I64, _P, _I32, _P, _P, _I32,
                                               _I32, _P, _P, _I64, _I64, _P, _SZ, _P, _P,
@@ -94,6 +99,8 @@ _SIGS = {
     "rkv_attn_workspace_size": (_SZ, [_PP, _I32, _I32]),
     "rkv_decode_attn": (ctypes.c_int, [_PP, _P, _P, _P, _I64, _P, _P, _I32, _P, _I32,
                                        _P, _P, _SZ, _P]),
+    "rkv_decode_attn_lse": (ctypes.c_int, [_PP, _P, _P, _P, _I64, _P, _P, _I32, _P, _I32,
+                                           _P, _P, _P, _P, _P, _SZ, _P]),
     "rkv_attn_cascade_workspace_size": (_SZ, [_PP, _I32, _I32, _I32]),
     "rkv_decode_attn_cascade": (ctypes.c_int, [_PP, _P, _P, _P, _I64, _P, _P, _I32, _P,
                                                _P, _I32, _P, _I32, _I32, _P, _I32, _P,
@@ -367,6 +374,54 @@ def stage_resident(p: Params, host_k, host_v, host_table, block_table, lens,
         _ptr(workspace, None, "workspace", None, d), ws_bytes, _stream(k_pages)))
 
 
+def stage_plan(p: Params, host_table, block_table, lens, sel_ids, n_sel, slot_ids,
+               slot_cursor, n_pages: int, stage_page0: int, merged, n_merged, workspace,
+               merged_new=None, n_new=None, n_staged=None):
+    """The residency planner alone (rkv_stage_plan); with merged_new / n_new,
+    split mode: merged keeps the entries in HBM before the copies, merged_new
+    the staging pages of the blocks copied now."""
+    batch, mb = block_table.shape
+    d = block_table.device
+    hkv = p.n_kv_heads
+    ws_bytes = workspace.numel() * workspace.element_size()
+    k_cap = sel_ids.shape[-1]
+    _check(lib().rkv_stage_plan(
+        ctypes.byref(p), _ptr(host_table, torch.int32, "host_table", (batch, mb), d),
+        _ptr(block_table, torch.int32, "block_table", None, d), mb,
+        _ptr(lens, torch.int32, "lens", (batch,), d),
+        _ptr(sel_ids, torch.int32, "sel_ids", (batch, hkv, k_cap), d),
+        _ptr(n_sel, torch.int32, "n_sel", (batch, hkv), d), k_cap, batch,
+        slot_ids.shape[-1],
+        _ptr(slot_ids, torch.int32, "slot_ids", (batch, hkv, slot_ids.shape[-1]), d),
+        _ptr(slot_cursor, torch.int32, "slot_cursor", (batch, hkv), d),
+        n_pages, stage_page0,
+        _ptr(merged, torch.int32, "merged", (batch, hkv, merged.shape[-1]), d),
+        _ptr(n_merged, torch.int32, "n_merged", (batch, hkv), d), merged.shape[-1],
+        None if merged_new is None else _ptr(merged_new, torch.int32, "merged_new",
+                                             (batch, hkv, k_cap), d),
+        None if n_new is None else _ptr(n_new, torch.int32, "n_new", (batch, hkv), d),
+        None if n_staged is None else _ptr(n_staged, torch.int32, "n_staged",
+                                           (batch, hkv), d),
+        _ptr(workspace, None, "workspace", None, d), ws_bytes, _stream(block_table)))
+
+
+def stage_copy(p: Params, host_k, host_v, host_table, k_cap: int, slot_cap: int,
+               k_pages, v_pages, stage_page0: int, workspace):
+    """The copies of the list the last stage_plan left in `workspace`
+    (rkv_stage_copy), on the current stream."""
+    batch, mb = host_table.shape
+    d = k_pages.device
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().rkv_stage_copy(
+        ctypes.byref(p), _host_ptr(host_k, "host_k", _pool_shape(p, host_k)),
+        _host_ptr(host_v, "host_v", _pool_shape(p, host_k)), host_k.shape[0],
+        _ptr(host_table, torch.int32, "host_table", (batch, mb), d), mb, k_cap, batch,
+        slot_cap, _ptr(k_pages, torch.int16, "k_pages", _pool_shape(p, k_pages), d),
+        _ptr(v_pages, torch.int16, "v_pages", _pool_shape(p, k_pages), d),
+        k_pages.shape[0], stage_page0, _ptr(workspace, None, "workspace", None, d),
+        ws_bytes, _stream(k_pages)))
+
+
 def stage_host_list_size(p: Params, batch: int, k_cap: int) -> int:
     return lib().rkv_stage_host_list_size(ctypes.byref(p), batch, k_cap)
 
@@ -466,6 +521,31 @@ def decode_attn(p: Params, q, k_pages, v_pages, merged, n_merged, lens, out,
         _ptr(lens, torch.int32, "lens", (batch,), d), batch,
         _ptr(out, torch.float32, "out", rows, d), _ptr(workspace, None, "workspace", None, d),
         ws_bytes, _stream(q)))
+
+
+def decode_attn_lse(p: Params, q, k_pages, v_pages, merged, n_merged, lens, out,
+                    workspace, prev_out=None, prev_lse=None, lse=None):
+    """rkv_decode_attn_lse: attention over the merged lists, folded with a
+    previous part (prev_out, prev_lse) and leaving the rows' log-sum-exp."""
+    batch = lens.shape[0]
+    d = q.device
+    hkv = p.n_kv_heads
+    rows = (batch, p.n_q_heads, HEAD_DIM)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().rkv_decode_attn_lse(
+        ctypes.byref(p), _ptr(q, torch.int16, "q", rows, d),
+        _ptr(k_pages, torch.int16, "k_pages", _pool_shape(p, k_pages), d),
+        _ptr(v_pages, torch.int16, "v_pages", _pool_shape(p, k_pages), d),
+        k_pages.shape[0],
+        _ptr(merged, torch.int32, "merged", (batch, hkv, merged.shape[-1]), d),
+        _ptr(n_merged, torch.int32, "n_merged", (batch, hkv), d), merged.shape[-1],
+        _ptr(lens, torch.int32, "lens", (batch,), d), batch,
+        None if prev_out is None else _ptr(prev_out, torch.float32, "prev_out", rows, d),
+        None if prev_lse is None else _ptr(prev_lse, torch.float32, "prev_lse",
+                                           rows[:2], d),
+        _ptr(out, torch.float32, "out", rows, d),
+        None if lse is None else _ptr(lse, torch.float32, "lse", rows[:2], d),
+        _ptr(workspace, None, "workspace", None, d), ws_bytes, _stream(q)))
 
 
 def attn_cascade_workspace_size(p: Params, batch: int, m_cap: int,

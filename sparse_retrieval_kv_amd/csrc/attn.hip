@@ -138,6 +138,11 @@ struct AttnArgs {
   int c_shared;            // shared blocks named by the caller
   int c_waves;             // n_kv * c_groups * c_chunks, or 0
   int64_t c_slot0;         // first cascade slot; wave cw writes c_q slots
+  // a previous part of every row's attention to fold in (prev_lse null:
+  // none), and where to leave each row's log-sum-exp (null: nowhere)
+  const float* prev_out;   // [batch][n_q][128], normalized
+  const float* prev_lse;   // [batch][n_q]: log2 of the row's softmax sum
+  float* lse_out;          // [batch][n_q]
 };
 
 // ---------------------------------------------------------------------------
@@ -1301,10 +1306,20 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a,
     a2.w = __shfl_xor(acc.w, off);
     lse_fold(m, l, acc, m2, l2, a2);
   }
+  // a previous part of the row (its normalized output and log2 softmax
+  // sum): one more piece with m = its log-sum-exp and l = 1
+  if (a.prev_lse) {  // uniform
+    const float pm = a.prev_lse[bq];
+    const float4 po =
+        *reinterpret_cast<const float4*>(a.prev_out + (int64_t)bq * kDim + dim0);
+    if (pm > kNegInf) lse_fold(m, l, acc, pm, 1.f, po);
+  }
   if (pg == 0) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
     *dst = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
+  if (a.lse_out && slice == 0 && lane == 0)
+    a.lse_out[bq] = l > 0.f ? m + log2f(l) : kNegInf;
 }
 
 // Shared-prefix cascade, first launch: per (sequence, KV head) list, the
@@ -1468,6 +1483,9 @@ AttnArgs attn_args(const Method& m, const AttnPlan& plan, float scale,
   a.c_words = a.c_q = a.c_groups = a.c_chunks = a.c_chunk_blocks = 0;
   a.c_shared = a.c_waves = 0;
   a.c_slot0 = 0;
+  a.prev_out = nullptr;
+  a.prev_lse = nullptr;
+  a.lse_out = nullptr;
   return a;
 }
 
@@ -1487,10 +1505,15 @@ hipError_t launch_decode_attn(const Method& m, bool use_mfma,
                               const uint16_t* v_pages, int64_t n_pages,
                               const int32_t* merged, const int32_t* n_merged,
                               int m_cap, const int32_t* lens, int batch,
-                              float* out, void* workspace, hipStream_t stream) {
+                              float* out, void* workspace, hipStream_t stream,
+                              const float* prev_out, const float* prev_lse,
+                              float* lse_out) {
   if (batch == 0) return hipSuccess;
-  const AttnArgs a = attn_args(m, plan, scale, q, k_pages, v_pages, n_pages, merged,
-                               n_merged, m_cap, lens, batch, workspace);
+  AttnArgs a = attn_args(m, plan, scale, q, k_pages, v_pages, n_pages, merged,
+                         n_merged, m_cap, lens, batch, workspace);
+  a.prev_out = prev_out;
+  a.prev_lse = prev_lse;
+  a.lse_out = lse_out;
   const int64_t waves =
       plan.per_list > 0 ? (int64_t)batch * m.n_kv_heads * plan.per_list : plan.n_waves;
   const dim3 grid((unsigned)waves), block(64);

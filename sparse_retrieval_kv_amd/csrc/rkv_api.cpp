@@ -468,6 +468,95 @@ rkv_status rkv_stage_resident(const rkv_params* params, const uint16_t* host_k,
                     "rkv_stage_resident launch");
 }
 
+rkv_status rkv_stage_plan(const rkv_params* params, const int32_t* host_table,
+                          const int32_t* block_table, int32_t max_blocks,
+                          const int32_t* lens, const int32_t* sel_ids,
+                          const int32_t* n_sel, int32_t k_cap, int32_t batch,
+                          int32_t slot_cap, int32_t* slot_ids, int32_t* slot_cursor,
+                          int64_t n_pages, int64_t stage_page0, int32_t* merged,
+                          int32_t* n_merged, int32_t m_cap, int32_t* merged_new,
+                          int32_t* n_new, int32_t* n_staged, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  rkv::Method m;
+  RKV_TRY(check_params(params, &m));
+  RKV_TRY(check_sizes(batch, max_blocks));
+  RKV_REQUIRE(host_table && block_table && lens && sel_ids && n_sel && slot_ids &&
+                  slot_cursor && merged && n_merged,
+              RKV_ERR_INVALID_ARG, "a required pointer is NULL");
+  RKV_REQUIRE((merged_new == nullptr) == (n_new == nullptr), RKV_ERR_INVALID_ARG,
+              "merged_new and n_new must be given together");
+  RKV_REQUIRE(k_cap >= 1 && k_cap <= RKV_MAX_BLOCKS, RKV_ERR_INVALID_ARG,
+              "k_cap %d outside [1, %d]", k_cap, RKV_MAX_BLOCKS);
+  RKV_REQUIRE(slot_cap >= 1 && slot_cap <= RKV_MAX_BLOCKS, RKV_ERR_INVALID_ARG,
+              "slot_cap %d outside [1, %d]", slot_cap, RKV_MAX_BLOCKS);
+  RKV_REQUIRE(m_cap >= max_blocks, RKV_ERR_INVALID_ARG,
+              "m_cap %d below max_blocks %d", m_cap, max_blocks);
+  RKV_REQUIRE(n_pages >= 1, RKV_ERR_INVALID_ARG, "n_pages %lld < 1",
+              (long long)n_pages);
+  RKV_TRY(check_extent(params, batch, max3(m_cap, k_cap, slot_cap)));
+  RKV_REQUIRE(stage_page0 >= 0 &&
+                  stage_page0 + (int64_t)batch * slot_cap <= n_pages &&
+                  stage_page0 + (int64_t)batch * slot_cap <= (int64_t)INT32_MAX,
+              RKV_ERR_INVALID_ARG,
+              "staging pages [%lld, +%lld) do not fit in the %lld-page pool",
+              (long long)stage_page0, (long long)batch * slot_cap,
+              (long long)n_pages);
+  const size_t need = rkv_stage_workspace_size(params, batch, k_cap);
+  RKV_REQUIRE(workspace_bytes >= need && (need == 0 || workspace),
+              RKV_ERR_WORKSPACE, "staging workspace %zu bytes, need %zu",
+              workspace_bytes, need);
+  RKV_REQUIRE(aligned16(workspace), RKV_ERR_INVALID_ARG,
+              "workspace is not 16-byte aligned");
+  return hip_status(rkv::launch_stage_plan(m, host_table, block_table, lens, max_blocks,
+                                           sel_ids, n_sel, k_cap, batch, slot_cap,
+                                           slot_ids, slot_cursor, stage_page0, merged,
+                                           n_merged, m_cap, n_staged, workspace, stream,
+                                           merged_new, n_new),
+                    "rkv_stage_plan launch");
+}
+
+rkv_status rkv_stage_copy(const rkv_params* params, const uint16_t* host_k,
+                          const uint16_t* host_v, int64_t n_host_pages,
+                          const int32_t* host_table, int32_t max_blocks, int32_t k_cap,
+                          int32_t batch, int32_t slot_cap, uint16_t* k_pages,
+                          uint16_t* v_pages, int64_t n_pages, int64_t stage_page0,
+                          const void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  rkv::Method m;
+  RKV_TRY(check_params(params, &m));
+  RKV_TRY(check_sizes(batch, max_blocks));
+  RKV_TRY(check_pool(k_pages, n_pages, "k_pages"));
+  RKV_TRY(check_pool(v_pages, n_pages, "v_pages"));
+  RKV_TRY(check_pool(host_k, n_host_pages, "host_k"));
+  RKV_TRY(check_pool(host_v, n_host_pages, "host_v"));
+  RKV_REQUIRE(host_table != nullptr, RKV_ERR_INVALID_ARG, "host_table is NULL");
+  RKV_REQUIRE(k_cap >= 1 && k_cap <= RKV_MAX_BLOCKS, RKV_ERR_INVALID_ARG,
+              "k_cap %d outside [1, %d]", k_cap, RKV_MAX_BLOCKS);
+  RKV_REQUIRE(slot_cap >= 1 && slot_cap <= RKV_MAX_BLOCKS, RKV_ERR_INVALID_ARG,
+              "slot_cap %d outside [1, %d]", slot_cap, RKV_MAX_BLOCKS);
+  RKV_TRY(check_extent(params, batch, max3(k_cap, slot_cap, 1)));
+  RKV_REQUIRE(stage_page0 >= 0 &&
+                  stage_page0 + (int64_t)batch * slot_cap <= n_pages &&
+                  stage_page0 + (int64_t)batch * slot_cap <= (int64_t)INT32_MAX,
+              RKV_ERR_INVALID_ARG,
+              "staging pages [%lld, +%lld) do not fit in the %lld-page pool",
+              (long long)stage_page0, (long long)batch * slot_cap,
+              (long long)n_pages);
+  const size_t need = rkv_stage_workspace_size(params, batch, k_cap);
+  RKV_REQUIRE(workspace_bytes >= need && (need == 0 || workspace),
+              RKV_ERR_WORKSPACE, "staging workspace %zu bytes, need %zu",
+              workspace_bytes, need);
+  RKV_REQUIRE(aligned16(workspace), RKV_ERR_INVALID_ARG,
+              "workspace is not 16-byte aligned");
+  const uint16_t* dev_view[2] = {nullptr, nullptr};
+  RKV_TRY(host_views(host_k, host_v, dev_view));
+  return hip_status(rkv::launch_stage_copy(m, dev_view[0], dev_view[1], n_host_pages,
+                                           host_table, max_blocks, k_cap, batch,
+                                           slot_cap, k_pages, v_pages, n_pages,
+                                           stage_page0, workspace, stream),
+                    "rkv_stage_copy launch");
+}
+
 size_t rkv_stage_host_list_size(const rkv_params* params, int32_t batch,
                                 int32_t k_cap) {
   if (!params || params->n_kv_heads <= 0 || batch <= 0 || k_cap <= 0) return 0;
@@ -694,6 +783,52 @@ rkv_status rkv_decode_attn(const rkv_params* params, const uint16_t* q,
                               merged, n_merged, m_cap, lens, batch, out,
                               workspace, stream),
       "rkv_decode_attn launch");
+}
+
+rkv_status rkv_decode_attn_lse(const rkv_params* params, const uint16_t* q,
+                               const uint16_t* k_pages, const uint16_t* v_pages,
+                               int64_t n_pages, const int32_t* merged,
+                               const int32_t* n_merged, int32_t m_cap,
+                               const int32_t* lens, int32_t batch,
+                               const float* prev_out, const float* prev_lse,
+                               float* out, float* lse, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  rkv::Method m;
+  RKV_TRY(check_params(params, &m));
+  RKV_REQUIRE(batch >= 0, RKV_ERR_INVALID_ARG, "batch %d < 0", batch);
+  RKV_REQUIRE(m_cap >= 1 && m_cap <= RKV_MAX_BLOCKS, RKV_ERR_INVALID_ARG,
+              "m_cap %d outside [1, %d]", m_cap, RKV_MAX_BLOCKS);
+  RKV_TRY(check_pool(k_pages, n_pages, "k_pages"));
+  RKV_TRY(check_pool(v_pages, n_pages, "v_pages"));
+  RKV_REQUIRE(q && merged && n_merged && lens && out, RKV_ERR_INVALID_ARG,
+              "q, merged, n_merged, lens and out must not be NULL");
+  RKV_REQUIRE((prev_out == nullptr) == (prev_lse == nullptr), RKV_ERR_INVALID_ARG,
+              "prev_out and prev_lse must be given together");
+  RKV_REQUIRE(aligned16(q) && aligned16(out) && aligned16(prev_out),
+              RKV_ERR_INVALID_ARG, "q, out and prev_out must be 16-byte aligned");
+  RKV_REQUIRE(prev_out == nullptr || prev_out != out, RKV_ERR_INVALID_ARG,
+              "prev_out must not be out");
+  const bool use_mfma = params->attn_impl != RKV_ATTN_VALU;
+  RKV_REQUIRE(use_mfma || m.group == 1 || m.group == 2 || m.group == 4 ||
+                  m.group == 8,
+              RKV_ERR_UNSUPPORTED,
+              "the VALU attention variant supports groups 1, 2, 4 and 8 (got %d)",
+              m.group);
+  RKV_TRY(check_extent(params, batch, m_cap));
+  const rkv::AttnPlan plan = rkv::plan_attention(
+      batch, m.n_q_heads, m.n_kv_heads, params->split_waves, m_cap,
+      rkv::device_cu_count());
+  const size_t need = plan.total_bytes;
+  RKV_REQUIRE(workspace_bytes >= need && (need == 0 || workspace != nullptr),
+              RKV_ERR_WORKSPACE, "attention workspace %zu bytes, need %zu",
+              workspace_bytes, need);
+  RKV_REQUIRE(aligned16(workspace), RKV_ERR_INVALID_ARG,
+              "workspace is not 16-byte aligned");
+  return hip_status(
+      rkv::launch_decode_attn(m, use_mfma, plan, params->scale, q, k_pages, v_pages,
+                              n_pages, merged, n_merged, m_cap, lens, batch, out,
+                              workspace, stream, prev_out, prev_lse, lse),
+      "rkv_decode_attn_lse launch");
 }
 
 size_t rkv_attn_cascade_workspace_size(const rkv_params* params, int32_t batch,

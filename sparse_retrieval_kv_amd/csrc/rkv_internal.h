@@ -121,7 +121,16 @@ hipError_t launch_stage_plan(const Method& m, const int32_t* host_table,
                              int slot_cap, int32_t* slot_ids, int32_t* slot_cursor,
                              int64_t stage_page0, int32_t* merged,
                              int32_t* n_merged, int m_cap, int32_t* n_staged,
-                             void* workspace, hipStream_t stream);
+                             void* workspace, hipStream_t stream,
+                             int32_t* merged_new = nullptr, int32_t* n_new = nullptr);
+// The copy launch of launch_stage_resident alone, over the copy list a
+// launch_stage_plan left in `workspace`.
+hipError_t launch_stage_copy(const Method& m, const uint16_t* host_k,
+                             const uint16_t* host_v, int64_t n_host_pages,
+                             const int32_t* host_table, int max_blocks, int k_cap,
+                             int batch, int slot_cap, uint16_t* k_pages,
+                             uint16_t* v_pages, int64_t n_pages, int64_t stage_page0,
+                             const void* workspace, hipStream_t stream);
 
 // Copy-engine staging from a host copy of a list: kept ids (pairs null; the
 // r-th kept block goes to slot r) or (block, slot) pairs, rows of `row`
@@ -186,7 +195,9 @@ hipError_t launch_decode_attn(const Method& m, bool use_mfma,
                               const uint16_t* v_pages, int64_t n_pages,
                               const int32_t* merged, const int32_t* n_merged,
                               int m_cap, const int32_t* lens, int batch,
-                              float* out, void* workspace, hipStream_t stream);
+                              float* out, void* workspace, hipStream_t stream,
+                              const float* prev_out = nullptr,
+                              const float* prev_lse = nullptr, float* lse_out = nullptr);
 
 // Top-k + merge folded into the attention launch, for the shapes
 // fused_select_attn_ok accepts (a batch of one, MFMA, per-head selection,

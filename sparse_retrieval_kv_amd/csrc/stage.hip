@@ -122,6 +122,11 @@ struct ResArgs {
   int32_t* merged;
   int32_t* n_merged;
   int m_cap;
+  // split mode (non-null): merged keeps the entries whose pages are in HBM
+  // before this call's copies; merged_new [bh][k_cap] gets the staging pages
+  // of the blocks copied now
+  int32_t* merged_new;
+  int32_t* n_new;
 };
 
 // Position of this thread's flag among the set flags of the workgroup (in
@@ -253,10 +258,40 @@ __global__ __launch_bounds__(kPlanThreads) void stage_plan_kernel(ResArgs a) {
   // the block costs no copy if it is kept again later
   if (tid == 0 && n_cp > 0) a.slot_cursor[bh] = (free_slots[n_cp - 1] + 1) % S;
   const int cnt = write_fixed_entries_stage(R, k, trow, mrow);
+  int n_res = cnt;
+  if (a.merged_new) {  // uniform: split the table
+    // positions of the entries copied now (the kept-block bits are no
+    // longer needed: reused as a position bitmap)
+    __syncthreads();
+    for (int i = tid; i < RKV_MAX_BLOCKS / 32; i += kPlanThreads) selbits[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < n_cp; i += kPlanThreads) {
+      const int e = R.n_init + new_ranks[i];
+      atomicOr(&selbits[e >> 5], 1u << (e & 31));
+    }
+    int32_t* nrow = a.merged_new + (int64_t)bh * k_cap;
+    for (int i = tid; i < n_cp; i += kPlanThreads)
+      nrow[i] = (int32_t)(page0 + free_slots[i]);
+    __syncthreads();
+    // the other entries, in order, compacted in place (every value of a
+    // round is read before the round's scan, whose barrier precedes the
+    // writes, and a round writes only below its own first entry)
+    n_res = 0;
+    for (int base = 0; base < cnt; base += kPlanThreads) {
+      const int e = base + tid;
+      const int v = e < cnt ? mrow[e] : -1;
+      const bool keep = e < cnt && v != -1 && !bit(selbits, e);
+      int tot;
+      const int pos = plan_scan(keep, sh, &tot);
+      if (keep) mrow[n_res + pos] = v;
+      n_res += tot;
+    }
+  }
   if (tid == 0) {
-    a.n_merged[bh] = cnt;
+    a.n_merged[bh] = n_res;
     a.n_copies[bh] = n_cp;
     if (a.n_staged) a.n_staged[bh] = n_new > n_cp ? -1 : n_cp;
+    if (a.merged_new) a.n_new[bh] = n_cp;
   }
 }
 
@@ -379,6 +414,8 @@ ResArgs resident_args(const Method& m, const int32_t* host_table, const int32_t*
   a.merged = merged;
   a.n_merged = n_merged;
   a.m_cap = m_cap;
+  a.merged_new = nullptr;
+  a.n_new = nullptr;
   return a;
 }
 
@@ -391,14 +428,37 @@ hipError_t launch_stage_plan(const Method& m, const int32_t* host_table,
                              int slot_cap, int32_t* slot_ids, int32_t* slot_cursor,
                              int64_t stage_page0, int32_t* merged,
                              int32_t* n_merged, int m_cap, int32_t* n_staged,
-                             void* workspace, hipStream_t stream) {
+                             void* workspace, hipStream_t stream, int32_t* merged_new,
+                             int32_t* n_new) {
   const int lists = batch * m.n_kv_heads;
   if (lists == 0) return hipSuccess;
-  const ResArgs a = resident_args(m, host_table, table, lens, max_blocks, sel_ids, n_sel,
-                                  k_cap, batch, slot_cap, slot_ids, slot_cursor,
-                                  stage_page0, merged, n_merged, m_cap, n_staged,
-                                  workspace);
+  ResArgs a = resident_args(m, host_table, table, lens, max_blocks, sel_ids, n_sel,
+                            k_cap, batch, slot_cap, slot_ids, slot_cursor, stage_page0,
+                            merged, n_merged, m_cap, n_staged, workspace);
+  a.merged_new = merged_new;
+  a.n_new = n_new;
   hipLaunchKernelGGL(stage_plan_kernel, dim3(lists), dim3(kPlanThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_stage_copy(const Method& m, const uint16_t* host_k,
+                             const uint16_t* host_v, int64_t n_host_pages,
+                             const int32_t* host_table, int max_blocks, int k_cap,
+                             int batch, int slot_cap, uint16_t* k_pages,
+                             uint16_t* v_pages, int64_t n_pages, int64_t stage_page0,
+                             const void* workspace, hipStream_t stream) {
+  const int lists = batch * m.n_kv_heads;
+  if (lists == 0) return hipSuccess;
+  const int2* copies = static_cast<const int2*>(workspace);
+  const int32_t* n_copies = reinterpret_cast<const int32_t*>(
+      static_cast<const char*>(workspace) + (size_t)lists * k_cap * sizeof(int2));
+  const int64_t items = (int64_t)lists * k_cap;
+  hipLaunchKernelGGL(stage_copy_kernel, dim3((unsigned)items), dim3(kStageThreads), 0,
+                     stream, reinterpret_cast<const uint4*>(host_k),
+                     reinterpret_cast<const uint4*>(host_v), n_host_pages, host_table,
+                     max_blocks, copies, n_copies, k_cap, slot_cap, m.n_kv_heads,
+                     reinterpret_cast<uint4*>(k_pages), reinterpret_cast<uint4*>(v_pages),
+                     n_pages, stage_page0);
   return hipGetLastError();
 }
 

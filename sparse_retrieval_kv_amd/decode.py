@@ -270,6 +270,50 @@ class HostTierSession(DecodeSession):
                         self.reps, self.block_table, lens, self.sel_ids,
                         self.n_sel, None, None, self.prompt_lens, self.ws_select)
 
+    def step_overlapped(self, q, k_new, v_new, lens):
+        """One decode step whose copies overlap the attention over the blocks
+        already in HBM: the residency planner in split mode on the current
+        stream, the copies of the blocks new to the kept set on the side
+        stream while the current stream attends the rest
+        (rkv_decode_attn_lse), then the newly staged blocks folded in by
+        log-sum-exp.  The same result as step() up to rounding (the softmax
+        partials are merged in another grouping); the same slot state.
+        Gather-kernel staging with residency only."""
+        if self.side is None or not self.resident or self.copy_mode != "kernel":
+            raise ValueError("the overlapped step needs the side stream, residency "
+                             "and the gather-kernel staging")
+        dev = self.k_pages.device
+        if getattr(self, "merged_new", None) is None:
+            hkv = self.p.n_kv_heads
+            self.merged_new = torch.zeros((self.batch, hkv, self.k_cap),
+                                          dtype=torch.int32, device=dev)
+            self.n_new = torch.zeros((self.batch, hkv), dtype=torch.int32, device=dev)
+            self.out_res = torch.zeros_like(self.out)
+            self.lse_res = torch.zeros(self.out.shape[:2], dtype=torch.float32,
+                                       device=dev)
+            # every newly staged entry is a whole block
+            self.lens_whole = torch.full((self.batch,), 128 * self.k_cap,
+                                         dtype=torch.int32, device=dev)
+        self.append_select(q, k_new, v_new, lens)
+        B.stage_plan(self.p, self.host_table, self.block_table, lens, self.sel_ids,
+                     self.n_sel, self.slot_ids, self.slot_cursor, self.k_pages.shape[0],
+                     self.stage_page0, self.merged, self.n_merged, self.ws_stage,
+                     self.merged_new, self.n_new, self.n_staged)
+        main = torch.cuda.current_stream(dev)
+        self.side.wait_stream(main)
+        with torch.cuda.stream(self.side):
+            B.stage_copy(self.p, self.host_k, self.host_v, self.host_table, self.k_cap,
+                         self.slot_cap, self.k_pages, self.v_pages, self.stage_page0,
+                         self.ws_stage)
+        B.decode_attn_lse(self.p, q, self.k_pages, self.v_pages, self.merged,
+                          self.n_merged, lens, self.out_res, self.ws_attn,
+                          lse=self.lse_res)
+        main.wait_stream(self.side)
+        B.decode_attn_lse(self.p, q, self.k_pages, self.v_pages, self.merged_new,
+                          self.n_new, self.lens_whole, self.out, self.ws_attn,
+                          prev_out=self.out_res, prev_lse=self.lse_res)
+        return self.out
+
     def step(self, q, k_new, v_new, lens):
         self.append_select(q, k_new, v_new, lens)
         if self.side is None or self.copy_mode == "memcpy":

@@ -742,6 +742,52 @@ def test_host_tier_small(resident, copy_mode):
         oracle_full_check(batch, sess, t, host=host)
 
 
+@pytest.mark.parametrize("slot_mult", [1, 2])
+def test_host_tier_overlapped_step(slot_mult):
+    """The step whose copies overlap the attention over the blocks already in
+    HBM (the planner in split mode, rkv_stage_copy on the side stream,
+    rkv_decode_attn_lse over the resident entries, then over the newly
+    staged ones with the first part folded in): the same selections and slot
+    state as the plain step, outputs within rounding of it and against the
+    oracle, and split tables that hold exactly the plain table's pages (the
+    resident ones in the plain order, the trailing block last)."""
+    spec = synth.scaled(synth.CONFIGS[5], batch=2, context=(20000, 23000), steps=6,
+                        plant_range=(8, 90), plant_count=5, local_tokens=7192,
+                        topk_ppm=200_000, dense_boundary=0, config_id=104)
+    say(f"host tier overlapped step (slots {slot_mult} x k_cap)")
+    batch_a, _, sess_a = make_host_session(spec, resident=True, slot_mult=slot_mult)
+    batch_b, host_b, sess_b = make_host_session(spec, resident=True, slot_mult=slot_mult)
+    for t in range(6):
+        step(batch_a, sess_a, t)
+        lens = i32(batch_b.lens_at(t))
+        kn, vn = batch_b.new_kv_bits(t)
+        sess_b.out.fill_(float("nan"))
+        sess_b.step_overlapped(batch_b.q_bits(t), kn, vn, lens)
+        torch.cuda.synchronize()
+        assert torch.equal(sess_a.n_sel, sess_b.n_sel), t
+        assert torch.equal(sess_a.slot_ids, sess_b.slot_ids), t
+        assert torch.equal(sess_a.slot_cursor, sess_b.slot_cursor), t
+        assert torch.equal(sess_a.n_staged, sess_b.n_staged), t
+        ma, na = sess_a.merged.cpu().numpy(), sess_a.n_merged.cpu().numpy()
+        mr, nr = sess_b.merged.cpu().numpy(), sess_b.n_merged.cpu().numpy()
+        mn, nn = sess_b.merged_new.cpu().numpy(), sess_b.n_new.cpu().numpy()
+        for b in range(2):
+            for h in range(8):
+                plain = [int(x) for x in ma[b, h, :na[b, h]] if x >= 0]
+                res = [int(x) for x in mr[b, h, :nr[b, h]]]
+                new = [int(x) for x in mn[b, h, :nn[b, h]]]
+                assert sorted(plain) == sorted(res + new), (t, b, h)
+                assert [x for x in plain if x not in set(new)] == res, (t, b, h)
+                assert res[-1] == plain[-1], (t, b, h)
+        scale = float(sess_a.out.abs().max())
+        assert float((sess_b.out - sess_a.out).abs().max()) <= 1e-5 * scale + 1e-7, t
+        if t in (0, 5):
+            # the oracle check reads the whole merged table: the plain one
+            sess_b.merged.copy_(sess_a.merged)
+            sess_b.n_merged.copy_(sess_a.n_merged)
+            oracle_full_check(batch_b, sess_b, t, host=host_b)
+
+
 def mirror_residency(slots, cursor, kept, on_host):
     """The slot policy of rkv_stage_resident, restated: slots holding a kept
     host block keep it; the other kept host blocks, ascending, take the slots
