@@ -430,3 +430,67 @@ def test_cascade_workspace_size(L):
     # at least the private tables (lists x m_cap int32) and masks on top
     assert big >= plain + 64 * 1025 * 4 + 64 * 4 * 4
     assert L.rkv_attn_cascade_workspace_size(ctypes.byref(p), 8, 1025, -1) == 0
+
+
+def test_split_staging_and_lse_attention_validation(L):
+    """rkv_stage_plan, rkv_stage_copy and rkv_decode_attn_lse reject bad
+    arguments before enqueuing."""
+    p = L.rkv_params_default(32, 8)
+    ws = L.rkv_stage_workspace_size(ctypes.byref(p), 2, 50)
+
+    def plan(**kw):
+        a = dict(host_table=FAKE, table=FAKE, max_blocks=100, lens=FAKE, sel=FAKE,
+                 n_sel=FAKE, k_cap=50, batch=2, slot_cap=60, slots=FAKE, cursor=FAKE,
+                 n_pages=1000, page0=500, merged=FAKE, n_merged=FAKE, m_cap=100,
+                 merged_new=FAKE, n_new=FAKE, n_staged=None, ws=FAKE, ws_bytes=ws)
+        a.update(kw)
+        return L.rkv_stage_plan(ctypes.byref(p), a["host_table"], a["table"],
+                                a["max_blocks"], a["lens"], a["sel"], a["n_sel"],
+                                a["k_cap"], a["batch"], a["slot_cap"], a["slots"],
+                                a["cursor"], a["n_pages"], a["page0"], a["merged"],
+                                a["n_merged"], a["m_cap"], a["merged_new"], a["n_new"],
+                                a["n_staged"], a["ws"], a["ws_bytes"], None)
+
+    assert plan(merged_new=None) == B.RKV_ERR_INVALID_ARG  # n_new without merged_new
+    assert plan(n_new=None) == B.RKV_ERR_INVALID_ARG
+    assert plan(host_table=None) == B.RKV_ERR_INVALID_ARG
+    assert plan(m_cap=99) == B.RKV_ERR_INVALID_ARG
+    assert plan(page0=1000 - 119) == B.RKV_ERR_INVALID_ARG  # 2 x 60 slots do not fit
+    assert plan(ws_bytes=ws - 1) == B.RKV_ERR_WORKSPACE
+    assert plan(k_cap=0) == B.RKV_ERR_INVALID_ARG
+
+    def copy(**kw):
+        a = dict(hk=FAKE, hv=FAKE, n_host=100, host_table=FAKE, max_blocks=100, k_cap=50,
+                 batch=2, slot_cap=60, k=FAKE, v=FAKE, n_pages=1000, page0=500, ws=FAKE,
+                 ws_bytes=ws)
+        a.update(kw)
+        return L.rkv_stage_copy(ctypes.byref(p), a["hk"], a["hv"], a["n_host"],
+                                a["host_table"], a["max_blocks"], a["k_cap"], a["batch"],
+                                a["slot_cap"], a["k"], a["v"], a["n_pages"], a["page0"],
+                                a["ws"], a["ws_bytes"], None)
+
+    assert copy(hk=None) == B.RKV_ERR_INVALID_ARG
+    assert copy(host_table=None) == B.RKV_ERR_INVALID_ARG
+    assert copy(page0=-1) == B.RKV_ERR_INVALID_ARG
+    assert copy(ws_bytes=0) == B.RKV_ERR_WORKSPACE
+    assert copy(slot_cap=0) == B.RKV_ERR_INVALID_ARG
+
+    need = L.rkv_attn_workspace_size(ctypes.byref(p), 2, 16)
+
+    def attn(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, n_pages=10, merged=FAKE, n_merged=FAKE, m_cap=16,
+                 lens=FAKE, batch=2, prev_out=FAKE + 4096, prev_lse=FAKE + 8192,
+                 out=FAKE, lse=None, ws=FAKE, ws_bytes=need)
+        a.update(kw)
+        return L.rkv_decode_attn_lse(ctypes.byref(p), a["q"], a["k"], a["v"],
+                                     a["n_pages"], a["merged"], a["n_merged"], a["m_cap"],
+                                     a["lens"], a["batch"], a["prev_out"], a["prev_lse"],
+                                     a["out"], a["lse"], a["ws"], a["ws_bytes"], None)
+
+    assert attn(prev_lse=None) == B.RKV_ERR_INVALID_ARG  # given together
+    assert attn(prev_out=None) == B.RKV_ERR_INVALID_ARG
+    assert attn(prev_out=FAKE) == B.RKV_ERR_INVALID_ARG  # prev_out is out
+    assert attn(prev_out=FAKE + 4100) == B.RKV_ERR_INVALID_ARG  # misaligned
+    assert attn(out=None) == B.RKV_ERR_INVALID_ARG
+    assert attn(ws_bytes=need - 1) == B.RKV_ERR_WORKSPACE
+    assert attn(m_cap=0) == B.RKV_ERR_INVALID_ARG
