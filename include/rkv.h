@@ -171,6 +171,16 @@ size_t rkv_select_workspace_size(const rkv_params* params, int32_t batch,
                                  int32_t max_blocks);
 
 /*
+ * The smallest k_cap (kept ids per list) rkv_select and the calls built on
+ * it accept for max_blocks blocks per sequence: max_blocks when a list can
+ * be dense (dense_boundary > 0, or topk_ppm = RKV_PPM_ONE), otherwise
+ * ceil(max_blocks * topk_ppm / RKV_PPM_ONE) (openGauss page, "Configuration
+ * Parameters": the top-k ratio of the offload blocks, which never exceed
+ * max_blocks).  0 for a NULL params or max_blocks < 0.
+ */
+int32_t rkv_topk_capacity(const rkv_params* params, int32_t max_blocks);
+
+/*
  * rkv_select -- inner-product retrieval and block-table merge (openGauss
  * page, "Overall Solution": the IP between the current token's query and
  * every representation, the top-K closest blocks, joined with the initial

@@ -68,6 +68,7 @@ _SIGS = {
     "rkv_append_kv": (ctypes.c_int, [_PP, _P, _P, _P, _P, _I64, _P, _I32, _P, _I32,
                                      _P, _P]),
     "rkv_select_workspace_size": (_SZ, [_PP, _I32, _I32]),
+    "rkv_topk_capacity": (_I32, [_PP, _I32]),
     "rkv_select": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _I32,
                                   _P, _P, _I32, _P, _SZ, _P]),
     "rkv_append_select": (ctypes.c_int, [_PP, _P, _P, _P, _P, _I64, _P, _P, _P, _P,
@@ -739,10 +740,8 @@ def ceil_div(a: int, b: int) -> int:
 
 
 def topk_capacity(p: Params, max_blocks: int) -> int:
-    """Smallest k_cap rkv_select accepts (the header's capacity rule)."""
-    if p.dense_boundary > 0 or p.topk_ppm >= 1_000_000:
-        return max_blocks
-    return ceil_div(max_blocks * p.topk_ppm, 1_000_000)
+    """Smallest k_cap rkv_select accepts (rkv_topk_capacity)."""
+    return int(lib().rkv_topk_capacity(ctypes.byref(p), max_blocks))
 
 
 __all__ = ["Params", "RkvError", "lib", "params", "build_reps", "append_kv",

@@ -214,6 +214,11 @@ rkv_status rkv_append_kv(const rkv_params* params, const uint16_t* k_new,
                     "rkv_append_kv launch");
 }
 
+int32_t rkv_topk_capacity(const rkv_params* params, int32_t max_blocks) {
+  if (!params || max_blocks < 0) return 0;
+  return (int32_t)topk_cap(params, max_blocks);
+}
+
 size_t rkv_select_workspace_size(const rkv_params* params, int32_t batch,
                                  int32_t max_blocks) {
   if (!params || batch <= 0 || max_blocks <= 0 || params->n_kv_heads <= 0) return 0;

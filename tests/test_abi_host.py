@@ -494,3 +494,23 @@ def test_split_staging_and_lse_attention_validation(L):
     assert attn(out=None) == B.RKV_ERR_INVALID_ARG
     assert attn(ws_bytes=need - 1) == B.RKV_ERR_WORKSPACE
     assert attn(m_cap=0) == B.RKV_ERR_INVALID_ARG
+
+
+def test_topk_capacity_rule(L):
+    """rkv_topk_capacity: max_blocks when a list can be dense, else
+    ceil(max_blocks * ppm / 10^6) in exact integers; rkv_select accepts
+    exactly that k_cap and rejects one less."""
+    from fractions import Fraction
+    import math
+    p = L.rkv_params_default(32, 8)
+    assert L.rkv_topk_capacity(ctypes.byref(p), 1000) == 1000  # dense boundary on
+    p.dense_boundary = 0
+    for mb in (0, 1, 5, 999, 1000, 8192):
+        for ppm in (1, 199_999, 200_000, 333_333, 999_999):
+            p.topk_ppm = ppm
+            want = math.ceil(Fraction(mb * ppm, 1_000_000))
+            assert L.rkv_topk_capacity(ctypes.byref(p), mb) == want, (mb, ppm)
+    p.topk_ppm = 1_000_000
+    assert L.rkv_topk_capacity(ctypes.byref(p), 77) == 77
+    assert L.rkv_topk_capacity(None, 77) == 0
+    assert L.rkv_topk_capacity(ctypes.byref(p), -1) == 0
