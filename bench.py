@@ -444,7 +444,7 @@ def run_workload(args, config, steps, warmup, cpu_budget, probe_gbs, dev,
     lens = [torch.as_tensor(base.lens_at(t), device=dev) for t in range(T)]
     torch.cuda.synchronize()
 
-    def run(s_idx):
+    def run(s_idx, overlap=None):
         layer = s_idx % n_layers
         t = (s_idx // n_layers) % T
         sess = sessions[layer]
@@ -456,6 +456,10 @@ def run_workload(args, config, steps, warmup, cpu_budget, probe_gbs, dev,
             sess.reset_residency()
         if host is None:
             sess.step(qs[t], kn, vn, lens[t])
+            return t
+        if (not args.no_overlap) if overlap is None else overlap:
+            # the copies overlap the attention over the blocks already in HBM
+            sess.step_overlapped(qs[t], kn, vn, lens[t])
             return t
         sess.append_select(qs[t], kn, vn, lens[t])
         # stage the kept host blocks on the side stream
@@ -519,6 +523,15 @@ def run_workload(args, config, steps, warmup, cpu_budget, probe_gbs, dev,
     # otherwise rkv_decode_attn over the current merged tables
     reps_attn = max(steps, 2 * n_layers)
     t_last = ts[-1]
+    if host is not None and not args.no_overlap:
+        # the overlapped steps leave only the resident entries in the merged
+        # table: the attention replay below runs over the whole table, as the
+        # plain step does (slots then hold step t_last's kept blocks)
+        for s_ in sessions:
+            s_.side.wait_stream(torch.cuda.current_stream(dev))
+            with torch.cuda.stream(s_.side):
+                s_.stage(lens[t_last])
+            torch.cuda.current_stream(dev).wait_stream(s_.side)
     ev0, ev1 = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     fused = host is None and fused_select_attend(args, spec, base.table_np.shape[1])
     torch.cuda.synchronize()
@@ -592,32 +605,33 @@ def run_workload(args, config, steps, warmup, cpu_budget, probe_gbs, dev,
                          "fraction_of_full": float(np.mean(steady)) * tile2 / kept},
             "path": ("pinned host DRAM -> HBM staging slots by a gather kernel reading "
                      "host memory, side stream; timed steps use residency across steps "
-                     "(rkv_stage_resident, first-in first-out slot reuse)"),
+                     "(first-in first-out slot reuse) and, unless --no-overlap, copy "
+                     "while the blocks already in HBM are attended (step_overlapped)"),
         }
         log(f"full staging {st_us:.0f} us ({staging['full']['gbs']:.1f} GB/s); "
             f"residency copies {staging['resident']['fraction_of_full'] * 100:.0f}% "
             "of the kept bytes per step")
         staging["copy_engines"] = measure_copy_engines(sess, spec, qs, news, lens, T,
                                                        t_last, kept, st_us, dev)
-        # the same steps with the copies overlapping the attention over the
-        # blocks already in HBM (planner in split mode, copies on the side
-        # stream, then the newly staged blocks folded in by log-sum-exp)
+        # the same steps in the other schedule: plain (staging, then the
+        # attention over the whole table) or overlapped (the planner in split
+        # mode, the copies on the side stream while the main stream attends
+        # the blocks already in HBM, then the newly staged ones folded in)
         torch.cuda.synchronize()
         t0o = time.perf_counter()
         for i in range(steps):
-            t = i % T
-            if t == 0:
-                sess.reset_residency()
-            kn, vn = news[t]
-            sess.step_overlapped(qs[t], kn, vn, lens[t])
+            run(i * n_layers, overlap=args.no_overlap)
         torch.cuda.synchronize()
-        ovl_us = (time.perf_counter() - t0o) * 1e6 / steps
+        other_us = (time.perf_counter() - t0o) * 1e6 / steps
+        ovl_us = ms_per_step * 1e3 if not args.no_overlap else other_us
+        plain_us = other_us if not args.no_overlap else ms_per_step * 1e3
         staging["overlapped"] = {
-            "step_us": ovl_us, "plain_step_us": ms_per_step * 1e3,
+            "timed_steps": "plain" if args.no_overlap else "overlapped",
+            "step_us": ovl_us, "plain_step_us": plain_us,
             "path": ("rkv_stage_plan (split mode) -> side stream: rkv_stage_copy; "
                      "main: rkv_decode_attn_lse over the entries already in HBM, then "
                      "over the newly staged ones with the first part folded in")}
-        log(f"overlapped step: {ovl_us:.0f} us (plain {ms_per_step * 1e3:.0f} us)")
+        log(f"overlapped step: {ovl_us:.0f} us, plain step {plain_us:.0f} us")
 
     kv_b = np.array([step_bytes(spec, base.context, t)[0] for t in ts], dtype=np.float64)
     rep_b = np.array([step_bytes(spec, base.context, t)[1] for t in ts], dtype=np.float64)
@@ -688,6 +702,10 @@ def main():
     ap.add_argument("--select", default="per-head", choices=["per-head", "per-sequence"],
                     help="selection per (sequence, KV head) or once per sequence")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="host tier: time the plain step (staging, then the attention "
+                         "over the whole table) instead of the one whose copies overlap "
+                         "the attention over the blocks already in HBM")
     ap.add_argument("--also", default="3,4,5",
                     help="other workloads measured after the headline one in the "
                          "same run (comma-separated config ids; empty: none)")
@@ -758,6 +776,8 @@ def main():
                "--select", args.select, "--layers", str(args.layers)]
         if args.no_cpu_baseline:
             cmd.append("--no-cpu-baseline")
+        if args.no_overlap:
+            cmd.append("--no-overlap")
         r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
         lines = [x for x in r.stdout.splitlines() if x.startswith("{")]
         if r.returncode != 0 or not lines:
