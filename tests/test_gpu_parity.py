@@ -379,14 +379,16 @@ def test_attention_workspace_reused_across_shapes():
         assert torch.equal(out, ref), spec.name
 
 
-@pytest.mark.parametrize("hq,hkv,dense_boundary,extra", [
-    (8, 2, 0, 0),        # group 4: four sequences per cascade wave
-    (16, 2, 0, 0),       # group 8: two
-    (4, 2, 0, 6),        # group 2: eight; shared count named 6 past the truth
-    (32, 2, 0, 0),       # group 16: one (no reuse, same results)
-    (16, 2, 12000, 0),   # one prompt below the dense boundary
+@pytest.mark.parametrize("hq,hkv,dense_boundary,extra,per_seq", [
+    (8, 2, 0, 0, False),        # group 4: four sequences per cascade wave
+    (16, 2, 0, 0, False),       # group 8: two
+    (4, 2, 0, 6, False),        # group 2: eight; shared count named 6 past the truth
+    (32, 2, 0, 0, False),       # group 16: one (no reuse, same results)
+    (16, 2, 12000, 0, False),   # one prompt below the dense boundary
+    (16, 4, 0, 0, True),        # one selection per sequence, shared by its heads
 ])
-def test_cascade_matches_oracle_and_plain_attention(hq, hkv, dense_boundary, extra):
+def test_cascade_matches_oracle_and_plain_attention(hq, hkv, dense_boundary, extra,
+                                                   per_seq):
     """rkv_decode_attn_cascade over a batch with a shared prefix: outputs
     against the oracle (selections and merged tables are the plain path's,
     checked too) and against rkv_decode_attn over the same tables.  The
@@ -399,7 +401,10 @@ def test_cascade_matches_oracle_and_plain_attention(hq, hkv, dense_boundary, ext
                         dense_boundary=dense_boundary, shared_prefix_pages=S,
                         shuffle=True, config_id=144)
     batch = synth.make_batch(spec, DEV)
-    prm, sess = make_session(batch)
+    if per_seq:
+        prm, sess = make_session(batch, select_mode=B.SELECT_PER_SEQUENCE)
+    else:
+        prm, sess = make_session(batch)
     prefill(batch, sess)
     for t in range(spec.steps):
         say("cascade", spec.name, "step", t)
@@ -413,7 +418,10 @@ def test_cascade_matches_oracle_and_plain_attention(hq, hkv, dense_boundary, ext
         assert torch.isfinite(got).all()
         scale = float(plain.abs().max())
         assert float((got - plain).abs().max()) <= 1e-5 * scale + 1e-7
-        oracle_full_check(batch, sess, t)
+        if per_seq:
+            per_sequence_check(batch, sess, t)
+        else:
+            oracle_full_check(batch, sess, t)
 
 
 def test_cascade_without_shared_blocks_is_plain_attention():
@@ -912,6 +920,36 @@ def test_host_tier_too_few_slots_is_reported():
             assert n_host > 3 and staged[b, h] == -1, (b, h)
             pages = [int(merged[b, h, n_init + q]) for q, j in enumerate(kept) if on_host[j]]
             assert sum(p >= 0 for p in pages) == 3 and pages.count(-1) == n_host - 3
+
+
+def test_host_tier_overlapped_step_with_too_few_slots():
+    """The overlapped step with slot_cap below the kept count: the blocks
+    without a slot are in neither split table, exactly as the plain step
+    leaves them out (page -1), and the outputs agree within rounding."""
+    spec = synth.scaled(synth.CONFIGS[5], batch=2, context=(20000, 23000), steps=1,
+                        plant_range=(8, 90), plant_count=5, local_tokens=7192,
+                        dense_boundary=0, config_id=109)
+    say("host tier overlapped step with too few staging slots")
+    batch_a, _, sess_a = make_host_session(spec, resident=True, slot_cap=3)
+    batch_b, _, sess_b = make_host_session(spec, resident=True, slot_cap=3)
+    step(batch_a, sess_a, 0)
+    lens = i32(batch_b.lens_at(0))
+    kn, vn = batch_b.new_kv_bits(0)
+    sess_b.step_overlapped(batch_b.q_bits(0), kn, vn, lens)
+    torch.cuda.synchronize()
+    assert torch.equal(sess_a.n_staged, sess_b.n_staged)
+    assert (sess_b.n_staged.cpu().numpy() == -1).all()
+    assert (sess_b.n_new.cpu().numpy() == 3).all()
+    ma, na = sess_a.merged.cpu().numpy(), sess_a.n_merged.cpu().numpy()
+    mr, nr = sess_b.merged.cpu().numpy(), sess_b.n_merged.cpu().numpy()
+    mn = sess_b.merged_new.cpu().numpy()
+    for b in range(2):
+        for h in range(8):
+            plain = [int(x) for x in ma[b, h, :na[b, h]] if x >= 0]
+            split = [int(x) for x in mr[b, h, :nr[b, h]]] + [int(x) for x in mn[b, h, :3]]
+            assert sorted(plain) == sorted(split), (b, h)
+    scale = float(sess_a.out.abs().max())
+    assert float((sess_b.out - sess_a.out).abs().max()) <= 1e-5 * scale + 1e-7
 
 
 @pytest.mark.parametrize("concurrent", [False, True])
