@@ -64,11 +64,12 @@ COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 ATTN_SOURCE = os.path.join(ROOT, "sparse_retrieval_kv_amd", "csrc", "attn.hip")
 MEASURED_TRAFFIC = {
     # config: (sha256 prefix of attn.hip, FETCH_SIZE KiB, WRITE_SIZE KiB) of
-    # the attention call's kernels (split or folded kernel + combine)
-    2: ("5e9f889585aa19e2", 40089.5 + 646.5, 1048.9 + 16.0),
-    3: ("5e9f889585aa19e2", 751671.8 + 830.5, 1302.6 + 256.0),
-    4: ("5e9f889585aa19e2", 506507.6 + 1275.5, 2081.1 + 256.0),
-    5: ("5e9f889585aa19e2", 474778.2 + 684.5, 1040.3 + 64.0),
+    # the attention call's kernels (split or folded kernel + combine; for the
+    # host tier the calls over the whole merged table)
+    2: ("3c52841b87c1a264", 40089.5 + 648.5, 1048.9 + 16.0),
+    3: ("3c52841b87c1a264", 751688.3 + 832.5, 1302.6 + 256.0),
+    4: ("3c52841b87c1a264", 506561.1 + 1277.5, 2081.1 + 256.0),
+    5: ("3c52841b87c1a264", 474790.5 + 686.5, 1040.3 + 64.0),
 }
 METRIC = "decode attn steps/s and attended-KV HBM GB/s (% of peak) at 64K-128K ctx, 1 GPU"
 
