@@ -45,6 +45,10 @@ import torch
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+if "--wave-timeline" in sys.argv:
+    # the per-wave timestamps need the RKV_WAVE_STAMPS build of the library
+    os.environ.setdefault("RKV_LIB", os.path.join(ROOT, "sparse_retrieval_kv_amd",
+                                                  "librkv_stamps.so"))
 
 from sparse_retrieval_kv_amd import binding as B  # noqa: E402
 from sparse_retrieval_kv_amd import synth  # noqa: E402
@@ -388,6 +392,64 @@ def measure_cascade(sessions, spec, q, lens, reps, plain_us, context, t):
             "bytes_saved": (per_list - per_group) * tile}
 
 
+def wave_timeline(args, dev, reps=4):
+    """Per-wave timeline of the 8B layer's folded-selection attention launch
+    (the RKV_WAVE_STAMPS build): the decode step runs over eight layer copies
+    as in the timed run, and the stamps of the last step's launch are read
+    back.  Prints percentiles of each event over the waves, in us from the
+    launch's first wave start, the unit completions per microsecond and the
+    finish times by unit count."""
+    spec = synth.CONFIGS[2]
+    base = synth.make_batch(spec, dev)
+    prm = B.params(spec.n_q_heads, spec.n_kv_heads, init_tokens=spec.init_tokens,
+                   local_tokens=spec.local_tokens, topk_ppm=spec.topk_ppm,
+                   dense_boundary=spec.dense_boundary)
+    ctx = torch.as_tensor(base.context.astype(np.int32), device=dev)
+    n_layers = args.layers or 8
+    sessions = []
+    for layer in range(n_layers):
+        kp = base.k_pages if layer == 0 else base.k_pages.clone()
+        vp = base.v_pages if layer == 0 else base.v_pages.clone()
+        sess = DecodeSession(prm, kp, vp, base.block_table, ctx)
+        sess.build_reps(ctx - 1)
+        sessions.append(sess)
+    T = spec.steps
+    names = ["wave start", "scores and table row arrived", "selection found",
+             "first unit's V tile requested", "merged list in LDS", "wave done"]
+    pct = (0, 10, 50, 90, 100)
+    print(f"per-wave timeline, {spec.name}: {n_layers} layer copies, "
+          f"{args.steps} steps per read-out, us from the first wave's start "
+          f"(percentiles {'/'.join(map(str, pct))})", flush=True)
+    for rep in range(reps):
+        for i in range(args.steps):
+            t = (rep * args.steps + i) % T
+            kn, vn = base.new_kv_bits(t)
+            sessions[i % n_layers].step(base.q_bits(t), kn, vn,
+                                        torch.as_tensor(base.lens_at(t), device=dev))
+        torch.cuda.synchronize()
+        st = B.wave_stamps(B.WAVE_STAMP_WAVES).astype(np.int64)
+        st = st[st[:, 0] > 0]
+        t0 = st[:, 0].min()
+        us = lambda x: (x - t0) / 100.0  # noqa: E731
+        print(f"read-out {rep}: {len(st)} waves", flush=True)
+        for k, name in enumerate(names):
+            col = st[:, k if k < 5 else 5]
+            col = col[col > 0]
+            print(f"  {name:30s} " + " ".join(f"{np.percentile(us(col), p):6.2f}"
+                                               for p in pct), flush=True)
+        units = st[:, 7:]
+        done_units = us(units[units > 0])
+        n_units = (units > 0).sum(axis=1)
+        hist = np.bincount(np.floor(done_units).astype(int))
+        print("  unit completions per 1 us window: " +
+              " ".join(f"{w}:{c}" for w, c in enumerate(hist) if c), flush=True)
+        for n in sorted(set(n_units.tolist())):
+            sel = n_units == n
+            print(f"  waves with {n} units: {sel.sum()}, done median "
+                  f"{np.median(us(st[sel, 5])):.2f} max {us(st[sel, 5]).max():.2f}",
+                  flush=True)
+
+
 def run_workload(args, config, steps, warmup, cpu_budget, probe_gbs, dev,
                  spread_budget=None):
     """Build one workload, time `steps` decode steps after `warmup`, the
@@ -723,6 +785,10 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device-to-device copy first "
                          "(a known-size reference for HBM byte counters)")
+    ap.add_argument("--wave-timeline", action="store_true",
+                    help="print the per-wave timeline of the 8B layer's attention "
+                         "launch (librkv_stamps.so, --steps steps per read-out) "
+                         "instead of timing")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -733,6 +799,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
+    if args.wave_timeline:
+        wave_timeline(args, dev)
+        return
     torch.cuda.set_device(dev)
     B.lib()
 

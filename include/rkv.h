@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define RKV_ABI_VERSION 4
+#define RKV_ABI_VERSION 5
 #define RKV_BLOCK_SIZE 128
 #define RKV_HEAD_DIM 128
 #define RKV_PPM_ONE 1000000
@@ -730,6 +730,30 @@ rkv_status rkv_decode_step_static(const rkv_params* params, const uint16_t* k_ne
  */
 rkv_status rkv_debug_set_report(uint64_t* word);
 rkv_status rkv_debug_check(uint64_t* word, hipStream_t stream);
+
+/*
+ * rkv_debug_wave_stamps -- measurement helper, not part of the method.  In
+ * a library built with RKV_WAVE_STAMPS, every wave of the folded-selection
+ * attention launch (rkv_select_attend / rkv_decode_step for a batch of one)
+ * records RKV_WAVE_STAMP_SLOTS 64-bit values, kept by the wave until it
+ * ends and then written to a device array (row = the wave's workgroup id,
+ * first RKV_WAVE_STAMP_WAVES waves; each launch overwrites the rows of its
+ * waves): slot 0 the wave's start, 1 its scores and table row arrived, 2
+ * its selection found, 3 its first unit's V tile requested, 4 its merged
+ * list in LDS, 5 its partials written, 6 (XCC_ID << 32) | HW_ID (where it
+ * ran), 7 + i its i-th unit attended (i < RKV_WAVE_STAMP_SLOTS - 7); times
+ * are s_memrealtime ticks (100 MHz), 0 for an event the wave did not
+ * reach.  This call copies the first `waves` rows to dst (host memory,
+ * waves * RKV_WAVE_STAMP_SLOTS values), blocking; call it after the
+ * launches have finished.  The stamps themselves cost the waves a few
+ * instructions each.
+ * Errors: RKV_ERR_INVALID_ARG (dst NULL with waves > 0, waves outside
+ * [0, RKV_WAVE_STAMP_WAVES]), RKV_ERR_UNSUPPORTED (a library built without
+ * RKV_WAVE_STAMPS), RKV_ERR_HIP.
+ */
+#define RKV_WAVE_STAMP_SLOTS 16
+#define RKV_WAVE_STAMP_WAVES 4096
+rkv_status rkv_debug_wave_stamps(uint64_t* dst, int32_t waves);
 
 /*
  * rkv_read_probe -- measurement helper, not part of the method: reads

@@ -12,12 +12,14 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 DEFAULT_LIB_PATH = os.path.join(HERE, "librkv.so")
 # the same library built with RKV_DEBUG: kernels report out-of-range values
 DEBUG_LIB_PATH = os.path.join(HERE, "librkv_debug.so")
+STAMPS_LIB_PATH = os.path.join(HERE, "librkv_stamps.so")
 LIB_PATH = os.environ.get("RKV_LIB") or DEFAULT_LIB_PATH
 HEADER = os.path.join(os.path.dirname(HERE), "include", "rkv.h")
 
@@ -118,6 +120,7 @@ _SIGS = {
     "rkv_read_probe": (ctypes.c_int, [_P, _SZ, _P, _P]),
     "rkv_debug_set_report": (ctypes.c_int, [_P]),
     "rkv_debug_check": (ctypes.c_int, [_P, _P]),
+    "rkv_debug_wave_stamps": (ctypes.c_int, [_P, _I32]),
 }
 RKV_STATIC_SCRATCH_BYTES = 64 << 20
 
@@ -726,6 +729,19 @@ def debug_check(word):
     """Waits for the current stream, reads and clears `word`; raises
     RkvError(RKV_ERR_BOUNDS) when a kernel reported a value."""
     _check(lib().rkv_debug_check(_ptr(word, torch.int64, "word", (1,)), _stream(word)))
+
+
+WAVE_STAMP_SLOTS = 16
+WAVE_STAMP_WAVES = 4096
+
+
+def wave_stamps(waves):
+    """rkv_debug_wave_stamps: the per-wave timestamps of the last
+    folded-selection launches, as a uint64 array [waves, WAVE_STAMP_SLOTS]
+    (a library built with RKV_WAVE_STAMPS only)."""
+    out = np.zeros((int(waves), WAVE_STAMP_SLOTS), dtype=np.uint64)
+    _check(lib().rkv_debug_wave_stamps(out.ctypes.data if waves else None, int(waves)))
+    return out
 
 
 def read_probe(buf, sink):

@@ -18,6 +18,9 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "librkv.so")
 # the same sources built with RKV_DEBUG: kernels report out-of-range values
 DEBUG_LIB = os.path.join(HERE, "librkv_debug.so")
+# the same sources built with RKV_WAVE_STAMPS: per-wave timestamps of the
+# folded-selection attention launch (rkv_debug_wave_stamps)
+STAMPS_LIB = os.path.join(HERE, "librkv_stamps.so")
 SOURCES = ["rkv_api.cpp", "reps.hip", "select.hip", "attn.hip", "stage.hip",
            "static_scratch.hip", "stage_copy.cpp"]
 ARCH = "gfx950"
@@ -31,20 +34,23 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build librkv.so)")
 
 
-def compile_flags(debug: bool = False) -> list:
+def compile_flags(debug: bool = False, stamps: bool = False) -> list:
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
             *(["-DRKV_DEBUG=1"] if debug else []),
+            *(["-DRKV_WAVE_STAMPS=1"] if stamps else []),
             # packed fp32 VALU forms are kept out of the generated code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-Wno-unused-command-line-argument",
             "-I", INCLUDE, "-I", CSRC]
 
 
-def build(verbose: bool = False, jobs: int = 4, debug: bool = False) -> str:
+def build(verbose: bool = False, jobs: int = 4, debug: bool = False,
+          stamps: bool = False) -> str:
     """Compile every source to an object, link librkv.so (librkv_debug.so
-    with `debug`: RKV_DEBUG bounds reports), return its path."""
+    with `debug`: RKV_DEBUG bounds reports; librkv_stamps.so with `stamps`:
+    per-wave timestamps), return its path."""
     cc = hipcc()
-    out_lib = DEBUG_LIB if debug else LIB
+    out_lib = DEBUG_LIB if debug else (STAMPS_LIB if stamps else LIB)
     with tempfile.TemporaryDirectory(prefix="rkv_build_") as tmp:
         procs = []
         objs = []
@@ -52,8 +58,8 @@ def build(verbose: bool = False, jobs: int = 4, debug: bool = False) -> str:
             obj = os.path.join(tmp, src + ".o")
             objs.append(obj)
             lang = ["-x", "hip"] if src.endswith(".hip") else []
-            cmd = [cc] + compile_flags(debug) + lang + ["-c", os.path.join(CSRC, src),
-                                                   "-o", obj]
+            cmd = [cc] + compile_flags(debug, stamps) + lang + [
+                "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,

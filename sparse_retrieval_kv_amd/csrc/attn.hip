@@ -214,6 +214,53 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 }
 
 // ---------------------------------------------------------------------------
+// Per-wave timestamps of the folded-selection launch (a library built with
+// RKV_WAVE_STAMPS; compiled out otherwise).  Lane 0 keeps s_memrealtime
+// values (100 MHz) in LDS and writes them out once, when the wave ends, so
+// that no global store sits in the wave's memory counter while it runs.
+// Slots: kStampStart, kStampScores (scores and table row arrived),
+// kStampSearch (selection found), kStampVreq (first unit's V tile
+// requested), kStampList (merged list in LDS), kStampDone (partials
+// written), kStampHwId (XCC_ID << 32 | HW_ID), then kStampUnit0 + i: the
+// wave's i-th unit attended (i < kStampUnits).
+// ---------------------------------------------------------------------------
+constexpr int kStampStart = 0, kStampScores = 1, kStampSearch = 2, kStampVreq = 3,
+              kStampList = 4, kStampDone = 5, kStampHwId = 6, kStampUnit0 = 7;
+constexpr int kStampUnits = kWaveStampSlots - kStampUnit0;
+
+#ifdef RKV_WAVE_STAMPS
+__device__ unsigned long long rkv_wave_stamps[kWaveStampWaves][kWaveStampSlots];
+__shared__ unsigned long long stamp_lds[kWaveStampSlots];
+__device__ __forceinline__ void stamp(int k) {
+  if (threadIdx.x == 0) stamp_lds[k] = __builtin_amdgcn_s_memrealtime();
+}
+// stamp k once x is computed (x is made to depend on)
+__device__ __forceinline__ void stamp_after(int k, uint32_t x) {
+  if (__builtin_amdgcn_readfirstlane(x) != 0x9e3779b9u) stamp(k);
+}
+__device__ __forceinline__ void stamp_begin() {
+  if (threadIdx.x == 0) {
+    for (int k = 0; k < kWaveStampSlots; ++k) stamp_lds[k] = 0;
+    stamp_lds[kStampHwId] =
+        ((unsigned long long)__builtin_amdgcn_s_getreg(63508) << 32) |  // XCC_ID
+        (unsigned)__builtin_amdgcn_s_getreg(63492);                     // HW_ID
+  }
+  stamp(kStampStart);
+}
+__device__ __forceinline__ void stamp_flush() {
+  __builtin_amdgcn_s_waitcnt(0);
+  stamp(kStampDone);
+  if (threadIdx.x == 0 && blockIdx.x < (unsigned)kWaveStampWaves)
+    for (int k = 0; k < kWaveStampSlots; ++k) rkv_wave_stamps[blockIdx.x][k] = stamp_lds[k];
+}
+#else
+__device__ __forceinline__ void stamp(int) {}
+__device__ __forceinline__ void stamp_after(int, uint32_t) {}
+__device__ __forceinline__ void stamp_begin() {}
+__device__ __forceinline__ void stamp_flush() {}
+#endif
+
+// ---------------------------------------------------------------------------
 // One unit's K and V tiles.
 // ---------------------------------------------------------------------------
 
@@ -680,6 +727,12 @@ __device__ __forceinline__ void strided_loop(const AttnArgs& a, Math& math, int 
       load_k_unit(kf, a.k_pages + tile, (u - P) & 1, col, grp);
     }
     if (cur_ok && valid > 0) math.accumulate(s, vf, valid, a.scale_log2, col, grp);
+#ifdef RKV_WAVE_STAMPS
+    if constexpr (std::is_same<Math, MfmaMath>::value) {
+      const int ord = n_mine - 1 - i;  // the wave's ord-th unit
+      if (ord < kStampUnits) stamp_after(kStampUnit0 + ord, __float_as_uint(math.l_run));
+    }
+#endif
   };
   if (PRE) {
     unit(std::false_type());
@@ -972,9 +1025,14 @@ __device__ __forceinline__ uint32_t kept_blocks(const uint32_t (&key)[kFusedRegs
   for (int i = 0; i < NR; ++i) keyc[i] = ((cbits >> i) & 1u) ? key[i] : 0u;
   uint32_t T = 0;
   int cT = n_off;  // offload keys >= T
-  for (int bit = 31; bit >= 0; --bit) {
+  // the bit mask and the candidate in scalar registers, so that a pass's
+  // only vector work is its compares (with the loop counter and the
+  // candidate in vector registers, every pass waited on the vector unit
+  // two more times)
+  for (uint32_t bm = 0x80000000u; bm != 0u;
+       bm = (uint32_t)__builtin_amdgcn_readfirstlane((int)(bm >> 1))) {
     if (cT == k) break;  // exactly k keys >= T: they are the top k
-    const uint32_t t = T | (1u << bit);
+    const uint32_t t = T | bm;
     // every compare of the pass first, then the counts: a count read
     // right after its compare waits for the vector unit's mask write
     uint64_t m[NR];
@@ -984,10 +1042,9 @@ __device__ __forceinline__ uint32_t kept_blocks(const uint32_t (&key)[kFusedRegs
     int cnt = 0;
 #pragma unroll
     for (int i = 0; i < NR; ++i) cnt += __popcll(m[i]);
-    if (cnt >= k) {
-      T = t;
-      cT = cnt;
-    }
+    cnt = __builtin_amdgcn_readfirstlane(cnt);
+    T = cnt >= k ? t : T;
+    cT = cnt >= k ? cnt : cT;
   }
   uint32_t kbits = 0;
   if (cT == k) {  // here T >= 1 (k < n_off)
@@ -1052,6 +1109,14 @@ __device__ __forceinline__ void select_strided_body(const AttnArgs& a,
   // so the region arithmetic and the selection's branches stay scalar
   const int lraw = __builtin_amdgcn_readfirstlane(lraw_v);
   const int plen = __builtin_amdgcn_readfirstlane(plen_v);
+#ifdef RKV_WAVE_STAMPS
+  {
+    uint32_t x = 0;  // every score and table entry has arrived
+#pragma unroll
+    for (int i = 0; i < kFusedRegs; ++i) x ^= raw[i] ^ (uint32_t)tab[i];
+    stamp_after(kStampScores, x);
+  }
+#endif
 
   // --- regions and k, as the top-k launch takes them ---
   const int Ls = clamp_len(lraw, mb * kBlock);
@@ -1111,7 +1176,10 @@ __device__ __forceinline__ void select_strided_body(const AttnArgs& a,
   if (ranked)  // uniform
     kbits = (ls + 63) >> 6 <= 8 ? kept_blocks<8>(key, cbits, k, R.n_off, lane)
                                 : kept_blocks<16>(key, cbits, k, R.n_off, lane);
+  stamp_after(kStampSearch, kbits);
   load_v_unit(vf, a.v_pages + early_tile, u_first & 1, col, grp);
+  __builtin_amdgcn_sched_barrier(0);
+  stamp(kStampVreq);
 
   // --- merged page list (init blocks, kept blocks, local blocks), with
   // selects only: entry dst of block j, -1 when j is not attended (its LDS
@@ -1147,6 +1215,7 @@ __device__ __forceinline__ void select_strided_body(const AttnArgs& a,
     f.n_merged[bh] = n_m;
   }
   __syncthreads();  // the list in LDS is complete (one wave per workgroup)
+  stamp(kStampList);
 
   const int L = clamp_len(lraw, a.max_len);
   auto page_at = [&](int i) { return mlist[(c + i * P) >> 1]; };
@@ -1155,10 +1224,12 @@ __device__ __forceinline__ void select_strided_body(const AttnArgs& a,
                        early_page);
   else
     strided_loop<false>(a, math, bh, c, 2 * n_m, L, page_at, lane, col, grp, kf, vf, 0);
+  stamp_flush();
 }
 
 __global__ __launch_bounds__(64) void attn_select_mfma_kernel(AttnArgs a,
                                                               SelectIn f) {
+  stamp_begin();
   select_strided_body<MfmaMath>(a, f);
 }
 
@@ -1690,5 +1761,18 @@ hipError_t launch_select_attn(const Method& m, bool use_mfma, const AttnPlan& pl
 }
 
 RKV_BOUNDS_SETTER(set_bounds_word_attn)
+
+hipError_t read_wave_stamps(uint64_t* dst, int waves) {
+#ifdef RKV_WAVE_STAMPS
+  if (waves < 0 || waves > kWaveStampWaves) return hipErrorInvalidValue;
+  return hipMemcpyFromSymbol(dst, HIP_SYMBOL(rkv_wave_stamps),
+                             (size_t)waves * kWaveStampSlots * sizeof(uint64_t), 0,
+                             hipMemcpyDeviceToHost);
+#else
+  (void)dst;
+  (void)waves;
+  return hipErrorNotSupported;
+#endif
+}
 
 }  // namespace rkv

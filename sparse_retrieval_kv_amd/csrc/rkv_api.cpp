@@ -1054,6 +1054,16 @@ rkv_status rkv_debug_check(uint64_t* word, hipStream_t stream) {
               kinds[kind < 6 ? kind : 0], (int)(int32_t)(uint32_t)v);
 }
 
+rkv_status rkv_debug_wave_stamps(uint64_t* dst, int32_t waves) {
+  RKV_REQUIRE(waves >= 0 && waves <= RKV_WAVE_STAMP_WAVES, RKV_ERR_INVALID_ARG,
+              "waves %d outside [0, %d]", waves, RKV_WAVE_STAMP_WAVES);
+  RKV_REQUIRE(dst != nullptr || waves == 0, RKV_ERR_INVALID_ARG, "dst is NULL");
+  const hipError_t e = rkv::read_wave_stamps(dst, waves);
+  if (e == hipErrorNotSupported)
+    return fail(RKV_ERR_UNSUPPORTED, "this library was built without RKV_WAVE_STAMPS");
+  return hip_status(e, "rkv_debug_wave_stamps");
+}
+
 rkv_status rkv_read_probe(const void* buffer, size_t bytes, uint32_t* sink,
                           hipStream_t stream) {
   RKV_REQUIRE(buffer && sink, RKV_ERR_INVALID_ARG, "buffer and sink must not be NULL");

@@ -206,6 +206,13 @@ hipError_t launch_decode_attn(const Method& m, bool use_mfma,
 // sel_ids / n_sel / merged / n_merged), then attends exactly as
 // launch_decode_attn's single-sequence partition does; then the combine.
 constexpr int kFusedMaxBlocks = 1024;
+// Per-wave timestamps of the folded-selection launch (built with
+// RKV_WAVE_STAMPS): kWaveStampSlots 64-bit values for each of the launch's
+// first kWaveStampWaves waves; read_wave_stamps copies the first `waves`
+// rows to host memory (hipErrorNotSupported in other builds).
+constexpr int kWaveStampWaves = RKV_WAVE_STAMP_WAVES;
+constexpr int kWaveStampSlots = RKV_WAVE_STAMP_SLOTS;
+hipError_t read_wave_stamps(uint64_t* dst, int waves);
 bool fused_select_attn_ok(const Method& m, bool use_mfma, const AttnPlan& plan,
                           int batch, int max_blocks);
 hipError_t launch_select_attn(const Method& m, bool use_mfma, const AttnPlan& plan,

@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from sparse_retrieval_kv_amd import binding as B
@@ -26,7 +27,7 @@ def test_every_declared_function_is_exported(L):
     assert len(names) >= 11
     for n in names:
         assert hasattr(L, n), n
-    assert L.rkv_abi_version() == 4
+    assert L.rkv_abi_version() == 5
 
 
 def test_defaults_follow_the_page(L):
@@ -274,6 +275,24 @@ def test_debug_build_exports_the_same_calls():
     if not os.path.exists(B.DEBUG_LIB_PATH):
         pytest.skip("debug library not built")
     D = ctypes.CDLL(B.DEBUG_LIB_PATH)
+    for n in B.header_functions():
+        assert hasattr(D, n), n
+
+
+def test_release_build_has_no_wave_stamps(L):
+    buf = np.zeros(16, dtype=np.uint64)
+    assert L.rkv_debug_wave_stamps(buf.ctypes.data, 1) == B.RKV_ERR_UNSUPPORTED
+    assert b"RKV_WAVE_STAMPS" in L.rkv_last_error()
+    assert L.rkv_debug_wave_stamps(None, 1) == B.RKV_ERR_INVALID_ARG
+    assert L.rkv_debug_wave_stamps(buf.ctypes.data, -1) == B.RKV_ERR_INVALID_ARG
+    assert L.rkv_debug_wave_stamps(buf.ctypes.data, 4097) == B.RKV_ERR_INVALID_ARG
+    assert B.WAVE_STAMP_SLOTS == 16 and B.WAVE_STAMP_WAVES == 4096
+
+
+def test_stamps_build_exports_the_same_calls():
+    if not os.path.exists(B.STAMPS_LIB_PATH):
+        pytest.skip("stamps library not built")
+    D = ctypes.CDLL(B.STAMPS_LIB_PATH)
     for n in B.header_functions():
         assert hasattr(D, n), n
 
