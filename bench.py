@@ -70,10 +70,10 @@ MEASURED_TRAFFIC = {
     # config: (sha256 prefix of attn.hip, FETCH_SIZE KiB, WRITE_SIZE KiB) of
     # the attention call's kernels (split or folded kernel + combine; for the
     # host tier the calls over the whole merged table)
-    2: ("3c52841b87c1a264", 40089.5 + 648.5, 1048.9 + 16.0),
-    3: ("3c52841b87c1a264", 751688.3 + 832.5, 1302.6 + 256.0),
-    4: ("3c52841b87c1a264", 506561.1 + 1277.5, 2081.1 + 256.0),
-    5: ("3c52841b87c1a264", 474790.5 + 686.5, 1040.3 + 64.0),
+    2: ("82fad60adbd6b78b", 40090.5 + 646.0, 1048.9 + 16.0),
+    3: ("82fad60adbd6b78b", 751662.1 + 832.0, 1302.6 + 256.0),
+    4: ("82fad60adbd6b78b", 506474.3 + 1277.0, 2081.1 + 256.0),
+    5: ("82fad60adbd6b78b", 474836.9 + 686.0, 1040.3 + 64.0),
 }
 METRIC = "decode attn steps/s and attended-KV HBM GB/s (% of peak) at 64K-128K ctx, 1 GPU"
 
