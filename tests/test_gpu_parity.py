@@ -213,6 +213,29 @@ def test_group_sizes(hq, hkv):
     oracle_full_check(batch, sess, 0)
 
 
+@pytest.mark.parametrize("hq,hkv,context", [(32, 32, (20000,)), (64, 64, (9000,)),
+                                             (40, 40, (12345,)),
+                                             (48, 24, (7000, 15000))])
+def test_many_kv_heads(hq, hkv, context):
+    """Models with many KV heads (G = 1 or 2): the single-sequence partition
+    then gives each list 512 / n_kv waves (16, 8, 12) and the lists no longer
+    line up with the eight dies; batch 2 takes the range partition."""
+    spec = synth.custom(f"kv{hkv}", batch=len(context), n_q_heads=hq, n_kv_heads=hkv,
+                        context=context, steps=2, init_tokens=256, local_tokens=1000,
+                        dense_boundary=0, config_id=160 + hkv)
+    say("many KV heads", hq, hkv, context)
+    if len(context) == 1:
+        fused_vs_separate(spec, oracle_check=True)
+        return
+    batch = synth.make_batch(spec, DEV)
+    prm, sess = make_session(batch)
+    prefill(batch, sess)
+    for t in range(2):
+        step(batch, sess, t)
+        torch.cuda.synchronize()
+        oracle_full_check(batch, sess, t)
+
+
 def test_short_and_degenerate_lengths():
     spec = synth.custom("short", batch=6, n_q_heads=8, n_kv_heads=2,
                         context=(1, 2, 127, 128, 129, 700), init_tokens=128,
