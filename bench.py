@@ -242,32 +242,39 @@ def measure_copy_engines(sess, spec, qs, news, lens, T, t_last, kept, gather_us,
     """Host tier through the copy engines (rkv_stage_*_async: coalesced
     hipMemcpy2DAsync / hipMemcpyAsync on the side stream) beside the gather
     kernel: every kept block staged per call, decode steps with residency,
-    and the HBM read rate another stream gets while each mode stages.
-    Leaves the session in the gather-kernel mode with empty slots."""
+    and the HBM read rate another stream gets while each mode stages; then
+    the copies over four copy lanes.  Leaves the session in the
+    gather-kernel mode, without lanes, with empty slots."""
     out = {}
-    n_st = 4
-    # every kept block, wall clock per call (the call waits for the kept ids
-    # on the host, then issues the copies; the time runs until they are done)
-    sess.copy_mode, sess.resident = "memcpy", False
-    sess.stage(lens[t_last])
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(n_st):
+
+    def full_and_resident():
+        """Every kept block staged per call (wall clock: the call waits for
+        the kept ids on the host, then issues the copies; the time runs until
+        they are done), then decode steps with residency from empty slots,
+        as the timed steps run."""
+        n_st = 4
+        sess.copy_mode, sess.resident = "memcpy", False
         sess.stage(lens[t_last])
-    torch.cuda.synchronize()
-    full_us = (time.perf_counter() - t0) * 1e6 / n_st
-    out["full"] = {"bytes_per_step": float(kept), "avg_us": full_us,
-                   "gbs": kept / (full_us * 1e-6) / 1e9}
-    # decode steps with residency from empty slots, as the timed steps run
-    sess.resident = True
-    sess.reset_residency()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for t in range(T):
-        kn, vn = news[t]
-        sess.step(qs[t], kn, vn, lens[t])
-    torch.cuda.synchronize()
-    step_us = (time.perf_counter() - t0) * 1e6 / T
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n_st):
+            sess.stage(lens[t_last])
+        torch.cuda.synchronize()
+        full_us = (time.perf_counter() - t0) * 1e6 / n_st
+        sess.resident = True
+        sess.reset_residency()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(T):
+            kn, vn = news[t]
+            sess.step(qs[t], kn, vn, lens[t])
+        torch.cuda.synchronize()
+        step_us = (time.perf_counter() - t0) * 1e6 / T
+        return ({"bytes_per_step": float(kept), "avg_us": full_us,
+                 "gbs": kept / (full_us * 1e-6) / 1e9}, step_us)
+
+    out["full"], step_us = full_and_resident()
+    full_us = out["full"]["avg_us"]
     out["resident_step_us"] = step_us
     out["resident_steps_per_s"] = 1e6 / step_us
     log(f"copy engines: full staging {full_us:.0f} us ({out['full']['gbs']:.1f} GB/s); "
@@ -315,13 +322,29 @@ def measure_copy_engines(sess, spec, qs, news, lens, T, t_last, kept, gather_us,
     log(f"HBM read probe: alone {out['read_probe_alone_gbs']:.0f} GB/s, beside the "
         f"gather kernel {out['read_probe_beside_kernel_gbs']:.0f} GB/s, beside the copy "
         f"engines {out['read_probe_beside_memcpy_gbs']:.0f} GB/s")
+
+    # the copies spread over copy lanes (rkv_params.copy_lanes), measured
+    # last: the lanes are streams of this process, and streams created after
+    # them would share the runtime's hardware queues with them
+    n_lanes = 4
+    sess.p.copy_lanes = n_lanes
+    try:
+        lanes_full, lanes_step_us = full_and_resident()
+    finally:
+        sess.p.copy_lanes = 0
+    out["lanes"] = {"copy_lanes": n_lanes, "full": lanes_full,
+                    "resident_step_us": lanes_step_us,
+                    "resident_steps_per_s": 1e6 / lanes_step_us}
+    log(f"copy engines over {n_lanes} lanes: full staging {lanes_full['avg_us']:.0f} us "
+        f"({lanes_full['gbs']:.1f} GB/s); steps with residency {lanes_step_us:.0f} us")
     sess.copy_mode, sess.resident = "kernel", True
     sess.reset_residency()
     torch.cuda.synchronize()
     out["path"] = ("kept ids (or the residency planner's copy list) to pinned host "
                    "memory, then one hipMemcpy2DAsync per run of consecutive blocks "
                    "and KV head (whole pages in the per-sequence mode) on the side "
-                   "stream; the main stream waits on an event")
+                   "stream (under 'lanes': spread over that many streams forked from "
+                   "and joined back to it); the main stream waits on an event")
     return out
 
 

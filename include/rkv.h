@@ -17,8 +17,9 @@
  *  - Pointers are DEVICE pointers unless a parameter says "host".  The caller
  *    owns every buffer; the library allocates nothing and keeps no state
  *    between calls except the calling thread's last error text and, per
- *    device, its compute-unit count (queried once) and the address of the
- *    static scratch array of rkv_decode_step_static.
+ *    device, its compute-unit count (queried once), the address of the
+ *    static scratch array of rkv_decode_step_static and, once a copy-engine
+ *    staging call asks for them (rkv_params.copy_lanes), its copy streams.
  *  - bf16 values travel as their 16-bit patterns (uint16_t).
  *  - All work is enqueued asynchronously on the given HIP stream; a call
  *    returns once the work is enqueued.  Arguments are validated on the host
@@ -59,11 +60,12 @@
 extern "C" {
 #endif
 
-#define RKV_ABI_VERSION 5
+#define RKV_ABI_VERSION 6
 #define RKV_BLOCK_SIZE 128
 #define RKV_HEAD_DIM 128
 #define RKV_PPM_ONE 1000000
 #define RKV_MAX_GROUP 16        /* query heads per KV head */
+#define RKV_MAX_COPY_LANES 8    /* rkv_params.copy_lanes */
 #define RKV_MAX_BLOCKS 8192     /* blocks per sequence (1M tokens) */
 /* Extent of one call, so that every launch grid fits the 32-bit work-item
  * count of a dispatch: batch * n_q_heads query rows, and batch * n_kv_heads
@@ -114,10 +116,16 @@ typedef struct rkv_params {
                               unit: 512 on MI355X) */
   int32_t select_mode;     /* RKV_SELECT_PER_HEAD (default) or
                               RKV_SELECT_PER_SEQUENCE, see rkv_select */
+  int32_t copy_lanes;      /* streams the copy-engine staging calls spread
+                              their copies over: 0 or 1 (default 0) = the
+                              caller's side stream only; 2 ..
+                              RKV_MAX_COPY_LANES = that many streams of the
+                              library's own, see rkv_stage_blocks_async */
 } rkv_params;
 
 /* Defaults of the page (init 1024, local 7192, ratio 0.2, dense boundary
- * 32K, block 128) for the given head counts. */
+ * 32K, block 128) for the given head counts; automatic attention variant
+ * and split, per-head selection, copies on the side stream only. */
 rkv_params rkv_params_default(int32_t n_q_heads, int32_t n_kv_heads);
 
 int32_t rkv_abi_version(void);
@@ -448,7 +456,21 @@ size_t rkv_stage_host_list_size(const rkv_params* params, int32_t batch,
  * pages (per KV head, a 2-D copy with a one-page pitch; in the per-sequence
  * selection mode, where every head keeps the same blocks, whole pages in one
  * contiguous copy).  `done` (may be NULL) is recorded on `side` after the
- * last copy: make the attention's stream wait for it.  The merged table
+ * last copy: make the attention's stream wait for it.
+ * Copy lanes: each copy command costs the copy engines about 10 us however
+ * small it is, and the commands of one stream run one after another.  With
+ * params->copy_lanes = n >= 2 the copies go instead to n streams the
+ * library creates on the current device at the first such call (default
+ * priority, kept until the process ends), each command to the one with the
+ * least work queued by this call; they start after the work queued on
+ * `side` so far (an event) and `side` waits for them (one event per lane),
+ * so `done` and everything later on `side` still follow every copy.  On
+ * MI355X four lanes copy whole pages about 2x and 32 KiB tiles about 3x
+ * faster than one stream.  The lanes are streams of the calling process:
+ * when it has more streams than the runtime has hardware queues
+ * (GPU_MAX_HW_QUEUES), streams share queues and work on them can no
+ * longer overlap, so lanes are off by default.  Calls that use lanes are
+ * serialized by a lock inside the library.  The merged table
  * comes from rkv_merge_table with the device host table, as for
  * rkv_stage_blocks.  The call blocks the calling thread until the ids are
  * on the host, so it cannot be captured in a graph.
@@ -477,8 +499,9 @@ rkv_status rkv_stage_blocks_async(const rkv_params* params, const uint16_t* host
  * to the pinned host buffer host_list, the calling thread waits for them,
  * and the copies are issued on `side` as for rkv_stage_blocks_async (runs
  * of consecutive blocks, host pages and slots; whole pages in the
- * per-sequence mode).  `done` (may be NULL) is recorded on `side` after the
- * last copy.  Blocks the calling thread until the list is on the host.
+ * per-sequence mode; over params->copy_lanes lanes when that is 2 or
+ * more).  `done` (may be NULL) is recorded on `side` after the last copy.
+ * Blocks the calling thread until the list is on the host.
  *   host_table      [batch][max_blocks] DEVICE int32 (read by the planner)
  *   host_table_host the same table in HOST memory (read by the copy issue)
  *   host_list       pinned host memory, >= rkv_stage_host_list_size bytes

@@ -39,7 +39,8 @@ class Params(ctypes.Structure):
                 ("init_tokens", ctypes.c_int32), ("local_tokens", ctypes.c_int32),
                 ("topk_ppm", ctypes.c_int32), ("dense_boundary", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("attn_impl", ctypes.c_int32),
-                ("split_waves", ctypes.c_int32), ("select_mode", ctypes.c_int32)]
+                ("split_waves", ctypes.c_int32), ("select_mode", ctypes.c_int32),
+                ("copy_lanes", ctypes.c_int32)]
 
     def __repr__(self):
         return "Params(" + ", ".join(f"{n}={getattr(self, n)}"
@@ -54,6 +55,7 @@ class RkvError(RuntimeError):
 
 SELECT_PER_HEAD = 0
 SELECT_PER_SEQUENCE = 1
+MAX_COPY_LANES = 8  # rkv_params.copy_lanes
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32

@@ -72,6 +72,9 @@ rkv_status check_params(const rkv_params* p, rkv::Method* m) {
   RKV_REQUIRE(p->select_mode == RKV_SELECT_PER_HEAD ||
                   p->select_mode == RKV_SELECT_PER_SEQUENCE,
               RKV_ERR_INVALID_ARG, "select_mode %d unknown", p->select_mode);
+  RKV_REQUIRE(p->copy_lanes >= 0 && p->copy_lanes <= RKV_MAX_COPY_LANES,
+              RKV_ERR_INVALID_ARG, "copy_lanes %d outside [0, %d]", p->copy_lanes,
+              RKV_MAX_COPY_LANES);
   if (m) {
     m->per_sequence = p->select_mode == RKV_SELECT_PER_SEQUENCE;
     m->n_q_heads = p->n_q_heads;
@@ -153,6 +156,7 @@ rkv_params rkv_params_default(int32_t n_q_heads, int32_t n_kv_heads) {
   p.attn_impl = RKV_ATTN_AUTO;
   p.split_waves = 0;
   p.select_mode = RKV_SELECT_PER_HEAD;
+  p.copy_lanes = 0;
   return p;
 }
 
@@ -655,6 +659,7 @@ rkv_status rkv_stage_blocks_async(const rkv_params* params, const uint16_t* host
   a.counts = counts;
   a.row = k_cap;
   a.side = side;
+  a.lanes = params->copy_lanes;
   return copy_issue(a, nullptr, done, "rkv_stage_blocks_async copies");
 }
 
@@ -734,6 +739,7 @@ rkv_status rkv_stage_resident_async(
   a.counts = reinterpret_cast<const int32_t*>(static_cast<char*>(host_list) + pair_bytes);
   a.row = k_cap;
   a.side = side;
+  a.lanes = params->copy_lanes;
   return copy_issue(a, nullptr, done, "rkv_stage_resident_async copies");
 }
 

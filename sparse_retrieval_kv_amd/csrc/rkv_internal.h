@@ -154,6 +154,7 @@ struct StageCopyArgs {
   const int32_t* counts;  // [lists]
   int row;
   hipStream_t side;
+  int lanes;  // >= 2: copies spread over that many streams of the library
   int count(int bh) const {
     const int n = counts[bh];
     return n < 0 ? 0 : (n > row ? row : n);

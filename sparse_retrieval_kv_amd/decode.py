@@ -134,9 +134,10 @@ class HostTierSession(DecodeSession):
     With `copy_mode="memcpy"` the copies go through the copy engines
     (rkv_stage_resident_async / rkv_stage_blocks_async: the kept ids or the
     residency planner's copy list go to the host, which issues coalesced
-    hipMemcpy2DAsync / hipMemcpyAsync calls on the side stream and records an
-    event the main stream waits for); the default "kernel" mode copies with a
-    gather kernel that reads the pinned host pools directly.
+    hipMemcpy2DAsync / hipMemcpyAsync calls on the side stream, or spread
+    over `prm.copy_lanes` streams of the library forked from it, and records
+    an event the main stream waits for); the default "kernel" mode copies
+    with a gather kernel that reads the pinned host pools directly.
 
     Representations are built while every block is still in HBM (after
     prefill); `attach_host` then hands over the host pools that hold the

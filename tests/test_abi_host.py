@@ -27,7 +27,7 @@ def test_every_declared_function_is_exported(L):
     assert len(names) >= 11
     for n in names:
         assert hasattr(L, n), n
-    assert L.rkv_abi_version() == 5
+    assert L.rkv_abi_version() == 6
 
 
 def test_defaults_follow_the_page(L):
@@ -36,6 +36,9 @@ def test_defaults_follow_the_page(L):
             p.topk_ppm, p.dense_boundary) == (128, 128, 1024, 7192, 200000, 32768)
     assert p.scale == pytest.approx(128 ** -0.5)
     assert (p.n_q_heads, p.n_kv_heads, p.attn_impl, p.split_waves) == (32, 8, 0, 0)
+    assert (p.select_mode, p.copy_lanes) == (B.SELECT_PER_HEAD, 0)
+    # the binding's struct has the header's size (every field mirrored)
+    assert ctypes.sizeof(B.Params) == 13 * 4
     assert L.rkv_status_string(0) == b"ok"
     assert L.rkv_status_string(3) == b"workspace too small"
 
@@ -74,6 +77,8 @@ def test_param_validation(L):
         (with_(split_waves=(1 << 16) + 1), B.RKV_ERR_INVALID_ARG),
         (with_(select_mode=2), B.RKV_ERR_INVALID_ARG),
         (with_(select_mode=-1), B.RKV_ERR_INVALID_ARG),
+        (with_(copy_lanes=-1), B.RKV_ERR_INVALID_ARG),
+        (with_(copy_lanes=B.MAX_COPY_LANES + 1), B.RKV_ERR_INVALID_ARG),
     ]
     for p, want in cases:
         assert _attn(L, p) == want, p

@@ -892,19 +892,23 @@ def test_host_tier_residency_matches_full_staging(slot_mult):
     assert copied_total < kept_total
 
 
+@pytest.mark.parametrize("resident", [True, False])
 @pytest.mark.parametrize("select_mode", [B.SELECT_PER_HEAD, B.SELECT_PER_SEQUENCE])
-def test_host_tier_copy_engine_equals_gather_kernel(select_mode):
-    """The copy engines and the gather kernel stage the same bytes to the
-    same slots: pools, slot state, merged tables and outputs bit-identical
-    over steps with residency (2x slots)."""
+def test_host_tier_copy_engine_equals_gather_kernel(select_mode, resident):
+    """The copy engines -- on the side stream, or spread over 3 or 4 copy
+    lanes -- and the gather kernel stage the same bytes to the same slots:
+    pools, slot state, merged tables and outputs bit-identical over four
+    steps (with residency: 2x slots)."""
     spec = synth.scaled(synth.CONFIGS[5], batch=2, context=(20000, 23000), steps=4,
                         plant_range=(8, 90), plant_count=5, local_tokens=7192,
                         dense_boundary=0, config_id=110)
-    say(f"host tier: copy engines vs gather kernel, select mode {select_mode}")
+    say(f"host tier: copy engines vs gather kernel, select mode {select_mode}, "
+        f"resident {resident}")
     runs = {}
-    for mode in ("kernel", "memcpy"):
-        batch, host, sess = make_host_session(spec, resident=True, slot_mult=2,
-                                              copy_mode=mode, select_mode=select_mode)
+    for mode, lanes in (("kernel", 0), ("memcpy", 0), ("memcpy", 4), ("memcpy", 3)):
+        batch, host, sess = make_host_session(spec, resident=resident, slot_mult=2,
+                                              copy_mode=mode, select_mode=select_mode,
+                                              copy_lanes=lanes)
         rec = []
         for t in range(4):
             step(batch, sess, t)
@@ -912,11 +916,12 @@ def test_host_tier_copy_engine_equals_gather_kernel(select_mode):
             rec.append((sess.out.clone(), sess.merged.clone(), sess.n_merged.clone(),
                         sess.slot_ids.clone(), sess.n_staged.clone()))
         rec.append((batch.k_pages.clone(), batch.v_pages.clone()))
-        runs[mode] = rec
+        runs[(mode, lanes)] = rec
         del batch, host, sess
-    for a, b in zip(runs["kernel"], runs["memcpy"]):
-        for x, y in zip(a, b):
-            assert torch.equal(x, y)
+    for key in (("memcpy", 0), ("memcpy", 4), ("memcpy", 3)):
+        for a, b in zip(runs[("kernel", 0)], runs[key]):
+            for x, y in zip(a, b):
+                assert torch.equal(x, y), key
 
 
 def test_host_tier_too_few_slots_is_reported():
