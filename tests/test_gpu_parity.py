@@ -709,6 +709,18 @@ def test_70b_shared_prefix_full_size_per_sequence(t_check):
     per_sequence_check(batch, sess, t_check)
 
 
+@pytest.mark.parametrize("t_check", [0, 31])
+def test_batched_ragged_full_size_per_sequence(t_check):
+    """The per-sequence selection reading on the batched workload (16 x
+    U[32K, 128K], shuffled pool) at full size: every sequence against the
+    head-summed oracle step, at the first and the last step."""
+    batch = synth.make_batch(synth.CONFIGS[3], DEV)
+    prm, sess = make_session(batch, select_mode=B.SELECT_PER_SEQUENCE)
+    say("batched, per-sequence selection, step", t_check)
+    run_to_step(batch, sess, t_check)
+    per_sequence_check(batch, sess, t_check)
+
+
 @pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (16, 4), (64, 8)])
 def test_valu_variant_matches_oracle_and_mfma(hq, hkv):
     spec = synth.custom("valu", batch=2, n_q_heads=hq, n_kv_heads=hkv,
