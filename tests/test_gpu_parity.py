@@ -1055,6 +1055,20 @@ def test_host_tier_full_size(t_check):
     oracle_full_check(batch, sess, t_check, host=host)
 
 
+def test_host_tier_full_size_per_sequence_copy_lanes():
+    """Host tier at full size (4 x 256K) with the per-sequence selection and
+    whole-page staging by the copy engines over four copy lanes, with
+    residency: every sequence against the head-summed oracle at step 7."""
+    say("host tier (4 x 256K), per-sequence selection, copy engines over 4 lanes")
+    batch, host, sess = make_host_session(synth.CONFIGS[5], copy_mode="memcpy",
+                                          select_mode=B.SELECT_PER_SEQUENCE,
+                                          copy_lanes=4)
+    for t in range(8):
+        step(batch, sess, t)
+    torch.cuda.synchronize()
+    per_sequence_check(batch, sess, 7, host=host)
+
+
 def per_sequence_check(batch, sess, t, seqs=None, host=None):
     """Per-sequence selection mode: one oracle step over all KV heads of each
     sequence (scores summed over the heads), every head's GPU selection equal
